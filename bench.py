@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed linear layer (libgemmq) on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for each activation width K, quantize X to q8_K, then run every matrix of the
+layer through the packed matmul.  The default workload is the Qwen3-8B-shaped
+layer (q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 12288x4096, down
+4096x12288, all q4_K; 108,527,616 weight bytes), run at M = 1 (decode GEMV,
+weight GB/s) and M = 512 (prefill GEMM, int8 TOP/s).
+
+Inputs are resident in HBM before timing starts.  So that the weights are
+really streamed from HBM and not from the 256 MB last-level cache, the step
+rotates over R copies of the layer's weights (R * 108.5 MB >= 1 GiB).
+
+Output: one JSON line.  `value` is the M=1 weight throughput of the whole step
+(quantizer launches included); `secondary` the M=512 int8 throughput;
+`roofline` / `roofline_m512` give the dominant kernels' algorithmic rate from
+per-launch HIP events against the MI355X peaks (HBM 8 TB/s; dense int8 MFMA
+5.0 POP/s); `cpu_baseline` times the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, TOP/s
+GIB = 1 << 30
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="qwen3-8b-q4K")
+    p.add_argument("--m", type=int, nargs="+", default=[1, 512],
+                   help="activation rows; the first is the headline (value), the second secondary")
+    p.add_argument("--copies", type=int, default=0, help="rotating weight copies (0: auto, >=1 GiB)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+class Layer:
+    """Device buffers for one workload: rotating weight copies, activations,
+    q8_K buffers and outputs, all allocated before timing."""
+
+    def __init__(self, wl, gen, Ms, copies):
+        import torch
+
+        import quant_packed_weight_amd as gq
+
+        self.gq = gq
+        self.wl = wl
+        self.Ms = Ms
+        self.w = []
+        base = {m.name: torch.from_numpy(gen.weights[m.name]).to("cuda:0") for m in wl.matrices}
+        for r in range(copies):
+            self.w.append({k: (v if r == 0 else v.clone()) for k, v in base.items()})
+        self.x, self.xq, self.y = {}, {}, {}
+        for M in Ms:
+            for K in wl.ks():
+                self.x[(M, K)] = torch.from_numpy(gen.activations[(M, K)]).to("cuda:0")
+                self.xq[(M, K)] = torch.empty(gq.q8K_bytes(M, K), dtype=torch.uint8,
+                                              device="cuda:0")
+            for m in wl.matrices:
+                self.y[(M, m.name)] = torch.empty((M, m.N), dtype=torch.float32, device="cuda:0")
+        torch.cuda.synchronize()
+
+    def run(self, M, r, stream, events=None):
+        """Enqueue one pass at M rows on weight copy r.  With `events`, every
+        launch is bracketed by a pair of timing events on the same stream."""
+        gq = self.gq
+        st = stream.cuda_stream
+        for K in self.wl.ks():
+            rc = gq.quantize_q8K_ptr(self.x[(M, K)].data_ptr(), self.xq[(M, K)].data_ptr(), M, K,
+                                     st)
+            if rc:
+                raise gq.GemmqError(rc, "quantize")
+        for m in self.wl.matrices:
+            if events is not None:
+                e0, e1 = events.pop()
+                e0.record(stream)
+            rc = gq.gemm_ptr(m.fmt, self.w[r][m.name].data_ptr(), self.xq[(M, m.K)].data_ptr(),
+                             self.y[(M, m.name)].data_ptr(), M, m.N, m.K, gq.PATH_AUTO, st)
+            if rc:
+                raise gq.GemmqError(rc, "gemm " + m.name)
+            if events is not None:
+                e1.record(stream)
+                events.used.append((m, e0, e1))
+
+
+class EventPool(list):
+    def __init__(self, n):
+        import torch
+
+        super().__init__((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                         for _ in range(n))
+        self.used = []
+
+
+def time_passes(layer, M, steps, warmup, copies, stream):
+    import torch
+
+    for s in range(warmup):
+        layer.run(M, s % copies, stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        layer.run(M, (warmup + s) % copies, stream)
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def kernel_rates(layer, M, steps, copies, stream):
+    """Per-launch HIP-event durations of the matmul kernel at M rows."""
+    import torch
+
+    nmat = len(layer.wl.matrices)
+    pool = EventPool(steps * nmat)
+    for s in range(steps):
+        layer.run(M, s % copies, stream, events=pool)
+    torch.cuda.synchronize()
+    per = {}
+    for m, e0, e1 in pool.used:
+        per.setdefault(m.name, []).append(e0.elapsed_time(e1) * 1e-3)
+    return per
+
+
+def cpu_baseline(wl, gen, M1, M2, seconds):
+    """The oracle, single-threaded, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+
+    out = {"kind": "oracle", "cores": 1}
+    # M = M1 (decode): whole passes over all matrices until `seconds` elapse
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        xq = {K: oracle.quantize_q8K(gen.activations[(M1, K)]) for K in wl.ks()}
+        for m in wl.matrices:
+            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.K], M1, m.N, m.K)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or passes >= 50:
+            break
+    wbytes = sum(m.nbytes for m in wl.matrices)
+    out["value"] = wbytes * passes / el / 1e9
+    out["unit"] = "GB/s"
+    out["sample"] = ("%d full pass(es) of the %d-matrix layer at M=%d (quantize + integer-route "
+                     "matmul), %.1f s" % (passes, len(wl.matrices), M1, el))
+    if M2:
+        rows = np.array([0, M2 - 1])
+        xq = {K: oracle.quantize_q8K(gen.activations[(M2, K)][rows]) for K in wl.ks()}
+        t0 = time.perf_counter()
+        ops = 0
+        for m in wl.matrices:
+            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.K], len(rows), m.N, m.K)
+            ops += 2 * len(rows) * m.N * m.K
+        el = time.perf_counter() - t0
+        out["value_m%d" % M2] = ops / el / 1e12
+        out["unit_m%d" % M2] = "TOP/s"
+        out["sample_m%d" % M2] = ("rows {0, %d} of M=%d through all %d matrices, %.1f s"
+                                  % (M2 - 1, M2, len(wl.matrices), el))
+    return out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU (the packed linear layer has no "
+              "collective); --gpus %d is not supported" % a.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quant_packed_weight_amd as gq
+    from quant_packed_weight_amd import synth
+
+    assert torch.cuda.is_available(), "no GPU"
+    gq.lib()
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[a.workload]
+    Ms = [M for M in a.m]
+    gen = synth.generate(a.workload, Ms=None if set(Ms) - set(wl.Ms) else set(Ms))
+    if set(Ms) - set(wl.Ms):
+        raise SystemExit("workload %s has M in %s" % (a.workload, wl.Ms))
+    wbytes = sum(m.nbytes for m in wl.matrices)
+    copies = a.copies or max(1, math.ceil(GIB / wbytes))
+    layer = Layer(wl, gen, Ms, copies)
+    stream = torch.cuda.current_stream()
+
+    t = {M: time_passes(layer, M, a.steps, a.warmup, copies, stream) for M in Ms}
+    rates = {M: kernel_rates(layer, M, a.steps, copies, stream) for M in Ms}
+
+    M1 = Ms[0]
+    M2 = Ms[1] if len(Ms) > 1 else None
+    ops = {M: sum(2 * M * m.N * m.K for m in wl.matrices) for M in Ms}
+
+    def roof(M):
+        per = rates[M]
+        tot_t = sum(sum(v) for v in per.values())
+        n_l = sum(len(v) for v in per.values())
+        if M <= 8:
+            algo = sum(m.nbytes * len(per[m.name]) for m in wl.matrices)
+            ach = algo / tot_t / 1e9
+            return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "gemv_q4K_kernel", "launches": n_l,
+                    "avg_launch_us": round(tot_t / n_l * 1e6, 2),
+                    "per_matrix_GBs": {m.name: round(m.nbytes * len(per[m.name]) /
+                                                     sum(per[m.name]) / 1e9, 1)
+                                       for m in wl.matrices}}
+        algo = sum(2 * M * m.N * m.K * len(per[m.name]) for m in wl.matrices)
+        ach = algo / tot_t / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS,
+                "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None,
+                "kernel": "gemm_kernel<12>", "launches": n_l,
+                "avg_launch_us": round(tot_t / n_l * 1e6, 2),
+                "per_matrix_TOPs": {m.name: round(2 * M * m.N * m.K * len(per[m.name]) /
+                                                  sum(per[m.name]) / 1e12, 1)
+                                    for m in wl.matrices}}
+
+    value = wbytes / t[M1] / 1e9 if M1 <= 8 else ops[M1] / t[M1] / 1e12
+    res = {
+        "metric": "q4_K gemm_quant: weight GB/s at M=1 & int8 TOPS at M=512, % of roofline",
+        "value": round(value, 1),
+        "unit": "GB/s" if M1 <= 8 else "TOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(sum(t.values()) * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": a.workload, "M": Ms, "matrices": len(wl.matrices),
+                   "weight_bytes": wbytes, "rotating_copies": copies,
+                   "ms_per_pass": {str(M): round(t[M] * 1e3, 4) for M in Ms}},
+        "roofline": roof(M1),
+    }
+    if M2:
+        res["secondary"] = {"metric": "int8 TOP/s at M=%d" % M2,
+                            "value": round(ops[M2] / t[M2] / 1e12, 1), "unit": "TOP/s"}
+        res["roofline_m%d" % M2] = roof(M2)
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, gen, M1, M2, a.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

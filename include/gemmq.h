@@ -1,0 +1,145 @@
+/*
+ * gemmq.h -- C ABI of libgemmq, the packed-weight linear layer for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation is gemm_quant from the PocketLLM pages: a Qwen3 linear layer
+ * y = W x evaluated directly on ggml K-quant packed weights, with the weights
+ * decoded inside the kernel and never widened in device memory (PocketLLM
+ * README, "What it runs" and "Roadmap": the K-quant rung is decoded in-kernel,
+ * packed, never widened), after the activations have been quantized to int8
+ * blocks (molayo article "PocketLLM: 단일 가속기에서 대규모 언어 모델 실행",
+ * status row "src/ -- C++ engine": the CPU gemm_quant quantizes activations to
+ * int8 the way llama.cpp does).  One process owns one device and the ABI has no
+ * rank or collective (README, "The rule").
+ *
+ * Conventions for every entry point:
+ *  - Pointers named X, Xq, W, Wf, Y are DEVICE pointers on the current HIP device.
+ *    The caller allocates and frees every buffer; the library allocates nothing
+ *    and keeps no per-call state, so calls are reentrant.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    A return of GEMMQ_OK means the work is enqueued on that stream; results are
+ *    valid once the stream has synchronised.  The library never synchronises.
+ *  - Arguments are validated before anything is launched; a negative status
+ *    names the failing condition (gemmq_status_str) and nothing was launched.
+ *    No C++ exception crosses this ABI.  The calling thread's pending HIP error
+ *    (hipGetLastError) is cleared just before a launch, so GEMMQ_E_LAUNCH always
+ *    refers to the library's own launch.
+ *  - M == 0 or N == 0 is a valid empty call: GEMMQ_OK, nothing is touched.
+ *  - Layouts: X is f32 [M, K] row-major; Y is f32 [M, N] row-major and is
+ *    overwritten (no accumulation into it); W is N rows, each K/256 consecutive
+ *    super-blocks (row n's block b at byte offset (n*K/256 + b) * block_bytes);
+ *    Xq is M rows of K/256 consecutive q8_K blocks, same order.
+ *
+ * Block formats (little-endian; the pages name the ggml formats but print no
+ * layout, so these are the public ggml layouts):
+ *  q4_K  144 B / 256 weights: f16 d | f16 dmin | 12 B of 6-bit scales and mins |
+ *        128 B of 4-bit quants; sub-block j (32 weights): w = d*sc_j*q - dmin*m_j.
+ *  q6_K  210 B / 256 weights: 128 B low nibbles | 64 B 2-bit highs | 16 int8
+ *        scales | f16 d; sub-block j (16 weights): w = d*sc_j*(q - 32).
+ *  q8_K  292 B / 256 activations: f32 d | 256 int8 q | 16 int16 group sums.
+ */
+#ifndef GEMMQ_H
+#define GEMMQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GEMMQ_ABI_VERSION 1
+
+/* Weight formats, numbered as the GGUF tensor type ids. */
+#define GEMMQ_Q4_K 12
+#define GEMMQ_Q6_K 14
+
+#define GEMMQ_Q4_K_BYTES 144
+#define GEMMQ_Q6_K_BYTES 210
+#define GEMMQ_Q8_K_BYTES 292
+#define GEMMQ_QK 256
+
+/* Status codes. */
+#define GEMMQ_OK 0
+#define GEMMQ_E_INVALID_ARG (-1)        /* null pointer, negative size, bad path id */
+#define GEMMQ_E_UNSUPPORTED_FORMAT (-2) /* fmt is not GEMMQ_Q4_K or GEMMQ_Q6_K */
+#define GEMMQ_E_SHAPE (-3)              /* K not a positive multiple of 256, or M too large for the path */
+#define GEMMQ_E_ALIGNMENT (-4)          /* a pointer breaks the alignment stated below */
+#define GEMMQ_E_DEVICE (-5)             /* current device is not gfx950, or no device */
+#define GEMMQ_E_LAUNCH (-6)             /* the HIP runtime rejected a launch */
+
+/* Paths for gemmq_gemm_ex. */
+#define GEMMQ_PATH_AUTO 0 /* M <= 8: decode GEMV, else the MFMA GEMM */
+#define GEMMQ_PATH_GEMV 1 /* decode GEMV, M in 1..8 only */
+#define GEMMQ_PATH_GEMM 2 /* MFMA GEMM, any M */
+
+/* ABI version (GEMMQ_ABI_VERSION of the library that was loaded). */
+int gemmq_abi_version(void);
+
+/* Static string naming a status code; never NULL. */
+const char *gemmq_status_str(int status);
+
+/* Bytes of one super-block of `fmt` (144, 210), or 0 for an unknown format. */
+size_t gemmq_block_bytes(int fmt);
+
+/* Bytes of an N x K packed weight matrix: N * K/256 * block_bytes; 0 when fmt is
+ * unknown, N or K is negative, or K % 256 != 0. */
+size_t gemmq_weight_bytes(int fmt, int64_t N, int64_t K);
+
+/* Bytes of M x K activations in q8_K: M * K/256 * 292; 0 on bad sizes. */
+size_t gemmq_q8K_bytes(int64_t M, int64_t K);
+
+/*
+ * Quantize f32 activations to q8_K blocks (step a1).  For every 256 consecutive
+ * values of a row: amax = max|x|, d = amax/127 (f32, correctly rounded division),
+ * q = round-half-even(x/d) clamped to [-127, 127], group sums over 16 values;
+ * a block whose d is 0 is stored as all zeros.  Inputs must be finite.
+ * This is the int8 activation quantization that precedes the packed dot in the
+ * molayo article's description of the CPU gemm_quant (status row "src/").
+ *   X   device, f32 [M, K], 16-byte aligned.
+ *   Xq  device, gemmq_q8K_bytes(M, K) bytes, 4-byte aligned; fully overwritten.
+ * Errors: GEMMQ_E_INVALID_ARG (null pointer when M > 0, M < 0),
+ *         GEMMQ_E_SHAPE (K <= 0 or K % 256 != 0), GEMMQ_E_ALIGNMENT,
+ *         GEMMQ_E_DEVICE, GEMMQ_E_LAUNCH.
+ */
+int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *stream);
+
+/*
+ * Y[m, n] = sum_k w[n, k] * d_x[m, k/256] * q_x[m, k]  -- the packed linear layer
+ * (steps a2..a5: in-kernel unpack, GEMV for M <= 8, MFMA GEMM otherwise).
+ *   fmt  GEMMQ_Q4_K or GEMMQ_Q6_K.
+ *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K,
+ *        4-byte aligned for q6_K.
+ *   Xq   device, gemmq_q8K_bytes(M, K) bytes from gemmq_quantize_q8K (or any
+ *        valid q8_K blocks: |q| <= 127 and sums equal to the sums of q),
+ *        4-byte aligned.
+ *   Y    device, f32 [M, N], 4-byte aligned; overwritten.
+ * The f32 result differs from the exact value by at most 1e-5 * sum_k|w_k*xhat_k|
+ * + 1e-6 (xhat = d_x*q_x); within one path, an output depends only on its own
+ * activation row and weight row, so any subset of rows gives identical bits.
+ * Errors: GEMMQ_E_INVALID_ARG, GEMMQ_E_UNSUPPORTED_FORMAT, GEMMQ_E_SHAPE,
+ *         GEMMQ_E_ALIGNMENT, GEMMQ_E_DEVICE, GEMMQ_E_LAUNCH.
+ */
+int gemmq_gemm(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int64_t N,
+               int64_t K, void *stream);
+
+/* gemmq_gemm with an explicit path (GEMMQ_PATH_*).  GEMMQ_PATH_GEMV with M > 8
+ * returns GEMMQ_E_SHAPE.  Same arguments, layout and errors otherwise. */
+int gemmq_gemm_ex(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int64_t N,
+                  int64_t K, int path, void *stream);
+
+/*
+ * Diagnostic export: decode packed weights to f32 with the same device unpacker
+ * (step a2) the matmul kernels use.  Never used on the compute path.
+ *   W   device, gemmq_weight_bytes(fmt, N, K) bytes, alignment as in gemmq_gemm.
+ *   Wf  device, f32 [N, K], 16-byte aligned; overwritten.
+ * q4_K weights are the single f32 rounding of d*sc*q - dmin*m; q6_K weights are
+ * exact.  Errors as gemmq_gemm.
+ */
+int gemmq_decode(int fmt, const void *W, float *Wf, int64_t N, int64_t K, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMMQ_H */

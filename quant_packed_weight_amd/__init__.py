@@ -1,0 +1,35 @@
+"""quant_packed_weight_amd -- libgemmq, the packed-weight linear layer on MI355X.
+
+The HIP library (libgemmq.so, C ABI in include/gemmq.h) computes y = W x on ggml
+q4_K / q6_K packed weights with q8_K-quantized activations; this package is its
+thin ctypes binding plus the seeded synthetic input generator (``synth``).
+The library is loaded on first use; nothing here computes on the CPU.
+"""
+from ._lib import (  # noqa: F401
+    ABI_VERSION,
+    BLOCK_BYTES,
+    EXPORTS,
+    FMT_Q4K,
+    FMT_Q6K,
+    LIB_PATH,
+    PATH_AUTO,
+    PATH_GEMM,
+    PATH_GEMV,
+    Q8K_BYTES,
+    QK,
+    GemmqError,
+    block_bytes,
+    decode,
+    decode_ptr,
+    gemm,
+    gemm_ptr,
+    lib,
+    linear,
+    q8K_bytes,
+    quantize_q8K,
+    quantize_q8K_ptr,
+    status_str,
+    weight_bytes,
+)
+
+__version__ = "0.1.0"

@@ -1,0 +1,178 @@
+"""ctypes binding of libgemmq (include/gemmq.h).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels
+of libgemmq.so.  Torch supplies device memory and the current stream.  There is
+no fallback: if the library is missing or the device is not a gfx950, calls
+raise GemmqError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+FMT_Q4K = 12
+FMT_Q6K = 14
+BLOCK_BYTES = {FMT_Q4K: 144, FMT_Q6K: 210}
+Q8K_BYTES = 292
+QK = 256
+PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+ABI_VERSION = 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
+
+# every entry point include/gemmq.h declares: name -> (restype, argtypes)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+EXPORTS = {
+    "gemmq_abi_version": (_I, []),
+    "gemmq_status_str": (ctypes.c_char_p, [_I]),
+    "gemmq_block_bytes": (ctypes.c_size_t, [_I]),
+    "gemmq_weight_bytes": (ctypes.c_size_t, [_I, _I64, _I64]),
+    "gemmq_q8K_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "gemmq_quantize_q8K": (_I, [_P, _P, _I64, _I64, _P]),
+    "gemmq_gemm": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "gemmq_gemm_ex": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
+    "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
+}
+
+
+class GemmqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = status_str(status) if _lib is not None else str(status)
+        super().__init__("%s: %s" % (where, name))
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libgemmq.so once (raises GemmqError(-100) when it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise GemmqError(-100, "libgemmq.so is not built (%s); run "
+                                       "python -m quant_packed_weight_amd.build" % LIB_PATH)
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in EXPORTS.items():
+                fn = getattr(L, name)
+                fn.restype = res
+                fn.argtypes = args
+            if L.gemmq_abi_version() != ABI_VERSION:
+                raise GemmqError(-101, "libgemmq ABI %d, binding expects %d"
+                                 % (L.gemmq_abi_version(), ABI_VERSION))
+            _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().gemmq_status_str(int(status)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise GemmqError(rc, where)
+
+
+def block_bytes(fmt: int) -> int:
+    return lib().gemmq_block_bytes(fmt)
+
+
+def weight_bytes(fmt: int, N: int, K: int) -> int:
+    return lib().gemmq_weight_bytes(fmt, N, K)
+
+
+def q8K_bytes(M: int, K: int) -> int:
+    return lib().gemmq_q8K_bytes(M, K)
+
+
+# ------------------------------------------------------------ raw-pointer calls
+def quantize_q8K_ptr(X: int, Xq: int, M: int, K: int, stream: int = 0) -> int:
+    return lib().gemmq_quantize_q8K(X, Xq, M, K, stream or None)
+
+
+def gemm_ptr(fmt: int, W: int, Xq: int, Y: int, M: int, N: int, K: int, path: int = PATH_AUTO,
+             stream: int = 0) -> int:
+    return lib().gemmq_gemm_ex(fmt, W, Xq, Y, M, N, K, path, stream or None)
+
+
+def decode_ptr(fmt: int, W: int, Wf: int, N: int, K: int, stream: int = 0) -> int:
+    return lib().gemmq_decode(fmt, W, Wf, N, K, stream or None)
+
+
+# ------------------------------------------------------------ torch-tensor calls
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t, name, dtype):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def quantize_q8K(x, out=None, stream=None):
+    """f32 [M, K] device tensor -> uint8 [M, K/256*292] q8_K blocks."""
+    torch = _torch()
+    M, K = x.shape
+    if out is None:
+        out = torch.empty((M, (K // QK) * Q8K_BYTES), dtype=torch.uint8, device=x.device)
+    elif out.numel() < q8K_bytes(M, K):
+        raise ValueError("out too small")
+    _check(lib().gemmq_quantize_q8K(_dev(x, "x", torch.float32), _dev(out, "out", torch.uint8),
+                                    M, K, _stream(stream)), "gemmq_quantize_q8K")
+    return out
+
+
+def gemm(fmt, w, xq, M, N, K, out=None, path=PATH_AUTO, stream=None):
+    """Packed weights (uint8) x q8_K activations (uint8) -> f32 [M, N]."""
+    torch = _torch()
+    if w.numel() < weight_bytes(fmt, N, K) or xq.numel() < q8K_bytes(M, K):
+        raise ValueError("buffer smaller than the stated shape")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=xq.device)
+    elif out.numel() < M * N:
+        raise ValueError("out too small")
+    _check(lib().gemmq_gemm_ex(fmt, _dev(w, "w", torch.uint8), _dev(xq, "xq", torch.uint8),
+                               _dev(out, "out", torch.float32), M, N, K, path, _stream(stream)),
+           "gemmq_gemm")
+    return out
+
+
+def decode(fmt, w, N, K, out=None, stream=None):
+    """Packed weights -> f32 [N, K] (diagnostic)."""
+    torch = _torch()
+    if w.numel() < weight_bytes(fmt, N, K):
+        raise ValueError("w smaller than the stated shape")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=w.device)
+    _check(lib().gemmq_decode(fmt, _dev(w, "w", torch.uint8), _dev(out, "out", torch.float32),
+                              N, K, _stream(stream)), "gemmq_decode")
+    return out
+
+
+def linear(fmt, w, x, N, path=PATH_AUTO, stream=None):
+    """y = W x for f32 activations x [M, K]: quantize to q8_K, then the packed matmul."""
+    M, K = x.shape
+    xq = quantize_q8K(x, stream=stream)
+    return gemm(fmt, w, xq, M, N, K, path=path, stream=stream)

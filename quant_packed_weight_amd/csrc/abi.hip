@@ -1,0 +1,151 @@
+// abi.hip -- the C ABI of libgemmq (declared in include/gemmq.h).
+//
+// Every entry point validates its arguments before touching the device, so a
+// bad call returns a named status and launches nothing (the pages refuse what
+// they do not implement by name rather than guessing -- PocketLLM README,
+// "Roadmap" and "Try it").  The library owns no memory and keeps no per-call
+// state; the only process-wide state is a per-device cache of the
+// architecture check.
+#include <atomic>
+#include <cstring>
+
+#include "gemmq.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return GEMMQ_E_DEVICE;
+  if (dev >= kMaxDevices) return GEMMQ_E_DEVICE;
+  int state = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMMQ_E_DEVICE;
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(state, std::memory_order_release);
+  }
+  return state == 1 ? GEMMQ_OK : GEMMQ_E_DEVICE;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int fmt_bytes(int fmt) {
+  return fmt == GEMMQ_Q4_K ? GEMMQ_Q4_K_BYTES : fmt == GEMMQ_Q6_K ? GEMMQ_Q6_K_BYTES : 0;
+}
+
+// Launch outcome.  The thread's pending HIP error is cleared just before each
+// launch (see clear_pending), so an error read here belongs to our launch.
+int launched(int rc) {
+  if (rc != 0) return GEMMQ_E_SHAPE;
+  return hipGetLastError() == hipSuccess ? GEMMQ_OK : GEMMQ_E_LAUNCH;
+}
+
+void clear_pending() { (void)hipGetLastError(); }
+
+// Bounds that keep every byte offset below 2^62 and every grid dimension legal.
+constexpr int64_t kMaxK = (int64_t)1 << 24;
+constexpr int64_t kMaxRows = (int64_t)1 << 31;
+
+int check_weights(int fmt, const void* W, int64_t N, int64_t K) {
+  if (fmt_bytes(fmt) == 0) return GEMMQ_E_UNSUPPORTED_FORMAT;
+  if (N < 0) return GEMMQ_E_INVALID_ARG;
+  if (K <= 0 || K % GEMMQ_QK != 0 || K > kMaxK || N > kMaxRows) return GEMMQ_E_SHAPE;
+  if (N > 0 && !W) return GEMMQ_E_INVALID_ARG;
+  if (W && !aligned(W, fmt == GEMMQ_Q4_K ? 16 : 4)) return GEMMQ_E_ALIGNMENT;
+  return GEMMQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemmq_abi_version(void) { return GEMMQ_ABI_VERSION; }
+
+const char* gemmq_status_str(int status) {
+  switch (status) {
+    case GEMMQ_OK: return "GEMMQ_OK";
+    case GEMMQ_E_INVALID_ARG: return "GEMMQ_E_INVALID_ARG: null pointer, negative size or bad path";
+    case GEMMQ_E_UNSUPPORTED_FORMAT:
+      return "GEMMQ_E_UNSUPPORTED_FORMAT: only q4_K (12) and q6_K (14) are implemented";
+    case GEMMQ_E_SHAPE:
+      return "GEMMQ_E_SHAPE: K must be a positive multiple of 256 within limits, and the GEMV "
+             "path takes M <= 8";
+    case GEMMQ_E_ALIGNMENT: return "GEMMQ_E_ALIGNMENT: a pointer breaks the documented alignment";
+    case GEMMQ_E_DEVICE: return "GEMMQ_E_DEVICE: the current HIP device is not a gfx950";
+    case GEMMQ_E_LAUNCH: return "GEMMQ_E_LAUNCH: the HIP runtime rejected a kernel launch";
+    default: return "GEMMQ_E_UNKNOWN: not a libgemmq status";
+  }
+}
+
+size_t gemmq_block_bytes(int fmt) { return (size_t)fmt_bytes(fmt); }
+
+size_t gemmq_weight_bytes(int fmt, int64_t N, int64_t K) {
+  const int bb = fmt_bytes(fmt);
+  if (!bb || N < 0 || K < 0 || K % GEMMQ_QK != 0 || K > kMaxK || N > kMaxRows) return 0;
+  return (size_t)N * (size_t)(K / GEMMQ_QK) * (size_t)bb;
+}
+
+size_t gemmq_q8K_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || K % GEMMQ_QK != 0 || K > kMaxK || M > kMaxRows) return 0;
+  return (size_t)M * (size_t)(K / GEMMQ_QK) * GEMMQ_Q8_K_BYTES;
+}
+
+int gemmq_quantize_q8K(const float* X, void* Xq, int64_t M, int64_t K, void* stream) {
+  if (M < 0) return GEMMQ_E_INVALID_ARG;
+  if (K <= 0 || K % GEMMQ_QK != 0 || K > kMaxK || M > kMaxRows) return GEMMQ_E_SHAPE;
+  if (M == 0) return GEMMQ_OK;
+  if (!X || !Xq) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  clear_pending();
+  return launched(gemmq::launch_quantize_q8K(X, static_cast<uint8_t*>(Xq), M, K,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int gemmq_gemm_ex(int fmt, const void* W, const void* Xq, float* Y, int64_t M, int64_t N,
+                  int64_t K, int path, void* stream) {
+  int rc = check_weights(fmt, W, N, K);
+  if (rc != GEMMQ_OK) return rc;
+  if (M < 0) return GEMMQ_E_INVALID_ARG;
+  if (M > kMaxRows) return GEMMQ_E_SHAPE;
+  if (path != GEMMQ_PATH_AUTO && path != GEMMQ_PATH_GEMV && path != GEMMQ_PATH_GEMM)
+    return GEMMQ_E_INVALID_ARG;
+  if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
+  if (M == 0 || N == 0) return GEMMQ_OK;
+  if (!Xq || !Y) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(Xq, 4) || !aligned(Y, 4)) return GEMMQ_E_ALIGNMENT;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  const uint8_t* w = static_cast<const uint8_t*>(W);
+  const uint8_t* xq = static_cast<const uint8_t*>(Xq);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool gemv = path == GEMMQ_PATH_GEMV || (path == GEMMQ_PATH_AUTO && M <= 8);
+  clear_pending();
+  if (gemv) return launched(gemmq::launch_gemv(fmt, w, xq, Y, (int)M, N, K, st));
+  return launched(gemmq::launch_gemm(fmt, w, xq, Y, M, N, K, st));
+}
+
+int gemmq_gemm(int fmt, const void* W, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,
+               void* stream) {
+  return gemmq_gemm_ex(fmt, W, Xq, Y, M, N, K, GEMMQ_PATH_AUTO, stream);
+}
+
+int gemmq_decode(int fmt, const void* W, float* Wf, int64_t N, int64_t K, void* stream) {
+  const int rc = check_weights(fmt, W, N, K);
+  if (rc != GEMMQ_OK) return rc;
+  if (N == 0) return GEMMQ_OK;
+  if (!Wf) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(Wf, 16)) return GEMMQ_E_ALIGNMENT;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  clear_pending();
+  return launched(gemmq::launch_decode(fmt, static_cast<const uint8_t*>(W), Wf, N, K,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

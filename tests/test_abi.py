@@ -1,0 +1,130 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments with a named status before it
+touches the device.  Every call below fails validation, so none reaches HIP.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quant_packed_weight_amd as gq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemmq.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemmq_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(gq.LIB_PATH):
+        pytest.fail("libgemmq.so not built: run python -m quant_packed_weight_amd.build")
+    return gq.lib()
+
+
+def test_every_declared_symbol_exported(L):
+    names = _declared()
+    assert len(names) == 9
+    assert set(names) == set(gq.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(gemmq_\w+)", out))
+    assert set(names) <= exported
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_version_and_status_names(L):
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 1
+    for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
+                       (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
+                       (-77, "UNKNOWN")]:
+        assert word in gq.status_str(code)
+
+
+def test_size_helpers(L):
+    assert gq.block_bytes(12) == 144 and gq.block_bytes(14) == 210 and gq.block_bytes(13) == 0
+    assert gq.weight_bytes(12, 4096, 4096) == 4096 * 16 * 144
+    assert gq.weight_bytes(14, 151936, 2048) == 255252480
+    assert gq.weight_bytes(12, 10, 300) == 0 and gq.weight_bytes(12, -1, 256) == 0
+    assert gq.weight_bytes(99, 10, 256) == 0
+    assert gq.q8K_bytes(512, 1024) == 598016
+    assert gq.q8K_bytes(1, 12288) == 14016
+    assert gq.q8K_bytes(1, 100) == 0 and gq.q8K_bytes(-1, 256) == 0
+
+
+FAKE16 = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,status", [
+    ((13, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -2),      # unknown format
+    ((12, FAKE16, FAKE16, FAKE16, 1, 1, 300, 0), -3),      # K % 256 != 0
+    ((12, FAKE16, FAKE16, FAKE16, 1, 1, 0, 0), -3),        # K = 0
+    ((12, FAKE16, FAKE16, FAKE16, 1, -1, 256, 0), -1),     # N < 0
+    ((12, FAKE16, FAKE16, FAKE16, -1, 1, 256, 0), -1),     # M < 0
+    ((12, None, FAKE16, FAKE16, 1, 1, 256, 0), -1),        # null W
+    ((12, FAKE16, None, FAKE16, 1, 1, 256, 0), -1),        # null Xq
+    ((12, FAKE16, FAKE16, None, 1, 1, 256, 0), -1),        # null Y
+    ((12, FAKE16 + 4, FAKE16, FAKE16, 1, 1, 256, 0), -4),  # q4_K weights need 16 B
+    ((14, FAKE16 + 2, FAKE16, FAKE16, 1, 1, 256, 0), -4),  # q6_K weights need 4 B
+    ((12, FAKE16, FAKE16 + 2, FAKE16, 1, 1, 256, 0), -4),  # Xq needs 4 B
+    ((12, FAKE16, FAKE16, FAKE16 + 1, 1, 1, 256, 0), -4),  # Y needs 4 B
+    ((12, FAKE16, FAKE16, FAKE16, 1, 1, 256, 7), -1),      # unknown path
+    ((12, FAKE16, FAKE16, FAKE16, 9, 1, 256, 1), -3),      # GEMV path with M > 8
+    ((12, FAKE16, FAKE16, FAKE16, 0, 5, 256, 0), 0),       # M = 0: empty, nothing touched
+    ((12, FAKE16, FAKE16, FAKE16, 5, 0, 256, 0), 0),       # N = 0: empty
+])
+def test_gemm_validation(L, args, status):
+    fmt, W, Xq, Y, M, N, K, path = args
+    assert L.gemmq_gemm_ex(fmt, W, Xq, Y, M, N, K, path, None) == status
+    if path == 0:
+        assert L.gemmq_gemm(fmt, W, Xq, Y, M, N, K, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE16, FAKE16, -1, 256), -1),
+    ((FAKE16, FAKE16, 1, 255), -3),
+    ((FAKE16, FAKE16, 1, 0), -3),
+    ((None, FAKE16, 1, 256), -1),
+    ((FAKE16, None, 1, 256), -1),
+    ((FAKE16 + 4, FAKE16, 1, 256), -4),   # X needs 16 B
+    ((FAKE16, FAKE16 + 1, 1, 256), -4),   # Xq needs 4 B
+    ((None, None, 0, 256), 0),            # M = 0: empty
+])
+def test_quantize_validation(L, args, status):
+    X, Xq, M, K = args
+    assert L.gemmq_quantize_q8K(X, Xq, M, K, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((99, FAKE16, FAKE16, 1, 256), -2),
+    ((12, FAKE16, FAKE16, 1, 512 + 3), -3),
+    ((12, None, FAKE16, 1, 256), -1),
+    ((12, FAKE16, None, 1, 256), -1),
+    ((12, FAKE16, FAKE16 + 4, 1, 256), -4),  # Wf needs 16 B
+    ((12, FAKE16, FAKE16, 0, 256), 0),
+])
+def test_decode_validation(L, args, status):
+    assert L.gemmq_decode(*args, None) == status
+
+
+def test_binding_raises_named_error(L):
+    with pytest.raises(gq.GemmqError) as e:
+        gq._lib._check(-2, "gemmq_gemm")
+    assert "UNSUPPORTED_FORMAT" in str(e.value)
+
+
+def test_product_path_never_imports_oracle():
+    # the product package and its binding must not reach the CPU oracle
+    pkg = os.path.join(ROOT, "quant_packed_weight_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"import\s+oracle|from\s+oracle|liboracle|oracle[./]", text), f

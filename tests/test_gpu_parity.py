@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path against the CPU oracle, element by element.
+
+Bit-exact: q8_K bytes and decoded weights.  Tolerance: |y - y_oracle| <=
+1e-5 * sum_k |w_k * xhat_k| + 1e-6 per output (the pages' 1e-5 scaled relative
+bound for reordered f32 sums; molayo article, status row "src/ -- C++ engine").
+Bit identity inside a path: GEMV rows do not depend on M, GEMM rows do not
+depend on which other rows are in the call (the pages' tiled equals single-row
+rule, same row of the article).
+"""
+import numpy as np
+import pytest
+
+from gpu_util import assert_within, device, log, to_dev, to_host
+from packer import pack_q4K, pack_q6K
+from quant_packed_weight_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+Q4, Q6 = 12, 14
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+@pytest.fixture(scope="module")
+def gq():
+    import quant_packed_weight_amd
+
+    return quant_packed_weight_amd
+
+
+def _acts(rng, M, K, kind="normal"):
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    if kind == "outliers" and K >= 4:
+        x[:, rng.choice(K, 4, replace=False)] *= 20
+    return x
+
+
+# ------------------------------------------------------------------ q8_K
+@pytest.mark.parametrize("M,K", [(1, 256), (3, 768), (8, 4096), (37, 1024), (512, 2048),
+                                 (2, 12288)])
+def test_quantize_bit_exact(dev, gq, orc, M, K):
+    log("quantize M=%d K=%d" % (M, K))
+    rng = np.random.default_rng(M * 7 + K)
+    x = _acts(rng, M, K, "outliers")
+    # special blocks: all zero, exact ties, tiny values, a single spike
+    nb = K // 256
+    if M * nb >= 4:
+        xb = x.reshape(-1, 256)
+        xb[0] = 0
+        # d = 2^-7 exactly, so x/d hits every k + 1/2 tie exactly
+        xb[1, :254] = ((np.arange(-127, 127) + 0.5) * 2.0 ** -7).astype(np.float32)
+        xb[1, 254] = 127 * 2.0 ** -7
+        xb[1, 255] = 0
+        xb[2] = np.float32(1e-39) * np.sign(xb[2])
+        xb[3] = 0
+        xb[3, 17] = -3.0
+    got = to_host(gq.quantize_q8K(to_dev(x)))
+    want = orc.quantize_q8K(x)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ decode
+def _adversarial_q4K(rng, n):
+    d = (np.abs(rng.standard_normal(n)) * 2e-3).astype(np.float16)
+    dmin = (np.abs(rng.standard_normal(n)) * 2e-3).astype(np.float16)
+    sc = rng.integers(0, 64, (n, 8))
+    mn = rng.integers(0, 64, (n, 8))
+    q = rng.integers(0, 16, (n, 256))
+    d[0::7] = np.float16(6e-8)     # f16 subnormal
+    dmin[1::7] = np.float16(3e-6)  # f16 subnormal
+    d[2::7] = 0
+    d[3::7] = -d[3::7]             # negative scales
+    dmin[4::7] = -np.float16(0.5)
+    sc[5::7] = 63
+    mn[5::7] = 63
+    q[5::7] = 15
+    d[6::7] = np.float16(65504.0)
+    return pack_q4K(d, dmin, sc, mn, q)
+
+
+def _adversarial_q6K(rng, n):
+    d = (np.abs(rng.standard_normal(n)) * 1e-3).astype(np.float16)
+    sc = rng.integers(-128, 128, (n, 16))
+    q = rng.integers(0, 64, (n, 256))
+    d[0::5] = np.float16(6e-8)
+    d[1::5] = 0
+    d[2::5] = -d[2::5]
+    sc[3::5] = -128
+    q[3::5] = 0  # (0 - 32) * -128 = 4096, the largest magnitude
+    sc[4::5] = 127
+    q[4::5] = 63
+    return pack_q6K(d, sc, q)
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("N,K", [(1, 256), (33, 768), (1000, 512), (7, 3072)])
+def test_decode_bit_exact(dev, gq, orc, fmt, N, K):
+    log("decode fmt=%d N=%d K=%d" % (fmt, N, K))
+    rng = np.random.default_rng(N + K + fmt)
+    nb = K // 256
+    if N * nb >= 10:
+        raw = (_adversarial_q4K if fmt == Q4 else _adversarial_q6K)(rng, N * nb).reshape(N, -1)
+    else:
+        raw = synth.make_weights(rng, fmt, N, K)
+    got = to_host(gq.decode(fmt, to_dev(raw), N, K))
+    want = orc.decode(fmt, raw, N, K)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ matmul
+def _case(orc, fmt, M, N, K, seed, adversarial=False):
+    rng = np.random.default_rng(seed)
+    nb = K // 256
+    if adversarial:
+        W = (_adversarial_q4K if fmt == Q4 else _adversarial_q6K)(rng, N * nb).reshape(N, -1)
+    else:
+        W = synth.make_weights(rng, fmt, N, K)
+    x = _acts(rng, M, K, "outliers")
+    if adversarial:
+        x[:, 0] = np.abs(x).max() * 3  # x = +amax in some blocks
+        x[0, 1] = -x[0, 0]            # and -amax
+    xq = orc.quantize_q8K(x)
+    return W, x, xq
+
+
+def _run(gq, fmt, W, xq, M, N, K, path):
+    return to_host(gq.gemm(fmt, to_dev(W), to_dev(xq), M, N, K, path=path))
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("N,K", [(1, 256), (31, 512), (33, 768), (1000, 1024), (64, 3072)])
+def test_gemv_parity(dev, gq, orc, fmt, M, N, K):
+    log("gemv fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
+    W, _, xq = _case(orc, fmt, M, N, K, seed=100 * M + N + K + fmt)
+    y = _run(gq, fmt, W, xq, M, N, K, gq.PATH_GEMV)
+    yo = orc.gemm_int(fmt, W, xq, M, N, K)
+    _, S = orc.gemm_dequant(fmt, W, xq, M, N, K)
+    assert_within(y, yo, S, "gemv")
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("K", [256, 1024, 3072, 4096])
+def test_gemv_rows_independent_of_M(dev, gq, orc, fmt, K):
+    log("gemv M-invariance fmt=%d K=%d" % (fmt, K))
+    N = 333
+    W, _, xq = _case(orc, fmt, 8, N, K, seed=K + fmt)
+    Wd = to_dev(W)
+    y8 = to_host(gq.gemm(fmt, Wd, to_dev(xq), 8, N, K, path=gq.PATH_GEMV))
+    for m in range(8):
+        y1 = to_host(gq.gemm(fmt, Wd, to_dev(xq[m:m + 1]), 1, N, K, path=gq.PATH_GEMV))
+        assert np.array_equal(y1[0].view(np.uint32), y8[m].view(np.uint32)), m
+    for M in (3, 5):
+        yM = to_host(gq.gemm(fmt, Wd, to_dev(xq[:M]), M, N, K, path=gq.PATH_GEMV))
+        assert np.array_equal(yM.view(np.uint32), y8[:M].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("M,N,K", [(9, 1, 256), (16, 33, 512), (31, 64, 256), (32, 65, 768),
+                                   (33, 200, 1024), (128, 64, 512), (129, 127, 256),
+                                   (300, 130, 1024), (511, 96, 3072), (1, 70, 512), (8, 64, 256)])
+def test_gemm_parity(dev, gq, orc, fmt, M, N, K):
+    log("gemm fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
+    W, _, xq = _case(orc, fmt, M, N, K, seed=7 * M + 3 * N + K + fmt)
+    y = _run(gq, fmt, W, xq, M, N, K, gq.PATH_GEMM)
+    yo = orc.gemm_int(fmt, W, xq, M, N, K)
+    _, S = orc.gemm_dequant(fmt, W, xq, M, N, K)
+    assert_within(y, yo, S, "gemm")
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+def test_gemm_rows_independent_of_call(dev, gq, orc, fmt):
+    log("gemm row-subset fmt=%d" % fmt)
+    M, N, K = 300, 150, 1024
+    W, _, xq = _case(orc, fmt, M, N, K, seed=77 + fmt)
+    Wd = to_dev(W)
+    full = to_host(gq.gemm(fmt, Wd, to_dev(xq), M, N, K, path=gq.PATH_GEMM))
+    for a, b in [(0, 9), (37, 87), (128, 300), (299, 300), (5, 6)]:
+        part = to_host(gq.gemm(fmt, Wd, to_dev(xq[a:b]), b - a, N, K, path=gq.PATH_GEMM))
+        assert np.array_equal(part.view(np.uint32), full[a:b].view(np.uint32)), (a, b)
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("path", [1, 2])
+def test_adversarial_blocks(dev, gq, orc, fmt, path):
+    log("adversarial fmt=%d path=%d" % (fmt, path))
+    M = 8 if path == 1 else 40
+    N, K = 70, 1792
+    W, _, xq = _case(orc, fmt, M, N, K, seed=5 + fmt, adversarial=True)
+    y = _run(gq, fmt, W, xq, M, N, K, path)
+    yo = orc.gemm_int(fmt, W, xq, M, N, K)
+    _, S = orc.gemm_dequant(fmt, W, xq, M, N, K)
+    assert_within(y, yo, S, "adversarial")
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+def test_auto_dispatch_and_linear(dev, gq, orc, fmt):
+    log("dispatch fmt=%d" % fmt)
+    N, K = 96, 512
+    for M in (1, 8, 9, 64):
+        W, x, xq = _case(orc, fmt, M, N, K, seed=M + fmt)
+        auto = to_host(gq.gemm(fmt, to_dev(W), to_dev(xq), M, N, K))
+        forced = _run(gq, fmt, W, xq, M, N, K, gq.PATH_GEMV if M <= 8 else gq.PATH_GEMM)
+        assert np.array_equal(auto.view(np.uint32), forced.view(np.uint32))
+        lin = to_host(gq.linear(fmt, to_dev(W), to_dev(x), N))
+        assert np.array_equal(lin.view(np.uint32), auto.view(np.uint32))
+
+
+def test_empty_calls_touch_nothing(dev, gq):
+    import torch
+
+    y = torch.full((4, 4), 7.0, device="cuda:0")
+    w = torch.zeros(4 * 144, dtype=torch.uint8, device="cuda:0")
+    xq = torch.zeros(4 * 292, dtype=torch.uint8, device="cuda:0")
+    assert gq.gemm_ptr(Q4, w.data_ptr(), xq.data_ptr(), y.data_ptr(), 0, 4, 256) == 0
+    assert gq.gemm_ptr(Q4, w.data_ptr(), xq.data_ptr(), y.data_ptr(), 4, 0, 256) == 0
+    assert gq.quantize_q8K_ptr(y.data_ptr(), xq.data_ptr(), 0, 256) == 0
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
+    assert bool((xq == 0).all())
