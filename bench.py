@@ -8,15 +8,22 @@ layer (q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 12288x4096, down
 4096x12288, all q4_K; 108,527,616 weight bytes), run at M = 1 (decode GEMV,
 weight GB/s) and M = 512 (prefill GEMM, int8 TOP/s).
 
+Each matrix reads the activation of its place in the layer (q/k/v the attention
+input, o the attention output, gate/up the MLP input, down the MLP activation),
+so a pass quantizes four activation tensors and runs seven matmuls.
+
 Inputs are resident in HBM before timing starts.  So that the weights are
 really streamed from HBM and not from the 256 MB last-level cache, the step
-rotates over R copies of the layer's weights (R * 108.5 MB >= 1 GiB).
+rotates over R copies of the layer's weights (R * 108.5 MB >= 1 GiB).  Passes
+are submitted as eager launches on one stream; --graph instead captures one pass
+per weight copy in a HIP graph and times the replays (slower on this stack).
 
 Output: one JSON line.  `value` is the M=1 weight throughput of the whole step
 (quantizer launches included); `secondary` the M=512 int8 throughput;
 `roofline` / `roofline_m512` give the dominant kernels' algorithmic rate from
-per-launch HIP events against the MI355X peaks (HBM 8 TB/s; dense int8 MFMA
-5.0 POP/s); `cpu_baseline` times the CPU oracle on a bounded sample.
+HIP events around batches of back-to-back launches against the MI355X peaks
+(HBM 8 TB/s; dense int8 MFMA 5.0 POP/s); `cpu_baseline` times the CPU oracle
+on a bounded sample.
 """
 from __future__ import annotations
 
@@ -46,7 +53,12 @@ def parse():
                    help="activation rows; the first is the headline (value), the second secondary")
     p.add_argument("--copies", type=int, default=0, help="rotating weight copies (0: auto, >=1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="time HIP-graph replays of each pass instead of eager launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="first run one plain device-to-device copy of MIB MiB (reference dispatch "
+                        "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -68,47 +80,34 @@ class Layer:
             self.w.append({k: (v if r == 0 else v.clone()) for k, v in base.items()})
         self.x, self.xq, self.y = {}, {}, {}
         for M in Ms:
-            for K in wl.ks():
-                self.x[(M, K)] = torch.from_numpy(gen.activations[(M, K)]).to("cuda:0")
-                self.xq[(M, K)] = torch.empty(gq.q8K_bytes(M, K), dtype=torch.uint8,
-                                              device="cuda:0")
+            for inp, K in wl.inputs():
+                self.x[(M, inp)] = torch.from_numpy(gen.activations[(M, inp)]).to("cuda:0")
+                self.xq[(M, inp)] = torch.empty(gq.q8K_bytes(M, K), dtype=torch.uint8,
+                                                device="cuda:0")
             for m in wl.matrices:
                 self.y[(M, m.name)] = torch.empty((M, m.N), dtype=torch.float32, device="cuda:0")
         torch.cuda.synchronize()
 
-    def run(self, M, r, stream, events=None):
-        """Enqueue one pass at M rows on weight copy r.  With `events`, every
-        launch is bracketed by a pair of timing events on the same stream."""
+    def run(self, M, r, stream):
+        """Enqueue one pass at M rows on weight copy r."""
         gq = self.gq
         st = stream.cuda_stream
-        for K in self.wl.ks():
-            rc = gq.quantize_q8K_ptr(self.x[(M, K)].data_ptr(), self.xq[(M, K)].data_ptr(), M, K,
-                                     st)
-            if rc:
-                raise gq.GemmqError(rc, "quantize")
+        done = set()
         for m in self.wl.matrices:
-            if events is not None:
-                e0, e1 = events.pop()
-                e0.record(stream)
-            rc = gq.gemm_ptr(m.fmt, self.w[r][m.name].data_ptr(), self.xq[(M, m.K)].data_ptr(),
+            if m.inp not in done:  # quantize each activation just before its first use
+                rc = gq.quantize_q8K_ptr(self.x[(M, m.inp)].data_ptr(),
+                                         self.xq[(M, m.inp)].data_ptr(), M, m.K, st)
+                if rc:
+                    raise gq.GemmqError(rc, "quantize")
+                done.add(m.inp)
+            rc = gq.gemm_ptr(m.fmt, self.w[r][m.name].data_ptr(), self.xq[(M, m.inp)].data_ptr(),
                              self.y[(M, m.name)].data_ptr(), M, m.N, m.K, gq.PATH_AUTO, st)
             if rc:
                 raise gq.GemmqError(rc, "gemm " + m.name)
-            if events is not None:
-                e1.record(stream)
-                events.used.append((m, e0, e1))
-
-
-class EventPool(list):
-    def __init__(self, n):
-        import torch
-
-        super().__init__((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                         for _ in range(n))
-        self.used = []
 
 
 def time_passes(layer, M, steps, warmup, copies, stream):
+    """Eager launches: seconds per pass."""
     import torch
 
     for s in range(warmup):
@@ -121,18 +120,70 @@ def time_passes(layer, M, steps, warmup, copies, stream):
     return (time.perf_counter() - t0) / steps
 
 
-def kernel_rates(layer, M, steps, copies, stream):
-    """Per-launch HIP-event durations of the matmul kernel at M rows."""
+def capture_graphs(layer, M, copies):
+    """One HIP graph per weight copy, each holding one whole pass."""
     import torch
 
-    nmat = len(layer.wl.matrices)
-    pool = EventPool(steps * nmat)
-    for s in range(steps):
-        layer.run(M, s % copies, stream, events=pool)
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layer.run(M, 0, side)
+    torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
+    for r in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layer.run(M, r, torch.cuda.current_stream())
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def time_graphs(graphs, steps, warmup):
+    """Graph replays: seconds per pass."""
+    import torch
+
+    n = len(graphs)
+    for s in range(warmup):
+        graphs[s % n].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        graphs[(warmup + s) % n].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def kernel_rates(layer, M, steps, copies, stream):
+    """Average duration of each matrix's matmul kernel: two HIP events on the
+    launch stream around a batch of back-to-back launches of that matrix (weight
+    copies rotated, its activation quantized once beforehand)."""
+    import torch
+
+    gq = layer.gq
+    st = stream.cuda_stream
+    for m in layer.wl.matrices:
+        rc = gq.quantize_q8K_ptr(layer.x[(M, m.inp)].data_ptr(), layer.xq[(M, m.inp)].data_ptr(),
+                                 M, m.K, st)
+        if rc:
+            raise gq.GemmqError(rc, "quantize")
     per = {}
-    for m, e0, e1 in pool.used:
-        per.setdefault(m.name, []).append(e0.elapsed_time(e1) * 1e-3)
+    n = max(steps, copies)
+    for m in layer.wl.matrices:
+        args = [(layer.w[r % copies][m.name].data_ptr(), layer.xq[(M, m.inp)].data_ptr(),
+                 layer.y[(M, m.name)].data_ptr()) for r in range(n)]
+        for w, xq, y in args[:copies]:  # warm the launch path
+            gq.gemm_ptr(m.fmt, w, xq, y, M, m.N, m.K, gq.PATH_AUTO, st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for w, xq, y in args:
+            rc = gq.gemm_ptr(m.fmt, w, xq, y, M, m.N, m.K, gq.PATH_AUTO, st)
+            if rc:
+                raise gq.GemmqError(rc, "gemm " + m.name)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per[m.name] = [e0.elapsed_time(e1) * 1e-3 / n] * n
     return per
 
 
@@ -146,9 +197,9 @@ def cpu_baseline(wl, gen, M1, M2, seconds):
     # M = M1 (decode): whole passes over all matrices until `seconds` elapse
     passes, t0 = 0, time.perf_counter()
     while True:
-        xq = {K: oracle.quantize_q8K(gen.activations[(M1, K)]) for K in wl.ks()}
+        xq = {inp: oracle.quantize_q8K(gen.activations[(M1, inp)]) for inp, _ in wl.inputs()}
         for m in wl.matrices:
-            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.K], M1, m.N, m.K)
+            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.inp], M1, m.N, m.K)
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds or passes >= 50:
@@ -160,11 +211,12 @@ def cpu_baseline(wl, gen, M1, M2, seconds):
                      "matmul), %.1f s" % (passes, len(wl.matrices), M1, el))
     if M2:
         rows = np.array([0, M2 - 1])
-        xq = {K: oracle.quantize_q8K(gen.activations[(M2, K)][rows]) for K in wl.ks()}
+        xq = {inp: oracle.quantize_q8K(gen.activations[(M2, inp)][rows])
+              for inp, _ in wl.inputs()}
         t0 = time.perf_counter()
         ops = 0
         for m in wl.matrices:
-            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.K], len(rows), m.N, m.K)
+            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.inp], len(rows), m.N, m.K)
             ops += 2 * len(rows) * m.N * m.K
         el = time.perf_counter() - t0
         out["value_m%d" % M2] = ops / el / 1e12
@@ -197,9 +249,26 @@ def main():
     copies = a.copies or max(1, math.ceil(GIB / wbytes))
     layer = Layer(wl, gen, Ms, copies)
     stream = torch.cuda.current_stream()
+    if a.copy_calibration:
+        # a plain device copy of known size whose source is cold: after filling
+        # it, 1 GiB of other writes pushes it out of L2 and the 256 MB MALL
+        n = a.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        flush = torch.empty(GIB, dtype=torch.uint8, device="cuda:0")
+        flush.fill_(7)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst, flush
 
-    t = {M: time_passes(layer, M, a.steps, a.warmup, copies, stream) for M in Ms}
+    t_eager = {M: time_passes(layer, M, a.steps, a.warmup, copies, stream) for M in Ms}
     rates = {M: kernel_rates(layer, M, a.steps, copies, stream) for M in Ms}
+    if not a.graph:
+        t = t_eager
+    else:
+        graphs = {M: capture_graphs(layer, M, copies) for M in Ms}
+        t = {M: time_graphs(graphs[M], a.steps, a.warmup) for M in Ms}
 
     M1 = Ms[0]
     M2 = Ms[1] if len(Ms) > 1 else None
@@ -244,8 +313,10 @@ def main():
         "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": a.workload, "M": Ms, "matrices": len(wl.matrices),
-                   "weight_bytes": wbytes, "rotating_copies": copies,
-                   "ms_per_pass": {str(M): round(t[M] * 1e3, 4) for M in Ms}},
+                   "activations": len(wl.inputs()), "weight_bytes": wbytes,
+                   "rotating_copies": copies, "submit": "hip_graph" if a.graph else "eager",
+                   "ms_per_pass": {str(M): round(t[M] * 1e3, 4) for M in Ms},
+                   "ms_per_pass_eager": {str(M): round(t_eager[M] * 1e3, 4) for M in Ms}},
         "roofline": roof(M1),
     }
     if M2:

@@ -3,236 +3,423 @@
 // Decode time on the pages is the walk over the packed weights (molayo article
 // "PocketLLM: 단일 가속기에서 대규모 언어 모델 실행", status row "src/ -- C++
 // engine": the packed dot walks each weight row once per tile of activation
-// rows).  On gfx950 that walk is an HBM stream, so the kernel is shaped for it:
+// rows).  On gfx950 that walk is an HBM stream, and a plain one-shot read kernel
+// (one wave per row slice, all loads issued at once) already reaches ~5.8 TB/s
+// on a 28 MB matrix, so this kernel keeps exactly that access shape and spends
+// as few vector instructions per weight byte as it can:
 //
-//  * one 64-lane wavefront owns a tile of R weight rows; eight lanes share a
-//    super-block, each taking one 16-byte chunk of its packed quants (q4_K) or
-//    one 32-weight quarter (q6_K), so a wave reads eight consecutive blocks of a
-//    row per step and the row's bytes stream in order;
-//  * the lane's activation fragment for a block position is loaded once and
-//    reused for all R rows of the tile;
-//  * integer dot products run on v_dot4 (int8 x int8 -> int32); the sub-block
-//    scale/min correction stays in integers and one f32 fold per block and lane
-//    applies d_w, dmin and d_x;
-//  * the 64 lane partials of each output are summed by a fixed xor butterfly.
+//  * One 64-lane wavefront owns P weight rows and issues every weight load of
+//    them before any arithmetic.  Four lanes share a super-block: q4_K lane g
+//    takes the 32 quant bytes of 64-weight group g (sub-blocks 2g and 2g+1);
+//    q6_K lane (half hh, pair p) takes quarters p and p+2 of half hh.  A round
+//    is 16 consecutive blocks of a row (or, for rows of 16/P blocks, P rows side
+//    by side), so one load instruction of the wave covers 2.3 KiB (q4_K) of
+//    contiguous weight bytes.
+//  * Activation fragments are read straight from global memory: the q8_K rows
+//    are small and stay cache-resident, and staging them in LDS (tried) costs a
+//    barrier and a second round trip that the stream cannot hide.
+//  * Integer dot products on v_dot4 (int8 x int8 -> int32); the scale and min
+//    corrections use 24-bit multiplies and v_dot2 on the int16 group sums; one
+//    f32 fold per block and lane applies d_w, dmin and d_x.
+//  * The 64/P lane partials of each output are combined by a fixed xor tree.
 //
-// Every output's arithmetic (per-lane block order, butterfly shape) depends only
-// on K, never on M or R, so row m of an M-row call equals a one-row call on that
-// row bit for bit.
+// Every output's arithmetic (per-lane block order and the xor tree) depends only
+// on K, never on M or N, so row m of an M-row call equals a one-row call on
+// that row bit for bit.
 #include "device.h"
 #include "launch.h"
 
 namespace gemmq {
 
-// ---------------------------------------------------------------- q4_K
-// Lane (G = lane/8, c = lane%8) takes qs bytes 16c..16c+15 of blocks G, G+8, ...
-// Those bytes hold, as low nibbles, weights 64g+16h+t of sub-block 2g and, as high
-// nibbles, weights 64g+32+16h+t of sub-block 2g+1 (g = c/2, h = c%2, t < 16); the
-// matching activation sums are groups 4g+h and 4g+2+h.
-template <int MT, int R>
-__global__ __launch_bounds__(256) void gemv_q4K_kernel(const uint8_t* __restrict__ W,
-                                                       const uint8_t* __restrict__ Xq,
-                                                       float* __restrict__ Y, int64_t N, int nb) {
-  const int lane = lane_id();
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-  if (n0 >= N) return;  // wave-uniform
-  const int G = lane >> 3, c = lane & 7, g = c >> 1, h = c & 1;
-  const int xoff = 4 + 64 * g + 16 * h;
-  const int bsoff = 260 + 8 * g;
-  const int bshift = 16 * h;
-  const bool upper = g >= 2;        // sub-blocks 4..7 use the second packed word
-  const int sshift = 16 * (g & 1);  // byte position of sub-block 2g inside it
-
-  float acc[R][MT];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
-
-  for (int b = G; b < nb; b += 8) {
-    float dx[MT];
-    u32x4 xl[MT], xh[MT];
-    int bs0[MT], bs1[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const uint8_t* xb = Xq + ((int64_t)m * nb + b) * kQ8KBytes;
-      dx[m] = *reinterpret_cast<const float*>(xb);
-      xl[m] = ld16(xb + xoff);
-      xh[m] = ld16(xb + xoff + 32);
-      const uint2 s = ld8(xb + bsoff);
-      bs0[m] = (int)(int16_t)(s.x >> bshift);
-      bs1[m] = (int)(int16_t)(s.y >> bshift);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int64_t n = n0 + r;
-      if (n >= N) n = N - 1;  // tail rows: read a valid row, never stored
-      const uint8_t* wb = W + (n * nb + b) * kQ4KBytes;
-      const uint4 hd = ld16a(wb);
-      const uint4 qv = ld16a(wb + 16 + 16 * c);
-      const float d = f16_to_f32(hd.x), dmin = f16_to_f32(hd.x >> 16);
-      const Q4KScales s = q4k_scales(hd.y, hd.z, hd.w);
-      const uint32_t scw = upper ? s.sc_hi : s.sc_lo;
-      const uint32_t mnw = upper ? s.mn_hi : s.mn_lo;
-      const int sc0 = (scw >> sshift) & 0xff, sc1 = (scw >> (sshift + 8)) & 0xff;
-      const int mn0 = (mnw >> sshift) & 0xff, mn1 = (mnw >> (sshift + 8)) & 0xff;
-      const uint32_t l0 = lo_nib(qv.x), l1 = lo_nib(qv.y), l2 = lo_nib(qv.z), l3 = lo_nib(qv.w);
-      const uint32_t h0 = hi_nib(qv.x), h1 = hi_nib(qv.y), h2 = hi_nib(qv.z), h3 = hi_nib(qv.w);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        int dl = __builtin_amdgcn_sdot4((int)l0, (int)xl[m].x, 0, false);
-        dl = __builtin_amdgcn_sdot4((int)l1, (int)xl[m].y, dl, false);
-        dl = __builtin_amdgcn_sdot4((int)l2, (int)xl[m].z, dl, false);
-        dl = __builtin_amdgcn_sdot4((int)l3, (int)xl[m].w, dl, false);
-        int dh = __builtin_amdgcn_sdot4((int)h0, (int)xh[m].x, 0, false);
-        dh = __builtin_amdgcn_sdot4((int)h1, (int)xh[m].y, dh, false);
-        dh = __builtin_amdgcn_sdot4((int)h2, (int)xh[m].z, dh, false);
-        dh = __builtin_amdgcn_sdot4((int)h3, (int)xh[m].w, dh, false);
-        const int isc = sc0 * dl + sc1 * dh;
-        const int imn = mn0 * bs0[m] + mn1 * bs1[m];
-        float t = d * (float)isc;
-        t = fmaf(-dmin, (float)imn, t);
-        acc[r][m] = fmaf(dx[m], t, acc[r][m]);
-      }
-    }
-  }
-
-  float out = 0.0f;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float v = acc[r][m];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v = wave_sum_xor(v, off);
-      if (lane == r * MT + m) out = v;
-    }
-  if (lane < R * MT) {
-    const int r = lane / MT, m = lane - (lane / MT) * MT;
-    const int64_t n = n0 + r;
-    if (n < N) Y[(int64_t)m * N + n] = out;
-  }
-}
-
-// ---------------------------------------------------------------- q6_K
-// Lane (G = lane/8, c = lane%8) takes the 32-weight quarter q = c%4 of half
-// hh = c/4 of blocks G, G+8, ...: weights 128hh + 32q + l, low bits from ql bytes
-// 64hh + 32(q&1) + l, top bits from qh bytes 32hh + l, sub-blocks 8hh+2q and
-// 8hh+2q+1.  Blocks are 210 bytes, so fields are only 2-byte aligned: they are
-// read as dword-aligned spans and realigned in registers.
-template <int MT, int R>
-__global__ __launch_bounds__(256) void gemv_q6K_kernel(const uint8_t* __restrict__ W,
-                                                       const uint8_t* __restrict__ Xq,
-                                                       float* __restrict__ Y, int64_t N, int nb) {
-  const int lane = lane_id();
-  const int64_t n0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-  if (n0 >= N) return;
-  const int G = lane >> 3, c = lane & 7, hh = c >> 2, q = c & 3;
-  const int qloff = 64 * hh + 32 * (q & 1);
-  const int qhoff = 128 + 32 * hh;
-  const int scoff = 192 + 8 * hh + 2 * q;
-  const int xoff = 4 + 128 * hh + 32 * q;
-  const int bsoff = 260 + 2 * (8 * hh + 2 * q);
-
-  float acc[R][MT];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
-
-  for (int b = G; b < nb; b += 8) {
-    float dx[MT];
-    u32x4 xa[MT], xb2[MT];
-    int bs0[MT], bs1[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const uint8_t* xb = Xq + ((int64_t)m * nb + b) * kQ8KBytes;
-      dx[m] = *reinterpret_cast<const float*>(xb);
-      xa[m] = ld16(xb + xoff);
-      xb2[m] = ld16(xb + xoff + 16);
-      const uint32_t s = ld4(xb + bsoff);
-      bs0[m] = (int)(int16_t)(s & 0xffffu);
-      bs1[m] = (int)(int16_t)(s >> 16);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      int64_t n = n0 + r;
-      if (n >= N) n = N - 1;
-      const uint8_t* wb = W + (n * nb + b) * kQ6KBytes;
-      uint32_t ql[8], qh[8];
-      ld_dwords_a2<8>(wb + qloff, ql);
-      ld_dwords_a2<8>(wb + qhoff, qh);
-      const uint32_t scp = ld2(wb + scoff);
-      const int sc0 = (int)(int8_t)(scp & 0xffu), sc1 = (int)(int8_t)(scp >> 8);
-      const float d = f16_to_f32(ld2(wb + 208));
-      uint32_t qq[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) qq[k] = q6k_quad(ql[k], qh[k], q);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        int d0 = __builtin_amdgcn_sdot4((int)qq[0], (int)xa[m].x, 0, false);
-        d0 = __builtin_amdgcn_sdot4((int)qq[1], (int)xa[m].y, d0, false);
-        d0 = __builtin_amdgcn_sdot4((int)qq[2], (int)xa[m].z, d0, false);
-        d0 = __builtin_amdgcn_sdot4((int)qq[3], (int)xa[m].w, d0, false);
-        int d1 = __builtin_amdgcn_sdot4((int)qq[4], (int)xb2[m].x, 0, false);
-        d1 = __builtin_amdgcn_sdot4((int)qq[5], (int)xb2[m].y, d1, false);
-        d1 = __builtin_amdgcn_sdot4((int)qq[6], (int)xb2[m].z, d1, false);
-        d1 = __builtin_amdgcn_sdot4((int)qq[7], (int)xb2[m].w, d1, false);
-        const int isc = sc0 * (d0 - 32 * bs0[m]) + sc1 * (d1 - 32 * bs1[m]);
-        acc[r][m] = fmaf(dx[m], d * (float)isc, acc[r][m]);
-      }
-    }
-  }
-
-  float out = 0.0f;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float v = acc[r][m];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v = wave_sum_xor(v, off);
-      if (lane == r * MT + m) out = v;
-    }
-  if (lane < R * MT) {
-    const int r = lane / MT, m = lane - (lane / MT) * MT;
-    const int64_t n = n0 + r;
-    if (n < N) Y[(int64_t)m * N + n] = out;
-  }
-}
-
-// ---------------------------------------------------------------- launch
 namespace {
 
-// Rows per wave: as many as keep at least ~2048 waves in flight (8 per CU on
-// 256 CUs), at most 32 accumulators per lane.
-int pick_rows(int M, int64_t N) {
-  int R = 8;
-  while (R > 1 && (N / R < 2048 || R * M > 32)) R >>= 1;
-  return R;
+constexpr int kXS = 304;  // LDS bytes per staged q8_K block: q[256] | sums[16] | d | pad
+constexpr int kMaxIT = 4; // rounds of 16 blocks whose loads are in flight together
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ int dot2(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot2(__builtin_bit_cast(i16x2, a), __builtin_bit_cast(i16x2, b), c,
+                                false);
+}
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
 }
 
-template <int MT, int R>
-void launch_one(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int64_t N, int nb,
-                hipStream_t st) {
-  const int64_t waves = (N + R - 1) / R;
-  const dim3 grid((uint32_t)((waves + 3) / 4));
-  if (fmt == 12)
-    hipLaunchKernelGGL((gemv_q4K_kernel<MT, R>), grid, dim3(256), 0, st, W, Xq, Y, N, nb);
+// 36 bytes from a dword-aligned address in three loads (two of 16 B).
+__device__ __forceinline__ void ld36(const uint8_t* p, uint32_t (&o)[9]) {
+  const u32x4 a = ld16(p), b = ld16(p + 16);
+  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+  o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  o[8] = ld4(p + 32);
+}
+
+// 32 bytes at a 2-byte-aligned address: the dword-aligned 36-byte span that
+// covers them (never past p + 34), shifted into place.
+__device__ __forceinline__ void ld32_a2(const uint8_t* p, uint32_t (&o)[8]) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  uint32_t raw[9];
+  ld36(reinterpret_cast<const uint8_t*>(a & ~uintptr_t(3)), raw);
+  const uint32_t sh = (uint32_t)(a & 3u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+}
+
+// Exchange with lane ^ D: DPP quad permutes for 1 and 2, ds_swizzle (xor mode,
+// inside 32-lane halves) for 4, 8 and 16, a bpermute for 32.
+template <int D>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int i = __builtin_bit_cast(int, v);
+  int r;
+  if constexpr (D == 1)
+    r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  else if constexpr (D == 2)
+    r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  else if constexpr (D == 4 || D == 8 || D == 16)
+    r = __builtin_amdgcn_ds_swizzle(i, 0x1F | (D << 10));   // and 0x1F, or 0, xor D
   else
-    hipLaunchKernelGGL((gemv_q6K_kernel<MT, R>), grid, dim3(256), 0, st, W, Xq, Y, N, nb);
+    r = __shfl_xor(i, D, 64);
+  return __builtin_bit_cast(float, r);
 }
 
+// One step at xor distance D.  While a lane holds several values it keeps half
+// and sends half (reduce-scatter); otherwise it adds its partner's value.  Each
+// sum adds the partials of lanes l and l ^ D, so the f32 result of every output
+// is the same whichever lane computes it and however many values there are.
+template <int D, int V>
+__device__ __forceinline__ void seg_step(float (&v)[V], int& cnt, int lane) {
+  if (cnt > 1) {
+    const bool up = (lane & D) != 0;
+    const int h = cnt / 2;
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+      if (j < h) {
+        const float send = up ? v[j] : v[j + h];
+        const float keep = up ? v[j + h] : v[j];
+        v[j] = keep + xor_lane<D>(send);
+      }
+    }
+    cnt = h;
+  } else {
+    v[0] = v[0] + xor_lane<D>(v[0]);
+  }
+}
+
+// Reduce-scatter over segments of SEG lanes (V <= SEG, a power of two): lane l
+// ends with the total of value vidx<V, SEG>(l) in v[0].
+template <int V, int SEG>
+__device__ __forceinline__ void seg_reduce(float (&v)[V], int lane) {
+  int cnt = V;
+  if constexpr (SEG >= 64) seg_step<32>(v, cnt, lane);
+  if constexpr (SEG >= 32) seg_step<16>(v, cnt, lane);
+  if constexpr (SEG >= 16) seg_step<8>(v, cnt, lane);
+  if constexpr (SEG >= 8) seg_step<4>(v, cnt, lane);
+  if constexpr (SEG >= 4) seg_step<2>(v, cnt, lane);
+  seg_step<1>(v, cnt, lane);
+}
+
+// Full butterfly of one value over a segment of SEG lanes (same pairs).
+template <int SEG>
+__device__ __forceinline__ float seg_all(float v) {
+  if constexpr (SEG >= 64) v = v + xor_lane<32>(v);
+  if constexpr (SEG >= 32) v = v + xor_lane<16>(v);
+  if constexpr (SEG >= 16) v = v + xor_lane<8>(v);
+  if constexpr (SEG >= 8) v = v + xor_lane<4>(v);
+  if constexpr (SEG >= 4) v = v + xor_lane<2>(v);
+  return v + xor_lane<1>(v);
+}
+
+template <int V, int SEG>
+__device__ __forceinline__ int vidx(int lane) {
+  int idx = 0, cnt = V;
+#pragma unroll
+  for (int d = SEG / 2; d >= 1; d >>= 1)
+    if (cnt > 1) {
+      cnt /= 2;
+      if (lane & d) idx += cnt;
+    }
+  return idx;
+}
+
+template <int V, int SEG>
+__device__ __forceinline__ bool holder(int lane) {
+  int cnt = V;
+  bool ok = true;
+#pragma unroll
+  for (int d = SEG / 2; d >= 1; d >>= 1) {
+    if (cnt > 1)
+      cnt /= 2;
+    else if (lane & d)
+      ok = false;
+  }
+  return ok;
+}
+
+// Stage MT activation rows (nb q8_K blocks each) into LDS, one 304-byte slot per
+// block: the 256 values and 16 group sums (raw bytes 4..291, eighteen 16-byte
+// chunks) at 0, d at 288.  All 256 threads copy.
 template <int MT>
-void launch_m(int fmt, int R, const uint8_t* W, const uint8_t* Xq, float* Y, int64_t N, int nb,
-              hipStream_t st) {
-  switch (R) {
-    case 8: if constexpr (MT * 8 <= 32) { launch_one<MT, 8>(fmt, W, Xq, Y, N, nb, st); return; }
-      [[fallthrough]];
-    case 4: if constexpr (MT * 4 <= 32) { launch_one<MT, 4>(fmt, W, Xq, Y, N, nb, st); return; }
-      [[fallthrough]];
-    case 2: launch_one<MT, 2>(fmt, W, Xq, Y, N, nb, st); return;
-    default: launch_one<MT, 1>(fmt, W, Xq, Y, N, nb, st); return;
+__device__ __forceinline__ void stage_x(uint8_t* xs, const uint8_t* __restrict__ Xq, int M,
+                                        int nb) {
+  const int per_row = nb * 19;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int mm = m < M ? m : M - 1;  // rows past M: a copy of a valid row, never stored
+    const uint8_t* src = Xq + (int64_t)mm * nb * kQ8KBytes;
+    uint8_t* dst = xs + m * nb * kXS;
+    for (int t = threadIdx.x; t < per_row; t += 256) {
+      const int b = t / 19, k = t - b * 19;
+      if (k < 18) {
+        const u32x4 v = ld16(src + b * kQ8KBytes + 4 + 16 * k);
+        *reinterpret_cast<uint4*>(dst + b * kXS + 16 * k) = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst + b * kXS + 288) = ld4(src + b * kQ8KBytes);
+      }
+    }
+  }
+}
+
+// Activation fragment of block b, row m: two 32-byte runs of values at byte
+// offsets qoff and qoff2, the dwords of group sums at soff and soff2 (offsets
+// into the 32 bytes of sums), and d.
+struct XFrag {
+  u32x4 a0, a1, b0, b1;
+  uint32_t s0, s1;
+  float d;
+};
+
+template <bool XLDS>
+__device__ __forceinline__ XFrag x_frag(const uint8_t* xs, const uint8_t* __restrict__ Xq, int nb,
+                                        int m, int b, int qoff, int qoff2, int soff, int soff2) {
+  XFrag f;
+  if constexpr (XLDS) {
+    const uint8_t* p = xs + (m * nb + b) * kXS;
+    const uint4 a0 = *reinterpret_cast<const uint4*>(p + qoff);
+    const uint4 a1 = *reinterpret_cast<const uint4*>(p + qoff + 16);
+    const uint4 b0 = *reinterpret_cast<const uint4*>(p + qoff2);
+    const uint4 b1 = *reinterpret_cast<const uint4*>(p + qoff2 + 16);
+    f.a0 = {a0.x, a0.y, a0.z, a0.w};
+    f.a1 = {a1.x, a1.y, a1.z, a1.w};
+    f.b0 = {b0.x, b0.y, b0.z, b0.w};
+    f.b1 = {b1.x, b1.y, b1.z, b1.w};
+    f.s0 = *reinterpret_cast<const uint32_t*>(p + 256 + soff);
+    f.s1 = *reinterpret_cast<const uint32_t*>(p + 256 + soff2);
+    f.d = *reinterpret_cast<const float*>(p + 288);
+  } else {
+    const uint8_t* p = Xq + ((int64_t)m * nb + b) * kQ8KBytes;
+    f.a0 = ld16(p + 4 + qoff);
+    f.a1 = ld16(p + 4 + qoff + 16);
+    f.b0 = ld16(p + 4 + qoff2);
+    f.b1 = ld16(p + 4 + qoff2 + 16);
+    f.s0 = ld4(p + 260 + soff);
+    f.s1 = ld4(p + 260 + soff2);
+    f.d = *reinterpret_cast<const float*>(p);
+  }
+  return f;
+}
+
+__device__ __forceinline__ int dot16(const uint32_t* w, const u32x4& x, int s) {
+  s = dot4(w[0], x.x, s);
+  s = dot4(w[1], x.y, s);
+  s = dot4(w[2], x.z, s);
+  return dot4(w[3], x.w, s);
+}
+
+// ---------------------------------------------------------------- kernel
+// FMT: 12 q4_K, 14 q6_K.  MT activation rows computed (>= M).  IT rounds of 16
+// blocks loaded together.  P rows per round.  XLDS: activations staged in LDS.
+template <int FMT, int MT, int IT, int P, bool XLDS>
+__global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __restrict__ W,
+                                                   const uint8_t* __restrict__ Xq,
+                                                   float* __restrict__ Y, int64_t N, int nb, int M) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+  constexpr int SEG = 64 / P;  // lanes that share a row
+  constexpr int BPR = 16 / P;  // blocks of a row per round when P > 1
+  constexpr int BB = FMT == 12 ? kQ4KBytes : kQ6KBytes;
+  const int lane = lane_id();
+  const int wave = XLDS ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  constexpr int WPB = XLDS ? 4 : 1;  // waves per workgroup
+  const int G = lane >> 2, c = lane & 3;
+  const int prow = P > 1 ? G / BPR : 0;
+  const int bl0 = P > 1 ? G % BPR : G;
+  const int64_t n0 = ((int64_t)blockIdx.x * WPB + wave) * P;  // first row of this wave
+  const bool active = n0 < N;                                 // wave-uniform
+  int64_t n = n0 + prow;
+  if (n >= N) n = N - 1;  // tail rows: a valid row, never stored
+  const uint8_t* wrow = W + n * nb * BB;
+
+  // per-lane constants
+  // q4_K lane c = group g: values 64g..64g+63 (sub-blocks 2g, 2g+1), sums 4g..4g+3.
+  // q6_K lane c = (hh, p) = (c/2, c%2): quarters p and p+2 of half hh, i.e. values
+  //   128hh+32p.. and 128hh+32p+64.., sums 8hh+2p, +1 and 8hh+2p+4, +5.
+  const int qoff = FMT == 12 ? 64 * c : 128 * (c >> 1) + 32 * (c & 1);
+  const int qoff2 = FMT == 12 ? 64 * c + 32 : qoff + 64;
+  const int soff = FMT == 12 ? 8 * c : 2 * (8 * (c >> 1) + 2 * (c & 1));
+  const int soff2 = soff + (FMT == 12 ? 4 : 8);
+
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+
+  bool staged = false;
+  for (int s0 = 0; s0 < nb; s0 += 16 * IT) {
+    // ---- 1. every weight load of these IT rounds
+    uint32_t wq[IT][8], wh[IT][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
+    uint32_t hd[IT][4];             // q4_K: block header; q6_K: [0] scale bytes, [1] d
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < IT; ++i) {
+        const int b = s0 + bl0 + 16 * i;
+        if (b < nb) {
+          const uint8_t* wb = wrow + b * BB;
+          if constexpr (FMT == 12) {
+            const uint4 h = ld16a(wb);
+            const uint4 q0 = ld16a(wb + 16 + 32 * c), q1 = ld16a(wb + 32 + 32 * c);
+            hd[i][0] = h.x; hd[i][1] = h.y; hd[i][2] = h.z; hd[i][3] = h.w;
+            wq[i][0] = q0.x; wq[i][1] = q0.y; wq[i][2] = q0.z; wq[i][3] = q0.w;
+            wq[i][4] = q1.x; wq[i][5] = q1.y; wq[i][6] = q1.z; wq[i][7] = q1.w;
+          } else {
+            const int hh = c >> 1, p = c & 1;
+            ld32_a2(wb + 64 * hh + 32 * p, wq[i]);
+            ld32_a2(wb + 128 + 32 * hh, wh[i]);
+            hd[i][0] = (uint32_t)ld2(wb + 192 + 8 * hh + 2 * p) |
+                       ((uint32_t)ld2(wb + 196 + 8 * hh + 2 * p) << 16);
+            hd[i][1] = ld2(wb + 208);
+          }
+        }
+      }
+    }
+    // ---- 2. activations into LDS, once (whole workgroup, before any early exit)
+    if constexpr (XLDS) {
+      if (!staged) {
+        stage_x<MT>(xs, Xq, M, nb);
+        __syncthreads();
+        staged = true;
+      }
+    }
+    if (!active) return;  // wave-uniform; after the barrier
+
+    // ---- 3. arithmetic, block by block
+#pragma unroll
+    for (int i = 0; i < IT; ++i) {
+      const int b = s0 + bl0 + 16 * i;
+      if (b >= nb) break;
+      if constexpr (FMT == 12) {
+        // scales and mins of sub-blocks 2c and 2c+1 as byte pairs
+        const uint32_t h1 = hd[i][1], h2 = hd[i][2], h3 = hd[i][3];
+        const int s = 16 * (c & 1);
+        uint32_t scp, mnp;
+        if (c < 2) {
+          scp = (h1 >> s) & 0x3f3fu;
+          mnp = (h2 >> s) & 0x3f3fu;
+        } else {
+          scp = ((h3 >> s) & 0x0f0fu) | ((h1 >> (s + 2)) & 0x3030u);
+          mnp = ((h3 >> (s + 4)) & 0x0f0fu) | ((h2 >> (s + 2)) & 0x3030u);
+        }
+        const int sc0 = (int)(scp & 0xffu), sc1 = (int)(scp >> 8);
+        const uint32_t m0 = (mnp & 0xffu) * 0x10001u, m1 = (mnp >> 8) * 0x10001u;
+        const float d = f16_to_f32(hd[i][0]), dmin = f16_to_f32(hd[i][0] >> 16);
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          lo[k] = lo_nib(wq[i][k]);
+          hi[k] = hi_nib(wq[i][k]);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const XFrag x = x_frag<XLDS>(xs, Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
+          const int dl = dot16(lo + 4, x.a1, dot16(lo, x.a0, 0));
+          const int dh = dot16(hi + 4, x.b1, dot16(hi, x.b0, 0));
+          const int isc = __mul24(sc0, dl) + __mul24(sc1, dh);
+          const int imn = dot2(x.s0, m0, dot2(x.s1, m1, 0));
+          float t = d * (float)isc;
+          t = fmaf(-dmin, (float)imn, t);
+          acc[m] = fmaf(x.d, t, acc[m]);
+        }
+      } else {
+        const int p = c & 1;
+        const uint32_t sp = hd[i][0];  // bytes 0,1: quarter p; bytes 2,3: quarter p+2
+        const float d = f16_to_f32(hd[i][1]);
+        uint32_t qa[8], qb[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          qa[k] = q6k_quad(wq[i][k], wh[i][k], p);
+          qb[k] = q6k_quad(wq[i][k], wh[i][k], p + 2);
+        }
+        const int e0 = (int)(int8_t)(sp & 0xffu), e1 = (int)(int8_t)((sp >> 8) & 0xffu);
+        const int e2 = (int)(int8_t)((sp >> 16) & 0xffu), e3 = (int)(int8_t)(sp >> 24);
+        const uint32_t spa = (uint32_t)(e0 & 0xffff) | ((uint32_t)e1 << 16);
+        const uint32_t spb = (uint32_t)(e2 & 0xffff) | ((uint32_t)e3 << 16);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const XFrag x = x_frag<XLDS>(xs, Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
+          // sum_j sc_j * (dot_j - 32 * sum_j) over the lane's four 16-weight sub-blocks
+          int isc = __mul24(e0, dot16(qa, x.a0, 0)) + __mul24(e1, dot16(qa + 4, x.a1, 0)) +
+                    __mul24(e2, dot16(qb, x.b0, 0)) + __mul24(e3, dot16(qb + 4, x.b1, 0));
+          isc -= 32 * dot2(x.s0, spa, dot2(x.s1, spb, 0));
+          acc[m] = fmaf(x.d, d * (float)isc, acc[m]);
+        }
+      }
+    }
+  }
+
+  // ---- 4. lane reduction and store
+  const int64_t nn = n0 + prow;
+  if constexpr (MT <= SEG) {
+    float v[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) v[m] = acc[m];
+    seg_reduce<MT, SEG>(v, lane);
+    if (holder<MT, SEG>(lane)) {
+      const int m = vidx<MT, SEG>(lane);
+      if (m < M && nn < N) Y[(int64_t)m * N + nn] = v[0];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float v = seg_all<SEG>(acc[m]);
+      if ((lane & (SEG - 1)) == 0 && m < M && nn < N) Y[(int64_t)m * N + nn] = v;
+    }
+  }
+}
+
+template <int FMT, int MT, int IT, int P>
+void launch_cfg(const uint8_t* W, const uint8_t* Xq, float* Y, int64_t N, int nb, int M,
+                hipStream_t st) {
+  const int64_t waves = (N + P - 1) / P;
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, false>), dim3((uint32_t)waves), dim3(64), 0, st,
+                     W, Xq, Y, N, nb, M);
+}
+
+// The lane mapping depends on K only: P rows side by side when a row has 16/P
+// blocks, otherwise IT rounds of 16 blocks in flight together (longer rows loop
+// over groups of kMaxIT rounds).
+template <int FMT, int MT>
+void launch_mt(const uint8_t* W, const uint8_t* Xq, float* Y, int64_t N, int nb, int M,
+               hipStream_t st) {
+  if (nb == 1) return launch_cfg<FMT, MT, 1, 16>(W, Xq, Y, N, nb, M, st);
+  if (nb == 2) return launch_cfg<FMT, MT, 1, 8>(W, Xq, Y, N, nb, M, st);
+  if (nb == 4) return launch_cfg<FMT, MT, 1, 4>(W, Xq, Y, N, nb, M, st);
+  if (nb == 8) return launch_cfg<FMT, MT, 1, 2>(W, Xq, Y, N, nb, M, st);
+  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1>(W, Xq, Y, N, nb, M, st);
+  if (nb <= 32) return launch_cfg<FMT, MT, 2, 1>(W, Xq, Y, N, nb, M, st);
+  if (nb <= 48) return launch_cfg<FMT, MT, 3, 1>(W, Xq, Y, N, nb, M, st);
+  return launch_cfg<FMT, MT, kMaxIT, 1>(W, Xq, Y, N, nb, M, st);
+}
+
+template <int FMT>
+int launch_fmt(const uint8_t* W, const uint8_t* Xq, float* Y, int M, int64_t N, int nb,
+               hipStream_t st) {
+  switch (M) {
+    case 1: launch_mt<FMT, 1>(W, Xq, Y, N, nb, M, st); return 0;
+    case 2: launch_mt<FMT, 2>(W, Xq, Y, N, nb, M, st); return 0;
+    case 3:
+    case 4: launch_mt<FMT, 4>(W, Xq, Y, N, nb, M, st); return 0;
+    case 5:
+    case 6:
+    case 7:
+    case 8: launch_mt<FMT, 8>(W, Xq, Y, N, nb, M, st); return 0;
+    default: return -1;
   }
 }
 
@@ -241,22 +428,9 @@ void launch_m(int fmt, int R, const uint8_t* W, const uint8_t* Xq, float* Y, int
 int launch_gemv(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int M, int64_t N,
                 int64_t K, hipStream_t st) {
   const int64_t nb = K / kQK;
-  if (nb > 0x7fffffffLL) return -1;
-  const int R = pick_rows(M, N);
-  const int64_t waves = (N + R - 1) / R;
-  if ((waves + 3) / 4 > 0x7fffffffLL) return -1;
-  switch (M) {
-    case 1: launch_m<1>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    case 2: launch_m<2>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    case 3: launch_m<3>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    case 4: launch_m<4>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    case 5: launch_m<5>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    case 6: launch_m<6>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    case 7: launch_m<7>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    case 8: launch_m<8>(fmt, R, W, Xq, Y, N, (int)nb, st); break;
-    default: return -1;
-  }
-  return 0;
+  if (nb > 0x7fffffffLL / kXS || N > 0x7fffffffLL) return -1;
+  return fmt == 12 ? launch_fmt<12>(W, Xq, Y, M, N, (int)nb, st)
+                   : launch_fmt<14>(W, Xq, Y, M, N, (int)nb, st);
 }
 
 }  // namespace gemmq

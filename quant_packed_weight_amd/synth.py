@@ -14,7 +14,9 @@ available here; these stand in for them):
   activations: f32 N(0,1); optionally 4 distinct outlier columns (the same in
         every row) multiplied by 20.
 Draw order per workload: every matrix's weight bytes in list order, then the
-activations for each M in order, one tensor per distinct K in order of first use.
+activations for each M in order, one tensor per distinct input of the layer
+(attention input, attention output, MLP input, MLP activation, final hidden
+state) in order of first use.
 """
 from __future__ import annotations
 
@@ -36,6 +38,7 @@ class Matrix:
     N: int  # output rows
     K: int  # inputs
     fmt: int
+    inp: str = "x"  # name of the activation tensor this matrix reads
 
     @property
     def nbytes(self) -> int:
@@ -51,27 +54,30 @@ class Workload:
     outliers: bool = True
     doc: str = ""
 
-    def ks(self):
+    def inputs(self):
+        """Distinct activation tensors in order of first use: [(name, K)]."""
         out = []
         for m in self.matrices:
-            if m.K not in out:
-                out.append(m.K)
+            if (m.inp, m.K) not in out:
+                out.append((m.inp, m.K))
         return out
 
 
 def _qwen3(hidden, heads_dim, kv_dim, inter, fmts, head=None):
     q4, q6 = FMT_Q4K, FMT_Q6K
+    # q/k/v read the attention input, o the attention output, gate/up the MLP
+    # input, down the gated MLP activation, the head the final hidden state
     mats = [
-        Matrix("q_proj", heads_dim, hidden, fmts.get("q", q4)),
-        Matrix("k_proj", kv_dim, hidden, fmts.get("k", q4)),
-        Matrix("v_proj", kv_dim, hidden, fmts.get("v", q4)),
-        Matrix("o_proj", hidden, heads_dim, fmts.get("o", q4)),
-        Matrix("gate_proj", inter, hidden, fmts.get("gate", q4)),
-        Matrix("up_proj", inter, hidden, fmts.get("up", q4)),
-        Matrix("down_proj", hidden, inter, fmts.get("down", q4)),
+        Matrix("q_proj", heads_dim, hidden, fmts.get("q", q4), "attn_in"),
+        Matrix("k_proj", kv_dim, hidden, fmts.get("k", q4), "attn_in"),
+        Matrix("v_proj", kv_dim, hidden, fmts.get("v", q4), "attn_in"),
+        Matrix("o_proj", hidden, heads_dim, fmts.get("o", q4), "attn_out"),
+        Matrix("gate_proj", inter, hidden, fmts.get("gate", q4), "mlp_in"),
+        Matrix("up_proj", inter, hidden, fmts.get("up", q4), "mlp_in"),
+        Matrix("down_proj", hidden, inter, fmts.get("down", q4), "mlp_act"),
     ]
     if head:
-        mats.append(Matrix("output", head, hidden, fmts.get("head", q4)))
+        mats.append(Matrix("output", head, hidden, fmts.get("head", q4), "final"))
     return tuple(mats)
 
 
@@ -132,7 +138,7 @@ def make_activations(rng: np.random.Generator, M: int, K: int, outliers: bool) -
 class Generated:
     workload: Workload
     weights: dict = field(default_factory=dict)      # matrix name -> uint8 [N, bytes]
-    activations: dict = field(default_factory=dict)  # (M, K) -> f32 [M, K]
+    activations: dict = field(default_factory=dict)  # (M, input name) -> f32 [M, K]
 
 
 def generate(name: str, Ms=None, with_weights: bool = True) -> Generated:
@@ -148,8 +154,8 @@ def generate(name: str, Ms=None, with_weights: bool = True) -> Generated:
         else:
             del w
     for M in wl.Ms:
-        for K in wl.ks():
+        for inp, K in wl.inputs():
             x = make_activations(rng, M, K, wl.outliers)
             if Ms is None or M in Ms:
-                g.activations[(M, K)] = x
+                g.activations[(M, inp)] = x
     return g

@@ -39,23 +39,23 @@ def test_workload(dev, orc, name):
         rows = _rows(M, wl.seed * 1000 + M)
         xq_dev = {}
         xq_host = {}
-        for K in wl.ks():
-            x = g.activations[(M, K)]
+        for inp, K in wl.inputs():
+            x = g.activations[(M, inp)]
             xd = to_dev(x)
-            xq_dev[K] = gq.quantize_q8K(xd)
-            got = xq_dev[K][torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
+            xq_dev[inp] = gq.quantize_q8K(xd)
+            got = xq_dev[inp][torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
             want = orc.quantize_q8K(x[rows])
-            assert np.array_equal(got, want), (name, M, K)
-            xq_host[K] = want
+            assert np.array_equal(got, want), (name, M, inp)
+            xq_host[inp] = want
             del xd
         for mat in wl.matrices:
             log("  M=%d %s %dx%d fmt=%d" % (M, mat.name, mat.N, mat.K, mat.fmt))
             W = g.weights[mat.name]
             Wd = to_dev(W)
-            y = gq.gemm(mat.fmt, Wd, xq_dev[mat.K], M, mat.N, mat.K)
+            y = gq.gemm(mat.fmt, Wd, xq_dev[mat.inp], M, mat.N, mat.K)
             ys = y[torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
-            yo = orc.gemm_int(mat.fmt, W, xq_host[mat.K], len(rows), mat.N, mat.K)
-            _, S = orc.gemm_dequant(mat.fmt, W, xq_host[mat.K], len(rows), mat.N, mat.K)
+            yo = orc.gemm_int(mat.fmt, W, xq_host[mat.inp], len(rows), mat.N, mat.K)
+            _, S = orc.gemm_dequant(mat.fmt, W, xq_host[mat.inp], len(rows), mat.N, mat.K)
             worst = assert_within(ys, yo, S, "%s M=%d %s" % (name, M, mat.name))
             log("    worst |err|/S = %.3g" % worst)
             del Wd, y
