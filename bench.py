@@ -187,6 +187,30 @@ def kernel_rates(layer, M, steps, copies, stream):
     return per
 
 
+def profiled_traffic(fam, wl):
+    """HBM bytes per launch of kernel family `fam` ("gemv" / "gemm") on this
+    workload, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (profiles/traffic.json, FETCH scaled by the cold-copy factor).  None when
+    the kernel sources changed since those counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)[fam]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for src in t["sources"]:
+        with open(os.path.join(ROOT, "quant_packed_weight_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    per = t["per_matrix"]
+    if h.hexdigest() != t["source_sha256"] or any(m.name not in per for m in wl.matrices):
+        return None
+    tot = sum(per[m.name]["read_bytes"] + per[m.name]["write_bytes"] for m in wl.matrices)
+    return round(tot / len(wl.matrices))
+
+
 def cpu_baseline(wl, gen, M1, M2, seconds):
     """The oracle, single-threaded, on a bounded sample of the same workload."""
     import numpy as np
@@ -282,8 +306,10 @@ def main():
             algo = sum(m.nbytes * len(per[m.name]) for m in wl.matrices)
             ach = algo / tot_t / 1e9
             return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                    "kernel": "gemv_q4K_kernel", "launches": n_l,
+                    "frac": round(ach / HBM_PEAK_GBS, 4),
+                    "traffic": profiled_traffic("gemv", wl) if a.workload == "qwen3-8b-q4K" else None,
+                    "algo_bytes_per_launch": round(wbytes / len(wl.matrices)),
+                    "kernel": "gemv_kernel", "launches": n_l,
                     "avg_launch_us": round(tot_t / n_l * 1e6, 2),
                     "per_matrix_GBs": {m.name: round(m.nbytes * len(per[m.name]) /
                                                      sum(per[m.name]) / 1e9, 1)
@@ -291,7 +317,8 @@ def main():
         algo = sum(2 * M * m.N * m.K * len(per[m.name]) for m in wl.matrices)
         ach = algo / tot_t / 1e12
         return {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4), "traffic": None,
+                "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
+                "traffic": profiled_traffic("gemm", wl) if a.workload == "qwen3-8b-q4K" else None,
                 "kernel": "gemm_kernel<12>", "launches": n_l,
                 "avg_launch_us": round(tot_t / n_l * 1e6, 2),
                 "per_matrix_TOPs": {m.name: round(2 * M * m.N * m.K * len(per[m.name]) /
