@@ -4,25 +4,30 @@
 // activation rows and applies the block scales on the way (molayo article
 // "PocketLLM: 단일 가속기에서 대규모 언어 모델 실행", status row "src/ -- C++
 // engine": row tile of 8 activation rows; q4_K 8-column panels).  On gfx950
-// the dense contraction goes to v_mfma_i32_32x32x32_i8, and the design is set
-// by keeping the vector ALU off the critical path:
+// the dense contraction goes to v_mfma_i32_32x32x32_i8, and the design keeps
+// the vector ALU and the memory latency off the critical path:
 //
 //  * The sub-block scale is folded into the weight operand.  For q4_K,
 //    sc = 8a + b with a, b in 0..7, so sc*q = 8(a*q) + b*q with both products
 //    in 0..105: two int8 planes whose MFMA sums, combined as 8*A + B, give
-//    I_sc = sum_j sc_j * dot_j for the whole 256-weight super-block in int32.
+//    I_sc = sum_j sc_j * dot_j for a whole 256-weight super-block in int32.
 //    For q6_K, v = sc*(q-32) in -4064..4096 splits as 128*hi + lo with
 //    lo = v & 127 and hi = v >> 7 in -32..32.
-//  * The q4_K min term I_min = sum_j m_j * (bsum_2j + bsum_2j+1) is a K=16
-//    contraction of the activation group sums with the mins; the int16 sums are
-//    split into int8 planes (bsum = 128*bh + bl) and it runs as two more MFMAs.
+//  * The q4_K min term I_min = sum_g m_{g/2} * bsum_g is a K = 16 contraction
+//    of the activation group sums (|bsum| <= 2032) with the mins (<= 63): both
+//    are exact in f16 and every partial sum is below 2^24, so one
+//    v_mfma_f32_32x32x16_f16 gives it exactly, already in f32.
 //  * One f32 epilogue per super-block and output:
 //    y += d_x * (d * I_sc - dmin * I_min)   (q6_K: y += d_x * d * I_sc).
 //
-// Work decomposition: a 256-thread workgroup computes a 128 (M) x 64 (N) tile.
-// Per super-block it stages the activation tile (int8 values, d_x, sum planes)
-// and the weight tile, unpacked once into the two int8 planes, in LDS; then each
-// of the four waves runs a 64 x 32 sub-tile (two 32x32 MFMA tiles) from LDS.
+// Work decomposition: a 256-thread workgroup computes a 128 (M) x 64 (N) tile;
+// each of its four waves a 64 x 32 sub-tile (two 32x32 MFMA tiles).  Per
+// super-block the workgroup stages the activation tile (int8 values, d_x, f16
+// group sums) and the weight tile -- unpacked once into the two int8 planes,
+// with d, dmin and f16 mins -- in LDS.  The global loads of super-block b+1
+// are issued before the MFMAs of super-block b and held in registers; one
+// 75 KB stage lets two workgroups share a CU, so one computes while the other
+// stages.
 // Every output's arithmetic depends only on its own row and column, so any
 // subset of rows gives identical bits.
 #include "device.h"
@@ -30,25 +35,31 @@
 
 namespace gemmq {
 
+namespace {
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;       // activation rows per workgroup
-constexpr int kBN = 64;        // weight rows (output columns) per workgroup
-constexpr int kRow = 256 + 16; // LDS row stride of an int8 K-row (padded)
+constexpr int kBM = 128;        // activation rows per workgroup
+constexpr int kBN = 64;         // weight rows (output columns) per workgroup
+constexpr int kRow = 256 + 16;  // LDS stride of one int8 K-row (padded against bank conflicts)
 
-// LDS map (bytes)
-constexpr int kOffA = 0;                       // [kBM][kRow] activation int8
-constexpr int kOffPa = kOffA + kBM * kRow;     // [kBN][kRow] weight plane A (hi)
-constexpr int kOffPb = kOffPa + kBN * kRow;    // [kBN][kRow] weight plane B (lo)
-constexpr int kOffBs = kOffPb + kBN * kRow;    // [kBM][32]   sum planes bl | bh
-constexpr int kOffDx = kOffBs + kBM * 32;      // [kBM] f32   d_x
-constexpr int kOffD = kOffDx + kBM * 4;        // [kBN] f32   d
-constexpr int kOffDm = kOffD + kBN * 4;        // [kBN] f32   dmin
-constexpr int kOffMn = kOffDm + kBN * 4;       // [kBN][8]    mins
-constexpr int kLds = kOffMn + kBN * 8;
+// LDS map of one stage (bytes)
+constexpr int kOffA = 0;                     // [kBM][kRow] activation int8
+constexpr int kOffPa = kOffA + kBM * kRow;   // [kBN][kRow] weight plane A (weight 8 / 128)
+constexpr int kOffPb = kOffPa + kBN * kRow;  // [kBN][kRow] weight plane B
+constexpr int kOffBs = kOffPb + kBN * kRow;  // [kBM][16] f16 group sums
+constexpr int kOffDx = kOffBs + kBM * 32;    // [kBM] f32 d_x
+constexpr int kOffD = kOffDx + kBM * 4;      // [kBN] f32 d
+constexpr int kOffDm = kOffD + kBN * 4;      // [kBN] f32 dmin
+constexpr int kOffMn = kOffDm + kBN * 4;     // [kBN][16] f16 m_{t/2}, t = 0..15
+constexpr int kStage = kOffMn + kBN * 32;
+constexpr int kLds = kStage;  // one stage: two workgroups fit in a CU's 160 KB
 
 // bytes of w (each <= 15) times a (<= 7): per 16-bit half the product stays below
 // 2^16 and no byte carries into the next.
@@ -58,86 +69,101 @@ __device__ __forceinline__ uint32_t mul_bytes(uint32_t w, uint32_t a) {
   return __builtin_bit_cast(uint32_t, v * s);
 }
 
-__device__ __forceinline__ v16i mfma(v4i a, v4i b, v16i c) {
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
   return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ void st16(uint8_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   *reinterpret_cast<uint4*>(p) = make_uint4(a, b, c, d);
 }
 
-// ------------------------------------------------- staging: activation tile
+// two int16 (packed in a dword) -> two f16 (exact: |value| <= 2048)
+__device__ __forceinline__ uint32_t i16x2_to_h2(uint32_t w) {
+  const h2 v = {(_Float16)(short)(w & 0xffffu), (_Float16)(short)(w >> 16)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ------------------------------------------------- activation tile
 // thread t: row t/2, half t%2 of the 256 int8 values; half 0 also d_x, half 1
-// also the two int8 planes of the 16 group sums.
-__device__ __forceinline__ void stage_x(uint8_t* lds, const uint8_t* __restrict__ Xq, int64_t m0,
-                                        int64_t M, int nb, int b) {
-  const int t = threadIdx.x;
-  const int row = t >> 1, part = t & 1;
-  const int64_t m = m0 + row;
-  uint8_t* dstA = lds + kOffA + row * kRow + 128 * part;
-  if (m < M) {
-    const uint8_t* xb = Xq + (m * nb + b) * kQ8KBytes;
+// also the 16 group sums.
+struct XRegs {
+  u32x4 q[8];
+  uint32_t e[8];
+};
+
+// Rows past M load a copy of row M-1: MFMA rows are independent and those
+// outputs are never stored, so no branch is needed.
+__device__ __forceinline__ const uint8_t* x_row(const uint8_t* __restrict__ Xq, int64_t m0,
+                                                int64_t M, int nb) {
+  const int64_t m = m0 + (threadIdx.x >> 1);
+  return Xq + (m < M ? m : M - 1) * nb * kQ8KBytes;
+}
+
+__device__ __forceinline__ void load_x(XRegs& r, const uint8_t* xrow, int b) {
+  const int part = threadIdx.x & 1;
+  const uint8_t* xb = xrow + b * kQ8KBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4 v = ld16(xb + 4 + 128 * part + 16 * i);
-      st16(dstA + 16 * i, v.x, v.y, v.z, v.w);
-    }
-    if (part == 0) {
-      reinterpret_cast<float*>(lds + kOffDx)[row] = *reinterpret_cast<const float*>(xb);
-    } else {
-      const u32x4 s0 = ld16(xb + 260), s1 = ld16(xb + 276);
-      const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-      uint32_t bl[4], bh[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t u0 = sw[2 * k], u1 = sw[2 * k + 1];  // sums 4k..4k+3
-        bl[k] = (u0 & 0x7fu) | (((u0 >> 16) & 0x7fu) << 8) | ((u1 & 0x7fu) << 16) |
-                (((u1 >> 16) & 0x7fu) << 24);
-        const uint32_t h0 = (uint32_t)((int)(int16_t)(u0 & 0xffffu) >> 7) & 0xffu;
-        const uint32_t h1 = (uint32_t)((int)u0 >> 23) & 0xffu;
-        const uint32_t h2 = (uint32_t)((int)(int16_t)(u1 & 0xffffu) >> 7) & 0xffu;
-        const uint32_t h3 = (uint32_t)((int)u1 >> 23) & 0xffu;
-        bh[k] = h0 | (h1 << 8) | (h2 << 16) | (h3 << 24);
-      }
-      uint8_t* dstB = lds + kOffBs + row * 32;
-      st16(dstB, bl[0], bl[1], bl[2], bl[3]);
-      st16(dstB + 16, bh[0], bh[1], bh[2], bh[3]);
-    }
+  for (int i = 0; i < 8; ++i) r.q[i] = ld16(xb + 4 + 128 * part + 16 * i);
+  if (part == 0) {
+    r.e[0] = ld4(xb);
   } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) st16(dstA + 16 * i, 0, 0, 0, 0);
-    if (part == 0) {
-      reinterpret_cast<float*>(lds + kOffDx)[row] = 0.0f;
-    } else {
-      st16(lds + kOffBs + row * 32, 0, 0, 0, 0);
-      st16(lds + kOffBs + row * 32 + 16, 0, 0, 0, 0);
-    }
+    const u32x4 s0 = ld16(xb + 260), s1 = ld16(xb + 276);
+    r.e[0] = s0.x; r.e[1] = s0.y; r.e[2] = s0.z; r.e[3] = s0.w;
+    r.e[4] = s1.x; r.e[5] = s1.y; r.e[6] = s1.z; r.e[7] = s1.w;
   }
 }
 
-// ------------------------------------------------- staging: q4_K weight tile
+__device__ __forceinline__ void store_x(uint8_t* st, const XRegs& r) {
+  const int t = threadIdx.x, row = t >> 1, part = t & 1;
+  uint8_t* a = st + kOffA + row * kRow + 128 * part;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) st16(a + 16 * i, r.q[i].x, r.q[i].y, r.q[i].z, r.q[i].w);
+  if (part == 0) {
+    reinterpret_cast<uint32_t*>(st + kOffDx)[row] = r.e[0];
+  } else {
+    uint8_t* s = st + kOffBs + row * 32;
+    st16(s, i16x2_to_h2(r.e[0]), i16x2_to_h2(r.e[1]), i16x2_to_h2(r.e[2]), i16x2_to_h2(r.e[3]));
+    st16(s + 16, i16x2_to_h2(r.e[4]), i16x2_to_h2(r.e[5]), i16x2_to_h2(r.e[6]),
+         i16x2_to_h2(r.e[7]));
+  }
+}
+
+// ------------------------------------------------- q4_K weight tile
 // thread t: column t/4, 64-weight group g = t%4 (qs bytes 32g..32g+31, holding
 // sub-block 2g in the low nibbles and 2g+1 in the high nibbles).
-__device__ __forceinline__ void stage_w_q4K(uint8_t* lds, const uint8_t* __restrict__ W,
-                                            int64_t n0, int64_t N, int nb, int b) {
-  const int t = threadIdx.x;
-  const int col = t >> 2, g = t & 3;
-  const int64_t n = n0 + col;
-  uint4 hd = make_uint4(0, 0, 0, 0), q0 = hd, q1 = hd;
-  if (n < N) {
-    const uint8_t* wb = W + (n * nb + b) * kQ4KBytes;
-    hd = ld16a(wb);
-    q0 = ld16a(wb + 16 + 32 * g);
-    q1 = ld16a(wb + 32 + 32 * g);
-  }
-  const Q4KScales s = q4k_scales(hd.y, hd.z, hd.w);
+struct W4Regs {
+  uint4 hd, q0, q1;
+};
+
+// Columns past N load a copy of column N-1 (never stored).
+template <int BB>
+__device__ __forceinline__ const uint8_t* w_row(const uint8_t* __restrict__ W, int64_t n0,
+                                                int64_t N, int nb) {
+  const int64_t n = n0 + (threadIdx.x >> 2);
+  return W + (n < N ? n : N - 1) * nb * BB;
+}
+
+__device__ __forceinline__ void load_w(W4Regs& r, const uint8_t* wrow, int b) {
+  const int g = threadIdx.x & 3;
+  const uint8_t* wb = wrow + b * kQ4KBytes;
+  r.hd = ld16a(wb);
+  r.q0 = ld16a(wb + 16 + 32 * g);
+  r.q1 = ld16a(wb + 32 + 32 * g);
+}
+
+__device__ __forceinline__ void store_w(uint8_t* st, const W4Regs& r) {
+  const int t = threadIdx.x, col = t >> 2, g = t & 3;
+  const Q4KScales s = q4k_scales(r.hd.y, r.hd.z, r.hd.w);
   const uint32_t scw = g >= 2 ? s.sc_hi : s.sc_lo;
   const uint32_t mnw = g >= 2 ? s.mn_hi : s.mn_lo;
   const int sh = 16 * (g & 1);
   const uint32_t sc0 = (scw >> sh) & 0xffu, sc1 = (scw >> (sh + 8)) & 0xffu;
   const uint32_t mn0 = (mnw >> sh) & 0xffu, mn1 = (mnw >> (sh + 8)) & 0xffu;
   const uint32_t a0 = sc0 >> 3, b0 = sc0 & 7u, a1 = sc1 >> 3, b1 = sc1 & 7u;
-  const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+  const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
   uint32_t pal[8], pah[8], pbl[8], pbh[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
@@ -147,8 +173,8 @@ __device__ __forceinline__ void stage_w_q4K(uint8_t* lds, const uint8_t* __restr
     pah[k] = mul_bytes(hi, a1);
     pbh[k] = mul_bytes(hi, b1);
   }
-  uint8_t* pa = lds + kOffPa + col * kRow + 64 * g;
-  uint8_t* pb = lds + kOffPb + col * kRow + 64 * g;
+  uint8_t* pa = st + kOffPa + col * kRow + 64 * g;
+  uint8_t* pb = st + kOffPb + col * kRow + 64 * g;
   st16(pa, pal[0], pal[1], pal[2], pal[3]);
   st16(pa + 16, pal[4], pal[5], pal[6], pal[7]);
   st16(pa + 32, pah[0], pah[1], pah[2], pah[3]);
@@ -157,19 +183,49 @@ __device__ __forceinline__ void stage_w_q4K(uint8_t* lds, const uint8_t* __restr
   st16(pb + 16, pbl[4], pbl[5], pbl[6], pbl[7]);
   st16(pb + 32, pbh[0], pbh[1], pbh[2], pbh[3]);
   st16(pb + 48, pbh[4], pbh[5], pbh[6], pbh[7]);
-  *reinterpret_cast<uint16_t*>(lds + kOffMn + col * 8 + 2 * g) = (uint16_t)(mn0 | (mn1 << 8));
+  // mins as f16, each twice: entries 4g..4g+3 = m_{2g}, m_{2g}, m_{2g+1}, m_{2g+1}
+  const h2 f0 = {(_Float16)(float)mn0, (_Float16)(float)mn0};
+  const h2 f1 = {(_Float16)(float)mn1, (_Float16)(float)mn1};
+  *reinterpret_cast<uint2*>(st + kOffMn + col * 32 + 8 * g) =
+      make_uint2(__builtin_bit_cast(uint32_t, f0), __builtin_bit_cast(uint32_t, f1));
   if (g == 0) {
-    reinterpret_cast<float*>(lds + kOffD)[col] = f16_to_f32(hd.x);
-    reinterpret_cast<float*>(lds + kOffDm)[col] = f16_to_f32(hd.x >> 16);
+    reinterpret_cast<float*>(st + kOffD)[col] = f16_to_f32(r.hd.x);
+    reinterpret_cast<float*>(st + kOffDm)[col] = f16_to_f32(r.hd.x >> 16);
   }
 }
 
-// ------------------------------------------------- staging: q6_K weight tile
+// ------------------------------------------------- q6_K weight tile
 // thread t: column t/4, part p4 = t%4 -> half hh = p4/2, quarters q = p4%2 (low
 // nibbles of ql bytes 64hh+32q..) and q+2 (their high nibbles).  Plane A gets
 // hi = v >> 7, plane B gets lo = v & 127, v = sc * (quant - 32).
+struct W6Regs {
+  uint32_t ql[8], qh[8];
+  uint32_t sc, d;
+};
+
+// 32 bytes at a 2-byte-aligned address: the dword-aligned 36-byte span that
+// covers them (never past p + 34), shifted into place.
+__device__ __forceinline__ void ld32_a2(const uint8_t* p, uint32_t (&o)[8]) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(a & ~uintptr_t(3));
+  const u32x4 x0 = ld16(base), x1 = ld16(base + 16);
+  const uint32_t raw[9] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w, ld4(base + 32)};
+  const uint32_t sh = (uint32_t)(a & 3u);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
+}
+
+__device__ __forceinline__ void load_w(W6Regs& r, const uint8_t* wrow, int b) {
+  const int p4 = threadIdx.x & 3, hh = p4 >> 1, q = p4 & 1;
+  const uint8_t* wb = wrow + b * kQ6KBytes;
+  ld32_a2(wb + 64 * hh + 32 * q, r.ql);
+  ld32_a2(wb + 128 + 32 * hh, r.qh);
+  r.sc = (uint32_t)ld2(wb + 192 + 8 * hh + 2 * q) | ((uint32_t)ld2(wb + 196 + 8 * hh + 2 * q) << 16);
+  r.d = ld2(wb + 208);
+}
+
+// e holds bytes 0 and 2 as int16 lanes, o bytes 1 and 3: pack the plane bytes
 __device__ __forceinline__ uint32_t q6_pack_plane(uint32_t e, uint32_t o, bool hi) {
-  // e holds bytes 0 and 2 as 16-bit lanes, o holds bytes 1 and 3
   uint32_t pe, po;
   if (hi) {
     pe = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, e) >> (i16x2){7, 7});
@@ -181,32 +237,16 @@ __device__ __forceinline__ uint32_t q6_pack_plane(uint32_t e, uint32_t o, bool h
   return (pe & 0x00ff00ffu) | ((po & 0x00ff00ffu) << 8);
 }
 
-__device__ __forceinline__ void stage_w_q6K(uint8_t* lds, const uint8_t* __restrict__ W,
-                                            int64_t n0, int64_t N, int nb, int b) {
-  const int t = threadIdx.x;
-  const int col = t >> 2, p4 = t & 3, hh = p4 >> 1, q = p4 & 1;
-  const int64_t n = n0 + col;
-  uint32_t ql[8], qh[8];
-  uint32_t scA = 0, scB = 0, dbits = 0;
-  if (n < N) {
-    const uint8_t* wb = W + (n * nb + b) * kQ6KBytes;
-    ld_dwords_a2<8>(wb + 64 * hh + 32 * q, ql);
-    ld_dwords_a2<8>(wb + 128 + 32 * hh, qh);
-    scA = ld2(wb + 192 + 8 * hh + 2 * q);      // sub-blocks 8hh+2q, +1 (quarter q)
-    scB = ld2(wb + 192 + 8 * hh + 2 * q + 4);  // sub-blocks 8hh+2q+4, +5 (quarter q+2)
-    dbits = ld2(wb + 208);
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) ql[k] = qh[k] = 0;
-  }
+__device__ __forceinline__ void store_w(uint8_t* st, const W6Regs& r) {
+  const int t = threadIdx.x, col = t >> 2, p4 = t & 3, hh = p4 >> 1, q = p4 & 1;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const int quarter = q + 2 * which;
-    const uint32_t scp = which ? scB : scA;
+    const uint32_t scp = which ? (r.sc >> 16) : r.sc;
     uint32_t hiw[8], low[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t quad = q6k_quad(ql[k], qh[k], quarter);  // 4 quants 0..63
+      const uint32_t quad = q6k_quad(r.ql[k], r.qh[k], quarter);  // 4 quants 0..63
       const int s = (int)(int8_t)((k < 4 ? scp : (scp >> 8)) & 0xffu);
       const i16x2 sv = {(short)s, (short)s};
       const i16x2 off = {32, 32};
@@ -216,14 +256,91 @@ __device__ __forceinline__ void stage_w_q6K(uint8_t* lds, const uint8_t* __restr
       hiw[k] = q6_pack_plane(eu, ou, true);
       low[k] = q6_pack_plane(eu, ou, false);
     }
-    uint8_t* pa = lds + kOffPa + col * kRow + 128 * hh + 32 * quarter;
-    uint8_t* pb = lds + kOffPb + col * kRow + 128 * hh + 32 * quarter;
+    uint8_t* pa = st + kOffPa + col * kRow + 128 * hh + 32 * quarter;
+    uint8_t* pb = st + kOffPb + col * kRow + 128 * hh + 32 * quarter;
     st16(pa, hiw[0], hiw[1], hiw[2], hiw[3]);
     st16(pa + 16, hiw[4], hiw[5], hiw[6], hiw[7]);
     st16(pb, low[0], low[1], low[2], low[3]);
     st16(pb + 16, low[4], low[5], low[6], low[7]);
   }
-  if (p4 == 0) reinterpret_cast<float*>(lds + kOffD)[col] = f16_to_f32(dbits);
+  if (p4 == 0) reinterpret_cast<float*>(st + kOffD)[col] = f16_to_f32(r.d);
+}
+
+// ------------------------------------------------- one super-block from LDS
+// 32x32 accumulator layout: lane holds column lane%32; register r holds row
+// 8*(r/4) + 4*(lane/32) + r%4.
+template <int FMT>
+__device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], int arow0, int bcol,
+                                        int hsel) {
+  // plane A over the super-block, then acc <<= 3 (q4_K) or 7 (q6_K), then
+  // plane B on top: acc = I_sc, exact in int32; two independent chains
+  v16i acc[2];
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) acc[mt] = (v16i){0};
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    const int ko = 32 * kc + 16 * hsel;
+    const v4i ba = *reinterpret_cast<const v4i*>(st + kOffPa + bcol * kRow + ko);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
+                        ba, acc[mt]);
+  }
+  constexpr int kShift = FMT == 12 ? 3 : 7;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << kShift);
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    const int ko = 32 * kc + 16 * hsel;
+    const v4i bb = *reinterpret_cast<const v4i*>(st + kOffPb + bcol * kRow + ko);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
+                        bb, acc[mt]);
+  }
+  const float dcol = reinterpret_cast<const float*>(st + kOffD)[bcol];
+  if constexpr (FMT == 12) {
+    const float mcol = reinterpret_cast<const float*>(st + kOffDm)[bcol];
+    // min term: lane half h carries group sums 8h..8h+7 against m_{(8h+t)/2}
+    const v8h mfrag = *reinterpret_cast<const v8h*>(st + kOffMn + bcol * 32 + 16 * hsel);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const v8h sfrag =
+          *reinterpret_cast<const v8h*>(st + kOffBs + (arow0 + 32 * mt) * 32 + 16 * hsel);
+      const v16f am = mfma_f16(sfrag, mfrag, (v16f){0});
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 dx = *reinterpret_cast<const float4*>(st + kOffDx +
+                                                           4 * (arow0 - (arow0 & 31) + 32 * mt +
+                                                                8 * q4 + 4 * hsel));
+        const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = 4 * q4 + s;
+          float tt = dcol * (float)acc[mt][r];
+          tt = fmaf(-mcol, am[r], tt);
+          y[mt][r] = fmaf(dxs[s], tt, y[mt][r]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 dx = *reinterpret_cast<const float4*>(st + kOffDx +
+                                                           4 * (arow0 - (arow0 & 31) + 32 * mt +
+                                                                8 * q4 + 4 * hsel));
+        const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int r = 4 * q4 + s;
+          y[mt][r] = fmaf(dxs[s], dcol * (float)acc[mt][r], y[mt][r]);
+        }
+      }
+  }
 }
 
 // ------------------------------------------------- the kernel
@@ -233,14 +350,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict_
                                                       float* __restrict__ Y, int64_t M, int64_t N,
                                                       int nb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  using WRegs = typename std::conditional<FMT == 12, W4Regs, W6Regs>::type;
   const int64_t n0 = (int64_t)blockIdx.x * kBN;
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int i = lane & 31, hsel = lane >> 5;
-  const int arow0 = wm * 64 + i;       // LDS row of M-tile 0 (M-tile 1: +32)
-  const int bcol = wn * 32 + i;        // LDS column of this lane's B fragment
+  const int arow0 = wm * 64 + i;  // LDS row of M-tile 0 (M-tile 1: +32)
+  const int bcol = wn * 32 + i;   // LDS column of this lane's B fragment
 
   float y[2][16];
 #pragma unroll
@@ -248,95 +366,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int r = 0; r < 16; ++r) y[mt][r] = 0.0f;
 
+  const uint8_t* xrow = x_row(Xq, m0, M, nb);
+  const uint8_t* wrow = w_row<FMT == 12 ? kQ4KBytes : kQ6KBytes>(W, n0, N, nb);
+  XRegs xr;
+  WRegs wr;
+  load_x(xr, xrow, 0);
+  load_w(wr, wrow, 0);
   for (int b = 0; b < nb; ++b) {
-    stage_x(lds, Xq, m0, M, nb, b);
-    if constexpr (FMT == 12)
-      stage_w_q4K(lds, W, n0, N, nb, b);
-    else
-      stage_w_q6K(lds, W, n0, N, nb, b);
+    store_x(lds, xr);
+    store_w(lds, wr);
     __syncthreads();
-
-    v4i af[2][8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int kc = 0; kc < 8; ++kc)
-        af[mt][kc] = *reinterpret_cast<const v4i*>(lds + kOffA + (arow0 + 32 * mt) * kRow +
-                                                   32 * kc + 16 * hsel);
-    v16i acc[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) acc[mt] = (v16i){0};
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const v4i bf = *reinterpret_cast<const v4i*>(lds + kOffPa + bcol * kRow + 32 * kc + 16 * hsel);
-      acc[0] = mfma(af[0][kc], bf, acc[0]);
-      acc[1] = mfma(af[1][kc], bf, acc[1]);
+    if (b + 1 < nb) {  // in flight during the MFMAs below
+      load_x(xr, xrow, b + 1);
+      load_w(wr, wrow, b + 1);
     }
-    constexpr int kPlane = FMT == 12 ? 8 : 128;  // weight of plane A
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) acc[mt] = acc[mt] * kPlane;
-#pragma unroll
-    for (int kc = 0; kc < 8; ++kc) {
-      const v4i bf = *reinterpret_cast<const v4i*>(lds + kOffPb + bcol * kRow + 32 * kc + 16 * hsel);
-      acc[0] = mfma(af[0][kc], bf, acc[0]);
-      acc[1] = mfma(af[1][kc], bf, acc[1]);
-    }
-
-    const float dcol = reinterpret_cast<const float*>(lds + kOffD)[bcol];
-    if constexpr (FMT == 12) {
-      const float mcol = reinterpret_cast<const float*>(lds + kOffDm)[bcol];
-      // B fragments of the min term: bytes t = 0..15 carry m_{t/2}; the low
-      // lane half pairs them with bl, the high half with bh.
-      const uint2 mv = *reinterpret_cast<const uint2*>(lds + kOffMn + bcol * 8);
-      const uint32_t e0 = __builtin_amdgcn_perm(mv.x, mv.x, 0x01010000u);
-      const uint32_t e1 = __builtin_amdgcn_perm(mv.x, mv.x, 0x03030202u);
-      const uint32_t e2 = __builtin_amdgcn_perm(mv.y, mv.y, 0x01010000u);
-      const uint32_t e3 = __builtin_amdgcn_perm(mv.y, mv.y, 0x03030202u);
-      const v4i mfrag = {(int)e0, (int)e1, (int)e2, (int)e3};
-      const v4i zero = {0, 0, 0, 0};
-      const v4i bml = hsel == 0 ? mfrag : zero;
-      const v4i bmh = hsel == 1 ? mfrag : zero;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const v4i amin = *reinterpret_cast<const v4i*>(lds + kOffBs + (arow0 + 32 * mt) * 32 +
-                                                       16 * hsel);
-        v16i am = mfma(amin, bmh, (v16i){0});
-        am = am * 128;
-        am = mfma(amin, bml, am);
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 dx = *reinterpret_cast<const float4*>(
-              lds + kOffDx + 4 * (wm * 64 + 32 * mt + 8 * q4 + 4 * hsel));
-          const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int r = 4 * q4 + s;
-            float tt = dcol * (float)acc[mt][r];
-            tt = fmaf(-mcol, (float)am[r], tt);
-            y[mt][r] = fmaf(dxs[s], tt, y[mt][r]);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 dx = *reinterpret_cast<const float4*>(
-              lds + kOffDx + 4 * (wm * 64 + 32 * mt + 8 * q4 + 4 * hsel));
-          const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const int r = 4 * q4 + s;
-            y[mt][r] = fmaf(dxs[s], dcol * (float)acc[mt][r], y[mt][r]);
-          }
-        }
-    }
+    compute<FMT>(lds, y, arow0, bcol, hsel);
     __syncthreads();
   }
 
-  // 32x32 accumulator layout: lane holds column lane%32; register r holds row
-  // 8*(r/4) + 4*(lane/32) + r%4.
   const int64_t col = n0 + bcol;
   if (col < N) {
 #pragma unroll
@@ -348,6 +395,8 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict_
       }
   }
 }
+
+}  // namespace
 
 int launch_gemm(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int64_t M, int64_t N,
                 int64_t K, hipStream_t st) {
