@@ -396,28 +396,305 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict_
   }
 }
 
+// ------------------------------------------------- q4_K: streamed tiles
+// The q4_K kernel streams both operands through a ring of LDS stages filled by
+// direct buffer->LDS loads (no registers held for the prefetch, no copy loop):
+//   workgroup = 4 waves, tile 64 (M) x 128 (N); wave w: all 64 rows, weight
+//   columns 32w..32w+31, unpacking its own planes (shared by its two M-tiles);
+//   stage = int8 values [64][272] | group sums [64][16] | d_x [64] |
+//   raw q4_K blocks [128][144];
+//   the two planes go to two accumulators so every activation fragment is
+//   read from LDS once.
+// The loads are issued from inline assembly: the compiler then neither sees
+// them as LDS writes (it would drain every load before each LDS read) nor
+// tracks them, and the kernel waits on vmcnt itself: a stage's loads are
+// complete once fewer than one stage's worth of later loads is outstanding.
+namespace q4s {
+constexpr int kBM = 64;
+constexpr int kBN = 128;
+constexpr int kS = 3;                       // LDS stages
+constexpr int kOffQ = 0;                    // [kBM][kRow] int8
+constexpr int kOffBs = kBM * kRow;          // [kBM][16] int16 group sums
+constexpr int kOffDx = kOffBs + kBM * 32;   // [kBM] f32 d_x
+constexpr int kOffW = kOffDx + kBM * 4;     // [kBN][144] raw weight blocks
+constexpr int kStage = kOffW + kBN * kQ4KBytes;
+constexpr int kLds = kS * kStage;
+// loads per stage issued by each wave: 16 value rows + 2 group-sum blocks + 4
+// weight chunks (waves 0 and 1 a fifth, wave 0 also the 64 d_x); waits count
+// the smallest number, which can only wait for more than needed.
+constexpr int kDma = 22;
+constexpr int kWait = kDma * (kS - 2) < 63 ? kDma * (kS - 2) : 63;  // vmcnt field is 6 bits
+}  // namespace q4s
+
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Raw buffer descriptor over [base, base + bytes): offsets at or past `bytes`
+// read as zero.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (rsrc_t){(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
+}
+
+// 64 lanes x 4 bytes: lane l's dword from buffer byte voff(l) + soff to LDS
+// byte lds + 4 l (lds wave-uniform, through M0).  The s_nop covers the one
+// wait state an M0 write needs before a load into LDS.
+__device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff),
+               "{m0}"(lds)
+               : "memory");
+}
+
+// Same with 16 bytes per lane (16-byte aligned source) to LDS byte lds + 16 l.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs),
+               "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// own LDS writes done, then the workgroup barrier; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// f32 epilogue of accumulator registers r0..r0+n-1 of one 32x32 tile:
+// y += d_x * (d * I_sc - dmin * I_min), I_sc = 8 * A + B from the two plane
+// accumulators; dx[r] is d_x of the register's row.
+template <int n>
+__device__ __forceinline__ void q4s_epilogue(const v16i& acca, const v16i& accb, const v16f& am,
+                                             const float (&dx)[16], float dcol, float mcol,
+                                             float (&y)[16], int r0) {
+#pragma unroll
+  for (int r = r0; r < r0 + n; ++r) {
+    const int isc = (int)(((uint32_t)acca[r] << 3) + (uint32_t)accb[r]);
+    float tt = dcol * (float)isc;
+    tt = fmaf(-mcol, am[r], tt);
+    y[r] = fmaf(dx[r], tt, y[r]);
+  }
+}
+
+// d_x of the 16 rows a lane's accumulator registers hold in the tile whose
+// first row in the stage is row0 - 4h: register r <-> row row0 + 8(r/4) + r%4.
+__device__ __forceinline__ void q4s_load_dx(const uint8_t* st, int row0, float (&dx)[16]) {
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const float4 v = *reinterpret_cast<const float4*>(st + q4s::kOffDx + 4 * (row0 + 8 * q4));
+    dx[4 * q4] = v.x;
+    dx[4 * q4 + 1] = v.y;
+    dx[4 * q4 + 2] = v.z;
+    dx[4 * q4 + 3] = v.w;
+  }
+}
+
+// the two weight planes of MFMA step kc from the lane's raw quant bytes
+__device__ __forceinline__ void q4s_planes(const uint4 (&q)[4], const uint32_t (&aw)[2],
+                                           const uint32_t (&bw)[2], int kc, v4i& pa, v4i& pb) {
+  const uint4 raw = q[kc >> 1];
+  const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
+  const uint32_t a = (aw[kc >> 2] >> (8 * (kc & 3))) & 0xffu;
+  const uint32_t bb = (bw[kc >> 2] >> (8 * (kc & 3))) & 0xffu;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t nib = (kc & 1) ? hi_nib(r4[k]) : lo_nib(r4[k]);
+    pa[k] = (int)mul_bytes(nib, a);
+    pb[k] = (int)mul_bytes(nib, bb);
+  }
+}
+
+// One super-block for one wave from stage `st`: lane (i, h) holds weight row
+// i of the wave's 32 and K-half h of every 32-wide MFMA step (bytes 16h..16h+15
+// of the sub-block).  The work is laid out in fenced chunks so that vector
+// work sits beside independent matrix work: M-tile 0's MFMAs of step kc run
+// beside the unpacking of step kc+1, M-tile 1's MFMAs beside tile 0's
+// epilogue; tile 1's epilogue closes the super-block.
+__device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (&y)[2][16], int i,
+                                            int h) {
+  using q4s::kOffBs;
+  using q4s::kOffQ;
+  const uint8_t* wb = st + q4s::kOffW + wrow * kQ4KBytes;
+  const uint8_t* a0 = st + kOffQ + i * kRow + 16 * h;  // M-tile 0 fragments, step kc at +32 kc
+  const uint8_t* a1 = a0 + 32 * kRow;                  // M-tile 1
+  const uint4 hd = *reinterpret_cast<const uint4*>(wb);
+  uint4 q[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) q[p] = *reinterpret_cast<const uint4*>(wb + 16 + 32 * p + 16 * h);
+  v4i af = *reinterpret_cast<const v4i*>(a0);
+  const Q4KScales s = q4k_scales(hd.y, hd.z, hd.w);
+  const uint32_t aw[2] = {(s.sc_lo >> 3) & 0x07070707u, (s.sc_hi >> 3) & 0x07070707u};
+  const uint32_t bw[2] = {s.sc_lo & 0x07070707u, s.sc_hi & 0x07070707u};
+  v4i pa[8], pb[8];
+  q4s_planes(q, aw, bw, 0, pa[0], pb[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // phase A: M-tile 0, unpack one step ahead
+  v16i acca0 = (v16i){0}, accb0 = (v16i){0};
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    acca0 = mfma_i8(af, pa[kc], acca0);
+    accb0 = mfma_i8(af, pb[kc], accb0);
+    if (kc < 7) {
+      af = *reinterpret_cast<const v4i*>(a0 + 32 * (kc + 1));
+      q4s_planes(q, aw, bw, kc + 1, pa[kc + 1], pb[kc + 1]);
+    } else {
+      af = *reinterpret_cast<const v4i*>(a1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // min-term operands: lane half h carries group sums 8h..8h+7 against m_{(8h+t)/2}
+  const uint32_t mw = h ? s.mn_hi : s.mn_lo;
+  v8h mfrag;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const _Float16 m = (_Float16)(float)((mw >> (8 * k)) & 0xffu);
+    mfrag[2 * k] = m;
+    mfrag[2 * k + 1] = m;
+  }
+  v8h sfrag[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {  // group sums of row 32t+i: int16 -> f16 (exact, |sum| <= 2032)
+    const uint4 braw = *reinterpret_cast<const uint4*>(st + kOffBs + (32 * t + i) * 32 + 16 * h);
+    const uint32_t bh[4] = {i16x2_to_h2(braw.x), i16x2_to_h2(braw.y), i16x2_to_h2(braw.z),
+                            i16x2_to_h2(braw.w)};
+    sfrag[t] = __builtin_bit_cast(v8h, bh);
+  }
+  const float dcol = f16_to_f32(hd.x), mcol = f16_to_f32(hd.x >> 16);
+  float dx[16];
+  q4s_load_dx(st, 4 * h, dx);
+  const v16f am0 = mfma_f16(sfrag[0], mfrag, (v16f){0});
+  __builtin_amdgcn_sched_barrier(0);
+
+  // phase B: M-tile 1 beside tile 0's epilogue, two registers per step
+  v16i acca1 = (v16i){0}, accb1 = (v16i){0};
+#pragma unroll
+  for (int kc = 0; kc < 8; ++kc) {
+    acca1 = mfma_i8(af, pa[kc], acca1);
+    accb1 = mfma_i8(af, pb[kc], accb1);
+    if (kc < 7) af = *reinterpret_cast<const v4i*>(a1 + 32 * (kc + 1));
+    q4s_epilogue<2>(acca0, accb0, am0, dx, dcol, mcol, y[0], 2 * kc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // phase C: tile 1's epilogue
+  q4s_load_dx(st, 32 + 4 * h, dx);
+  const v16f am1 = mfma_f16(sfrag[1], mfrag, (v16f){0});
+  q4s_epilogue<16>(acca1, accb1, am1, dx, dcol, mcol, y[1], 0);
+}
+
+__global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(
+    const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xq, float* __restrict__ Y, int64_t M,
+    int64_t N, int nb) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = lane_id(), i = lane & 31, h = lane >> 5;
+  const int64_t n0 = (int64_t)blockIdx.x * q4s::kBN, m0 = (int64_t)blockIdx.y * q4s::kBM;
+  const uint32_t xstride = (uint32_t)nb * kQ8KBytes, wstride = (uint32_t)nb * kQ4KBytes;
+  // the workgroup's activation rows and weight rows as two buffers: rows past
+  // M or N read as zero (their outputs are never stored)
+  const int64_t mrows = M - m0 < q4s::kBM ? M - m0 : q4s::kBM;
+  const int64_t nrows = N - n0 < q4s::kBN ? N - n0 : q4s::kBN;
+  const rsrc_t xr = make_rsrc(Xq + m0 * xstride, (uint32_t)(mrows * xstride));
+  const rsrc_t wr = make_rsrc(W + n0 * wstride, (uint32_t)(nrows * wstride));
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)lds);
+
+  // per-lane source offsets within one super-block column
+  const uint32_t vq = 4 + 4 * lane;  // value bytes of a row: one dword per lane
+  uint32_t vbs[2];                   // group sums: row 8j + lane/8, dword lane%8
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+    vbs[jj] = (uint32_t)(8 * (wave + 4 * jj) + (lane >> 3)) * xstride + 260 + 4 * (lane & 7);
+  const uint32_t vdx = (uint32_t)lane * xstride;  // d_x of row lane
+  // weight load u = wave + 4j (u < 18) covers 16-byte chunks 64u..64u+63 of
+  // the 128 x 9-chunk tile, i.e. row c / 9, chunk c % 9 for c = 64u + lane
+  uint32_t vw[5];
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    const uint32_t c = 64u * (uint32_t)(wave + 4 * j) + (uint32_t)lane;
+    vw[j] = (c / 9u) * wstride + 16u * (c % 9u);
+  }
+
+  auto issue = [&](int b, int slot) {
+    const uint32_t st = lds0 + (uint32_t)slot * q4s::kStage;
+    const uint32_t xb = (uint32_t)b * kQ8KBytes, wb = (uint32_t)b * kQ4KBytes;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t r = (uint32_t)(wave + 4 * j);
+      dma4(xr, vq, r * xstride + xb, st + q4s::kOffQ + r * kRow);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) dma4(xr, vbs[jj], xb, st + q4s::kOffBs + (wave + 4 * jj) * 256);
+    if (wave == 0) dma4(xr, vdx, xb, st + q4s::kOffDx);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(wr, vw[j], wb, st + q4s::kOffW + 1024 * (wave + 4 * j));
+    if (wave < 2) dma16(wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
+  };
+  float y[2][16];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) y[t][r] = 0.0f;
+
+  // Every step issues one stage of loads -- past the last super-block they
+  // re-read it into a stage nobody reads -- so the wait count is static.
+  const int blast = nb - 1;
+#pragma unroll
+  for (int s = 0; s < q4s::kS - 1; ++s) issue(s < blast ? s : blast, s);
+  int slot = 0;
+  for (int b = 0; b < nb; ++b) {
+    wait_vm<q4s::kWait>();  // own loads of stage b landed
+    lds_barrier();  // stage b complete everywhere; the stage of b-1 is free
+    const int nxt = slot == 0 ? q4s::kS - 1 : slot - 1;
+    issue(b + q4s::kS - 1 < blast ? b + q4s::kS - 1 : blast, nxt);
+    q4s_compute(lds + slot * q4s::kStage, 32 * wave + i, y, i, h);
+    slot = slot + 1 == q4s::kS ? 0 : slot + 1;
+  }
+  wait_vm<0>();  // no load into LDS outlives the workgroup
+
+  const int64_t col = n0 + 32 * wave + i;
+  if (col < N) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < M) Y[row * N + col] = y[t][r];
+      }
+  }
+}
+
 }  // namespace
 
 int launch_gemm(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int64_t M, int64_t N,
                 int64_t K, hipStream_t st) {
   const int64_t nb = K / kQK;
-  const int64_t gx = (N + kBN - 1) / kBN, gy = (M + kBM - 1) / kBM;
-  if (nb > 0x7fffffffLL || gx > 0x7fffffffLL || gy > 65535) return -1;
+  if (nb > 0x7fffffffLL) return -1;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute((const void*)gemm_kernel<12>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
-      return -1;
     if (hipFuncSetAttribute((const void*)gemm_kernel<14>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
       return -1;
+    if (hipFuncSetAttribute((const void*)gemm_q4k_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, q4s::kLds) != hipSuccess)
+      return -1;
     attr_set = true;
   }
-  const dim3 grid((uint32_t)gx, (uint32_t)gy);
-  if (fmt == 12)
-    hipLaunchKernelGGL(gemm_kernel<12>, grid, dim3(256), kLds, st, W, Xq, Y, M, N, (int)nb);
-  else
-    hipLaunchKernelGGL(gemm_kernel<14>, grid, dim3(256), kLds, st, W, Xq, Y, M, N, (int)nb);
+  if (fmt == 12) {
+    const int64_t gx = (N + q4s::kBN - 1) / q4s::kBN, gy = (M + q4s::kBM - 1) / q4s::kBM;
+    if (gx > 0x7fffffffLL || gy > 65535) return -1;
+    hipLaunchKernelGGL(gemm_q4k_kernel, dim3((uint32_t)gx, (uint32_t)gy), dim3(256), q4s::kLds, st,
+                       W, Xq, Y, M, N, (int)nb);
+    return 0;
+  }
+  const int64_t gx = (N + kBN - 1) / kBN, gy = (M + kBM - 1) / kBM;
+  if (gx > 0x7fffffffLL || gy > 65535) return -1;
+  hipLaunchKernelGGL(gemm_kernel<14>, dim3((uint32_t)gx, (uint32_t)gy), dim3(256), kLds, st, W, Xq,
+                     Y, M, N, (int)nb);
   return 0;
 }
 
