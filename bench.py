@@ -10,7 +10,10 @@ weight GB/s) and M = 512 (prefill GEMM, int8 TOP/s).
 
 Each matrix reads the activation of its place in the layer (q/k/v the attention
 input, o the attention output, gate/up the MLP input, down the MLP activation),
-so a pass quantizes four activation tensors and runs seven matmuls.
+so a pass quantizes four activation tensors and runs seven matmuls.  Matrices
+that read the same activation in the same format run as one grouped launch
+(gemmq_gemm_group: q/k/v, then gate/up), so the default pass is four quantizer
+launches and four matmul launches; --no-group launches every matrix on its own.
 
 Inputs are resident in HBM before timing starts.  So that the weights are
 really streamed from HBM and not from the 256 MB last-level cache, the step
@@ -56,6 +59,8 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time HIP-graph replays of each pass instead of eager launches")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--no-group", action="store_true",
+                   help="one launch per matrix instead of grouping matrices that share an input")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one plain device-to-device copy of MIB MiB (reference dispatch "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -66,7 +71,7 @@ class Layer:
     """Device buffers for one workload: rotating weight copies, activations,
     q8_K buffers and outputs, all allocated before timing."""
 
-    def __init__(self, wl, gen, Ms, copies):
+    def __init__(self, wl, gen, Ms, copies, group=True):
         import torch
 
         import quant_packed_weight_amd as gq
@@ -74,6 +79,15 @@ class Layer:
         self.gq = gq
         self.wl = wl
         self.Ms = Ms
+        # launches: runs of consecutive matrices with one input and one format
+        self.launches = []
+        for m in wl.matrices:
+            last = self.launches[-1] if self.launches else None
+            if (group and last and last[-1].inp == m.inp and last[-1].fmt == m.fmt
+                    and len(last) < gq.MAX_GROUP):
+                last.append(m)
+            else:
+                self.launches.append([m])
         self.w = []
         base = {m.name: torch.from_numpy(gen.weights[m.name]).to("cuda:0") for m in wl.matrices}
         for r in range(copies):
@@ -88,22 +102,52 @@ class Layer:
                 self.y[(M, m.name)] = torch.empty((M, m.N), dtype=torch.float32, device="cuda:0")
         torch.cuda.synchronize()
 
+        # every launch's C arguments, built once: the timed loops only call the
+        # library, so host-side Python stays well below the kernels' duration
+        import ctypes
+
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        self.lib = gq.lib()
+        self.args = {}
+        for M in Ms:
+            for r in range(copies):
+                for ms in self.launches:
+                    n = len(ms)
+                    m0 = ms[0]
+                    self.args[(M, r, launch_name(ms))] = (
+                        m0.fmt, n, (P * n)(*[self.w[r][m.name].data_ptr() for m in ms]),
+                        (P * n)(*[self.y[(M, m.name)].data_ptr() for m in ms]),
+                        (I64 * n)(*[m.N for m in ms]), self.xq[(M, m0.inp)].data_ptr(), M, m0.K,
+                        gq.PATH_AUTO)
+            for inp, K in wl.inputs():
+                self.args[(M, "q", inp)] = (self.x[(M, inp)].data_ptr(),
+                                            self.xq[(M, inp)].data_ptr(), M, K)
+
+    def launch(self, ms, M, r, st):
+        """Enqueue the matmul launch of the matrices `ms` (one input, one format)."""
+        rc = self.lib.gemmq_gemm_group(*self.args[(M, r, launch_name(ms))], st)
+        if rc:
+            raise self.gq.GemmqError(rc, "gemm " + launch_name(ms))
+
+    def quantize(self, inp, K, M, st):
+        rc = self.lib.gemmq_quantize_q8K(*self.args[(M, "q", inp)], st)
+        if rc:
+            raise self.gq.GemmqError(rc, "quantize")
+
     def run(self, M, r, stream):
         """Enqueue one pass at M rows on weight copy r."""
-        gq = self.gq
         st = stream.cuda_stream
         done = set()
-        for m in self.wl.matrices:
-            if m.inp not in done:  # quantize each activation just before its first use
-                rc = gq.quantize_q8K_ptr(self.x[(M, m.inp)].data_ptr(),
-                                         self.xq[(M, m.inp)].data_ptr(), M, m.K, st)
-                if rc:
-                    raise gq.GemmqError(rc, "quantize")
-                done.add(m.inp)
-            rc = gq.gemm_ptr(m.fmt, self.w[r][m.name].data_ptr(), self.xq[(M, m.inp)].data_ptr(),
-                             self.y[(M, m.name)].data_ptr(), M, m.N, m.K, gq.PATH_AUTO, st)
-            if rc:
-                raise gq.GemmqError(rc, "gemm " + m.name)
+        for ms in self.launches:
+            inp = ms[0].inp
+            if inp not in done:  # quantize each activation just before its first use
+                self.quantize(inp, ms[0].K, M, st)
+                done.add(inp)
+            self.launch(ms, M, r, st)
+
+
+def launch_name(ms):
+    return "+".join(m.name for m in ms)
 
 
 def time_passes(layer, M, steps, warmup, copies, stream):
@@ -156,40 +200,32 @@ def time_graphs(graphs, steps, warmup):
 
 
 def kernel_rates(layer, M, steps, copies, stream):
-    """Average duration of each matrix's matmul kernel: two HIP events on the
-    launch stream around a batch of back-to-back launches of that matrix (weight
+    """Average duration of each matmul launch of the pass: two HIP events on the
+    launch stream around a batch of back-to-back copies of that launch (weight
     copies rotated, its activation quantized once beforehand)."""
     import torch
 
-    gq = layer.gq
     st = stream.cuda_stream
-    for m in layer.wl.matrices:
-        rc = gq.quantize_q8K_ptr(layer.x[(M, m.inp)].data_ptr(), layer.xq[(M, m.inp)].data_ptr(),
-                                 M, m.K, st)
-        if rc:
-            raise gq.GemmqError(rc, "quantize")
+    for ms in layer.launches:
+        layer.quantize(ms[0].inp, ms[0].K, M, st)
     per = {}
     n = max(steps, copies)
-    for m in layer.wl.matrices:
-        args = [(layer.w[r % copies][m.name].data_ptr(), layer.xq[(M, m.inp)].data_ptr(),
-                 layer.y[(M, m.name)].data_ptr()) for r in range(n)]
-        for w, xq, y in args[:copies]:  # warm the launch path
-            gq.gemm_ptr(m.fmt, w, xq, y, M, m.N, m.K, gq.PATH_AUTO, st)
+    for ms in layer.launches:
+        for r in range(copies):  # warm the launch path
+            layer.launch(ms, M, r, st)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for w, xq, y in args:
-            rc = gq.gemm_ptr(m.fmt, w, xq, y, M, m.N, m.K, gq.PATH_AUTO, st)
-            if rc:
-                raise gq.GemmqError(rc, "gemm " + m.name)
+        for r in range(n):
+            layer.launch(ms, M, r % copies, st)
         e1.record(stream)
         torch.cuda.synchronize()
-        per[m.name] = [e0.elapsed_time(e1) * 1e-3 / n] * n
+        per[launch_name(ms)] = (ms, e0.elapsed_time(e1) * 1e-3 / n)
     return per
 
 
-def profiled_traffic(fam, wl):
-    """HBM bytes per launch of kernel family `fam` ("gemv" / "gemm") on this
-    workload, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+def profiled_traffic(fam, launches):
+    """HBM bytes per launch of kernel family `fam` ("gemv" / "gemm") over the
+    pass's launches, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     (profiles/traffic.json, FETCH scaled by the cold-copy factor).  None when
     the kernel sources changed since those counters were taken."""
     import hashlib
@@ -201,14 +237,15 @@ def profiled_traffic(fam, wl):
     except (OSError, KeyError, ValueError):
         return None
     h = hashlib.sha256()
-    for src in t["sources"]:
+    for src in t.get("sources", []):
         with open(os.path.join(ROOT, "quant_packed_weight_amd", "csrc", src), "rb") as f:
             h.update(f.read())
-    per = t["per_matrix"]
-    if h.hexdigest() != t["source_sha256"] or any(m.name not in per for m in wl.matrices):
+    per = t.get("per_launch", {})
+    names = [launch_name(ms) for ms in launches]
+    if h.hexdigest() != t.get("source_sha256") or any(n not in per for n in names):
         return None
-    tot = sum(per[m.name]["read_bytes"] + per[m.name]["write_bytes"] for m in wl.matrices)
-    return round(tot / len(wl.matrices))
+    tot = sum(per[n]["read_bytes"] + per[n]["write_bytes"] for n in names)
+    return round(tot / len(names))
 
 
 def cpu_baseline(wl, gen, M1, M2, seconds):
@@ -271,7 +308,7 @@ def main():
         raise SystemExit("workload %s has M in %s" % (a.workload, wl.Ms))
     wbytes = sum(m.nbytes for m in wl.matrices)
     copies = a.copies or max(1, math.ceil(GIB / wbytes))
-    layer = Layer(wl, gen, Ms, copies)
+    layer = Layer(wl, gen, Ms, copies, group=not a.no_group)
     stream = torch.cuda.current_stream()
     if a.copy_calibration:
         # a plain device copy of known size whose source is cold: after filling
@@ -300,30 +337,32 @@ def main():
 
     def roof(M):
         per = rates[M]
-        tot_t = sum(sum(v) for v in per.values())
-        n_l = sum(len(v) for v in per.values())
+        n_l = len(per)
+        tot_t = sum(dt for _, dt in per.values())
+        kname = "gemv_kernel" if M <= 8 else "gemm_q4k_kernel"
         if M <= 8:
-            algo = sum(m.nbytes * len(per[m.name]) for m in wl.matrices)
+            algo = sum(sum(m.nbytes for m in ms) for ms, _ in per.values())
             ach = algo / tot_t / 1e9
             return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": profiled_traffic("gemv", wl) if a.workload == "qwen3-8b-q4K" else None,
-                    "algo_bytes_per_launch": round(wbytes / len(wl.matrices)),
-                    "kernel": "gemv_kernel", "launches": n_l,
+                    "traffic": (profiled_traffic("gemv", layer.launches)
+                                if a.workload == "qwen3-8b-q4K" else None),
+                    "algo_bytes_per_launch": round(algo / n_l),
+                    "kernel": kname, "launches_per_pass": n_l,
                     "avg_launch_us": round(tot_t / n_l * 1e6, 2),
-                    "per_matrix_GBs": {m.name: round(m.nbytes * len(per[m.name]) /
-                                                     sum(per[m.name]) / 1e9, 1)
-                                       for m in wl.matrices}}
-        algo = sum(2 * M * m.N * m.K * len(per[m.name]) for m in wl.matrices)
+                    "per_launch_GBs": {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
+                                       for k, (ms, dt) in per.items()}}
+        algo = sum(sum(2 * M * m.N * m.K for m in ms) for ms, _ in per.values())
         ach = algo / tot_t / 1e12
         return {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
-                "traffic": profiled_traffic("gemm", wl) if a.workload == "qwen3-8b-q4K" else None,
-                "kernel": "gemm_kernel<12>", "launches": n_l,
+                "traffic": (profiled_traffic("gemm", layer.launches)
+                            if a.workload == "qwen3-8b-q4K" else None),
+                "algo_ops_per_launch": round(algo / n_l),
+                "kernel": kname, "launches_per_pass": n_l,
                 "avg_launch_us": round(tot_t / n_l * 1e6, 2),
-                "per_matrix_TOPs": {m.name: round(2 * M * m.N * m.K * len(per[m.name]) /
-                                                  sum(per[m.name]) / 1e12, 1)
-                                    for m in wl.matrices}}
+                "per_launch_TOPs": {k: round(sum(2 * M * m.N * m.K for m in ms) / dt / 1e12, 1)
+                                    for k, (ms, dt) in per.items()}}
 
     value = wbytes / t[M1] / 1e9 if M1 <= 8 else ops[M1] / t[M1] / 1e12
     res = {
@@ -342,6 +381,7 @@ def main():
         "config": {"workload": a.workload, "M": Ms, "matrices": len(wl.matrices),
                    "activations": len(wl.inputs()), "weight_bytes": wbytes,
                    "rotating_copies": copies, "submit": "hip_graph" if a.graph else "eager",
+                   "launches": [launch_name(ms) for ms in layer.launches],
                    "ms_per_pass": {str(M): round(t[M] * 1e3, 4) for M in Ms},
                    "ms_per_pass_eager": {str(M): round(t_eager[M] * 1e3, 4) for M in Ms}},
         "roofline": roof(M1),

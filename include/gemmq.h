@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 1
+#define GEMMQ_ABI_VERSION 2
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q4_K 12
@@ -58,6 +58,7 @@ extern "C" {
 #define GEMMQ_Q6_K_BYTES 210
 #define GEMMQ_Q8_K_BYTES 292
 #define GEMMQ_QK 256
+#define GEMMQ_MAX_GROUP 4 /* matrices per gemmq_gemm_group call */
 
 /* Status codes. */
 #define GEMMQ_OK 0
@@ -127,6 +128,23 @@ int gemmq_gemm(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int6
  * returns GEMMQ_E_SHAPE.  Same arguments, layout and errors otherwise. */
 int gemmq_gemm_ex(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int64_t N,
                   int64_t K, int path, void *stream);
+
+/*
+ * Several weight matrices of one format that read the same activations, in one
+ * launch: for g < count, Y[g] = W[g] applied to Xq exactly as
+ * gemmq_gemm_ex(fmt, W[g], Xq, Y[g], M, N[g], K, path, stream) computes it (the
+ * same bits).  Sharing one input is what a transformer layer's q/k/v
+ * projections and its gate/up projections do; one launch instead of several
+ * removes the per-launch cost that dominates at small M.
+ *   count  1..4.
+ *   W, Y, N  HOST arrays of `count` entries, read during the call only; each
+ *        W[g] / Y[g] / N[g] as in gemmq_gemm.  N[g] == 0 entries are skipped.
+ *   Xq, M, K, path, stream  as in gemmq_gemm_ex.
+ * Errors: those of gemmq_gemm_ex for any entry, and GEMMQ_E_INVALID_ARG for a
+ * count outside 1..4 or a null array; nothing is launched on an error.
+ */
+int gemmq_gemm_group(int fmt, int count, const void *const *W, float *const *Y, const int64_t *N,
+                     const void *Xq, int64_t M, int64_t K, int path, void *stream);
 
 /*
  * Diagnostic export: decode packed weights to f32 with the same device unpacker

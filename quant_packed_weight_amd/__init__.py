@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     FMT_Q4K,
     FMT_Q6K,
     LIB_PATH,
+    MAX_GROUP,
     PATH_AUTO,
     PATH_GEMM,
     PATH_GEMV,
@@ -22,6 +23,8 @@ from ._lib import (  # noqa: F401
     decode,
     decode_ptr,
     gemm,
+    gemm_group,
+    gemm_group_ptr,
     gemm_ptr,
     lib,
     linear,

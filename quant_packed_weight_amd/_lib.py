@@ -17,7 +17,8 @@ BLOCK_BYTES = {FMT_Q4K: 144, FMT_Q6K: 210}
 Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
-ABI_VERSION = 1
+MAX_GROUP = 4  # matrices per gemmq_gemm_group call
+ABI_VERSION = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 
@@ -34,6 +35,8 @@ EXPORTS = {
     "gemmq_quantize_q8K": (_I, [_P, _P, _I64, _I64, _P]),
     "gemmq_gemm": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _P]),
     "gemmq_gemm_ex": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
+    "gemmq_gemm_group": (_I, [_I, _I, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                              ctypes.POINTER(_I64), _P, _I64, _I64, _I, _P]),
     "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
 }
 
@@ -102,6 +105,18 @@ def gemm_ptr(fmt: int, W: int, Xq: int, Y: int, M: int, N: int, K: int, path: in
     return lib().gemmq_gemm_ex(fmt, W, Xq, Y, M, N, K, path, stream or None)
 
 
+def gemm_group_ptr(fmt: int, Ws, Ys, Ns, Xq: int, M: int, K: int, path: int = PATH_AUTO,
+                   stream: int = 0) -> int:
+    """Ws, Ys, Ns: sequences of equal length (the matrices sharing Xq)."""
+    n = len(Ws)
+    if len(Ys) != n or len(Ns) != n:
+        raise ValueError("Ws, Ys and Ns must have the same length")
+    wa = (_P * max(n, 1))(*Ws)
+    ya = (_P * max(n, 1))(*Ys)
+    na = (_I64 * max(n, 1))(*Ns)
+    return lib().gemmq_gemm_group(fmt, n, wa, ya, na, Xq, M, K, path, stream or None)
+
+
 def decode_ptr(fmt: int, W: int, Wf: int, N: int, K: int, stream: int = 0) -> int:
     return lib().gemmq_decode(fmt, W, Wf, N, K, stream or None)
 
@@ -157,6 +172,29 @@ def gemm(fmt, w, xq, M, N, K, out=None, path=PATH_AUTO, stream=None):
                                _dev(out, "out", torch.float32), M, N, K, path, _stream(stream)),
            "gemmq_gemm")
     return out
+
+
+def gemm_group(fmt, ws, xq, M, Ns, K, outs=None, path=PATH_AUTO, stream=None):
+    """Several packed weight matrices sharing the activations xq, one launch:
+    returns [f32 [M, N_g]]."""
+    torch = _torch()
+    if len(ws) != len(Ns):
+        raise ValueError("ws and Ns must have the same length")
+    if xq.numel() < q8K_bytes(M, K):
+        raise ValueError("xq smaller than the stated shape")
+    for w, N in zip(ws, Ns):
+        if w.numel() < weight_bytes(fmt, N, K):
+            raise ValueError("buffer smaller than the stated shape")
+    if outs is None:
+        outs = [torch.empty((M, N), dtype=torch.float32, device=xq.device) for N in Ns]
+    for o, N in zip(outs, Ns):
+        if o.numel() < M * N:
+            raise ValueError("out too small")
+    _check(gemm_group_ptr(fmt, [_dev(w, "w", torch.uint8) for w in ws],
+                          [_dev(o, "out", torch.float32) for o in outs], list(Ns),
+                          _dev(xq, "xq", torch.uint8), M, K, path, _stream(stream)),
+           "gemmq_gemm_group")
+    return outs
 
 
 def decode(fmt, w, N, K, out=None, stream=None):

@@ -4,8 +4,8 @@
 // bad call returns a named status and launches nothing (the pages refuse what
 // they do not implement by name rather than guessing -- PocketLLM README,
 // "Roadmap" and "Try it").  The library owns no memory and keeps no per-call
-// state; the only process-wide state is a per-device cache of the
-// architecture check.
+// state; the only process-wide state is per device: the architecture check
+// and whether the GEMM kernels' LDS limit has been raised.
 #include <atomic>
 #include <cstring>
 
@@ -107,27 +107,50 @@ int gemmq_quantize_q8K(const float* X, void* Xq, int64_t M, int64_t K, void* str
                                              static_cast<hipStream_t>(stream)));
 }
 
-int gemmq_gemm_ex(int fmt, const void* W, const void* Xq, float* Y, int64_t M, int64_t N,
-                  int64_t K, int path, void* stream) {
-  int rc = check_weights(fmt, W, N, K);
-  if (rc != GEMMQ_OK) return rc;
+int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
+                     const int64_t* N, const void* Xq, int64_t M, int64_t K, int path,
+                     void* stream) {
+  if (count < 1 || count > gemmq::kMaxGroup || !W || !Y || !N) return GEMMQ_E_INVALID_ARG;
+  gemmq::Group g{};
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) {
+    const int rc = check_weights(fmt, W[i], N[i], K);
+    if (rc != GEMMQ_OK) return rc;
+    rows += N[i];
+  }
   if (M < 0) return GEMMQ_E_INVALID_ARG;
-  if (M > kMaxRows) return GEMMQ_E_SHAPE;
+  if (M > kMaxRows || rows > kMaxRows) return GEMMQ_E_SHAPE;
   if (path != GEMMQ_PATH_AUTO && path != GEMMQ_PATH_GEMV && path != GEMMQ_PATH_GEMM)
     return GEMMQ_E_INVALID_ARG;
   if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
-  if (M == 0 || N == 0) return GEMMQ_OK;
-  if (!Xq || !Y) return GEMMQ_E_INVALID_ARG;
-  if (!aligned(Xq, 4) || !aligned(Y, 4)) return GEMMQ_E_ALIGNMENT;
+  if (M == 0 || rows == 0) return GEMMQ_OK;
+  if (!Xq) return GEMMQ_E_INVALID_ARG;
+  for (int i = 0; i < count; ++i)
+    if (N[i] > 0 && !Y[i]) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
+  for (int i = 0; i < count; ++i)
+    if (N[i] > 0 && !aligned(Y[i], 4)) return GEMMQ_E_ALIGNMENT;
   const int dv = check_device();
   if (dv != GEMMQ_OK) return dv;
-  const uint8_t* w = static_cast<const uint8_t*>(W);
+  // empty matrices are dropped; the others keep their order
+  for (int i = 0; i < count; ++i) {
+    if (N[i] == 0) continue;
+    g.W[g.count] = static_cast<const uint8_t*>(W[i]);
+    g.Y[g.count] = Y[i];
+    g.N[g.count] = N[i];
+    ++g.count;
+  }
   const uint8_t* xq = static_cast<const uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool gemv = path == GEMMQ_PATH_GEMV || (path == GEMMQ_PATH_AUTO && M <= 8);
   clear_pending();
-  if (gemv) return launched(gemmq::launch_gemv(fmt, w, xq, Y, (int)M, N, K, st));
-  return launched(gemmq::launch_gemm(fmt, w, xq, Y, M, N, K, st));
+  if (gemv) return launched(gemmq::launch_gemv(fmt, g, xq, (int)M, K, st));
+  return launched(gemmq::launch_gemm(fmt, g, xq, M, K, st));
+}
+
+int gemmq_gemm_ex(int fmt, const void* W, const void* Xq, float* Y, int64_t M, int64_t N,
+                  int64_t K, int path, void* stream) {
+  return gemmq_gemm_group(fmt, 1, &W, &Y, &N, Xq, M, K, path, stream);
 }
 
 int gemmq_gemm(int fmt, const void* W, const void* Xq, float* Y, int64_t M, int64_t N, int64_t K,

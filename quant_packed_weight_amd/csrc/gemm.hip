@@ -30,6 +30,8 @@
 // stages.
 // Every output's arithmetic depends only on its own row and column, so any
 // subset of rows gives identical bits.
+#include <atomic>
+
 #include "device.h"
 #include "launch.h"
 
@@ -345,13 +347,17 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
 
 // ------------------------------------------------- the kernel
 template <int FMT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const uint8_t* __restrict__ W,
-                                                      const uint8_t* __restrict__ Xq,
-                                                      float* __restrict__ Y, int64_t M, int64_t N,
+__global__ __launch_bounds__(256, 2) void gemm_kernel(const GroupTiles gt,
+                                                      const uint8_t* __restrict__ Xq, int64_t M,
                                                       int nb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   using WRegs = typename std::conditional<FMT == 12, W4Regs, W6Regs>::type;
-  const int64_t n0 = (int64_t)blockIdx.x * kBN;
+  const TileMatrix tm = tile_matrix(gt, blockIdx.x);
+  const uint8_t* __restrict__ W = tm.W;
+  float* __restrict__ Y = tm.Y;
+  const int64_t N = tm.N;
+  const uint32_t tile = tm.local;
+  const int64_t n0 = (int64_t)tile * kBN;
   const int64_t m0 = (int64_t)blockIdx.y * kBM;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
@@ -587,13 +593,18 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   q4s_epilogue<16>(acca1, accb1, am1, dx, dcol, mcol, y[1], 0);
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(
-    const uint8_t* __restrict__ W, const uint8_t* __restrict__ Xq, float* __restrict__ Y, int64_t M,
-    int64_t N, int nb) {
+__global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
+                                                          const uint8_t* __restrict__ Xq, int64_t M,
+                                                          int nb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = lane_id(), i = lane & 31, h = lane >> 5;
-  const int64_t n0 = (int64_t)blockIdx.x * q4s::kBN, m0 = (int64_t)blockIdx.y * q4s::kBM;
+  const TileMatrix tm = tile_matrix(gt, blockIdx.x);
+  const uint8_t* __restrict__ W = tm.W;
+  float* __restrict__ Y = tm.Y;
+  const int64_t N = tm.N;
+  const uint32_t tile = tm.local;
+  const int64_t n0 = (int64_t)tile * q4s::kBN, m0 = (int64_t)blockIdx.y * q4s::kBM;
   const uint32_t xstride = (uint32_t)nb * kQ8KBytes, wstride = (uint32_t)nb * kQ4KBytes;
   // the workgroup's activation rows and weight rows as two buffers: rows past
   // M or N read as zero (their outputs are never stored)
@@ -670,31 +681,36 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(
 
 }  // namespace
 
-int launch_gemm(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int64_t M, int64_t N,
-                int64_t K, hipStream_t st) {
+int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
+                hipStream_t st) {
   const int64_t nb = K / kQK;
   if (nb > 0x7fffffffLL) return -1;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic LDS limit is a per-device attribute of each kernel
+  static std::atomic<int> attr_done[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (attr_done[dev].load(std::memory_order_acquire) == 0) {
     if (hipFuncSetAttribute((const void*)gemm_kernel<14>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
       return -1;
     if (hipFuncSetAttribute((const void*)gemm_q4k_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, q4s::kLds) != hipSuccess)
       return -1;
-    attr_set = true;
+    attr_done[dev].store(1, std::memory_order_release);
   }
-  if (fmt == 12) {
-    const int64_t gx = (N + q4s::kBN - 1) / q4s::kBN, gy = (M + q4s::kBM - 1) / q4s::kBM;
-    if (gx > 0x7fffffffLL || gy > 65535) return -1;
-    hipLaunchKernelGGL(gemm_q4k_kernel, dim3((uint32_t)gx, (uint32_t)gy), dim3(256), q4s::kLds, st,
-                       W, Xq, Y, M, N, (int)nb);
-    return 0;
-  }
-  const int64_t gx = (N + kBN - 1) / kBN, gy = (M + kBM - 1) / kBM;
-  if (gx > 0x7fffffffLL || gy > 65535) return -1;
-  hipLaunchKernelGGL(gemm_kernel<14>, dim3((uint32_t)gx, (uint32_t)gy), dim3(256), kLds, st, W, Xq,
-                     Y, M, N, (int)nb);
+  GroupTiles gt;
+  const int64_t bn = fmt == 12 ? q4s::kBN : kBN, bm = fmt == 12 ? q4s::kBM : kBM;
+  if (!make_tiles(grp, bn, gt)) return -1;
+  const uint32_t gx = gt.start[kMaxGroup];
+  const int64_t gy = (M + bm - 1) / bm;
+  if (gy > 65535) return -1;
+  if (gx == 0) return 0;
+  if (fmt == 12)
+    hipLaunchKernelGGL(gemm_q4k_kernel, dim3(gx, (uint32_t)gy), dim3(256), q4s::kLds, st, gt, Xq,
+                       M, (int)nb);
+  else
+    hipLaunchKernelGGL(gemm_kernel<14>, dim3(gx, (uint32_t)gy), dim3(256), kLds, st, gt, Xq, M,
+                       (int)nb);
   return 0;
 }
 

@@ -33,8 +33,7 @@ namespace gemmq {
 
 namespace {
 
-constexpr int kXS = 304;  // LDS bytes per staged q8_K block: q[256] | sums[16] | d | pad
-constexpr int kMaxIT = 4; // rounds of 16 blocks whose loads are in flight together
+constexpr int kMaxIT = 4;  // rounds of 16 blocks whose loads are in flight together
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
@@ -155,30 +154,6 @@ __device__ __forceinline__ bool holder(int lane) {
   return ok;
 }
 
-// Stage MT activation rows (nb q8_K blocks each) into LDS, one 304-byte slot per
-// block: the 256 values and 16 group sums (raw bytes 4..291, eighteen 16-byte
-// chunks) at 0, d at 288.  All 256 threads copy.
-template <int MT>
-__device__ __forceinline__ void stage_x(uint8_t* xs, const uint8_t* __restrict__ Xq, int M,
-                                        int nb) {
-  const int per_row = nb * 19;
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int mm = m < M ? m : M - 1;  // rows past M: a copy of a valid row, never stored
-    const uint8_t* src = Xq + (int64_t)mm * nb * kQ8KBytes;
-    uint8_t* dst = xs + m * nb * kXS;
-    for (int t = threadIdx.x; t < per_row; t += 256) {
-      const int b = t / 19, k = t - b * 19;
-      if (k < 18) {
-        const u32x4 v = ld16(src + b * kQ8KBytes + 4 + 16 * k);
-        *reinterpret_cast<uint4*>(dst + b * kXS + 16 * k) = make_uint4(v.x, v.y, v.z, v.w);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst + b * kXS + 288) = ld4(src + b * kQ8KBytes);
-      }
-    }
-  }
-}
-
 // Activation fragment of block b, row m: two 32-byte runs of values at byte
 // offsets qoff and qoff2, the dwords of group sums at soff and soff2 (offsets
 // into the 32 bytes of sums), and d.
@@ -188,33 +163,17 @@ struct XFrag {
   float d;
 };
 
-template <bool XLDS>
-__device__ __forceinline__ XFrag x_frag(const uint8_t* xs, const uint8_t* __restrict__ Xq, int nb,
-                                        int m, int b, int qoff, int qoff2, int soff, int soff2) {
+__device__ __forceinline__ XFrag x_frag(const uint8_t* __restrict__ Xq, int nb, int m, int b,
+                                        int qoff, int qoff2, int soff, int soff2) {
   XFrag f;
-  if constexpr (XLDS) {
-    const uint8_t* p = xs + (m * nb + b) * kXS;
-    const uint4 a0 = *reinterpret_cast<const uint4*>(p + qoff);
-    const uint4 a1 = *reinterpret_cast<const uint4*>(p + qoff + 16);
-    const uint4 b0 = *reinterpret_cast<const uint4*>(p + qoff2);
-    const uint4 b1 = *reinterpret_cast<const uint4*>(p + qoff2 + 16);
-    f.a0 = {a0.x, a0.y, a0.z, a0.w};
-    f.a1 = {a1.x, a1.y, a1.z, a1.w};
-    f.b0 = {b0.x, b0.y, b0.z, b0.w};
-    f.b1 = {b1.x, b1.y, b1.z, b1.w};
-    f.s0 = *reinterpret_cast<const uint32_t*>(p + 256 + soff);
-    f.s1 = *reinterpret_cast<const uint32_t*>(p + 256 + soff2);
-    f.d = *reinterpret_cast<const float*>(p + 288);
-  } else {
-    const uint8_t* p = Xq + ((int64_t)m * nb + b) * kQ8KBytes;
-    f.a0 = ld16(p + 4 + qoff);
-    f.a1 = ld16(p + 4 + qoff + 16);
-    f.b0 = ld16(p + 4 + qoff2);
-    f.b1 = ld16(p + 4 + qoff2 + 16);
-    f.s0 = ld4(p + 260 + soff);
-    f.s1 = ld4(p + 260 + soff2);
-    f.d = *reinterpret_cast<const float*>(p);
-  }
+  const uint8_t* p = Xq + ((int64_t)m * nb + b) * kQ8KBytes;
+  f.a0 = ld16(p + 4 + qoff);
+  f.a1 = ld16(p + 4 + qoff + 16);
+  f.b0 = ld16(p + 4 + qoff2);
+  f.b1 = ld16(p + 4 + qoff2 + 16);
+  f.s0 = ld4(p + 260 + soff);
+  f.s1 = ld4(p + 260 + soff2);
+  f.d = *reinterpret_cast<const float*>(p);
   return f;
 }
 
@@ -227,23 +186,26 @@ __device__ __forceinline__ int dot16(const uint32_t* w, const u32x4& x, int s) {
 
 // ---------------------------------------------------------------- kernel
 // FMT: 12 q4_K, 14 q6_K.  MT activation rows computed (>= M).  IT rounds of 16
-// blocks loaded together.  P rows per round.  XLDS: activations staged in LDS.
-template <int FMT, int MT, int IT, int P, bool XLDS>
-__global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __restrict__ W,
-                                                   const uint8_t* __restrict__ Xq,
-                                                   float* __restrict__ Y, int64_t N, int nb, int M) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];
+// blocks loaded together.  P rows per round.  One wave per workgroup; the
+// grid is the concatenation of every grouped matrix's waves.
+template <int FMT, int MT, int IT, int P>
+__global__ __launch_bounds__(64) void gemv_kernel(const GroupTiles gt,
+                                                  const uint8_t* __restrict__ Xq, int nb, int M) {
   constexpr int SEG = 64 / P;  // lanes that share a row
   constexpr int BPR = 16 / P;  // blocks of a row per round when P > 1
   constexpr int BB = FMT == 12 ? kQ4KBytes : kQ6KBytes;
   const int lane = lane_id();
-  const int wave = XLDS ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
-  constexpr int WPB = XLDS ? 4 : 1;  // waves per workgroup
   const int G = lane >> 2, c = lane & 3;
   const int prow = P > 1 ? G / BPR : 0;
   const int bl0 = P > 1 ? G % BPR : G;
-  const int64_t n0 = ((int64_t)blockIdx.x * WPB + wave) * P;  // first row of this wave
-  const bool active = n0 < N;                                 // wave-uniform
+  const TileMatrix tm = tile_matrix(gt, blockIdx.x);
+  // take Xq with the rest of the kernel arguments, so the weight loads below
+  // do not wait for a second round of scalar loads
+  asm volatile("" ::"s"(Xq));
+  const uint8_t* __restrict__ W = tm.W;
+  float* __restrict__ Y = tm.Y;
+  const int64_t N = tm.N;
+  const int64_t n0 = (int64_t)tm.local * P;  // first row of this wave
   int64_t n = n0 + prow;
   if (n >= N) n = N - 1;  // tail rows: a valid row, never stored
   const uint8_t* wrow = W + n * nb * BB;
@@ -261,12 +223,11 @@ __global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 
-  bool staged = false;
   for (int s0 = 0; s0 < nb; s0 += 16 * IT) {
     // ---- 1. every weight load of these IT rounds
     uint32_t wq[IT][8], wh[IT][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
     uint32_t hd[IT][4];             // q4_K: block header; q6_K: [0] scale bytes, [1] d
-    if (active) {
+    {
 #pragma unroll
       for (int i = 0; i < IT; ++i) {
         const int b = s0 + bl0 + 16 * i;
@@ -289,17 +250,7 @@ __global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __
         }
       }
     }
-    // ---- 2. activations into LDS, once (whole workgroup, before any early exit)
-    if constexpr (XLDS) {
-      if (!staged) {
-        stage_x<MT>(xs, Xq, M, nb);
-        __syncthreads();
-        staged = true;
-      }
-    }
-    if (!active) return;  // wave-uniform; after the barrier
-
-    // ---- 3. arithmetic, block by block
+    // ---- 2. arithmetic, block by block
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int b = s0 + bl0 + 16 * i;
@@ -327,7 +278,7 @@ __global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const XFrag x = x_frag<XLDS>(xs, Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
+          const XFrag x = x_frag(Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
           const int dl = dot16(lo + 4, x.a1, dot16(lo, x.a0, 0));
           const int dh = dot16(hi + 4, x.b1, dot16(hi, x.b0, 0));
           const int isc = __mul24(sc0, dl) + __mul24(sc1, dh);
@@ -352,7 +303,7 @@ __global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __
         const uint32_t spb = (uint32_t)(e2 & 0xffff) | ((uint32_t)e3 << 16);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const XFrag x = x_frag<XLDS>(xs, Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
+          const XFrag x = x_frag(Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
           // sum_j sc_j * (dot_j - 32 * sum_j) over the lane's four 16-weight sub-blocks
           int isc = __mul24(e0, dot16(qa, x.a0, 0)) + __mul24(e1, dot16(qa + 4, x.a1, 0)) +
                     __mul24(e2, dot16(qb, x.b0, 0)) + __mul24(e3, dot16(qb + 4, x.b1, 0));
@@ -363,7 +314,7 @@ __global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __
     }
   }
 
-  // ---- 4. lane reduction and store
+  // ---- 3. lane reduction and store
   const int64_t nn = n0 + prow;
   if constexpr (MT <= SEG) {
     float v[MT];
@@ -384,53 +335,51 @@ __global__ __launch_bounds__(XLDS ? 256 : 64) void gemv_kernel(const uint8_t* __
 }
 
 template <int FMT, int MT, int IT, int P>
-void launch_cfg(const uint8_t* W, const uint8_t* Xq, float* Y, int64_t N, int nb, int M,
-                hipStream_t st) {
-  const int64_t waves = (N + P - 1) / P;
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, false>), dim3((uint32_t)waves), dim3(64), 0, st,
-                     W, Xq, Y, N, nb, M);
+int launch_cfg(const Group& grp, const uint8_t* Xq, int nb, int M, hipStream_t st) {
+  GroupTiles gt;
+  if (!make_tiles(grp, P, gt)) return -1;
+  const uint32_t waves = gt.start[kMaxGroup];
+  if (waves == 0) return 0;
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P>), dim3(waves), dim3(64), 0, st, gt, Xq, nb, M);
+  return 0;
 }
 
 // The lane mapping depends on K only: P rows side by side when a row has 16/P
 // blocks, otherwise IT rounds of 16 blocks in flight together (longer rows loop
 // over groups of kMaxIT rounds).
 template <int FMT, int MT>
-void launch_mt(const uint8_t* W, const uint8_t* Xq, float* Y, int64_t N, int nb, int M,
-               hipStream_t st) {
-  if (nb == 1) return launch_cfg<FMT, MT, 1, 16>(W, Xq, Y, N, nb, M, st);
-  if (nb == 2) return launch_cfg<FMT, MT, 1, 8>(W, Xq, Y, N, nb, M, st);
-  if (nb == 4) return launch_cfg<FMT, MT, 1, 4>(W, Xq, Y, N, nb, M, st);
-  if (nb == 8) return launch_cfg<FMT, MT, 1, 2>(W, Xq, Y, N, nb, M, st);
-  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1>(W, Xq, Y, N, nb, M, st);
-  if (nb <= 32) return launch_cfg<FMT, MT, 2, 1>(W, Xq, Y, N, nb, M, st);
-  if (nb <= 48) return launch_cfg<FMT, MT, 3, 1>(W, Xq, Y, N, nb, M, st);
-  return launch_cfg<FMT, MT, kMaxIT, 1>(W, Xq, Y, N, nb, M, st);
+int launch_mt(const Group& g, const uint8_t* Xq, int nb, int M, hipStream_t st) {
+  if (nb == 1) return launch_cfg<FMT, MT, 1, 16>(g, Xq, nb, M, st);
+  if (nb == 2) return launch_cfg<FMT, MT, 1, 8>(g, Xq, nb, M, st);
+  if (nb == 4) return launch_cfg<FMT, MT, 1, 4>(g, Xq, nb, M, st);
+  if (nb == 8) return launch_cfg<FMT, MT, 1, 2>(g, Xq, nb, M, st);
+  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1>(g, Xq, nb, M, st);
+  if (nb <= 32) return launch_cfg<FMT, MT, 2, 1>(g, Xq, nb, M, st);
+  if (nb <= 48) return launch_cfg<FMT, MT, 3, 1>(g, Xq, nb, M, st);
+  return launch_cfg<FMT, MT, kMaxIT, 1>(g, Xq, nb, M, st);
 }
 
 template <int FMT>
-int launch_fmt(const uint8_t* W, const uint8_t* Xq, float* Y, int M, int64_t N, int nb,
-               hipStream_t st) {
+int launch_fmt(const Group& g, const uint8_t* Xq, int M, int nb, hipStream_t st) {
   switch (M) {
-    case 1: launch_mt<FMT, 1>(W, Xq, Y, N, nb, M, st); return 0;
-    case 2: launch_mt<FMT, 2>(W, Xq, Y, N, nb, M, st); return 0;
+    case 1: return launch_mt<FMT, 1>(g, Xq, nb, M, st);
+    case 2: return launch_mt<FMT, 2>(g, Xq, nb, M, st);
     case 3:
-    case 4: launch_mt<FMT, 4>(W, Xq, Y, N, nb, M, st); return 0;
+    case 4: return launch_mt<FMT, 4>(g, Xq, nb, M, st);
     case 5:
     case 6:
     case 7:
-    case 8: launch_mt<FMT, 8>(W, Xq, Y, N, nb, M, st); return 0;
+    case 8: return launch_mt<FMT, 8>(g, Xq, nb, M, st);
     default: return -1;
   }
 }
 
 }  // namespace
 
-int launch_gemv(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int M, int64_t N,
-                int64_t K, hipStream_t st) {
+int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st) {
   const int64_t nb = K / kQK;
-  if (nb > 0x7fffffffLL / kXS || N > 0x7fffffffLL) return -1;
-  return fmt == 12 ? launch_fmt<12>(W, Xq, Y, M, N, (int)nb, st)
-                   : launch_fmt<14>(W, Xq, Y, M, N, (int)nb, st);
+  if (nb > 0x7fffffffLL) return -1;
+  return fmt == 12 ? launch_fmt<12>(g, Xq, M, (int)nb, st) : launch_fmt<14>(g, Xq, M, (int)nb, st);
 }
 
 }  // namespace gemmq

@@ -8,13 +8,73 @@
 
 namespace gemmq {
 
+// Up to kMaxGroup weight matrices of one format that read the same activations
+// and run as one launch: matrix g has N[g] rows at W[g] and writes Y[g].
+constexpr int kMaxGroup = 4;
+struct Group {
+  const uint8_t* W[kMaxGroup];
+  float* Y[kMaxGroup];
+  int64_t N[kMaxGroup];
+  int count;
+};
+
+// Kernel-side view: the launch's first grid dimension is the concatenation of
+// every matrix's tiles; tile t belongs to matrix g with start[g] <= t < start[g+1].
+struct GroupTiles {
+  const uint8_t* W[kMaxGroup];
+  float* Y[kMaxGroup];
+  int64_t N[kMaxGroup];
+  uint32_t start[kMaxGroup + 1];
+  int count;
+};
+
+// Fills `t` from `g` with ceil(N/rows_per_tile) tiles per matrix; false when the
+// total does not fit a grid dimension.
+inline bool make_tiles(const Group& g, int64_t rows_per_tile, GroupTiles& t) {
+  int64_t s = 0;
+  t.count = g.count;
+  for (int i = 0; i < kMaxGroup; ++i) {
+    const bool on = i < g.count;
+    t.W[i] = on ? g.W[i] : nullptr;
+    t.Y[i] = on ? g.Y[i] : nullptr;
+    t.N[i] = on ? g.N[i] : 0;
+    t.start[i] = (uint32_t)s;
+    if (on) s += (g.N[i] + rows_per_tile - 1) / rows_per_tile;
+    if (s > 0x7fffffffLL) return false;
+  }
+  t.start[kMaxGroup] = (uint32_t)s;
+  return true;
+}
+
+// The matrix that tile `tile` (wave-uniform) belongs to: its weights, output,
+// rows, and the tile's index within it.  Every field is read at a fixed offset
+// and chosen by selects, so the kernel arguments arrive in one round of scalar
+// loads instead of a second, dependent one.
+struct TileMatrix {
+  const uint8_t* W;
+  float* Y;
+  int64_t N;
+  uint32_t local;
+};
+
+__device__ __forceinline__ TileMatrix tile_matrix(const GroupTiles& t, uint32_t tile) {
+  TileMatrix m{t.W[0], t.Y[0], t.N[0], tile};
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) {
+    const bool in = i < t.count && tile >= t.start[i];
+    m.W = in ? t.W[i] : m.W;
+    m.Y = in ? t.Y[i] : m.Y;
+    m.N = in ? t.N[i] : m.N;
+    m.local = in ? tile - t.start[i] : m.local;
+  }
+  return m;
+}
+
 int launch_quantize_q8K(const float* X, uint8_t* Xq, int64_t M, int64_t K, hipStream_t st);
 
-int launch_gemv(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int M, int64_t N,
-                int64_t K, hipStream_t st);
+int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 
-int launch_gemm(int fmt, const uint8_t* W, const uint8_t* Xq, float* Y, int64_t M, int64_t N,
-                int64_t K, hipStream_t st);
+int launch_gemm(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K, hipStream_t st);
 
 int launch_decode(int fmt, const uint8_t* W, float* Wf, int64_t N, int64_t K, hipStream_t st);
 

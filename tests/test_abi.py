@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_exported(L):
     names = _declared()
-    assert len(names) == 9
+    assert len(names) == 10
     assert set(names) == set(gq.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 1
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 2
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -85,6 +85,37 @@ def test_gemm_validation(L, args, status):
     assert L.gemmq_gemm_ex(fmt, W, Xq, Y, M, N, K, path, None) == status
     if path == 0:
         assert L.gemmq_gemm(fmt, W, Xq, Y, M, N, K, None) == status
+
+
+@pytest.mark.parametrize("count,Ws,Ys,Ns,M,path,status", [
+    (0, [FAKE16], [FAKE16], [1], 1, 0, -1),                           # count < 1
+    (5, [FAKE16] * 5, [FAKE16] * 5, [1] * 5, 1, 0, -1),               # count > 4
+    (2, [FAKE16, None], [FAKE16, FAKE16], [1, 1], 1, 0, -1),          # null W in entry 1
+    (2, [FAKE16, FAKE16], [FAKE16, None], [1, 1], 1, 0, -1),          # null Y in entry 1
+    (2, [FAKE16, FAKE16], [FAKE16, FAKE16], [1, -3], 1, 0, -1),       # N < 0
+    (2, [FAKE16, FAKE16 + 8], [FAKE16, FAKE16], [1, 1], 1, 0, -4),    # W alignment
+    (2, [FAKE16, FAKE16], [FAKE16, FAKE16 + 2], [1, 1], 1, 0, -4),    # Y alignment
+    (3, [FAKE16] * 3, [FAKE16] * 3, [1] * 3, 9, 1, -3),               # GEMV path, M > 8
+    (3, [FAKE16] * 3, [FAKE16] * 3, [1] * 3, 1, 5, -1),               # unknown path
+    (2, [FAKE16, None], [FAKE16, None], [4, 0], 0, 0, 0),             # M = 0: empty
+    (2, [None, None], [None, None], [0, 0], 3, 0, 0),                 # all N = 0: empty
+])
+def test_group_validation(L, count, Ws, Ys, Ns, M, path, status):
+    n = max(len(Ws), 1)
+    P = ctypes.c_void_p
+    wa, ya = (P * n)(*Ws), (P * n)(*Ys)
+    na = (ctypes.c_int64 * n)(*Ns)
+    assert L.gemmq_gemm_group(12, count, wa, ya, na, FAKE16, M, 256, path, None) == status
+
+
+def test_group_null_arrays(L):
+    P = ctypes.c_void_p
+    one_p, one_n = (P * 1)(FAKE16), (ctypes.c_int64 * 1)(1)
+    assert L.gemmq_gemm_group(12, 1, None, one_p, one_n, FAKE16, 1, 256, 0, None) == -1
+    assert L.gemmq_gemm_group(12, 1, one_p, None, one_n, FAKE16, 1, 256, 0, None) == -1
+    assert L.gemmq_gemm_group(12, 1, one_p, one_p, None, FAKE16, 1, 256, 0, None) == -1
+    assert L.gemmq_gemm_group(13, 1, one_p, one_p, one_n, FAKE16, 1, 256, 0, None) == -2
+    assert L.gemmq_gemm_group(12, 1, one_p, one_p, one_n, None, 1, 256, 0, None) == -1
 
 
 @pytest.mark.parametrize("args,status", [

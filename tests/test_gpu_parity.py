@@ -222,3 +222,24 @@ def test_empty_calls_touch_nothing(dev, gq):
     torch.cuda.synchronize()
     assert bool((y == 7.0).all())
     assert bool((xq == 0).all())
+
+
+@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("path,M", [(1, 1), (1, 5), (2, 9), (2, 130)])
+def test_group_equals_single_calls(dev, gq, orc, fmt, path, M):
+    # one launch over several matrices sharing the activations gives each matrix
+    # the bits of its own call; an empty entry is skipped
+    log("group fmt=%d path=%d M=%d" % (fmt, path, M))
+    K = 1024
+    Ns = [300, 0, 65, 1000]
+    rng = np.random.default_rng(31 * M + fmt + path)
+    Ws = [synth.make_weights(rng, fmt, N, K) for N in Ns]
+    xq = orc.quantize_q8K(_acts(rng, M, K, "outliers"))
+    xqd = to_dev(xq)
+    outs = gq.gemm_group(fmt, [to_dev(W) for W in Ws], xqd, M, Ns, K, path=path)
+    for W, N, o in zip(Ws, Ns, outs):
+        single = to_host(gq.gemm(fmt, to_dev(W), xqd, M, N, K, path=path))
+        assert np.array_equal(to_host(o).view(np.uint32), single.view(np.uint32)), N
+    yo = orc.gemm_int(fmt, Ws[2], xq, M, Ns[2], K)
+    _, S = orc.gemm_dequant(fmt, Ws[2], xq, M, Ns[2], K)
+    assert_within(to_host(outs[2]), yo, S, "group")
