@@ -22,9 +22,13 @@
 //    corrections use 24-bit multiplies and v_dot2 on the int16 group sums; one
 //    f32 fold per block and lane applies d_w, dmin and d_x.
 //  * The 64/P lane partials of each output are combined by a fixed xor tree.
+//  * Rows longer than one round are split over up to four waves of one
+//    workgroup (a round each, looping beyond 64 blocks): more, shorter waves
+//    keep the stream as parallel as for short rows; the waves' partial sums
+//    are added in LDS in wave order.
 //
-// Every output's arithmetic (per-lane block order and the xor tree) depends only
-// on K, never on M or N, so row m of an M-row call equals a one-row call on
+// Every output's arithmetic (per-lane block order, the xor tree and the wave
+// order) depends only on K, never on M or N, so row m of an M-row call equals a one-row call on
 // that row bit for bit.
 #include "device.h"
 #include "launch.h"
@@ -33,7 +37,6 @@ namespace gemmq {
 
 namespace {
 
-constexpr int kMaxIT = 4;  // rounds of 16 blocks whose loads are in flight together
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
@@ -186,11 +189,14 @@ __device__ __forceinline__ int dot16(const uint32_t* w, const u32x4& x, int s) {
 
 // ---------------------------------------------------------------- kernel
 // FMT: 12 q4_K, 14 q6_K.  MT activation rows computed (>= M).  IT rounds of 16
-// blocks loaded together.  P rows per round.  One wave per workgroup; the
-// grid is the concatenation of every grouped matrix's waves.
-template <int FMT, int MT, int IT, int P>
-__global__ __launch_bounds__(64) void gemv_kernel(const GroupTiles gt,
-                                                  const uint8_t* __restrict__ Xq, int nb, int M) {
+// blocks loaded together.  P rows per round.  KS waves share one row (P = 1):
+// wave w takes rounds w, w + KS, ... and the KS partial sums meet in LDS, added
+// in wave order.  The grid is the concatenation of every grouped matrix's
+// tiles (one tile = P rows, one workgroup of KS waves).
+template <int FMT, int MT, int IT, int P, int KS>
+__global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
+                                                       const uint8_t* __restrict__ Xq, int nb,
+                                                       int M) {
   constexpr int SEG = 64 / P;  // lanes that share a row
   constexpr int BPR = 16 / P;  // blocks of a row per round when P > 1
   constexpr int BB = FMT == 12 ? kQ4KBytes : kQ6KBytes;
@@ -198,6 +204,8 @@ __global__ __launch_bounds__(64) void gemv_kernel(const GroupTiles gt,
   const int G = lane >> 2, c = lane & 3;
   const int prow = P > 1 ? G / BPR : 0;
   const int bl0 = P > 1 ? G % BPR : G;
+  static_assert(KS == 1 || P == 1, "split rows only when one row fills a round");
+  const int w = KS > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
   // take Xq with the rest of the kernel arguments, so the weight loads below
   // do not wait for a second round of scalar loads
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(64) void gemv_kernel(const GroupTiles gt,
 #pragma unroll
   for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
 
-  for (int s0 = 0; s0 < nb; s0 += 16 * IT) {
+  for (int s0 = 16 * IT * w; s0 < nb; s0 += 16 * IT * KS) {
     // ---- 1. every weight load of these IT rounds
     uint32_t wq[IT][8], wh[IT][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
     uint32_t hd[IT][4];             // q4_K: block header; q6_K: [0] scale bytes, [1] d
@@ -316,7 +324,25 @@ __global__ __launch_bounds__(64) void gemv_kernel(const GroupTiles gt,
 
   // ---- 3. lane reduction and store
   const int64_t nn = n0 + prow;
-  if constexpr (MT <= SEG) {
+  if constexpr (KS > 1) {
+    // lanes of the xor tree hold the wave's partial of value vidx; the KS
+    // partials of each value are added in wave order by wave 0
+    __shared__ float red[KS][MT];
+    float v[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) v[m] = acc[m];
+    seg_reduce<MT, 64>(v, lane);
+    const bool hold = holder<MT, 64>(lane);
+    const int m = vidx<MT, 64>(lane);
+    if (hold) red[w][m] = v[0];
+    __syncthreads();
+    if (w == 0 && hold) {
+      float t = red[0][m];
+#pragma unroll
+      for (int k = 1; k < KS; ++k) t += red[k][m];
+      if (m < M && nn < N) Y[(int64_t)m * N + nn] = t;
+    }
+  } else if constexpr (MT <= SEG) {
     float v[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) v[m] = acc[m];
@@ -334,29 +360,31 @@ __global__ __launch_bounds__(64) void gemv_kernel(const GroupTiles gt,
   }
 }
 
-template <int FMT, int MT, int IT, int P>
+template <int FMT, int MT, int IT, int P, int KS>
 int launch_cfg(const Group& grp, const uint8_t* Xq, int nb, int M, hipStream_t st) {
   GroupTiles gt;
   if (!make_tiles(grp, P, gt)) return -1;
-  const uint32_t waves = gt.start[kMaxGroup];
-  if (waves == 0) return 0;
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P>), dim3(waves), dim3(64), 0, st, gt, Xq, nb, M);
+  const uint32_t tiles = gt.start[kMaxGroup];
+  if (tiles == 0) return 0;
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS>), dim3(tiles), dim3(64 * KS), 0, st, gt, Xq,
+                     nb, M);
   return 0;
 }
 
 // The lane mapping depends on K only: P rows side by side when a row has 16/P
-// blocks, otherwise IT rounds of 16 blocks in flight together (longer rows loop
-// over groups of kMaxIT rounds).
+// blocks; one round of 16 blocks per wave for rows of up to 16 blocks, and up
+// to four waves per row beyond that (each looping over rounds for longer rows).
 template <int FMT, int MT>
 int launch_mt(const Group& g, const uint8_t* Xq, int nb, int M, hipStream_t st) {
-  if (nb == 1) return launch_cfg<FMT, MT, 1, 16>(g, Xq, nb, M, st);
-  if (nb == 2) return launch_cfg<FMT, MT, 1, 8>(g, Xq, nb, M, st);
-  if (nb == 4) return launch_cfg<FMT, MT, 1, 4>(g, Xq, nb, M, st);
-  if (nb == 8) return launch_cfg<FMT, MT, 1, 2>(g, Xq, nb, M, st);
-  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1>(g, Xq, nb, M, st);
-  if (nb <= 32) return launch_cfg<FMT, MT, 2, 1>(g, Xq, nb, M, st);
-  if (nb <= 48) return launch_cfg<FMT, MT, 3, 1>(g, Xq, nb, M, st);
-  return launch_cfg<FMT, MT, kMaxIT, 1>(g, Xq, nb, M, st);
+  if (nb == 1) return launch_cfg<FMT, MT, 1, 16, 1>(g, Xq, nb, M, st);
+  if (nb == 2) return launch_cfg<FMT, MT, 1, 8, 1>(g, Xq, nb, M, st);
+  if (nb == 4) return launch_cfg<FMT, MT, 1, 4, 1>(g, Xq, nb, M, st);
+  if (nb == 8) return launch_cfg<FMT, MT, 1, 2, 1>(g, Xq, nb, M, st);
+  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1, 1>(g, Xq, nb, M, st);
+  if (nb <= 32) return launch_cfg<FMT, MT, 1, 1, 2>(g, Xq, nb, M, st);
+  if (nb <= 48) return launch_cfg<FMT, MT, 1, 1, 3>(g, Xq, nb, M, st);
+  if (nb <= 64) return launch_cfg<FMT, MT, 1, 1, 4>(g, Xq, nb, M, st);
+  return launch_cfg<FMT, MT, 2, 1, 4>(g, Xq, nb, M, st);
 }
 
 template <int FMT>

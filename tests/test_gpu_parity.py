@@ -133,7 +133,8 @@ def _run(gq, fmt, W, xq, M, N, K, path):
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6, 7, 8])
-@pytest.mark.parametrize("N,K", [(1, 256), (31, 512), (33, 768), (1000, 1024), (64, 3072)])
+@pytest.mark.parametrize("N,K", [(1, 256), (31, 512), (33, 768), (1000, 1024), (64, 3072),
+                                 (40, 8192), (33, 12288), (17, 20480)])
 def test_gemv_parity(dev, gq, orc, fmt, M, N, K):
     log("gemv fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
     W, _, xq = _case(orc, fmt, M, N, K, seed=100 * M + N + K + fmt)
@@ -144,7 +145,7 @@ def test_gemv_parity(dev, gq, orc, fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
-@pytest.mark.parametrize("K", [256, 1024, 3072, 4096])
+@pytest.mark.parametrize("K", [256, 1024, 3072, 4096, 12288, 20480])
 def test_gemv_rows_independent_of_M(dev, gq, orc, fmt, K):
     log("gemv M-invariance fmt=%d K=%d" % (fmt, K))
     N = 333
