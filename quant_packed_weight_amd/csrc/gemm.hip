@@ -20,16 +20,20 @@
 //  * One f32 epilogue per super-block and output:
 //    y += d_x * (d * I_sc - dmin * I_min)   (q6_K: y += d_x * d * I_sc).
 //
-// Work decomposition: a 256-thread workgroup computes a 128 (M) x 64 (N) tile;
-// each of its four waves a 64 x 32 sub-tile (two 32x32 MFMA tiles).  Per
-// super-block the workgroup stages the activation tile (int8 values, d_x, f16
-// group sums) and the weight tile -- unpacked once into the two int8 planes,
-// with d, dmin and f16 mins -- in LDS.  The global loads of super-block b+1
-// are issued before the MFMAs of super-block b and held in registers; one
-// 75 KB stage lets two workgroups share a CU, so one computes while the other
-// stages.
-// Every output's arithmetic depends only on its own row and column, so any
-// subset of rows gives identical bits.
+// Two kernels:
+//  * q4_K (gemm_q4k_kernel, further below): activation and raw weight tiles
+//    stream through LDS stages filled by direct buffer->LDS loads; each wave
+//    unpacks its own 32 weight rows and computes a 64 x 32 tile.
+//  * q6_K (gemm_kernel<14>): a 256-thread workgroup computes a 128 (M) x 64
+//    (N) tile, each of its four waves a 64 x 32 sub-tile.  Per super-block the
+//    workgroup stages the activation tile (int8 values, d_x, f16 group sums)
+//    and the weight tile -- unpacked once into the two int8 planes -- in LDS;
+//    the global loads of super-block b+1 are issued before the MFMAs of
+//    super-block b and held in registers; one 75 KB stage lets two workgroups
+//    share a CU.
+// In both, every output's arithmetic depends only on its own row and column,
+// so any subset of rows gives identical bits.  The grid's first dimension is
+// the concatenation of every grouped matrix's column tiles.
 #include <atomic>
 
 #include "device.h"
@@ -408,17 +412,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GroupTiles gt,
 //   workgroup = 4 waves, tile 64 (M) x 128 (N); wave w: all 64 rows, weight
 //   columns 32w..32w+31, unpacking its own planes (shared by its two M-tiles);
 //   stage = int8 values [64][272] | group sums [64][16] | d_x [64] |
-//   raw q4_K blocks [128][144];
+//   raw q4_K blocks [128][144] (38 KB); two stages, so two workgroups share a
+//   CU and one computes while the other waits;
 //   the two planes go to two accumulators so every activation fragment is
-//   read from LDS once.
-// The loads are issued from inline assembly: the compiler then neither sees
-// them as LDS writes (it would drain every load before each LDS read) nor
-// tracks them, and the kernel waits on vmcnt itself: a stage's loads are
-// complete once fewer than one stage's worth of later loads is outstanding.
+//   read from LDS once, three MFMA steps ahead of its use.
+// The next stage's loads are issued a sixteenth at a time, one part per
+// compute chunk, so the load queue never stalls the wave for long.  They are
+// issued from inline assembly: the compiler then neither sees them as LDS
+// writes (it would drain every load before each LDS read) nor tracks them, and
+// the kernel waits on vmcnt itself: a stage's loads are complete once fewer
+// than one stage's worth of later loads is outstanding.
 namespace q4s {
 constexpr int kBM = 64;
 constexpr int kBN = 128;
-constexpr int kS = 3;                       // LDS stages
+constexpr int kS = 2;                       // LDS stages: 76 KB, two workgroups per CU
 constexpr int kOffQ = 0;                    // [kBM][kRow] int8
 constexpr int kOffBs = kBM * kRow;          // [kBM][16] int16 group sums
 constexpr int kOffDx = kOffBs + kBM * 32;   // [kBM] f32 d_x
@@ -518,19 +525,30 @@ __device__ __forceinline__ void q4s_planes(const uint4 (&q)[4], const uint32_t (
 // of the sub-block).  The work is laid out in fenced chunks so that vector
 // work sits beside independent matrix work: M-tile 0's MFMAs of step kc run
 // beside the unpacking of step kc+1, M-tile 1's MFMAs beside tile 0's
-// epilogue; tile 1's epilogue closes the super-block.
+// epilogue; tile 1's epilogue closes the super-block.  dma(p), p = 0..15, is
+// called at the head of chunk p: it issues part p of the next stage's loads,
+// so the load queue fills a little at a time instead of stalling the wave.
+template <typename Dma>
 __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (&y)[2][16], int i,
-                                            int h) {
+                                            int h, Dma&& dma) {
   using q4s::kOffBs;
   using q4s::kOffQ;
   const uint8_t* wb = st + q4s::kOffW + wrow * kQ4KBytes;
   const uint8_t* a0 = st + kOffQ + i * kRow + 16 * h;  // M-tile 0 fragments, step kc at +32 kc
   const uint8_t* a1 = a0 + 32 * kRow;                  // M-tile 1
+  // activation fragments are read kAhead chunks before their MFMAs: fragment
+  // f = 0..15 is M-tile f/8, step f%8
+  constexpr int kAhead = 3;
+  v4i af[16];
+  auto read_af = [&](int f) {
+    af[f] = *reinterpret_cast<const v4i*>((f < 8 ? a0 : a1) + 32 * (f & 7));
+  };
   const uint4 hd = *reinterpret_cast<const uint4*>(wb);
   uint4 q[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) q[p] = *reinterpret_cast<const uint4*>(wb + 16 + 32 * p + 16 * h);
-  v4i af = *reinterpret_cast<const v4i*>(a0);
+#pragma unroll
+  for (int f = 0; f < kAhead; ++f) read_af(f);
   const Q4KScales s = q4k_scales(hd.y, hd.z, hd.w);
   const uint32_t aw[2] = {(s.sc_lo >> 3) & 0x07070707u, (s.sc_hi >> 3) & 0x07070707u};
   const uint32_t bw[2] = {s.sc_lo & 0x07070707u, s.sc_hi & 0x07070707u};
@@ -542,14 +560,11 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   v16i acca0 = (v16i){0}, accb0 = (v16i){0};
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
-    acca0 = mfma_i8(af, pa[kc], acca0);
-    accb0 = mfma_i8(af, pb[kc], accb0);
-    if (kc < 7) {
-      af = *reinterpret_cast<const v4i*>(a0 + 32 * (kc + 1));
-      q4s_planes(q, aw, bw, kc + 1, pa[kc + 1], pb[kc + 1]);
-    } else {
-      af = *reinterpret_cast<const v4i*>(a1);
-    }
+    dma(kc);
+    acca0 = mfma_i8(af[kc], pa[kc], acca0);
+    accb0 = mfma_i8(af[kc], pb[kc], accb0);
+    read_af(kc + kAhead);
+    if (kc < 7) q4s_planes(q, aw, bw, kc + 1, pa[kc + 1], pb[kc + 1]);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -580,9 +595,10 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   v16i acca1 = (v16i){0}, accb1 = (v16i){0};
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
-    acca1 = mfma_i8(af, pa[kc], acca1);
-    accb1 = mfma_i8(af, pb[kc], accb1);
-    if (kc < 7) af = *reinterpret_cast<const v4i*>(a1 + 32 * (kc + 1));
+    dma(8 + kc);
+    acca1 = mfma_i8(af[8 + kc], pa[kc], acca1);
+    accb1 = mfma_i8(af[8 + kc], pb[kc], accb1);
+    if (8 + kc + kAhead < 16) read_af(8 + kc + kAhead);
     q4s_epilogue<2>(acca0, accb0, am0, dx, dcol, mcol, y[0], 2 * kc);
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -630,20 +646,27 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
     vw[j] = (c / 9u) * wstride + 16u * (c % 9u);
   }
 
-  auto issue = [&](int b, int slot) {
+  // part p (0..15) of the loads of super-block b into stage `slot`: value rows
+  // 2p, 2p+1 (p < 8), the two group-sum blocks (8, 9), d_x (10), the weight
+  // chunks (11..15)
+  auto issue = [&](int b, int slot, int p) {
     const uint32_t st = lds0 + (uint32_t)slot * q4s::kStage;
     const uint32_t xb = (uint32_t)b * kQ8KBytes, wb = (uint32_t)b * kQ4KBytes;
+    if (p < 8) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t r = (uint32_t)(wave + 4 * j);
-      dma4(xr, vq, r * xstride + xb, st + q4s::kOffQ + r * kRow);
+      for (int j = 2 * p; j < 2 * p + 2; ++j) {
+        const uint32_t r = (uint32_t)(wave + 4 * j);
+        dma4(xr, vq, r * xstride + xb, st + q4s::kOffQ + r * kRow);
+      }
+    } else if (p < 10) {
+      dma4(xr, vbs[p - 8], xb, st + q4s::kOffBs + (wave + 4 * (p - 8)) * 256);
+    } else if (p == 10) {
+      if (wave == 0) dma4(xr, vdx, xb, st + q4s::kOffDx);
+    } else if (p < 15) {
+      dma16(wr, vw[p - 11], wb, st + q4s::kOffW + 1024 * (wave + 4 * (p - 11)));
+    } else {
+      if (wave < 2) dma16(wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
     }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) dma4(xr, vbs[jj], xb, st + q4s::kOffBs + (wave + 4 * jj) * 256);
-    if (wave == 0) dma4(xr, vdx, xb, st + q4s::kOffDx);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(wr, vw[j], wb, st + q4s::kOffW + 1024 * (wave + 4 * j));
-    if (wave < 2) dma16(wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
   };
   float y[2][16];
 #pragma unroll
@@ -655,14 +678,17 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
   // re-read it into a stage nobody reads -- so the wait count is static.
   const int blast = nb - 1;
 #pragma unroll
-  for (int s = 0; s < q4s::kS - 1; ++s) issue(s < blast ? s : blast, s);
+  for (int s = 0; s < q4s::kS - 1; ++s)
+#pragma unroll
+    for (int p = 0; p < 16; ++p) issue(s < blast ? s : blast, s, p);
   int slot = 0;
   for (int b = 0; b < nb; ++b) {
     wait_vm<q4s::kWait>();  // own loads of stage b landed
     lds_barrier();  // stage b complete everywhere; the stage of b-1 is free
     const int nxt = slot == 0 ? q4s::kS - 1 : slot - 1;
-    issue(b + q4s::kS - 1 < blast ? b + q4s::kS - 1 : blast, nxt);
-    q4s_compute(lds + slot * q4s::kStage, 32 * wave + i, y, i, h);
+    const int bn = b + q4s::kS - 1 < blast ? b + q4s::kS - 1 : blast;
+    q4s_compute(lds + slot * q4s::kStage, 32 * wave + i, y, i, h,
+                [&](int p) { issue(bn, nxt, p); });
     slot = slot + 1 == q4s::kS ? 0 : slot + 1;
   }
   wait_vm<0>();  // no load into LDS outlives the workgroup
