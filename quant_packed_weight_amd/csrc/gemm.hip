@@ -615,12 +615,20 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = lane_id(), i = lane & 31, h = lane >> 5;
-  const TileMatrix tm = tile_matrix(gt, blockIdx.x);
+  // XCD-aware order: workgroup L (x fastest) runs on XCD L % 8, each XCD with
+  // its own L2.  Give XCD x a contiguous block of the (column tile, M-tile)
+  // order with the M-tiles fastest, so the workgroups that read one weight
+  // tile run together on one XCD and fetch it from HBM once.
+  const uint32_t gy = gridDim.y, total = gridDim.x * gy;
+  const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const uint32_t full = total & ~7u;
+  const uint32_t ord = lin < full ? (lin & 7u) * (full >> 3) + (lin >> 3) : lin;
+  const TileMatrix tm = tile_matrix(gt, ord / gy);
   const uint8_t* __restrict__ W = tm.W;
   float* __restrict__ Y = tm.Y;
   const int64_t N = tm.N;
   const uint32_t tile = tm.local;
-  const int64_t n0 = (int64_t)tile * q4s::kBN, m0 = (int64_t)blockIdx.y * q4s::kBM;
+  const int64_t n0 = (int64_t)tile * q4s::kBN, m0 = (int64_t)(ord % gy) * q4s::kBM;
   const uint32_t xstride = (uint32_t)nb * kQ8KBytes, wstride = (uint32_t)nb * kQ4KBytes;
   // the workgroup's activation rows and weight rows as two buffers: rows past
   // M or N read as zero (their outputs are never stored)
