@@ -25,8 +25,10 @@ Output: one JSON line.  `value` is the M=1 weight throughput of the whole step
 (quantizer launches included); `secondary` the M=512 int8 throughput;
 `roofline` / `roofline_m512` give the dominant kernels' algorithmic rate from
 HIP events around batches of back-to-back launches against the MI355X peaks
-(HBM 8 TB/s; dense int8 MFMA 5.0 POP/s); `cpu_baseline` times the CPU oracle
-on a bounded sample.
+(HBM 8 TB/s; dense int8 MFMA 5.0 POP/s) and against ceilings measured on the
+same GPU (`ceilings`: a plain 1 GiB device copy, and the vendor library's plain
+int8 GEMM at the largest matrix's shape); `cpu_baseline` times the CPU oracle
+on a bounded sample, on all host cores and on one.
 """
 from __future__ import annotations
 
@@ -49,7 +51,7 @@ GIB = 1 << 30
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qwen3-8b-q4K")
     p.add_argument("--m", type=int, nargs="+", default=[1, 512],
@@ -58,7 +60,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--graph", action="store_true",
                    help="time HIP-graph replays of each pass instead of eager launches")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=20.0)
     p.add_argument("--no-group", action="store_true",
                    help="one launch per matrix instead of grouping matrices that share an input")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -248,42 +250,123 @@ def profiled_traffic(fam, launches):
     return round(tot / len(names))
 
 
-def cpu_baseline(wl, gen, M1, M2, seconds):
-    """The oracle, single-threaded, on a bounded sample of the same workload."""
+def measured_ceilings(wl):
+    """Ceilings measured on this GPU beside the datasheet peaks: a plain 1 GiB
+    device-to-device copy (read + write bytes), and a plain int8 GEMM from the
+    vendor library (torch._int_mm, int8 x int8 -> int32, no quantized format) at
+    the largest matrix's shape with M = 512."""
+    import torch
+
+    out = {}
+    n = GIB
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_GBs"] = round(2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    big = max(wl.matrices, key=lambda m: m.N * m.K)
+    try:
+        a = torch.randint(-127, 128, (512, big.K), dtype=torch.int8, device="cuda:0")
+        b = torch.randint(-127, 128, (big.K, big.N), dtype=torch.int8, device="cuda:0")
+        for _ in range(3):
+            torch._int_mm(a, b)
+        e0.record()
+        for _ in range(10):
+            torch._int_mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        out["int8_gemm_TOPs"] = round(2 * 512 * big.N * big.K * 10 /
+                                      (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        out["int8_gemm_shape"] = "512x%dx%d (torch._int_mm)" % (big.N, big.K)
+    except Exception as e:  # not every build has an int8 GEMM
+        out["int8_gemm_TOPs"] = None
+        out["int8_gemm_error"] = type(e).__name__
+    return out
+
+
+def sample_rows(M, n=32, seed=512):
+    """A seeded sample of n activation rows of M, the first and last included."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, M - 1), size=min(n, M) - 2, replace=False)
+    return np.sort(np.concatenate([[0, M - 1], mid])).astype(np.int64)
+
+
+def _oracle_rate(wl, gen, M1, M2, seconds, threads):
+    """One bounded sample of the oracle with `threads` host threads: each matrix
+    split into row ranges run concurrently (the C oracle releases the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import oracle
 
-    out = {"kind": "oracle", "cores": 1}
-    # M = M1 (decode): whole passes over all matrices until `seconds` elapse
-    passes, t0 = 0, time.perf_counter()
-    while True:
-        xq = {inp: oracle.quantize_q8K(gen.activations[(M1, inp)]) for inp, _ in wl.inputs()}
+    def run_all(pool, xq, M, rows=None):
+        jobs = []
         for m in wl.matrices:
-            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.inp], M1, m.N, m.K)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or passes >= 50:
-            break
+            W = gen.weights[m.name]
+            step = -(-m.N // threads)
+            for n0 in range(0, m.N, step):
+                n1 = min(m.N, n0 + step)
+                jobs.append(pool.submit(oracle.gemm_int, m.fmt, W[n0:n1], xq[m.inp], M, n1 - n0,
+                                        m.K, rows))
+        for j in jobs:
+            j.result()
+
+    res = {}
+    with ThreadPoolExecutor(threads) as pool:
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            xq = {inp: oracle.quantize_q8K(gen.activations[(M1, inp)]) for inp, _ in wl.inputs()}
+            run_all(pool, xq, M1)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or passes >= 2000:
+                break
+        res["m1"] = (passes, el)
+        if M2:
+            rows = sample_rows(M2)
+            xq = {inp: oracle.quantize_q8K(gen.activations[(M2, inp)][rows])
+                  for inp, _ in wl.inputs()}
+            t0 = time.perf_counter()
+            run_all(pool, xq, len(rows))
+            res["m2"] = time.perf_counter() - t0
+    return res
+
+
+def cpu_baseline(wl, gen, M1, M2, seconds):
+    """The oracle on a bounded sample of the same workload, on all of this host's
+    cores (the row-parallel thin driver above) and on one core."""
+    cores = len(os.sched_getaffinity(0))
     wbytes = sum(m.nbytes for m in wl.matrices)
-    out["value"] = wbytes * passes / el / 1e9
-    out["unit"] = "GB/s"
-    out["sample"] = ("%d full pass(es) of the %d-matrix layer at M=%d (quantize + integer-route "
-                     "matmul), %.1f s" % (passes, len(wl.matrices), M1, el))
-    if M2:
-        rows = np.array([0, M2 - 1])
-        xq = {inp: oracle.quantize_q8K(gen.activations[(M2, inp)][rows])
-              for inp, _ in wl.inputs()}
-        t0 = time.perf_counter()
-        ops = 0
-        for m in wl.matrices:
-            oracle.gemm_int(m.fmt, gen.weights[m.name], xq[m.inp], len(rows), m.N, m.K)
-            ops += 2 * len(rows) * m.N * m.K
-        el = time.perf_counter() - t0
-        out["value_m%d" % M2] = ops / el / 1e12
-        out["unit_m%d" % M2] = "TOP/s"
-        out["sample_m%d" % M2] = ("rows {0, %d} of M=%d through all %d matrices, %.1f s"
-                                  % (M2 - 1, M2, len(wl.matrices), el))
+    nrows = len(sample_rows(M2)) if M2 else 0
+    ops2 = sum(2 * nrows * m.N * m.K for m in wl.matrices)
+    out = {"kind": "oracle", "cores": cores}
+    for label, threads in (("", cores), ("_1core", 1)):
+        r = _oracle_rate(wl, gen, M1, M2, seconds / 4, threads)
+        passes, el = r["m1"]
+        out["value" + label] = wbytes * passes / el / 1e9
+        if not label:
+            out["unit"] = "GB/s"
+            out["sample"] = ("%d full pass(es) of the %d-matrix layer at M=%d (quantize + "
+                             "integer-route matmul, each matrix's rows split over %d threads), "
+                             "%.1f s; the same with 1 thread in value_1core"
+                             % (passes, len(wl.matrices), M1, threads, el))
+        if M2:
+            out["value_m%d%s" % (M2, label)] = ops2 / r["m2"] / 1e12
+            if not label:
+                out["unit_m%d" % M2] = "TOP/s"
+                out["sample_m%d" % M2] = ("%d seeded rows of M=%d (first and last included) "
+                                          "through all %d matrices, %.1f s (1 thread: value_m%d_1core)"
+                                          % (nrows, M2, len(wl.matrices), r["m2"], M2))
     return out
 
 
@@ -390,6 +473,15 @@ def main():
         res["secondary"] = {"metric": "int8 TOP/s at M=%d" % M2,
                             "value": round(ops[M2] / t[M2] / 1e12, 1), "unit": "TOP/s"}
         res["roofline_m%d" % M2] = roof(M2)
+    c = res["ceilings"] = measured_ceilings(wl)
+    c["copy_frac_of_peak"] = round(c["copy_GBs"] / HBM_PEAK_GBS, 4)
+    if c.get("int8_gemm_TOPs"):
+        c["int8_gemm_frac_of_peak"] = round(c["int8_gemm_TOPs"] / INT8_PEAK_TOPS, 4)
+    # the kernels against the measured ceilings as well as the datasheet peaks
+    res["roofline"]["frac_of_measured_copy"] = round(res["roofline"]["achieved"] / c["copy_GBs"], 4)
+    if M2 and c.get("int8_gemm_TOPs"):
+        res["roofline_m%d" % M2]["vs_int8_gemm_library"] = round(
+            res["roofline_m%d" % M2]["achieved"] / c["int8_gemm_TOPs"], 4)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, gen, M1, M2, a.cpu_seconds)
     print(json.dumps(res), flush=True)
