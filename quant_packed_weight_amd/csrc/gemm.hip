@@ -425,13 +425,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GroupTiles gt,
 namespace q4s {
 constexpr int kBM = 64;
 constexpr int kBN = 128;
-constexpr int kS = 2;                       // LDS stages: 76 KB, two workgroups per CU
+constexpr int kS = 2;                       // LDS stages
 constexpr int kOffQ = 0;                    // [kBM][kRow] int8
 constexpr int kOffBs = kBM * kRow;          // [kBM][16] int16 group sums
 constexpr int kOffDx = kOffBs + kBM * 32;   // [kBM] f32 d_x
 constexpr int kOffW = kOffDx + kBM * 4;     // [kBN][144] raw weight blocks
 constexpr int kStage = kOffW + kBN * kQ4KBytes;
-constexpr int kLds = kS * kStage;
+// SPLIT K-groups of four waves per workgroup: 1 (76 KB, two workgroups per CU)
+// or 2 (152.6 KB, one workgroup of eight waves per CU, each group half of the
+// super-blocks); both give two waves per SIMD when the grid fills the CUs, and
+// the split keeps two per SIMD on grids of one workgroup per CU.  It is chosen
+// from K alone (rows of 32 super-blocks or more), so an output's summation
+// order never depends on M.
+template <int SPLIT>
+constexpr int lds_bytes() { return kS * SPLIT * kStage; }
 // loads per stage issued by each wave: 16 value rows + 2 group-sum blocks + 4
 // weight chunks (waves 0 and 1 a fifth, wave 0 also the 64 d_x); waits count
 // the smallest number, which can only wait for more than needed.
@@ -609,11 +616,14 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   q4s_epilogue<16>(acca1, accb1, am1, dx, dcol, mcol, y[1], 0);
 }
 
-__global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
-                                                          const uint8_t* __restrict__ Xq, int64_t M,
-                                                          int nb) {
+template <int SPLIT>
+__global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
+    const GroupTiles gt, const uint8_t* __restrict__ Xq, int64_t M, int nb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // SPLIT groups of four waves: K-group kg takes super-blocks [kg nb0, ...);
+  // in each group wave `wave` owns weight columns 32 wave .. 32 wave + 31
+  const int wave8 = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int kg = SPLIT > 1 ? wave8 >> 2 : 0, wave = wave8 & 3;
   const int lane = lane_id(), i = lane & 31, h = lane >> 5;
   // XCD-aware order: workgroup L (x fastest) runs on XCD L % 8, each XCD with
   // its own L2.  Give XCD x a contiguous block of the (column tile, M-tile)
@@ -636,7 +646,11 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
   const int64_t nrows = N - n0 < q4s::kBN ? N - n0 : q4s::kBN;
   const rsrc_t xr = make_rsrc(Xq + m0 * xstride, (uint32_t)(mrows * xstride));
   const rsrc_t wr = make_rsrc(W + n0 * wstride, (uint32_t)(nrows * wstride));
-  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)lds);
+  // this group's half of every stage
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)lds) +
+                        (uint32_t)kg * q4s::kStage;
+  uint8_t* const ldsg = lds + kg * q4s::kStage;
+  constexpr int kStride = SPLIT * q4s::kStage;  // bytes from one stage to the next
 
   // per-lane source offsets within one super-block column
   const uint32_t vq = 4 + 4 * lane;  // value bytes of a row: one dword per lane
@@ -658,7 +672,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
   // 2p, 2p+1 (p < 8), the two group-sum blocks (8, 9), d_x (10), the weight
   // chunks (11..15)
   auto issue = [&](int b, int slot, int p) {
-    const uint32_t st = lds0 + (uint32_t)slot * q4s::kStage;
+    const uint32_t st = lds0 + (uint32_t)slot * kStride;
     const uint32_t xb = (uint32_t)b * kQ8KBytes, wb = (uint32_t)b * kQ4KBytes;
     if (p < 8) {
 #pragma unroll
@@ -682,25 +696,50 @@ __global__ __launch_bounds__(256, 2) void gemm_q4k_kernel(const GroupTiles gt,
 #pragma unroll
     for (int r = 0; r < 16; ++r) y[t][r] = 0.0f;
 
-  // Every step issues one stage of loads -- past the last super-block they
-  // re-read it into a stage nobody reads -- so the wait count is static.
-  const int blast = nb - 1;
+  // Step s: group kg works on super-block b0 + s.  Every step issues one stage
+  // of loads -- past the group's last block they re-read a valid block into a
+  // stage nobody reads -- so the wait count is static.
+  const int nb0 = SPLIT > 1 ? (nb + 1) >> 1 : nb;
+  const int b0 = kg ? nb0 : 0, bend = kg ? nb : nb0;
+  auto blk = [&](int s) { return b0 + s < nb ? b0 + s : nb - 1; };
 #pragma unroll
   for (int s = 0; s < q4s::kS - 1; ++s)
 #pragma unroll
-    for (int p = 0; p < 16; ++p) issue(s < blast ? s : blast, s, p);
+    for (int p = 0; p < 16; ++p) issue(blk(s), s, p);
   int slot = 0;
-  for (int b = 0; b < nb; ++b) {
-    wait_vm<q4s::kWait>();  // own loads of stage b landed
-    lds_barrier();  // stage b complete everywhere; the stage of b-1 is free
+  for (int s = 0; s < nb0; ++s) {
+    wait_vm<q4s::kWait>();  // own loads of stage s landed
+    lds_barrier();  // stage s complete everywhere; the stage of s-1 is free
     const int nxt = slot == 0 ? q4s::kS - 1 : slot - 1;
-    const int bn = b + q4s::kS - 1 < blast ? b + q4s::kS - 1 : blast;
-    q4s_compute(lds + slot * q4s::kStage, 32 * wave + i, y, i, h,
-                [&](int p) { issue(bn, nxt, p); });
+    const int bn = blk(s + q4s::kS - 1);
+    if (b0 + s < bend)
+      q4s_compute(ldsg + slot * kStride, 32 * wave + i, y, i, h,
+                  [&](int p) { issue(bn, nxt, p); });
+    else  // the second group's idle last step (odd nb): only its loads
+#pragma unroll
+      for (int p = 0; p < 16; ++p) issue(bn, nxt, p);
     slot = slot + 1 == q4s::kS ? 0 : slot + 1;
   }
   wait_vm<0>();  // no load into LDS outlives the workgroup
 
+  if constexpr (SPLIT > 1) {
+    // the second K-group hands its partial sums to the first through LDS; the
+    // first adds them (its own first) and stores
+    lds_barrier();
+    float* red = reinterpret_cast<float*>(lds) + wave * (32 * 64) + lane;
+    if (kg == 1) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[(16 * t + r) * 64] = y[t][r];
+    }
+    lds_barrier();
+    if (kg == 1) return;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) y[t][r] += red[(16 * t + r) * 64];
+  }
   const int64_t col = n0 + 32 * wave + i;
   if (col < N) {
 #pragma unroll
@@ -725,10 +764,13 @@ int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
   if (attr_done[dev].load(std::memory_order_acquire) == 0) {
     if (hipFuncSetAttribute((const void*)gemm_kernel<14>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess)
-      return -1;
-    if (hipFuncSetAttribute((const void*)gemm_q4k_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, q4s::kLds) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
+        hipFuncSetAttribute((const void*)gemm_q4k_kernel<1>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            q4s::lds_bytes<1>()) != hipSuccess ||
+        hipFuncSetAttribute((const void*)gemm_q4k_kernel<2>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            q4s::lds_bytes<2>()) != hipSuccess)
       return -1;
     attr_done[dev].store(1, std::memory_order_release);
   }
@@ -739,12 +781,18 @@ int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t
   const int64_t gy = (M + bm - 1) / bm;
   if (gy > 65535) return -1;
   if (gx == 0) return 0;
-  if (fmt == 12)
-    hipLaunchKernelGGL(gemm_q4k_kernel, dim3(gx, (uint32_t)gy), dim3(256), q4s::kLds, st, gt, Xq,
-                       M, (int)nb);
-  else
-    hipLaunchKernelGGL(gemm_kernel<14>, dim3(gx, (uint32_t)gy), dim3(256), kLds, st, gt, Xq, M,
-                       (int)nb);
+  const dim3 grid(gx, (uint32_t)gy);
+  if (fmt == 12) {
+    // long rows run split over K (the choice depends on K only)
+    if (nb >= 32)
+      hipLaunchKernelGGL(gemm_q4k_kernel<2>, grid, dim3(512), q4s::lds_bytes<2>(), st, gt, Xq, M,
+                         (int)nb);
+    else
+      hipLaunchKernelGGL(gemm_q4k_kernel<1>, grid, dim3(256), q4s::lds_bytes<1>(), st, gt, Xq, M,
+                         (int)nb);
+  } else {
+    hipLaunchKernelGGL(gemm_kernel<14>, grid, dim3(256), kLds, st, gt, Xq, M, (int)nb);
+  }
   return 0;
 }
 

@@ -163,7 +163,8 @@ def test_gemv_rows_independent_of_M(dev, gq, orc, fmt, K):
 @pytest.mark.parametrize("fmt", [Q4, Q6])
 @pytest.mark.parametrize("M,N,K", [(9, 1, 256), (16, 33, 512), (31, 64, 256), (32, 65, 768),
                                    (33, 200, 1024), (128, 64, 512), (129, 127, 256),
-                                   (300, 130, 1024), (511, 96, 3072), (1, 70, 512), (8, 64, 256)])
+                                   (300, 130, 1024), (511, 96, 3072), (1, 70, 512), (8, 64, 256),
+                                   (40, 70, 8192), (70, 130, 12544), (600, 4500, 256)])
 def test_gemm_parity(dev, gq, orc, fmt, M, N, K):
     log("gemm fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
     W, _, xq = _case(orc, fmt, M, N, K, seed=7 * M + 3 * N + K + fmt)
@@ -174,9 +175,10 @@ def test_gemm_parity(dev, gq, orc, fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
-def test_gemm_rows_independent_of_call(dev, gq, orc, fmt):
-    log("gemm row-subset fmt=%d" % fmt)
-    M, N, K = 300, 150, 1024
+@pytest.mark.parametrize("K", [1024, 8192])
+def test_gemm_rows_independent_of_call(dev, gq, orc, fmt, K):
+    log("gemm row-subset fmt=%d K=%d" % (fmt, K))
+    M, N = 300, 150
     W, _, xq = _case(orc, fmt, M, N, K, seed=77 + fmt)
     Wd = to_dev(W)
     full = to_host(gq.gemm(fmt, Wd, to_dev(xq), M, N, K, path=gq.PATH_GEMM))
