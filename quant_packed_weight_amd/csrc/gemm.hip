@@ -24,12 +24,12 @@
 //  * q4_K (gemm_q4k_kernel, further below): activation and raw weight tiles
 //    stream through LDS stages filled by direct buffer->LDS loads; each wave
 //    unpacks its own 32 weight rows and computes a 64 x 32 tile.
-//  * q6_K (gemm_kernel<14>): a 256-thread workgroup computes a 128 (M) x 64
+//  * q6_K (gemm_q6k_kernel): a 256-thread workgroup computes a 128 (M) x 64
 //    (N) tile, each of its four waves a 64 x 32 sub-tile.  Per super-block the
 //    workgroup stages the activation tile (int8 values, d_x, f16 group sums)
 //    and the weight tile -- unpacked once into the two int8 planes -- in LDS;
 //    the global loads of super-block b+1 are issued before the MFMAs of
-//    super-block b and held in registers; one 75 KB stage lets two workgroups
+//    super-block b and held in registers; one 69 KB stage lets two workgroups
 //    share a CU.
 // In both, every output's arithmetic depends only on its own row and column,
 // so any subset of rows gives identical bits.  The grid's first dimension is
@@ -57,14 +57,11 @@ constexpr int kRow = 256 + 16;  // LDS stride of one int8 K-row (padded against 
 
 // LDS map of one stage (bytes)
 constexpr int kOffA = 0;                     // [kBM][kRow] activation int8
-constexpr int kOffPa = kOffA + kBM * kRow;   // [kBN][kRow] weight plane A (weight 8 / 128)
+constexpr int kOffPa = kOffA + kBM * kRow;   // [kBN][kRow] weight plane A (weight 128)
 constexpr int kOffPb = kOffPa + kBN * kRow;  // [kBN][kRow] weight plane B
-constexpr int kOffBs = kOffPb + kBN * kRow;  // [kBM][16] f16 group sums
-constexpr int kOffDx = kOffBs + kBM * 32;    // [kBM] f32 d_x
+constexpr int kOffDx = kOffPb + kBN * kRow;  // [kBM] f32 d_x
 constexpr int kOffD = kOffDx + kBM * 4;      // [kBN] f32 d
-constexpr int kOffDm = kOffD + kBN * 4;      // [kBN] f32 dmin
-constexpr int kOffMn = kOffDm + kBN * 4;     // [kBN][16] f16 m_{t/2}, t = 0..15
-constexpr int kStage = kOffMn + kBN * 32;
+constexpr int kStage = kOffD + kBN * 4;
 constexpr int kLds = kStage;  // one stage: two workgroups fit in a CU's 160 KB
 
 // bytes of w (each <= 15) times a (<= 7): per 16-bit half the product stays below
@@ -92,12 +89,12 @@ __device__ __forceinline__ uint32_t i16x2_to_h2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// ------------------------------------------------- activation tile
-// thread t: row t/2, half t%2 of the 256 int8 values; half 0 also d_x, half 1
-// also the 16 group sums.
+// ------------------------------------------------- activation tile (q6_K kernel)
+// thread t: row t/2, half t%2 of the 256 int8 values; half 0 also d_x (the
+// q6_K route needs no group sums: the -32 offset is in the weight planes).
 struct XRegs {
   u32x4 q[8];
-  uint32_t e[8];
+  uint32_t d;
 };
 
 // Rows past M load a copy of row M-1: MFMA rows are independent and those
@@ -113,13 +110,7 @@ __device__ __forceinline__ void load_x(XRegs& r, const uint8_t* xrow, int b) {
   const uint8_t* xb = xrow + b * kQ8KBytes;
 #pragma unroll
   for (int i = 0; i < 8; ++i) r.q[i] = ld16(xb + 4 + 128 * part + 16 * i);
-  if (part == 0) {
-    r.e[0] = ld4(xb);
-  } else {
-    const u32x4 s0 = ld16(xb + 260), s1 = ld16(xb + 276);
-    r.e[0] = s0.x; r.e[1] = s0.y; r.e[2] = s0.z; r.e[3] = s0.w;
-    r.e[4] = s1.x; r.e[5] = s1.y; r.e[6] = s1.z; r.e[7] = s1.w;
-  }
+  r.d = part == 0 ? ld4(xb) : 0u;
 }
 
 __device__ __forceinline__ void store_x(uint8_t* st, const XRegs& r) {
@@ -127,77 +118,14 @@ __device__ __forceinline__ void store_x(uint8_t* st, const XRegs& r) {
   uint8_t* a = st + kOffA + row * kRow + 128 * part;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st16(a + 16 * i, r.q[i].x, r.q[i].y, r.q[i].z, r.q[i].w);
-  if (part == 0) {
-    reinterpret_cast<uint32_t*>(st + kOffDx)[row] = r.e[0];
-  } else {
-    uint8_t* s = st + kOffBs + row * 32;
-    st16(s, i16x2_to_h2(r.e[0]), i16x2_to_h2(r.e[1]), i16x2_to_h2(r.e[2]), i16x2_to_h2(r.e[3]));
-    st16(s + 16, i16x2_to_h2(r.e[4]), i16x2_to_h2(r.e[5]), i16x2_to_h2(r.e[6]),
-         i16x2_to_h2(r.e[7]));
-  }
+  if (part == 0) reinterpret_cast<uint32_t*>(st + kOffDx)[row] = r.d;
 }
 
-// ------------------------------------------------- q4_K weight tile
-// thread t: column t/4, 64-weight group g = t%4 (qs bytes 32g..32g+31, holding
-// sub-block 2g in the low nibbles and 2g+1 in the high nibbles).
-struct W4Regs {
-  uint4 hd, q0, q1;
-};
-
 // Columns past N load a copy of column N-1 (never stored).
-template <int BB>
 __device__ __forceinline__ const uint8_t* w_row(const uint8_t* __restrict__ W, int64_t n0,
                                                 int64_t N, int nb) {
   const int64_t n = n0 + (threadIdx.x >> 2);
-  return W + (n < N ? n : N - 1) * nb * BB;
-}
-
-__device__ __forceinline__ void load_w(W4Regs& r, const uint8_t* wrow, int b) {
-  const int g = threadIdx.x & 3;
-  const uint8_t* wb = wrow + b * kQ4KBytes;
-  r.hd = ld16a(wb);
-  r.q0 = ld16a(wb + 16 + 32 * g);
-  r.q1 = ld16a(wb + 32 + 32 * g);
-}
-
-__device__ __forceinline__ void store_w(uint8_t* st, const W4Regs& r) {
-  const int t = threadIdx.x, col = t >> 2, g = t & 3;
-  const Q4KScales s = q4k_scales(r.hd.y, r.hd.z, r.hd.w);
-  const uint32_t scw = g >= 2 ? s.sc_hi : s.sc_lo;
-  const uint32_t mnw = g >= 2 ? s.mn_hi : s.mn_lo;
-  const int sh = 16 * (g & 1);
-  const uint32_t sc0 = (scw >> sh) & 0xffu, sc1 = (scw >> (sh + 8)) & 0xffu;
-  const uint32_t mn0 = (mnw >> sh) & 0xffu, mn1 = (mnw >> (sh + 8)) & 0xffu;
-  const uint32_t a0 = sc0 >> 3, b0 = sc0 & 7u, a1 = sc1 >> 3, b1 = sc1 & 7u;
-  const uint32_t w[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
-  uint32_t pal[8], pah[8], pbl[8], pbh[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint32_t lo = lo_nib(w[k]), hi = hi_nib(w[k]);
-    pal[k] = mul_bytes(lo, a0);
-    pbl[k] = mul_bytes(lo, b0);
-    pah[k] = mul_bytes(hi, a1);
-    pbh[k] = mul_bytes(hi, b1);
-  }
-  uint8_t* pa = st + kOffPa + col * kRow + 64 * g;
-  uint8_t* pb = st + kOffPb + col * kRow + 64 * g;
-  st16(pa, pal[0], pal[1], pal[2], pal[3]);
-  st16(pa + 16, pal[4], pal[5], pal[6], pal[7]);
-  st16(pa + 32, pah[0], pah[1], pah[2], pah[3]);
-  st16(pa + 48, pah[4], pah[5], pah[6], pah[7]);
-  st16(pb, pbl[0], pbl[1], pbl[2], pbl[3]);
-  st16(pb + 16, pbl[4], pbl[5], pbl[6], pbl[7]);
-  st16(pb + 32, pbh[0], pbh[1], pbh[2], pbh[3]);
-  st16(pb + 48, pbh[4], pbh[5], pbh[6], pbh[7]);
-  // mins as f16, each twice: entries 4g..4g+3 = m_{2g}, m_{2g}, m_{2g+1}, m_{2g+1}
-  const h2 f0 = {(_Float16)(float)mn0, (_Float16)(float)mn0};
-  const h2 f1 = {(_Float16)(float)mn1, (_Float16)(float)mn1};
-  *reinterpret_cast<uint2*>(st + kOffMn + col * 32 + 8 * g) =
-      make_uint2(__builtin_bit_cast(uint32_t, f0), __builtin_bit_cast(uint32_t, f1));
-  if (g == 0) {
-    reinterpret_cast<float*>(st + kOffD)[col] = f16_to_f32(r.hd.x);
-    reinterpret_cast<float*>(st + kOffDm)[col] = f16_to_f32(r.hd.x >> 16);
-  }
+  return W + (n < N ? n : N - 1) * nb * kQ6KBytes;
 }
 
 // ------------------------------------------------- q6_K weight tile
@@ -275,11 +203,10 @@ __device__ __forceinline__ void store_w(uint8_t* st, const W6Regs& r) {
 // ------------------------------------------------- one super-block from LDS
 // 32x32 accumulator layout: lane holds column lane%32; register r holds row
 // 8*(r/4) + 4*(lane/32) + r%4.
-template <int FMT>
 __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], int arow0, int bcol,
                                         int hsel) {
-  // plane A over the super-block, then acc <<= 3 (q4_K) or 7 (q6_K), then
-  // plane B on top: acc = I_sc, exact in int32; two independent chains
+  // plane A (hi) over the super-block, then acc <<= 7, then plane B (lo) on
+  // top: acc = I_sc, exact in int32; two independent chains
   v16i acc[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) acc[mt] = (v16i){0};
@@ -292,11 +219,10 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
       acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
                         ba, acc[mt]);
   }
-  constexpr int kShift = FMT == 12 ? 3 : 7;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << kShift);
+    for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << 7);
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
     const int ko = 32 * kc + 16 * hsel;
@@ -307,55 +233,26 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
                         bb, acc[mt]);
   }
   const float dcol = reinterpret_cast<const float*>(st + kOffD)[bcol];
-  if constexpr (FMT == 12) {
-    const float mcol = reinterpret_cast<const float*>(st + kOffDm)[bcol];
-    // min term: lane half h carries group sums 8h..8h+7 against m_{(8h+t)/2}
-    const v8h mfrag = *reinterpret_cast<const v8h*>(st + kOffMn + bcol * 32 + 16 * hsel);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const v8h sfrag =
-          *reinterpret_cast<const v8h*>(st + kOffBs + (arow0 + 32 * mt) * 32 + 16 * hsel);
-      const v16f am = mfma_f16(sfrag, mfrag, (v16f){0});
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 dx = *reinterpret_cast<const float4*>(st + kOffDx +
-                                                           4 * (arow0 - (arow0 & 31) + 32 * mt +
-                                                                8 * q4 + 4 * hsel));
-        const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const float4 dx = *reinterpret_cast<const float4*>(
+          st + kOffDx + 4 * (arow0 - (arow0 & 31) + 32 * mt + 8 * q4 + 4 * hsel));
+      const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int r = 4 * q4 + s;
-          float tt = dcol * (float)acc[mt][r];
-          tt = fmaf(-mcol, am[r], tt);
-          y[mt][r] = fmaf(dxs[s], tt, y[mt][r]);
-        }
+      for (int s = 0; s < 4; ++s) {
+        const int r = 4 * q4 + s;
+        y[mt][r] = fmaf(dxs[s], dcol * (float)acc[mt][r], y[mt][r]);
       }
     }
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const float4 dx = *reinterpret_cast<const float4*>(st + kOffDx +
-                                                           4 * (arow0 - (arow0 & 31) + 32 * mt +
-                                                                8 * q4 + 4 * hsel));
-        const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const int r = 4 * q4 + s;
-          y[mt][r] = fmaf(dxs[s], dcol * (float)acc[mt][r], y[mt][r]);
-        }
-      }
-  }
 }
 
-// ------------------------------------------------- the kernel
-template <int FMT>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const GroupTiles gt,
-                                                      const uint8_t* __restrict__ Xq, int64_t M,
-                                                      int nb) {
+// ------------------------------------------------- the q6_K kernel
+__global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
+                                                          const uint8_t* __restrict__ Xq, int64_t M,
+                                                          int nb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  using WRegs = typename std::conditional<FMT == 12, W4Regs, W6Regs>::type;
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
   const uint8_t* __restrict__ W = tm.W;
   float* __restrict__ Y = tm.Y;
@@ -377,9 +274,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GroupTiles gt,
     for (int r = 0; r < 16; ++r) y[mt][r] = 0.0f;
 
   const uint8_t* xrow = x_row(Xq, m0, M, nb);
-  const uint8_t* wrow = w_row<FMT == 12 ? kQ4KBytes : kQ6KBytes>(W, n0, N, nb);
+  const uint8_t* wrow = w_row(W, n0, N, nb);
   XRegs xr;
-  WRegs wr;
+  W6Regs wr;
   load_x(xr, xrow, 0);
   load_w(wr, wrow, 0);
   for (int b = 0; b < nb; ++b) {
@@ -390,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GroupTiles gt,
       load_x(xr, xrow, b + 1);
       load_w(wr, wrow, b + 1);
     }
-    compute<FMT>(lds, y, arow0, bcol, hsel);
+    compute(lds, y, arow0, bcol, hsel);
     __syncthreads();
   }
 
@@ -763,7 +660,7 @@ int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
   if (attr_done[dev].load(std::memory_order_acquire) == 0) {
-    if (hipFuncSetAttribute((const void*)gemm_kernel<14>,
+    if (hipFuncSetAttribute((const void*)gemm_q6k_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_q4k_kernel<1>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -791,7 +688,7 @@ int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t
       hipLaunchKernelGGL(gemm_q4k_kernel<1>, grid, dim3(256), q4s::lds_bytes<1>(), st, gt, Xq, M,
                          (int)nb);
   } else {
-    hipLaunchKernelGGL(gemm_kernel<14>, grid, dim3(256), kLds, st, gt, Xq, M, (int)nb);
+    hipLaunchKernelGGL(gemm_q6k_kernel, grid, dim3(256), kLds, st, gt, Xq, M, (int)nb);
   }
   return 0;
 }
