@@ -1,6 +1,7 @@
-"""HIP-graph capture of the hot path (quantize + GEMV + GEMM), as the benchmark
-submits it: every replay must equal the eager result bit for bit, with eager
-work, synchronisations and changed inputs between the replays."""
+"""HIP-graph capture of the hot path (quantize + GEMV + GEMM, single and grouped
+launches), as the benchmark submits it: every replay must equal the eager result
+bit for bit, with eager work, synchronisations and changed inputs between the
+replays."""
 import numpy as np
 import pytest
 
@@ -27,17 +28,38 @@ def test_graph_replays_match_eager():
         Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
         bufs.append((fmt, M, N, K, W, X, Xq, Y))
 
+    # grouped launches: two matrices sharing one input, GEMV and GEMM
+    groups = []
+    for M in (1, 40):
+        K, Ns = 1024, (300, 77)
+        Ws = [torch.from_numpy(synth.make_weights(rng, gq.FMT_Q4K, N, K)).cuda() for N in Ns]
+        X = torch.from_numpy(synth.make_activations(rng, M, K, True)).cuda()
+        Xq = torch.empty(gq.q8K_bytes(M, K), dtype=torch.uint8, device="cuda")
+        Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for N in Ns]
+        groups.append((M, K, Ns, Ws, X, Xq, Ys))
+
     def run(stream):
         st = stream.cuda_stream
         for fmt, M, N, K, W, X, Xq, Y in bufs:
             assert gq.quantize_q8K_ptr(X.data_ptr(), Xq.data_ptr(), M, K, st) == 0
             assert gq.gemm_ptr(fmt, W.data_ptr(), Xq.data_ptr(), Y.data_ptr(), M, N, K,
                                gq.PATH_AUTO, st) == 0
+        for M, K, Ns, Ws, X, Xq, Ys in groups:
+            assert gq.quantize_q8K_ptr(X.data_ptr(), Xq.data_ptr(), M, K, st) == 0
+            assert gq.gemm_group_ptr(gq.FMT_Q4K, [w.data_ptr() for w in Ws],
+                                     [y.data_ptr() for y in Ys], list(Ns), Xq.data_ptr(), M, K,
+                                     gq.PATH_AUTO, st) == 0
+
+    def outputs():
+        out = [(b[6], b[7]) for b in bufs]
+        for M, K, Ns, Ws, X, Xq, Ys in groups:
+            out += [(Xq, y) for y in Ys]
+        return out
 
     def eager_ref():
         run(torch.cuda.current_stream())
         torch.cuda.synchronize()
-        return [(b[6].clone(), b[7].clone()) for b in bufs]
+        return [(xq.clone(), y.clone()) for xq, y in outputs()]
 
     ref = eager_ref()
     side = torch.cuda.Stream()
@@ -53,18 +75,20 @@ def test_graph_replays_match_eager():
 
     for rep in range(4):
         log("replay %d" % rep)
-        for b in bufs:  # clobber outputs so a replay that skips work is caught
-            b[6].fill_(0xAB)
-            b[7].fill_(float("nan"))
+        for xq, y in outputs():  # clobber outputs so a replay that skips work is caught
+            xq.fill_(0xAB)
+            y.fill_(float("nan"))
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for (xq_ref, y_ref), b in zip(ref, bufs):
-            assert torch.equal(b[6], xq_ref)
-            assert torch.equal(b[7].view(torch.int32), y_ref.view(torch.int32))
+        for (xq_ref, y_ref), (xq, y) in zip(ref, outputs()):
+            assert torch.equal(xq, xq_ref)
+            assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
         # eager work between replays, then new inputs: the next replay must follow them
         eager_ref()
         if rep == 1:
             for b in bufs:
                 b[5].mul_(-0.5)
+            for grp in groups:
+                grp[4].mul_(-0.5)
             ref = eager_ref()

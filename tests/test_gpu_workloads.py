@@ -1,8 +1,10 @@
 """Parity on the five Qwen3-shaped workloads at full size, in the launch
 configuration the benchmark times (automatic path choice, activations quantized
-on the GPU).  Rows of large M are sampled (always the first and the last); the
-oracle computes those rows against every weight row.  Bit-exact q8_K bytes for
-the sampled rows; f32 outputs within 1e-5 * sum|w*xhat| + 1e-6.
+on the GPU, consecutive matrices that read one activation in one format run as
+one grouped launch).  Rows of large M are sampled (8 seeded rows, always the
+first and the last); the oracle computes those rows against every weight row.
+Bit-exact q8_K bytes for the sampled rows; f32 outputs within
+1e-5 * sum|w*xhat| + 1e-6.
 """
 import numpy as np
 import pytest
@@ -22,8 +24,20 @@ def _rows(M, seed):
     if M <= 8:
         return np.arange(M)
     rng = np.random.default_rng(seed)
-    mid = rng.choice(np.arange(1, M - 1), size=2, replace=False)
+    mid = rng.choice(np.arange(1, M - 1), size=6, replace=False)
     return np.array(sorted({0, M - 1, *mid.tolist()}))
+
+
+def _launches(wl, max_group):
+    """The benchmark's launches: runs of consecutive matrices with one input and
+    one format, at most max_group long."""
+    out = []
+    for m in wl.matrices:
+        if out and out[-1][-1].inp == m.inp and out[-1][-1].fmt == m.fmt and len(out[-1]) < max_group:
+            out[-1].append(m)
+        else:
+            out.append([m])
+    return out
 
 
 @pytest.mark.parametrize("name", list(synth.WORKLOADS))
@@ -48,16 +62,19 @@ def test_workload(dev, orc, name):
             assert np.array_equal(got, want), (name, M, inp)
             xq_host[inp] = want
             del xd
-        for mat in wl.matrices:
-            log("  M=%d %s %dx%d fmt=%d" % (M, mat.name, mat.N, mat.K, mat.fmt))
-            W = g.weights[mat.name]
-            Wd = to_dev(W)
-            y = gq.gemm(mat.fmt, Wd, xq_dev[mat.inp], M, mat.N, mat.K)
-            ys = y[torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
-            yo = orc.gemm_int(mat.fmt, W, xq_host[mat.inp], len(rows), mat.N, mat.K)
-            _, S = orc.gemm_dequant(mat.fmt, W, xq_host[mat.inp], len(rows), mat.N, mat.K)
-            worst = assert_within(ys, yo, S, "%s M=%d %s" % (name, M, mat.name))
-            log("    worst |err|/S = %.3g" % worst)
-            del Wd, y
+        for ms in _launches(wl, gq.MAX_GROUP):
+            m0 = ms[0]
+            log("  M=%d launch %s" % (M, "+".join(m.name for m in ms)))
+            Wd = [to_dev(g.weights[m.name]) for m in ms]
+            ys = gq.gemm_group(m0.fmt, Wd, xq_dev[m0.inp], M, [m.N for m in ms], m0.K)
+            for mat, y in zip(ms, ys):
+                W = g.weights[mat.name]
+                yr = y[torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
+                yo = orc.gemm_int(mat.fmt, W, xq_host[mat.inp], len(rows), mat.N, mat.K)
+                _, S = orc.gemm_dequant(mat.fmt, W, xq_host[mat.inp], len(rows), mat.N, mat.K)
+                worst = assert_within(yr, yo, S, "%s M=%d %s" % (name, M, mat.name))
+                log("    %s %dx%d fmt=%d worst |err|/S = %.3g"
+                    % (mat.name, mat.N, mat.K, mat.fmt, worst))
+            del Wd, ys
         del xq_dev
         torch.cuda.empty_cache()
