@@ -17,7 +17,11 @@
 //    contiguous weight bytes.
 //  * Activation fragments are read straight from global memory: the q8_K rows
 //    are small and stay cache-resident, and staging them in LDS (tried) costs a
-//    barrier and a second round trip that the stream cannot hide.
+//    barrier and a second round trip that the stream cannot hide.  A wave
+//    whose row fills a round takes two rows (R = 2): each activation fragment
+//    it loads serves both, which halves the cached activation traffic that
+//    otherwise slows the weight stream (measured: 3.6 -> 4.0 TB/s over the
+//    Qwen3-8B layer's launches).
 //  * Integer dot products on v_dot4 (int8 x int8 -> int32); the scale and min
 //    corrections use 24-bit multiplies and v_dot2 on the int16 group sums; one
 //    f32 fold per block and lane applies d_w, dmin and d_x.
@@ -191,9 +195,10 @@ __device__ __forceinline__ int dot16(const uint32_t* w, const u32x4& x, int s) {
 // FMT: 12 q4_K, 14 q6_K.  MT activation rows computed (>= M).  IT rounds of 16
 // blocks loaded together.  P rows per round.  KS waves share one row (P = 1):
 // wave w takes rounds w, w + KS, ... and the KS partial sums meet in LDS, added
-// in wave order.  The grid is the concatenation of every grouped matrix's
-// tiles (one tile = P rows, one workgroup of KS waves).
-template <int FMT, int MT, int IT, int P, int KS>
+// in wave order.  R rows per wave (P = 1), computed side by side on the same
+// activation fragments.  The grid is the concatenation of every grouped
+// matrix's tiles (one tile = P R rows, one workgroup of KS waves).
+template <int FMT, int MT, int IT, int P, int KS, int R>
 __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
                                                        const uint8_t* __restrict__ Xq, int nb,
                                                        int M) {
@@ -205,6 +210,8 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
   const int prow = P > 1 ? G / BPR : 0;
   const int bl0 = P > 1 ? G % BPR : G;
   static_assert(KS == 1 || P == 1, "split rows only when one row fills a round");
+  static_assert(R == 1 || P == 1, "several rows per wave only when one row fills a round");
+  constexpr int V = R * MT;  // outputs of a wave: value r * MT + m is row r, activation row m
   const int w = KS > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
   // take Xq with the rest of the kernel arguments, so the weight loads below
@@ -213,10 +220,14 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
   const uint8_t* __restrict__ W = tm.W;
   float* __restrict__ Y = tm.Y;
   const int64_t N = tm.N;
-  const int64_t n0 = (int64_t)tm.local * P;  // first row of this wave
-  int64_t n = n0 + prow;
-  if (n >= N) n = N - 1;  // tail rows: a valid row, never stored
-  const uint8_t* wrow = W + n * nb * BB;
+  const int64_t n0 = (int64_t)tm.local * (P * R);  // first row of this wave
+  const uint8_t* wrow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    int64_t n = n0 + prow + r;
+    if (n >= N) n = N - 1;  // tail rows: a valid row, never stored
+    wrow[r] = W + n * nb * BB;
+  }
 
   // per-lane constants
   // q4_K lane c = group g: values 64g..64g+63 (sub-blocks 2g, 2g+1), sums 4g..4g+3.
@@ -227,33 +238,34 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
   const int soff = FMT == 12 ? 8 * c : 2 * (8 * (c >> 1) + 2 * (c & 1));
   const int soff2 = soff + (FMT == 12 ? 4 : 8);
 
-  float acc[MT];
+  float acc[V];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+  for (int v = 0; v < V; ++v) acc[v] = 0.0f;
 
   for (int s0 = 16 * IT * w; s0 < nb; s0 += 16 * IT * KS) {
     // ---- 1. every weight load of these IT rounds
-    uint32_t wq[IT][8], wh[IT][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
-    uint32_t hd[IT][4];             // q4_K: block header; q6_K: [0] scale bytes, [1] d
-    {
+    uint32_t wq[IT][R][8], wh[IT][R][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
+    uint32_t hd[IT][R][4];  // q4_K: block header; q6_K: [0] scale bytes, [1] d
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int i = 0; i < IT; ++i) {
         const int b = s0 + bl0 + 16 * i;
         if (b < nb) {
-          const uint8_t* wb = wrow + b * BB;
+          const uint8_t* wb = wrow[r] + b * BB;
           if constexpr (FMT == 12) {
             const uint4 h = ld16a(wb);
             const uint4 q0 = ld16a(wb + 16 + 32 * c), q1 = ld16a(wb + 32 + 32 * c);
-            hd[i][0] = h.x; hd[i][1] = h.y; hd[i][2] = h.z; hd[i][3] = h.w;
-            wq[i][0] = q0.x; wq[i][1] = q0.y; wq[i][2] = q0.z; wq[i][3] = q0.w;
-            wq[i][4] = q1.x; wq[i][5] = q1.y; wq[i][6] = q1.z; wq[i][7] = q1.w;
+            hd[i][r][0] = h.x; hd[i][r][1] = h.y; hd[i][r][2] = h.z; hd[i][r][3] = h.w;
+            wq[i][r][0] = q0.x; wq[i][r][1] = q0.y; wq[i][r][2] = q0.z; wq[i][r][3] = q0.w;
+            wq[i][r][4] = q1.x; wq[i][r][5] = q1.y; wq[i][r][6] = q1.z; wq[i][r][7] = q1.w;
           } else {
             const int hh = c >> 1, p = c & 1;
-            ld32_a2(wb + 64 * hh + 32 * p, wq[i]);
-            ld32_a2(wb + 128 + 32 * hh, wh[i]);
-            hd[i][0] = (uint32_t)ld2(wb + 192 + 8 * hh + 2 * p) |
-                       ((uint32_t)ld2(wb + 196 + 8 * hh + 2 * p) << 16);
-            hd[i][1] = ld2(wb + 208);
+            ld32_a2(wb + 64 * hh + 32 * p, wq[i][r]);
+            ld32_a2(wb + 128 + 32 * hh, wh[i][r]);
+            hd[i][r][0] = (uint32_t)ld2(wb + 192 + 8 * hh + 2 * p) |
+                          ((uint32_t)ld2(wb + 196 + 8 * hh + 2 * p) << 16);
+            hd[i][r][1] = ld2(wb + 208);
           }
         }
       }
@@ -265,126 +277,156 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
       if (b >= nb) break;
       if constexpr (FMT == 12) {
         // scales and mins of sub-blocks 2c and 2c+1 as byte pairs
-        const uint32_t h1 = hd[i][1], h2 = hd[i][2], h3 = hd[i][3];
-        const int s = 16 * (c & 1);
-        uint32_t scp, mnp;
-        if (c < 2) {
-          scp = (h1 >> s) & 0x3f3fu;
-          mnp = (h2 >> s) & 0x3f3fu;
-        } else {
-          scp = ((h3 >> s) & 0x0f0fu) | ((h1 >> (s + 2)) & 0x3030u);
-          mnp = ((h3 >> (s + 4)) & 0x0f0fu) | ((h2 >> (s + 2)) & 0x3030u);
-        }
-        const int sc0 = (int)(scp & 0xffu), sc1 = (int)(scp >> 8);
-        const uint32_t m0 = (mnp & 0xffu) * 0x10001u, m1 = (mnp >> 8) * 0x10001u;
-        const float d = f16_to_f32(hd[i][0]), dmin = f16_to_f32(hd[i][0] >> 16);
-        uint32_t lo[8], hi[8];
+        int sc0[R], sc1[R];
+        uint32_t m0[R], m1[R], lo[R][8], hi[R][8];
+        float d[R], dmin[R];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          lo[k] = lo_nib(wq[i][k]);
-          hi[k] = hi_nib(wq[i][k]);
+        for (int r = 0; r < R; ++r) {
+          const uint32_t h1 = hd[i][r][1], h2 = hd[i][r][2], h3 = hd[i][r][3];
+          const int s = 16 * (c & 1);
+          uint32_t scp, mnp;
+          if (c < 2) {
+            scp = (h1 >> s) & 0x3f3fu;
+            mnp = (h2 >> s) & 0x3f3fu;
+          } else {
+            scp = ((h3 >> s) & 0x0f0fu) | ((h1 >> (s + 2)) & 0x3030u);
+            mnp = ((h3 >> (s + 4)) & 0x0f0fu) | ((h2 >> (s + 2)) & 0x3030u);
+          }
+          sc0[r] = (int)(scp & 0xffu);
+          sc1[r] = (int)(scp >> 8);
+          m0[r] = (mnp & 0xffu) * 0x10001u;
+          m1[r] = (mnp >> 8) * 0x10001u;
+          d[r] = f16_to_f32(hd[i][r][0]);
+          dmin[r] = f16_to_f32(hd[i][r][0] >> 16);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            lo[r][k] = lo_nib(wq[i][r][k]);
+            hi[r][k] = hi_nib(wq[i][r][k]);
+          }
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const XFrag x = x_frag(Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
-          const int dl = dot16(lo + 4, x.a1, dot16(lo, x.a0, 0));
-          const int dh = dot16(hi + 4, x.b1, dot16(hi, x.b0, 0));
-          const int isc = __mul24(sc0, dl) + __mul24(sc1, dh);
-          const int imn = dot2(x.s0, m0, dot2(x.s1, m1, 0));
-          float t = d * (float)isc;
-          t = fmaf(-dmin, (float)imn, t);
-          acc[m] = fmaf(x.d, t, acc[m]);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int dl = dot16(lo[r] + 4, x.a1, dot16(lo[r], x.a0, 0));
+            const int dh = dot16(hi[r] + 4, x.b1, dot16(hi[r], x.b0, 0));
+            const int isc = __mul24(sc0[r], dl) + __mul24(sc1[r], dh);
+            const int imn = dot2(x.s0, m0[r], dot2(x.s1, m1[r], 0));
+            float t = d[r] * (float)isc;
+            t = fmaf(-dmin[r], (float)imn, t);
+            acc[r * MT + m] = fmaf(x.d, t, acc[r * MT + m]);
+          }
         }
       } else {
         const int p = c & 1;
-        const uint32_t sp = hd[i][0];  // bytes 0,1: quarter p; bytes 2,3: quarter p+2
-        const float d = f16_to_f32(hd[i][1]);
-        uint32_t qa[8], qb[8];
+        uint32_t qa[R][8], qb[R][8], spa[R], spb[R];
+        int e0[R], e1[R], e2[R], e3[R];
+        float d[R];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          qa[k] = q6k_quad(wq[i][k], wh[i][k], p);
-          qb[k] = q6k_quad(wq[i][k], wh[i][k], p + 2);
+        for (int r = 0; r < R; ++r) {
+          const uint32_t sp = hd[i][r][0];  // bytes 0,1: quarter p; bytes 2,3: quarter p+2
+          d[r] = f16_to_f32(hd[i][r][1]);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            qa[r][k] = q6k_quad(wq[i][r][k], wh[i][r][k], p);
+            qb[r][k] = q6k_quad(wq[i][r][k], wh[i][r][k], p + 2);
+          }
+          e0[r] = (int)(int8_t)(sp & 0xffu);
+          e1[r] = (int)(int8_t)((sp >> 8) & 0xffu);
+          e2[r] = (int)(int8_t)((sp >> 16) & 0xffu);
+          e3[r] = (int)(int8_t)(sp >> 24);
+          spa[r] = (uint32_t)(e0[r] & 0xffff) | ((uint32_t)e1[r] << 16);
+          spb[r] = (uint32_t)(e2[r] & 0xffff) | ((uint32_t)e3[r] << 16);
         }
-        const int e0 = (int)(int8_t)(sp & 0xffu), e1 = (int)(int8_t)((sp >> 8) & 0xffu);
-        const int e2 = (int)(int8_t)((sp >> 16) & 0xffu), e3 = (int)(int8_t)(sp >> 24);
-        const uint32_t spa = (uint32_t)(e0 & 0xffff) | ((uint32_t)e1 << 16);
-        const uint32_t spb = (uint32_t)(e2 & 0xffff) | ((uint32_t)e3 << 16);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           const XFrag x = x_frag(Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
-          // sum_j sc_j * (dot_j - 32 * sum_j) over the lane's four 16-weight sub-blocks
-          int isc = __mul24(e0, dot16(qa, x.a0, 0)) + __mul24(e1, dot16(qa + 4, x.a1, 0)) +
-                    __mul24(e2, dot16(qb, x.b0, 0)) + __mul24(e3, dot16(qb + 4, x.b1, 0));
-          isc -= 32 * dot2(x.s0, spa, dot2(x.s1, spb, 0));
-          acc[m] = fmaf(x.d, d * (float)isc, acc[m]);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            // sum_j sc_j * (dot_j - 32 * sum_j) over the lane's four 16-weight sub-blocks
+            int isc = __mul24(e0[r], dot16(qa[r], x.a0, 0)) +
+                      __mul24(e1[r], dot16(qa[r] + 4, x.a1, 0)) +
+                      __mul24(e2[r], dot16(qb[r], x.b0, 0)) +
+                      __mul24(e3[r], dot16(qb[r] + 4, x.b1, 0));
+            isc -= 32 * dot2(x.s0, spa[r], dot2(x.s1, spb[r], 0));
+            acc[r * MT + m] = fmaf(x.d, d[r] * (float)isc, acc[r * MT + m]);
+          }
         }
       }
     }
   }
 
   // ---- 3. lane reduction and store
-  const int64_t nn = n0 + prow;
+  const int64_t nn0 = n0 + prow;
   if constexpr (KS > 1) {
     // lanes of the xor tree hold the wave's partial of value vidx; the KS
     // partials of each value are added in wave order by wave 0
-    __shared__ float red[KS][MT];
-    float v[MT];
+    __shared__ float red[KS][V];
+    float v[V];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) v[m] = acc[m];
-    seg_reduce<MT, 64>(v, lane);
-    const bool hold = holder<MT, 64>(lane);
-    const int m = vidx<MT, 64>(lane);
-    if (hold) red[w][m] = v[0];
+    for (int j = 0; j < V; ++j) v[j] = acc[j];
+    seg_reduce<V, 64>(v, lane);
+    const bool hold = holder<V, 64>(lane);
+    const int j = vidx<V, 64>(lane);
+    if (hold) red[w][j] = v[0];
     __syncthreads();
     if (w == 0 && hold) {
-      float t = red[0][m];
+      float t = red[0][j];
 #pragma unroll
-      for (int k = 1; k < KS; ++k) t += red[k][m];
+      for (int k = 1; k < KS; ++k) t += red[k][j];
+      const int m = j % MT;
+      const int64_t nn = nn0 + j / MT;
       if (m < M && nn < N) Y[(int64_t)m * N + nn] = t;
     }
-  } else if constexpr (MT <= SEG) {
-    float v[MT];
+  } else if constexpr (V <= SEG) {
+    float v[V];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) v[m] = acc[m];
-    seg_reduce<MT, SEG>(v, lane);
-    if (holder<MT, SEG>(lane)) {
-      const int m = vidx<MT, SEG>(lane);
+    for (int j = 0; j < V; ++j) v[j] = acc[j];
+    seg_reduce<V, SEG>(v, lane);
+    if (holder<V, SEG>(lane)) {
+      const int j = vidx<V, SEG>(lane);
+      const int m = j % MT;
+      const int64_t nn = nn0 + j / MT;
       if (m < M && nn < N) Y[(int64_t)m * N + nn] = v[0];
     }
   } else {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float v = seg_all<SEG>(acc[m]);
+    for (int j = 0; j < V; ++j) {
+      const float v = seg_all<SEG>(acc[j]);
+      const int m = j % MT;
+      const int64_t nn = nn0 + j / MT;
       if ((lane & (SEG - 1)) == 0 && m < M && nn < N) Y[(int64_t)m * N + nn] = v;
     }
   }
 }
 
-template <int FMT, int MT, int IT, int P, int KS>
+template <int FMT, int MT, int IT, int P, int KS, int R = 1>
 int launch_cfg(const Group& grp, const uint8_t* Xq, int nb, int M, hipStream_t st) {
   GroupTiles gt;
-  if (!make_tiles(grp, P, gt)) return -1;
+  if (!make_tiles(grp, P * R, gt)) return -1;
   const uint32_t tiles = gt.start[kMaxGroup];
   if (tiles == 0) return 0;
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS>), dim3(tiles), dim3(64 * KS), 0, st, gt, Xq,
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R>), dim3(tiles), dim3(64 * KS), 0, st, gt, Xq,
                      nb, M);
   return 0;
 }
 
 // The lane mapping depends on K only: P rows side by side when a row has 16/P
 // blocks; one round of 16 blocks per wave for rows of up to 16 blocks, and up
-// to four waves per row beyond that (each looping over rounds for longer rows).
+// to four waves per row beyond that (each looping over rounds for longer rows);
+// two rows per wave whenever a row fills a round.
 template <int FMT, int MT>
 int launch_mt(const Group& g, const uint8_t* Xq, int nb, int M, hipStream_t st) {
   if (nb == 1) return launch_cfg<FMT, MT, 1, 16, 1>(g, Xq, nb, M, st);
   if (nb == 2) return launch_cfg<FMT, MT, 1, 8, 1>(g, Xq, nb, M, st);
   if (nb == 4) return launch_cfg<FMT, MT, 1, 4, 1>(g, Xq, nb, M, st);
   if (nb == 8) return launch_cfg<FMT, MT, 1, 2, 1>(g, Xq, nb, M, st);
-  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1, 1>(g, Xq, nb, M, st);
-  if (nb <= 32) return launch_cfg<FMT, MT, 1, 1, 2>(g, Xq, nb, M, st);
-  if (nb <= 48) return launch_cfg<FMT, MT, 1, 1, 3>(g, Xq, nb, M, st);
-  if (nb <= 64) return launch_cfg<FMT, MT, 1, 1, 4>(g, Xq, nb, M, st);
-  return launch_cfg<FMT, MT, 2, 1, 4>(g, Xq, nb, M, st);
+  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1, 1, 2>(g, Xq, nb, M, st);
+  if (nb <= 32) return launch_cfg<FMT, MT, 1, 1, 2, 2>(g, Xq, nb, M, st);
+  if (nb <= 48) return launch_cfg<FMT, MT, 1, 1, 3, 2>(g, Xq, nb, M, st);
+  if (nb <= 64) return launch_cfg<FMT, MT, 1, 1, 4, 2>(g, Xq, nb, M, st);
+  return launch_cfg<FMT, MT, 2, 1, 4, 2>(g, Xq, nb, M, st);
 }
 
 template <int FMT>
