@@ -11,9 +11,12 @@ weight GB/s) and M = 512 (prefill GEMM, int8 TOP/s).
 Each matrix reads the activation of its place in the layer (q/k/v the attention
 input, o the attention output, gate/up the MLP input, down the MLP activation),
 so a pass quantizes four activation tensors and runs seven matmuls.  Matrices
-that read the same activation in the same format run as one grouped launch
-(gemmq_gemm_group: q/k/v, then gate/up), so the default pass is four quantizer
-launches and four matmul launches; --no-group launches every matrix on its own.
+that read the same activation in the same format run as one group, and each
+group is one gemmq_linear_group call: quantize its activation, then the packed
+matmul (q/k/v, o, gate/up, down).  At M = 1 each call is one fused launch (every
+GEMV workgroup quantizes the activation into its own LDS); at M = 512 it is a
+quantizer launch and a GEMM launch.  --no-fuse calls gemmq_quantize_q8K and
+gemmq_gemm_group separately; --no-group launches every matrix on its own.
 
 Inputs are resident in HBM before timing starts.  So that the weights are
 really streamed from HBM and not from the 256 MB last-level cache, the step
@@ -63,6 +66,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=20.0)
     p.add_argument("--no-group", action="store_true",
                    help="one launch per matrix instead of grouping matrices that share an input")
+    p.add_argument("--no-fuse", action="store_true",
+                   help="separate quantizer and matmul calls instead of gemmq_linear_group")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="first run one plain device-to-device copy of MIB MiB (reference dispatch "
                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -73,7 +78,7 @@ class Layer:
     """Device buffers for one workload: rotating weight copies, activations,
     q8_K buffers and outputs, all allocated before timing."""
 
-    def __init__(self, wl, gen, Ms, copies, group=True):
+    def __init__(self, wl, gen, Ms, copies, group=True, fuse=True):
         import torch
 
         import quant_packed_weight_amd as gq
@@ -81,6 +86,7 @@ class Layer:
         self.gq = gq
         self.wl = wl
         self.Ms = Ms
+        self.fuse = fuse
         # launches: runs of consecutive matrices with one input and one format
         self.launches = []
         for m in wl.matrices:
@@ -116,11 +122,15 @@ class Layer:
                 for ms in self.launches:
                     n = len(ms)
                     m0 = ms[0]
+                    wa = (P * n)(*[self.w[r][m.name].data_ptr() for m in ms])
+                    ya = (P * n)(*[self.y[(M, m.name)].data_ptr() for m in ms])
+                    na = (I64 * n)(*[m.N for m in ms])
                     self.args[(M, r, launch_name(ms))] = (
-                        m0.fmt, n, (P * n)(*[self.w[r][m.name].data_ptr() for m in ms]),
-                        (P * n)(*[self.y[(M, m.name)].data_ptr() for m in ms]),
-                        (I64 * n)(*[m.N for m in ms]), self.xq[(M, m0.inp)].data_ptr(), M, m0.K,
+                        m0.fmt, n, wa, ya, na, self.xq[(M, m0.inp)].data_ptr(), M, m0.K,
                         gq.PATH_AUTO)
+                    self.args[(M, r, launch_name(ms), "linear")] = (
+                        m0.fmt, n, wa, ya, na, self.x[(M, m0.inp)].data_ptr(),
+                        self.xq[(M, m0.inp)].data_ptr(), M, m0.K, gq.PATH_AUTO)
             for inp, K in wl.inputs():
                 self.args[(M, "q", inp)] = (self.x[(M, inp)].data_ptr(),
                                             self.xq[(M, inp)].data_ptr(), M, K)
@@ -130,6 +140,12 @@ class Layer:
         rc = self.lib.gemmq_gemm_group(*self.args[(M, r, launch_name(ms))], st)
         if rc:
             raise self.gq.GemmqError(rc, "gemm " + launch_name(ms))
+
+    def linear(self, ms, M, r, st):
+        """Enqueue quantize + matmul of the matrices `ms` in one library call."""
+        rc = self.lib.gemmq_linear_group(*self.args[(M, r, launch_name(ms), "linear")], st)
+        if rc:
+            raise self.gq.GemmqError(rc, "linear " + launch_name(ms))
 
     def quantize(self, inp, K, M, st):
         rc = self.lib.gemmq_quantize_q8K(*self.args[(M, "q", inp)], st)
@@ -142,9 +158,12 @@ class Layer:
         done = set()
         for ms in self.launches:
             inp = ms[0].inp
-            if inp not in done:  # quantize each activation just before its first use
-                self.quantize(inp, ms[0].K, M, st)
+            if inp not in done:  # quantize each activation with its first use
                 done.add(inp)
+                if self.fuse:
+                    self.linear(ms, M, r, st)
+                    continue
+                self.quantize(inp, ms[0].K, M, st)
             self.launch(ms, M, r, st)
 
 
@@ -201,10 +220,20 @@ def time_graphs(graphs, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
+def fused_launch(M, K):
+    """Whether gemmq_linear_group runs this shape as one fused quantize + GEMV
+    launch: the library's rule (gemv.hip: rows of at most 16 blocks, M <= 4,
+    M K/256 <= 32), restated here only to label the timings."""
+    nb = K // 256
+    return 1 <= M <= 4 and 1 <= nb <= 16 and M * nb <= 32
+
+
 def kernel_rates(layer, M, steps, copies, stream):
     """Average duration of each matmul launch of the pass: two HIP events on the
     launch stream around a batch of back-to-back copies of that launch (weight
-    copies rotated, its activation quantized once beforehand)."""
+    copies rotated).  Where the pass runs a group as one fused quantize + GEMV
+    launch, that launch is timed; otherwise the matmul launch alone, its
+    activation quantized once beforehand."""
     import torch
 
     st = stream.cuda_stream
@@ -213,15 +242,17 @@ def kernel_rates(layer, M, steps, copies, stream):
     per = {}
     n = max(steps, copies)
     for ms in layer.launches:
+        fused = layer.fuse and fused_launch(M, ms[0].K)
+        call = layer.linear if fused else layer.launch
         for r in range(copies):  # warm the launch path
-            layer.launch(ms, M, r, st)
+            call(ms, M, r, st)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for r in range(n):
-            layer.launch(ms, M, r % copies, st)
+            call(ms, M, r % copies, st)
         e1.record(stream)
         torch.cuda.synchronize()
-        per[launch_name(ms)] = (ms, e0.elapsed_time(e1) * 1e-3 / n)
+        per[launch_name(ms)] = (ms, e0.elapsed_time(e1) * 1e-3 / n, fused)
     return per
 
 
@@ -391,7 +422,7 @@ def main():
         raise SystemExit("workload %s has M in %s" % (a.workload, wl.Ms))
     wbytes = sum(m.nbytes for m in wl.matrices)
     copies = a.copies or max(1, math.ceil(GIB / wbytes))
-    layer = Layer(wl, gen, Ms, copies, group=not a.no_group)
+    layer = Layer(wl, gen, Ms, copies, group=not a.no_group, fuse=not a.no_fuse)
     stream = torch.cuda.current_stream()
     if a.copy_calibration:
         # a plain device copy of known size whose source is cold: after filling
@@ -421,10 +452,12 @@ def main():
     def roof(M):
         per = rates[M]
         n_l = len(per)
-        tot_t = sum(dt for _, dt in per.values())
-        kname = "gemv_kernel" if M <= 8 else "gemm_q4k_kernel"
+        tot_t = sum(dt for _, dt, _ in per.values())
+        fused = all(f for _, _, f in per.values())
+        kname = ("gemv_kernel (quantizer fused)" if fused else "gemv_kernel") if M <= 8 \
+            else "gemm_q4k_kernel"
         if M <= 8:
-            algo = sum(sum(m.nbytes for m in ms) for ms, _ in per.values())
+            algo = sum(sum(m.nbytes for m in ms) for ms, _, _ in per.values())
             ach = algo / tot_t / 1e9
             return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBS, 4),
@@ -434,8 +467,8 @@ def main():
                     "kernel": kname, "launches_per_pass": n_l,
                     "avg_launch_us": round(tot_t / n_l * 1e6, 2),
                     "per_launch_GBs": {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
-                                       for k, (ms, dt) in per.items()}}
-        algo = sum(sum(2 * M * m.N * m.K for m in ms) for ms, _ in per.values())
+                                       for k, (ms, dt, _) in per.items()}}
+        algo = sum(sum(2 * M * m.N * m.K for m in ms) for ms, _, _ in per.values())
         ach = algo / tot_t / 1e12
         return {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS,
                 "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
@@ -445,7 +478,7 @@ def main():
                 "kernel": kname, "launches_per_pass": n_l,
                 "avg_launch_us": round(tot_t / n_l * 1e6, 2),
                 "per_launch_TOPs": {k: round(sum(2 * M * m.N * m.K for m in ms) / dt / 1e12, 1)
-                                    for k, (ms, dt) in per.items()}}
+                                    for k, (ms, dt, _) in per.items()}}
 
     value = wbytes / t[M1] / 1e9 if M1 <= 8 else ops[M1] / t[M1] / 1e12
     res = {
@@ -464,6 +497,7 @@ def main():
         "config": {"workload": a.workload, "M": Ms, "matrices": len(wl.matrices),
                    "activations": len(wl.inputs()), "weight_bytes": wbytes,
                    "rotating_copies": copies, "submit": "hip_graph" if a.graph else "eager",
+                   "calls": "separate quantize + matmul" if a.no_fuse else "gemmq_linear_group",
                    "launches": [launch_name(ms) for ms in layer.launches],
                    "ms_per_pass": {str(M): round(t[M] * 1e3, 4) for M in Ms},
                    "ms_per_pass_eager": {str(M): round(t_eager[M] * 1e3, 4) for M in Ms}},

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 2
+#define GEMMQ_ABI_VERSION 3
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q4_K 12
@@ -145,6 +145,32 @@ int gemmq_gemm_ex(int fmt, const void *W, const void *Xq, float *Y, int64_t M, i
  */
 int gemmq_gemm_group(int fmt, int count, const void *const *W, float *const *Y, const int64_t *N,
                      const void *Xq, int64_t M, int64_t K, int path, void *stream);
+
+/*
+ * The whole linear layer from f32 activations: quantize X to q8_K into Xq, then
+ * apply every W[g] to it -- the same bits as gemmq_quantize_q8K(X, Xq, M, K)
+ * followed by gemmq_gemm_group(fmt, count, W, Y, N, Xq, M, K, path), for Xq and
+ * for every Y[g].  At decode shapes (GEMV path, M <= 4 and M*K/256 small) it is
+ * one launch: every workgroup quantizes X into its own LDS while its weight
+ * loads are in flight, and workgroup 0 also writes Xq.  Otherwise it enqueues
+ * the two launches.  Quantizing in the consuming launch is how the CPU
+ * gemm_quant on the pages treats the int8 activation step, as part of the
+ * matmul (molayo article, status row "src/").
+ *   X      device, f32 [M, K], 16-byte aligned (as gemmq_quantize_q8K).
+ *   Xq     device, gemmq_q8K_bytes(M, K) bytes, 4-byte aligned; fully
+ *          overwritten with the q8_K blocks of X when M > 0.
+ *   fmt, count, W, Y, N, M, K, path, stream  as in gemmq_gemm_group; all N[g]
+ *          == 0 still quantizes X.
+ * Errors: those of gemmq_quantize_q8K and gemmq_gemm_group; nothing is launched
+ * on an error.
+ */
+int gemmq_linear_group(int fmt, int count, const void *const *W, float *const *Y,
+                       const int64_t *N, const float *X, void *Xq, int64_t M, int64_t K,
+                       int path, void *stream);
+
+/* gemmq_linear_group for one matrix with GEMMQ_PATH_AUTO. */
+int gemmq_linear(int fmt, const void *W, const float *X, void *Xq, float *Y, int64_t M, int64_t N,
+                 int64_t K, void *stream);
 
 /*
  * Diagnostic export: decode packed weights to f32 with the same device unpacker

@@ -28,6 +28,8 @@ from ._lib import (  # noqa: F401
     gemm_ptr,
     lib,
     linear,
+    linear_group,
+    linear_group_ptr,
     q8K_bytes,
     quantize_q8K,
     quantize_q8K_ptr,

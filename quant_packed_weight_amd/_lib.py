@@ -17,8 +17,8 @@ BLOCK_BYTES = {FMT_Q4K: 144, FMT_Q6K: 210}
 Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
-MAX_GROUP = 4  # matrices per gemmq_gemm_group call
-ABI_VERSION = 2
+MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
+ABI_VERSION = 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 
@@ -37,6 +37,9 @@ EXPORTS = {
     "gemmq_gemm_ex": (_I, [_I, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "gemmq_gemm_group": (_I, [_I, _I, ctypes.POINTER(_P), ctypes.POINTER(_P),
                               ctypes.POINTER(_I64), _P, _I64, _I64, _I, _P]),
+    "gemmq_linear_group": (_I, [_I, _I, ctypes.POINTER(_P), ctypes.POINTER(_P),
+                                ctypes.POINTER(_I64), _P, _P, _I64, _I64, _I, _P]),
+    "gemmq_linear": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
 }
 
@@ -115,6 +118,18 @@ def gemm_group_ptr(fmt: int, Ws, Ys, Ns, Xq: int, M: int, K: int, path: int = PA
     ya = (_P * max(n, 1))(*Ys)
     na = (_I64 * max(n, 1))(*Ns)
     return lib().gemmq_gemm_group(fmt, n, wa, ya, na, Xq, M, K, path, stream or None)
+
+
+def linear_group_ptr(fmt: int, Ws, Ys, Ns, X: int, Xq: int, M: int, K: int,
+                     path: int = PATH_AUTO, stream: int = 0) -> int:
+    """Quantize X into Xq and apply the matrices Ws (gemmq_linear_group)."""
+    n = len(Ws)
+    if len(Ys) != n or len(Ns) != n:
+        raise ValueError("Ws, Ys and Ns must have the same length")
+    wa = (_P * max(n, 1))(*Ws)
+    ya = (_P * max(n, 1))(*Ys)
+    na = (_I64 * max(n, 1))(*Ns)
+    return lib().gemmq_linear_group(fmt, n, wa, ya, na, X, Xq, M, K, path, stream or None)
 
 
 def decode_ptr(fmt: int, W: int, Wf: int, N: int, K: int, stream: int = 0) -> int:
@@ -209,8 +224,33 @@ def decode(fmt, w, N, K, out=None, stream=None):
     return out
 
 
-def linear(fmt, w, x, N, path=PATH_AUTO, stream=None):
-    """y = W x for f32 activations x [M, K]: quantize to q8_K, then the packed matmul."""
+def linear_group(fmt, ws, x, Ns, xq=None, outs=None, path=PATH_AUTO, stream=None):
+    """f32 activations x [M, K] through several packed matrices (gemmq_linear_group):
+    returns ([f32 [M, N_g]], xq) with xq the q8_K blocks of x."""
+    torch = _torch()
     M, K = x.shape
-    xq = quantize_q8K(x, stream=stream)
-    return gemm(fmt, w, xq, M, N, K, path=path, stream=stream)
+    if len(ws) != len(Ns):
+        raise ValueError("ws and Ns must have the same length")
+    for w, N in zip(ws, Ns):
+        if w.numel() < weight_bytes(fmt, N, K):
+            raise ValueError("buffer smaller than the stated shape")
+    if xq is None:
+        xq = torch.empty((M, (K // QK) * Q8K_BYTES), dtype=torch.uint8, device=x.device)
+    elif xq.numel() < q8K_bytes(M, K):
+        raise ValueError("xq too small")
+    if outs is None:
+        outs = [torch.empty((M, N), dtype=torch.float32, device=x.device) for N in Ns]
+    for o, N in zip(outs, Ns):
+        if o.numel() < M * N:
+            raise ValueError("out too small")
+    _check(linear_group_ptr(fmt, [_dev(w, "w", torch.uint8) for w in ws],
+                            [_dev(o, "out", torch.float32) for o in outs], list(Ns),
+                            _dev(x, "x", torch.float32), _dev(xq, "xq", torch.uint8), M, K, path,
+                            _stream(stream)), "gemmq_linear_group")
+    return outs, xq
+
+
+def linear(fmt, w, x, N, path=PATH_AUTO, stream=None):
+    """y = W x for f32 activations x [M, K] (quantized to q8_K on the device)."""
+    outs, _ = linear_group(fmt, [w], x, [N], path=path, stream=stream)
+    return outs[0]

@@ -107,12 +107,17 @@ int gemmq_quantize_q8K(const float* X, void* Xq, int64_t M, int64_t K, void* str
                                              static_cast<hipStream_t>(stream)));
 }
 
-int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
-                     const int64_t* N, const void* Xq, int64_t M, int64_t K, int path,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the group entry points: fills `g` with the non-empty
+// matrices in order and `rows` with their total; GEMMQ_OK or the error.
+int check_group(int fmt, int count, const void* const* W, float* const* Y, const int64_t* N,
+                int64_t M, int64_t K, int path, gemmq::Group& g, int64_t& rows) {
   if (count < 1 || count > gemmq::kMaxGroup || !W || !Y || !N) return GEMMQ_E_INVALID_ARG;
-  gemmq::Group g{};
-  int64_t rows = 0;
+  g = gemmq::Group{};
+  rows = 0;
   for (int i = 0; i < count; ++i) {
     const int rc = check_weights(fmt, W[i], N[i], K);
     if (rc != GEMMQ_OK) return rc;
@@ -124,14 +129,10 @@ int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
     return GEMMQ_E_INVALID_ARG;
   if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
   if (M == 0 || rows == 0) return GEMMQ_OK;
-  if (!Xq) return GEMMQ_E_INVALID_ARG;
   for (int i = 0; i < count; ++i)
     if (N[i] > 0 && !Y[i]) return GEMMQ_E_INVALID_ARG;
-  if (!aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
   for (int i = 0; i < count; ++i)
     if (N[i] > 0 && !aligned(Y[i], 4)) return GEMMQ_E_ALIGNMENT;
-  const int dv = check_device();
-  if (dv != GEMMQ_OK) return dv;
   // empty matrices are dropped; the others keep their order
   for (int i = 0; i < count; ++i) {
     if (N[i] == 0) continue;
@@ -140,12 +141,61 @@ int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
     g.N[g.count] = N[i];
     ++g.count;
   }
+  return GEMMQ_OK;
+}
+
+bool use_gemv(int path, int64_t M) {
+  return path == GEMMQ_PATH_GEMV || (path == GEMMQ_PATH_AUTO && M <= 8);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
+                     const int64_t* N, const void* Xq, int64_t M, int64_t K, int path,
+                     void* stream) {
+  gemmq::Group g;
+  int64_t rows = 0;
+  int rc = check_group(fmt, count, W, Y, N, M, K, path, g, rows);
+  if (rc != GEMMQ_OK || M == 0 || rows == 0) return rc;
+  if (!Xq) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
   const uint8_t* xq = static_cast<const uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool gemv = path == GEMMQ_PATH_GEMV || (path == GEMMQ_PATH_AUTO && M <= 8);
   clear_pending();
+  if (use_gemv(path, M)) return launched(gemmq::launch_gemv(fmt, g, xq, (int)M, K, st));
+  return launched(gemmq::launch_gemm(fmt, g, xq, M, K, st));
+}
+
+int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y,
+                       const int64_t* N, const float* X, void* Xq, int64_t M, int64_t K,
+                       int path, void* stream) {
+  gemmq::Group g;
+  int64_t rows = 0;
+  int rc = check_group(fmt, count, W, Y, N, M, K, path, g, rows);
+  if (rc != GEMMQ_OK || M == 0) return rc;
+  if (!X || !Xq) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  uint8_t* xq = static_cast<uint8_t*>(Xq);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool gemv = use_gemv(path, M);
+  clear_pending();
+  if (rows > 0 && gemv && gemmq::gemv_fusable(M, K))
+    return launched(gemmq::launch_gemv_fused(fmt, g, X, xq, (int)M, K, st));
+  rc = launched(gemmq::launch_quantize_q8K(X, xq, M, K, st));
+  if (rc != GEMMQ_OK || rows == 0) return rc;
   if (gemv) return launched(gemmq::launch_gemv(fmt, g, xq, (int)M, K, st));
   return launched(gemmq::launch_gemm(fmt, g, xq, M, K, st));
+}
+
+int gemmq_linear(int fmt, const void* W, const float* X, void* Xq, float* Y, int64_t M, int64_t N,
+                 int64_t K, void* stream) {
+  return gemmq_linear_group(fmt, 1, &W, &Y, &N, X, Xq, M, K, GEMMQ_PATH_AUTO, stream);
 }
 
 int gemmq_gemm_ex(int fmt, const void* W, const void* Xq, float* Y, int64_t M, int64_t N,

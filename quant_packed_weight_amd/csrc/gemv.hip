@@ -36,6 +36,7 @@
 // that row bit for bit.
 #include "device.h"
 #include "launch.h"
+#include "quant_block.h"
 
 namespace gemmq {
 
@@ -184,6 +185,28 @@ __device__ __forceinline__ XFrag x_frag(const uint8_t* __restrict__ Xq, int nb, 
   return f;
 }
 
+// The fused form's LDS copy of the activations: block (m, b) at (m nb + b) kXL
+// bytes holds the 256 values (16-byte aligned), the 16 sums at +256 and d at +288.
+constexpr int kXL = 304;
+
+__device__ __forceinline__ XFrag x_frag_lds(const uint8_t* xl, int nb, int m, int b, int qoff,
+                                            int qoff2, int soff, int soff2) {
+  const uint8_t* p = xl + (m * nb + b) * kXL;
+  const uint4 a0 = *reinterpret_cast<const uint4*>(p + qoff);
+  const uint4 a1 = *reinterpret_cast<const uint4*>(p + qoff + 16);
+  const uint4 b0 = *reinterpret_cast<const uint4*>(p + qoff2);
+  const uint4 b1 = *reinterpret_cast<const uint4*>(p + qoff2 + 16);
+  XFrag f;
+  f.a0 = {a0.x, a0.y, a0.z, a0.w};
+  f.a1 = {a1.x, a1.y, a1.z, a1.w};
+  f.b0 = {b0.x, b0.y, b0.z, b0.w};
+  f.b1 = {b1.x, b1.y, b1.z, b1.w};
+  f.s0 = *reinterpret_cast<const uint32_t*>(p + 256 + soff);
+  f.s1 = *reinterpret_cast<const uint32_t*>(p + 256 + soff2);
+  f.d = *reinterpret_cast<const float*>(p + 288);
+  return f;
+}
+
 __device__ __forceinline__ int dot16(const uint32_t* w, const u32x4& x, int s) {
   s = dot4(w[0], x.x, s);
   s = dot4(w[1], x.y, s);
@@ -198,29 +221,33 @@ __device__ __forceinline__ int dot16(const uint32_t* w, const u32x4& x, int s) {
 // in wave order.  R rows per wave (P = 1), computed side by side on the same
 // activation fragments.  The grid is the concatenation of every grouped
 // matrix's tiles (one tile = P R rows, one workgroup of KS waves).
-template <int FMT, int MT, int IT, int P, int KS, int R>
-__global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
-                                                       const uint8_t* __restrict__ Xq, int nb,
-                                                       int M) {
+template <int FMT, int MT, int IT, int P, int KS, int R, int RG, bool FUSED>
+__global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
+                                                            uint8_t* __restrict__ Xq,
+                                                            const float* __restrict__ X, int nb,
+                                                            int M) {
   constexpr int SEG = 64 / P;  // lanes that share a row
   constexpr int BPR = 16 / P;  // blocks of a row per round when P > 1
   constexpr int BB = FMT == 12 ? kQ4KBytes : kQ6KBytes;
+  constexpr int NW = KS * RG;  // waves of the workgroup
   const int lane = lane_id();
   const int G = lane >> 2, c = lane & 3;
   const int prow = P > 1 ? G / BPR : 0;
   const int bl0 = P > 1 ? G % BPR : G;
   static_assert(KS == 1 || P == 1, "split rows only when one row fills a round");
   static_assert(R == 1 || P == 1, "several rows per wave only when one row fills a round");
+  static_assert(!FUSED || IT == 1, "the fused form takes one round per wave");
   constexpr int V = R * MT;  // outputs of a wave: value r * MT + m is row r, activation row m
-  const int w = KS > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+  const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
+  const int w = wv % KS, rg = wv / KS;  // K share and row group of this wave
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
-  // take Xq with the rest of the kernel arguments, so the weight loads below
-  // do not wait for a second round of scalar loads
-  asm volatile("" ::"s"(Xq));
+  // take the activation pointers with the rest of the kernel arguments, so the
+  // loads below do not wait for a second round of scalar loads
+  asm volatile("" ::"s"(Xq), "s"(X));
   const uint8_t* __restrict__ W = tm.W;
   float* __restrict__ Y = tm.Y;
   const int64_t N = tm.N;
-  const int64_t n0 = (int64_t)tm.local * (P * R);  // first row of this wave
+  const int64_t n0 = (int64_t)tm.local * (RG * P * R) + rg * (P * R);  // first row of this wave
   const uint8_t* wrow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -242,15 +269,27 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.0f;
 
-  for (int s0 = 16 * IT * w; s0 < nb; s0 += 16 * IT * KS) {
-    // ---- 1. every weight load of these IT rounds
-    uint32_t wq[IT][R][8], wh[IT][R][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
-    uint32_t hd[IT][R][4];  // q4_K: block header; q6_K: [0] scale bytes, [1] d
+  // the fused form quantizes the activations into this workgroup's LDS, one
+  // q8_K block per wave at a time, as [m][b] blocks of kXL bytes
+  extern __shared__ __attribute__((aligned(16))) uint8_t xl[];
+  auto xfrag = [&](int m, int b) {
+    if constexpr (FUSED)
+      return x_frag_lds(xl, nb, m, b, qoff, qoff2, soff, soff2);
+    else
+      return x_frag(Xq, nb, m, b, qoff, qoff2, soff, soff2);
+  };
+
+  uint32_t wq[IT][R][8], wh[IT][R][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
+  uint32_t hd[IT][R][4];  // q4_K: block header; q6_K: [0] scale bytes, [1] d
+  // ---- 1. every weight load of the IT rounds from block s0 on (lanes past the
+  // row's end load its last block when `clamp`, else nothing)
+  auto load_round = [&](int s0, bool clamp) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
 #pragma unroll
       for (int i = 0; i < IT; ++i) {
-        const int b = s0 + bl0 + 16 * i;
+        int b = s0 + bl0 + 16 * i;
+        if (clamp) b = b < nb ? b : nb - 1;
         if (b < nb) {
           const uint8_t* wb = wrow[r] + b * BB;
           if constexpr (FMT == 12) {
@@ -270,7 +309,9 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
         }
       }
     }
-    // ---- 2. arithmetic, block by block
+  };
+  // ---- 2. arithmetic, block by block
+  auto compute_round = [&](int s0) {
 #pragma unroll
     for (int i = 0; i < IT; ++i) {
       const int b = s0 + bl0 + 16 * i;
@@ -306,7 +347,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const XFrag x = x_frag(Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
+          const XFrag x = xfrag(m < M ? m : M - 1, b);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             const int dl = dot16(lo[r] + 4, x.a1, dot16(lo[r], x.a0, 0));
@@ -341,7 +382,7 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
-          const XFrag x = x_frag(Xq, nb, m < M ? m : M - 1, b, qoff, qoff2, soff, soff2);
+          const XFrag x = xfrag(m < M ? m : M - 1, b);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             // sum_j sc_j * (dot_j - 32 * sum_j) over the lane's four 16-weight sub-blocks
@@ -355,6 +396,44 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
         }
       }
     }
+  };
+
+  if constexpr (FUSED) {
+    // activation loads first, weight loads next, so quantizing waits only for
+    // the former; every load is unconditional (clamped), so the wait counts
+    // are exact
+    constexpr int QB = 4;  // blocks quantized per wave, at most
+    const int nq = M * nb;
+    float4 xv[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      int t = wv + NW * j;
+      t = t < nq ? t : nq - 1;
+      xv[j] = *reinterpret_cast<const float4*>(X + (int64_t)t * kQK + 4 * lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the two groups of loads in this order
+    const int s0 = 16 * w;
+    load_round(s0, true);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < QB; ++j) {
+      const int t = wv + NW * j;
+      if (t < nq) {  // wave-uniform
+        const Q8Lane q = q8k_block(xv[j]);
+        uint8_t* o = xl + t * kXL;
+        *reinterpret_cast<uint32_t*>(o + 4 * lane) = q.packed;
+        if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(o + 256 + 2 * (lane >> 2)) = q.sums;
+        if (lane == 0) *reinterpret_cast<float*>(o + 288) = q.d;
+        if (blockIdx.x == 0) q8k_store(Xq + (int64_t)t * kQ8KBytes, q, lane);
+      }
+    }
+    __syncthreads();
+    if (s0 < nb) compute_round(s0);
+  } else {
+    for (int s0 = 16 * IT * w; s0 < nb; s0 += 16 * IT * KS) {
+      load_round(s0, false);
+      compute_round(s0);
+    }
   }
 
   // ---- 3. lane reduction and store
@@ -362,19 +441,19 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
   if constexpr (KS > 1) {
     // lanes of the xor tree hold the wave's partial of value vidx; the KS
     // partials of each value are added in wave order by wave 0
-    __shared__ float red[KS][V];
+    __shared__ float red[RG][KS][V];
     float v[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) v[j] = acc[j];
     seg_reduce<V, 64>(v, lane);
     const bool hold = holder<V, 64>(lane);
     const int j = vidx<V, 64>(lane);
-    if (hold) red[w][j] = v[0];
+    if (hold) red[rg][w][j] = v[0];
     __syncthreads();
     if (w == 0 && hold) {
-      float t = red[0][j];
+      float t = red[rg][0][j];
 #pragma unroll
-      for (int k = 1; k < KS; ++k) t += red[k][j];
+      for (int k = 1; k < KS; ++k) t += red[rg][k][j];
       const int m = j % MT;
       const int64_t nn = nn0 + j / MT;
       if (m < M && nn < N) Y[(int64_t)m * N + nn] = t;
@@ -401,14 +480,39 @@ __global__ __launch_bounds__(64 * KS) void gemv_kernel(const GroupTiles gt,
   }
 }
 
+// The fused form: rows of at most 16 blocks (one wave per row group, one round
+// each), M <= 4 and M nb <= 32, in workgroups of kRG row groups whose waves
+// quantize up to kQB blocks each.  Longer rows are not fused: every workgroup
+// would quantize the whole longer activation (measured slower than the
+// separate quantizer launch at K = 12288).
+constexpr int kRG = 8;
+constexpr int kQB = 4;
+
+// X == nullptr: the plain form, reading the q8_K blocks at Xq.  Otherwise the
+// fused form: every workgroup quantizes X into its LDS and workgroup 0 also
+// writes the blocks to Xq.
 template <int FMT, int MT, int IT, int P, int KS, int R = 1>
-int launch_cfg(const Group& grp, const uint8_t* Xq, int nb, int M, hipStream_t st) {
+int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hipStream_t st) {
   GroupTiles gt;
+  if (X) {
+    if constexpr (IT == 1 && KS == 1 && MT <= 4) {
+      constexpr int RG = kRG;
+      if (M * nb > kQB * RG) return -1;
+      if (!make_tiles(grp, RG * P * R, gt)) return -1;
+      const uint32_t tiles = gt.start[kMaxGroup];
+      if (tiles == 0) return 0;
+      hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true>), dim3(tiles),
+                         dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
+      return 0;
+    } else {
+      return -1;
+    }
+  }
   if (!make_tiles(grp, P * R, gt)) return -1;
   const uint32_t tiles = gt.start[kMaxGroup];
   if (tiles == 0) return 0;
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R>), dim3(tiles), dim3(64 * KS), 0, st, gt, Xq,
-                     nb, M);
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, 1, false>), dim3(tiles), dim3(64 * KS),
+                     0, st, gt, Xq, (const float*)nullptr, nb, M);
   return 0;
 }
 
@@ -416,30 +520,34 @@ int launch_cfg(const Group& grp, const uint8_t* Xq, int nb, int M, hipStream_t s
 // blocks; one round of 16 blocks per wave for rows of up to 16 blocks, and up
 // to four waves per row beyond that (each looping over rounds for longer rows);
 // two rows per wave whenever a row fills a round.
+int split_waves(int nb) { return nb <= 16 ? 1 : nb <= 32 ? 2 : nb <= 48 ? 3 : nb <= 64 ? 4 : 0; }
+
 template <int FMT, int MT>
-int launch_mt(const Group& g, const uint8_t* Xq, int nb, int M, hipStream_t st) {
-  if (nb == 1) return launch_cfg<FMT, MT, 1, 16, 1>(g, Xq, nb, M, st);
-  if (nb == 2) return launch_cfg<FMT, MT, 1, 8, 1>(g, Xq, nb, M, st);
-  if (nb == 4) return launch_cfg<FMT, MT, 1, 4, 1>(g, Xq, nb, M, st);
-  if (nb == 8) return launch_cfg<FMT, MT, 1, 2, 1>(g, Xq, nb, M, st);
-  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1, 1, 2>(g, Xq, nb, M, st);
-  if (nb <= 32) return launch_cfg<FMT, MT, 1, 1, 2, 2>(g, Xq, nb, M, st);
-  if (nb <= 48) return launch_cfg<FMT, MT, 1, 1, 3, 2>(g, Xq, nb, M, st);
-  if (nb <= 64) return launch_cfg<FMT, MT, 1, 1, 4, 2>(g, Xq, nb, M, st);
-  return launch_cfg<FMT, MT, 2, 1, 4, 2>(g, Xq, nb, M, st);
+int launch_mt(const Group& g, uint8_t* Xq, const float* X, int nb, int M, hipStream_t st) {
+  if (nb == 1) return launch_cfg<FMT, MT, 1, 16, 1>(g, Xq, X, nb, M, st);
+  if (nb == 2) return launch_cfg<FMT, MT, 1, 8, 1>(g, Xq, X, nb, M, st);
+  if (nb == 4) return launch_cfg<FMT, MT, 1, 4, 1>(g, Xq, X, nb, M, st);
+  if (nb == 8) return launch_cfg<FMT, MT, 1, 2, 1>(g, Xq, X, nb, M, st);
+  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1, 1, 2>(g, Xq, X, nb, M, st);
+  if (nb <= 32) return launch_cfg<FMT, MT, 1, 1, 2, 2>(g, Xq, X, nb, M, st);
+  if (nb <= 48) return launch_cfg<FMT, MT, 1, 1, 3, 2>(g, Xq, X, nb, M, st);
+  if (nb <= 64) return launch_cfg<FMT, MT, 1, 1, 4, 2>(g, Xq, X, nb, M, st);
+  return launch_cfg<FMT, MT, 2, 1, 4, 2>(g, Xq, X, nb, M, st);
 }
 
 template <int FMT>
-int launch_fmt(const Group& g, const uint8_t* Xq, int M, int nb, hipStream_t st) {
+int launch_fmt(const Group& g, uint8_t* Xq, const float* X, int M, int nb, hipStream_t st) {
   switch (M) {
-    case 1: return launch_mt<FMT, 1>(g, Xq, nb, M, st);
-    case 2: return launch_mt<FMT, 2>(g, Xq, nb, M, st);
+    case 1: return launch_mt<FMT, 1>(g, Xq, X, nb, M, st);
+    case 2: return launch_mt<FMT, 2>(g, Xq, X, nb, M, st);
     case 3:
-    case 4: return launch_mt<FMT, 4>(g, Xq, nb, M, st);
+    case 4: return launch_mt<FMT, 4>(g, Xq, X, nb, M, st);
     case 5:
     case 6:
     case 7:
-    case 8: return launch_mt<FMT, 8>(g, Xq, nb, M, st);
+    case 8:
+      if (X) return -1;
+      return launch_mt<FMT, 8>(g, Xq, X, nb, M, st);
     default: return -1;
   }
 }
@@ -449,7 +557,22 @@ int launch_fmt(const Group& g, const uint8_t* Xq, int M, int nb, hipStream_t st)
 int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st) {
   const int64_t nb = K / kQK;
   if (nb > 0x7fffffffLL) return -1;
-  return fmt == 12 ? launch_fmt<12>(g, Xq, M, (int)nb, st) : launch_fmt<14>(g, Xq, M, (int)nb, st);
+  uint8_t* xq = const_cast<uint8_t*>(Xq);  // read only in the plain form
+  return fmt == 12 ? launch_fmt<12>(g, xq, nullptr, M, (int)nb, st)
+                   : launch_fmt<14>(g, xq, nullptr, M, (int)nb, st);
+}
+
+bool gemv_fusable(int64_t M, int64_t K) {
+  const int64_t nb = K / kQK;
+  if (M < 1 || M > 4 || nb < 1 || nb > 16) return false;
+  return split_waves((int)nb) == 1 && M * nb <= (int64_t)kQB * kRG;
+}
+
+int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,
+                      hipStream_t st) {
+  if (!gemv_fusable(M, K)) return -1;
+  const int nb = (int)(K / kQK);
+  return fmt == 12 ? launch_fmt<12>(g, Xq, X, M, nb, st) : launch_fmt<14>(g, Xq, X, M, nb, st);
 }
 
 }  // namespace gemmq

@@ -75,6 +75,12 @@ int launch_quantize_q8K(const float* X, uint8_t* Xq, int64_t M, int64_t K, hipSt
 int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 
 int launch_gemm(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K, hipStream_t st);
+// The fused decode form: quantize X (M x K f32) and run the GEMV in one launch,
+// each workgroup quantizing into its own LDS; Xq receives the q8_K blocks.
+// Taken when gemv_fusable(M, K): M <= 4 and M K / 256 small enough (see gemv.hip).
+bool gemv_fusable(int64_t M, int64_t K);
+int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,
+                      hipStream_t st);
 
 int launch_decode(int fmt, const uint8_t* W, float* Wf, int64_t N, int64_t K, hipStream_t st);
 

@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_exported(L):
     names = _declared()
-    assert len(names) == 10
+    assert len(names) == 12
     assert set(names) == set(gq.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 2
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 3
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -116,6 +116,44 @@ def test_group_null_arrays(L):
     assert L.gemmq_gemm_group(12, 1, one_p, one_p, None, FAKE16, 1, 256, 0, None) == -1
     assert L.gemmq_gemm_group(13, 1, one_p, one_p, one_n, FAKE16, 1, 256, 0, None) == -2
     assert L.gemmq_gemm_group(12, 1, one_p, one_p, one_n, None, 1, 256, 0, None) == -1
+
+
+@pytest.mark.parametrize("args,status", [
+    ((13, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256), -2),      # unknown format
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 300), -3),      # K % 256 != 0
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, -1, 1, 256), -1),     # M < 0
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, 1, -1, 256), -1),     # N < 0
+    ((12, None, FAKE16, FAKE16, FAKE16, 1, 1, 256), -1),        # null W
+    ((12, FAKE16, None, FAKE16, FAKE16, 1, 1, 256), -1),        # null X
+    ((12, FAKE16, FAKE16, None, FAKE16, 1, 1, 256), -1),        # null Xq
+    ((12, FAKE16, FAKE16, FAKE16, None, 1, 1, 256), -1),        # null Y
+    ((12, FAKE16 + 4, FAKE16, FAKE16, FAKE16, 1, 1, 256), -4),  # q4_K weights need 16 B
+    ((12, FAKE16, FAKE16 + 4, FAKE16, FAKE16, 1, 1, 256), -4),  # X needs 16 B
+    ((12, FAKE16, FAKE16, FAKE16 + 2, FAKE16, 1, 1, 256), -4),  # Xq needs 4 B
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16 + 1, 1, 1, 256), -4),  # Y needs 4 B
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, 0, 5, 256), 0),       # M = 0: empty
+])
+def test_linear_validation(L, args, status):
+    fmt, W, X, Xq, Y, M, N, K = args
+    assert L.gemmq_linear(fmt, W, X, Xq, Y, M, N, K, None) == status
+    P = ctypes.c_void_p
+    wa, ya, na = (P * 1)(W), (P * 1)(Y), (ctypes.c_int64 * 1)(N)
+    for path in (0, 1):
+        assert L.gemmq_linear_group(fmt, 1, wa, ya, na, X, Xq, M, K, path, None) == status
+
+
+def test_linear_group_arrays_and_paths(L):
+    P = ctypes.c_void_p
+    one_p, one_n = (P * 1)(FAKE16), (ctypes.c_int64 * 1)(1)
+    args = (FAKE16, FAKE16, 1, 256)
+    assert L.gemmq_linear_group(12, 0, one_p, one_p, one_n, *args, 0, None) == -1
+    assert L.gemmq_linear_group(12, 5, one_p, one_p, one_n, *args, 0, None) == -1
+    assert L.gemmq_linear_group(12, 1, None, one_p, one_n, *args, 0, None) == -1
+    assert L.gemmq_linear_group(12, 1, one_p, None, one_n, *args, 0, None) == -1
+    assert L.gemmq_linear_group(12, 1, one_p, one_p, None, *args, 0, None) == -1
+    assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, *args, 3, None) == -1
+    assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, FAKE16, FAKE16, 9, 256, 1,
+                                None) == -3
 
 
 @pytest.mark.parametrize("args,status", [

@@ -227,6 +227,32 @@ def test_empty_calls_touch_nothing(dev, gq):
     assert bool((xq == 0).all())
 
 
+def test_quantize_near_ties(dev, gq, orc):
+    # values whose x/d lies a little above, below or exactly on k + 1/2, with
+    # scales that are not powers of two: the quantizer's rounding must agree
+    # with the correctly rounded division everywhere, on both sides of a tie
+    log("quantize near ties")
+    rng = np.random.default_rng(77)
+    M, K = 6, 2048
+    x = np.empty((M, K), dtype=np.float32)
+    xb = x.reshape(-1, 256)
+    deltas = np.array([0, 2.0 ** -9, -2.0 ** -9, 2.0 ** -11, -2.0 ** -11, 2.0 ** -12,
+                       -2.0 ** -12, 2.0 ** -13, -2.0 ** -13, 2.0 ** -16, -2.0 ** -16,
+                       2.0 ** -20, -2.0 ** -20, 1e-7, -1e-7])
+    for i in range(xb.shape[0]):
+        amax = np.float32(rng.uniform(0.01, 50.0) if i % 5 else 3e-37)  # one tiny scale in 5
+        d = np.float32(amax / np.float32(127))
+        k = rng.integers(-127, 127, size=255)
+        dl = deltas[rng.integers(0, len(deltas), size=255)]
+        vals = ((k + 0.5 + dl) * np.float64(d)).astype(np.float32)
+        vals = np.clip(vals, -amax, amax)
+        xb[i, :255] = vals
+        xb[i, 255] = amax if i % 2 else -amax
+    got = to_host(gq.quantize_q8K(to_dev(x)))
+    want = orc.quantize_q8K(x)
+    assert np.array_equal(got.reshape(want.shape), want)
+
+
 @pytest.mark.parametrize("fmt", [Q4, Q6])
 @pytest.mark.parametrize("path,M", [(1, 1), (1, 5), (2, 9), (2, 130)])
 def test_group_equals_single_calls(dev, gq, orc, fmt, path, M):
