@@ -1,5 +1,6 @@
 """HIP-graph capture of the hot path (quantize + GEMV + GEMM, single and grouped
-launches), as the benchmark submits it: every replay must equal the eager result
+launches, and gemmq_linear_group: the fused quantize + GEMV launch and its
+two-launch form), as the benchmark submits it: every replay must equal the eager result
 bit for bit, with eager work, synchronisations and changed inputs between the
 replays."""
 import numpy as np
@@ -38,6 +39,17 @@ def test_graph_replays_match_eager():
         Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for N in Ns]
         groups.append((M, K, Ns, Ws, X, Xq, Ys))
 
+    # gemmq_linear_group: fused at (M 1, K 4096) and (M 2, K 1024), two launches
+    # at (M 1, K 12288) and (M 40, K 1024)
+    linears = []
+    for M, K in ((1, 4096), (2, 1024), (1, 12288), (40, 1024)):
+        Ns = (260, 33)
+        Ws = [torch.from_numpy(synth.make_weights(rng, gq.FMT_Q4K, N, K)).cuda() for N in Ns]
+        X = torch.from_numpy(synth.make_activations(rng, M, K, True)).cuda()
+        Xq = torch.empty(gq.q8K_bytes(M, K), dtype=torch.uint8, device="cuda")
+        Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for N in Ns]
+        linears.append((M, K, Ns, Ws, X, Xq, Ys))
+
     def run(stream):
         st = stream.cuda_stream
         for fmt, M, N, K, W, X, Xq, Y in bufs:
@@ -49,10 +61,14 @@ def test_graph_replays_match_eager():
             assert gq.gemm_group_ptr(gq.FMT_Q4K, [w.data_ptr() for w in Ws],
                                      [y.data_ptr() for y in Ys], list(Ns), Xq.data_ptr(), M, K,
                                      gq.PATH_AUTO, st) == 0
+        for M, K, Ns, Ws, X, Xq, Ys in linears:
+            assert gq.linear_group_ptr(gq.FMT_Q4K, [w.data_ptr() for w in Ws],
+                                       [y.data_ptr() for y in Ys], list(Ns), X.data_ptr(),
+                                       Xq.data_ptr(), M, K, gq.PATH_AUTO, st) == 0
 
     def outputs():
         out = [(b[6], b[7]) for b in bufs]
-        for M, K, Ns, Ws, X, Xq, Ys in groups:
+        for M, K, Ns, Ws, X, Xq, Ys in groups + linears:
             out += [(Xq, y) for y in Ys]
         return out
 

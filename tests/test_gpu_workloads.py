@@ -1,7 +1,8 @@
 """Parity on the five Qwen3-shaped workloads at full size, in the launch
-configuration the benchmark times (automatic path choice, activations quantized
-on the GPU, consecutive matrices that read one activation in one format run as
-one grouped launch).  Rows of large M are sampled (8 seeded rows, always the
+configuration the benchmark times (automatic path choice; consecutive matrices
+that read one activation in one format form one group, and each group is one
+gemmq_linear_group call: the activation quantized on the GPU with the matmul,
+fused into one launch at decode shapes).  Rows of large M are sampled (8 seeded rows, always the
 first and the last); the oracle computes those rows against every weight row.
 Bit-exact q8_K bytes for the sampled rows; f32 outputs within
 1e-5 * sum|w*xhat| + 1e-6.
@@ -53,20 +54,20 @@ def test_workload(dev, orc, name):
         rows = _rows(M, wl.seed * 1000 + M)
         xq_dev = {}
         xq_host = {}
-        for inp, K in wl.inputs():
-            x = g.activations[(M, inp)]
-            xd = to_dev(x)
-            xq_dev[inp] = gq.quantize_q8K(xd)
-            got = xq_dev[inp][torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
-            want = orc.quantize_q8K(x[rows])
-            assert np.array_equal(got, want), (name, M, inp)
-            xq_host[inp] = want
-            del xd
         for ms in _launches(wl, gq.MAX_GROUP):
             m0 = ms[0]
             log("  M=%d launch %s" % (M, "+".join(m.name for m in ms)))
             Wd = [to_dev(g.weights[m.name]) for m in ms]
-            ys = gq.gemm_group(m0.fmt, Wd, xq_dev[m0.inp], M, [m.N for m in ms], m0.K)
+            if m0.inp not in xq_dev:  # the activation's first group quantizes it
+                x = g.activations[(M, m0.inp)]
+                ys, xq_dev[m0.inp] = gq.linear_group(m0.fmt, Wd, to_dev(x),
+                                                     [m.N for m in ms])
+                got = xq_dev[m0.inp][torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
+                want = orc.quantize_q8K(x[rows])
+                assert np.array_equal(got, want), (name, M, m0.inp)
+                xq_host[m0.inp] = want
+            else:
+                ys = gq.gemm_group(m0.fmt, Wd, xq_dev[m0.inp], M, [m.N for m in ms], m0.K)
             for mat, y in zip(ms, ys):
                 W = g.weights[mat.name]
                 yr = y[torch.as_tensor(rows, device="cuda:0")].cpu().numpy()
