@@ -453,9 +453,10 @@ def main():
         per = rates[M]
         n_l = len(per)
         tot_t = sum(dt for _, dt, _ in per.values())
-        fused = all(f for _, _, f in per.values())
-        kname = ("gemv_kernel (quantizer fused)" if fused else "gemv_kernel") if M <= 8 \
-            else "gemm_q4k_kernel"
+        fused = [k for k, (_, _, f) in per.items() if f]
+        kname = "gemv_kernel" if M <= 8 else "gemm_q4k_kernel"
+        if fused:
+            kname += " (quantizer fused into: %s)" % ", ".join(fused)
         if M <= 8:
             algo = sum(sum(m.nbytes for m in ms) for ms, _, _ in per.values())
             ach = algo / tot_t / 1e9
