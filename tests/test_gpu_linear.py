@@ -64,6 +64,8 @@ CASES = [
     (2, 4096, [600, 5], 0),
     (4, 2048, [129], 1),
     (1, 4096, [0, 0], 0),       # no matrix: quantizes only
+    (1, 12800, [300, 5], 0),    # 50 blocks a row: two launches
+    (2, 12288, [40], 0),        # split rows with M = 2: two launches
     (1, 20480, [70], 0),        # 80 blocks a row: two launches
     (2, 8192, [100], 0),        # M K/256 too large to fuse
     (5, 1024, [100, 3], 0),     # M > 4
