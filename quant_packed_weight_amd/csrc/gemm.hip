@@ -460,7 +460,13 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   q4s_planes(q, aw, bw, 0, pa[0], pb[0]);
   __builtin_amdgcn_sched_barrier(0);
 
+  // Wave priorities (s_setprio) by phase: of the two waves that share a SIMD
+  // (one from each workgroup on the CU), the one whose matrix work is ahead
+  // gets the issue slots first -- phase A 2, phase B 1, the epilogue-only
+  // phase C 0 -- so MFMAs keep arriving while the other wave's vector work
+  // fills the gaps (measured +6% at M = 512, bit-identical results).
   // phase A: M-tile 0, unpack one step ahead
+  __builtin_amdgcn_s_setprio(2);
   v16i acca0 = (v16i){0}, accb0 = (v16i){0};
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
@@ -496,6 +502,7 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   __builtin_amdgcn_sched_barrier(0);
 
   // phase B: M-tile 1 beside tile 0's epilogue, two registers per step
+  __builtin_amdgcn_s_setprio(1);
   v16i acca1 = (v16i){0}, accb1 = (v16i){0};
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
@@ -508,6 +515,7 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   }
 
   // phase C: tile 1's epilogue
+  __builtin_amdgcn_s_setprio(0);
   q4s_load_dx(st, 32 + 4 * h, dx);
   const v16f am1 = mfma_f16(sfrag[1], mfrag, (v16f){0});
   q4s_epilogue<16>(acca1, accb1, am1, dx, dcol, mcol, y[1], 0);
