@@ -30,10 +30,17 @@
 //    workgroup (a round each, looping beyond 64 blocks): more, shorter waves
 //    keep the stream as parallel as for short rows; the waves' partial sums
 //    are added in LDS in wave order.
+//  * The fused form (FUSED, through gemmq_linear_group at decode shapes) also
+//    does the activation quantizer's work: a workgroup of eight row groups
+//    loads its share of the f32 activations first, then its weights, quantizes
+//    (the same q8k_block routine as the quantizer kernel) into LDS while the
+//    weights are in flight, and computes from LDS after one barrier.  That
+//    saves the quantizer launch; every workgroup repeats the quantization, so
+//    it is only used for rows of at most 16 blocks and M <= 4.
 //
 // Every output's arithmetic (per-lane block order, the xor tree and the wave
-// order) depends only on K, never on M or N, so row m of an M-row call equals a one-row call on
-// that row bit for bit.
+// order) depends only on K, never on M or N, and is the same in both forms, so
+// row m of an M-row call equals a one-row call on that row bit for bit.
 #include "device.h"
 #include "launch.h"
 #include "quant_block.h"
