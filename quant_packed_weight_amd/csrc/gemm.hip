@@ -23,11 +23,12 @@
 // Two kernels:
 //  * q4_K (gemm_q4k_kernel, further below): activation and raw weight tiles
 //    stream through LDS stages filled by direct buffer->LDS loads; each wave
-//    unpacks its own 32 weight rows and computes a 64 x 32 tile.
+//    unpacks its own 32 weight rows and computes a 64 x 32 tile; wave
+//    priorities by phase keep the two waves of a SIMD out of step.
 //  * q6_K (gemm_q6k_kernel): a 256-thread workgroup computes a 128 (M) x 64
 //    (N) tile, each of its four waves a 64 x 32 sub-tile.  Per super-block the
-//    workgroup stages the activation tile (int8 values, d_x, f16 group sums)
-//    and the weight tile -- unpacked once into the two int8 planes -- in LDS;
+//    workgroup stages the activation tile (int8 values, d_x) and the weight
+//    tile -- unpacked once into the two int8 planes -- in LDS;
 //    the global loads of super-block b+1 are issued before the MFMAs of
 //    super-block b and held in registers; one 69 KB stage lets two workgroups
 //    share a CU.
