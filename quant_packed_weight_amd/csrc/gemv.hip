@@ -409,7 +409,8 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     // activation loads first, weight loads next, so quantizing waits only for
     // the former; every load is unconditional (clamped), so the wait counts
     // are exact
-    constexpr int QB = 4;  // blocks quantized per wave, at most
+    // blocks quantized per wave, at most (M nb <= 16 MT when the form is used)
+    constexpr int QB = (16 * MT + NW - 1) / NW < 4 ? (16 * MT + NW - 1) / NW : 4;
     const int nq = M * nb;
     float4 xv[QB];
 #pragma unroll
@@ -422,16 +423,21 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     const int s0 = 16 * w;
     load_round(s0, true);
     __builtin_amdgcn_sched_barrier(0);
+    // every wave quantizes QB blocks without branches (past the last block it
+    // repeats it), so the blocks' reductions interleave; only real blocks are
+    // stored
+    Q8Lane q[QB];
+#pragma unroll
+    for (int j = 0; j < QB; ++j) q[j] = q8k_block(xv[j]);
 #pragma unroll
     for (int j = 0; j < QB; ++j) {
       const int t = wv + NW * j;
       if (t < nq) {  // wave-uniform
-        const Q8Lane q = q8k_block(xv[j]);
         uint8_t* o = xl + t * kXL;
-        *reinterpret_cast<uint32_t*>(o + 4 * lane) = q.packed;
-        if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(o + 256 + 2 * (lane >> 2)) = q.sums;
-        if (lane == 0) *reinterpret_cast<float*>(o + 288) = q.d;
-        if (blockIdx.x == 0) q8k_store(Xq + (int64_t)t * kQ8KBytes, q, lane);
+        *reinterpret_cast<uint32_t*>(o + 4 * lane) = q[j].packed;
+        if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(o + 256 + 2 * (lane >> 2)) = q[j].sums;
+        if (lane == 0) *reinterpret_cast<float*>(o + 288) = q[j].d;
+        if (blockIdx.x == 0) q8k_store(Xq + (int64_t)t * kQ8KBytes, q[j], lane);
       }
     }
     __syncthreads();
@@ -504,7 +510,9 @@ int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hip
   if (X) {
     if constexpr (IT == 1 && KS == 1 && MT <= 4) {
       constexpr int RG = kRG;
-      if (M * nb > kQB * RG) return -1;
+      // the kernel quantizes up to min(4, ceil(16 MT / RG)) blocks per wave
+      constexpr int QB = (16 * MT + RG - 1) / RG < 4 ? (16 * MT + RG - 1) / RG : 4;
+      if (M * nb > kQB * RG || M * nb > QB * RG) return -1;
       if (!make_tiles(grp, RG * P * R, gt)) return -1;
       const uint32_t tiles = gt.start[kMaxGroup];
       if (tiles == 0) return 0;

@@ -15,24 +15,16 @@
 
 namespace gemmq {
 
-// Exchange with lane ^ D inside the wave: DPP quad permutes for 1 and 2,
-// ds_swizzle (xor mode, within 32-lane halves) for 4, 8 and 16, a bpermute for 32.
-template <int D>
-__device__ __forceinline__ int qb_xor(int v) {
-  if constexpr (D == 1)
-    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-  else if constexpr (D == 2)
-    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
-  else if constexpr (D == 4 || D == 8 || D == 16)
-    return __builtin_amdgcn_ds_swizzle(v, 0x1F | (D << 10));
-  else
-    return __shfl_xor(v, D, 64);
+// DPP moves inside 16-lane rows (bound_ctrl: lanes without a source read 0).
+template <int CTRL>
+__device__ __forceinline__ int qb_dpp(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
-
-template <int D>
-__device__ __forceinline__ float qb_xor_f(float v) {
-  return __builtin_bit_cast(float, qb_xor<D>(__builtin_bit_cast(int, v)));
-}
+constexpr int kQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowRor4 = 0x124;  // rotate right by 4 within the row
+constexpr int kRowRor8 = 0x128;
+constexpr int kRowShl4 = 0x104;  // lane i reads lane i + 4 of its row
 
 // The lane's share of a quantized block.
 struct Q8Lane {
@@ -43,16 +35,25 @@ struct Q8Lane {
 
 // Every lane of the wave must be active.
 __device__ __forceinline__ Q8Lane q8k_block(float4 v) {
-  float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-  a = fmaxf(a, qb_xor_f<1>(a));
-  a = fmaxf(a, qb_xor_f<2>(a));
-  a = fmaxf(a, qb_xor_f<4>(a));
-  a = fmaxf(a, qb_xor_f<8>(a));
-  a = fmaxf(a, qb_xor_f<16>(a));
-  a = fmaxf(a, qb_xor_f<32>(a));
+  // amax as the largest |x| bit pattern (for non-negative finite floats the
+  // integer order is the float order): DPP inside each 16-lane row, then the
+  // four row maxima read back as scalars
+  uint32_t a = __builtin_bit_cast(uint32_t, v.x) & 0x7fffffffu;
+  a = max(a, __builtin_bit_cast(uint32_t, v.y) & 0x7fffffffu);
+  a = max(a, __builtin_bit_cast(uint32_t, v.z) & 0x7fffffffu);
+  a = max(a, __builtin_bit_cast(uint32_t, v.w) & 0x7fffffffu);
+  a = max(a, (uint32_t)qb_dpp<kQuadXor1>((int)a));
+  a = max(a, (uint32_t)qb_dpp<kQuadXor2>((int)a));
+  a = max(a, (uint32_t)qb_dpp<kRowRor4>((int)a));
+  a = max(a, (uint32_t)qb_dpp<kRowRor8>((int)a));
+  const uint32_t r01 = max((uint32_t)__builtin_amdgcn_readlane((int)a, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)a, 16));
+  const uint32_t r23 = max((uint32_t)__builtin_amdgcn_readlane((int)a, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)a, 48));
+  const float amax = __builtin_bit_cast(float, max(r01, r23));
 
   Q8Lane r;
-  r.d = a / 127.0f;
+  r.d = amax / 127.0f;
   int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
   if (r.d != 0.0f) {  // wave-uniform
     q0 = (int)fminf(fmaxf(rintf(v.x / r.d), -127.0f), 127.0f);
@@ -62,12 +63,12 @@ __device__ __forceinline__ Q8Lane q8k_block(float4 v) {
   }
   r.packed = (uint32_t)(q0 & 0xff) | ((uint32_t)(q1 & 0xff) << 8) |
              ((uint32_t)(q2 & 0xff) << 16) | ((uint32_t)(q3 & 0xff) << 24);
-  // group g = 16 values = lanes 4g..4g+3; after two xor steps every lane of the
-  // group holds its sum, and lane 8j reads group 2j+1's from lane 8j+4
+  // group g = 16 values = lanes 4g..4g+3; after two quad steps every lane of
+  // the group holds its sum, and lane 8j reads group 2j+1's from lane 8j+4
   int s = q0 + q1 + q2 + q3;
-  s += qb_xor<1>(s);
-  s += qb_xor<2>(s);
-  const int s_next = qb_xor<4>(s);
+  s += qb_dpp<kQuadXor1>(s);
+  s += qb_dpp<kQuadXor2>(s);
+  const int s_next = qb_dpp<kRowShl4>(s);
   r.sums = (uint32_t)(s & 0xffff) | ((uint32_t)(s_next & 0xffff) << 16);
   return r;
 }
