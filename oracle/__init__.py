@@ -13,4 +13,5 @@ from .oracle import (  # noqa: F401
     gemm_int,
     load,
     quantize_q8K,
+    silu_mul,
 )

@@ -339,5 +339,16 @@ int oracle_gemm_dequant(int fmt, const uint8_t *W, const uint8_t *Xq, int64_t M,
     return 0;
 }
 
+/* The SiLU-gated product of an MLP's two up-projections, element by element:
+ * y = silu(g) * u with silu(g) = g / (1 + e^-g), in double.  The pages name this
+ * step silu_mul and run it right after the gate/up matmuls (molayo article
+ * "PocketLLM: 단일 가속기에서 대규모 언어 모델 실행", status row "src/ -- C++
+ * engine": silu_mul's thread grain sized for decode shapes). */
+void oracle_silu_mul(const double *g, const double *u, int64_t n, double *y)
+{
+    for (int64_t i = 0; i < n; ++i)
+        y[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+}
+
 /* Version of this oracle's interface, for the test loader. */
-int oracle_version(void) { return 1; }
+int oracle_version(void) { return 2; }

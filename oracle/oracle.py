@@ -57,6 +57,8 @@ def load():
             lib.oracle_gemm_int.restype = ctypes.c_int
             lib.oracle_gemm_dequant.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, I64, P, P]
             lib.oracle_gemm_dequant.restype = ctypes.c_int
+            lib.oracle_silu_mul.argtypes = [P, P, I64, P]
+            lib.oracle_silu_mul.restype = None
             _lib = lib
     return _lib
 
@@ -123,3 +125,13 @@ def gemm_dequant(fmt, W, Xq, M, N, K, rows=None):
     if rc != 0:
         raise ValueError("oracle_gemm_dequant: bad arguments")
     return Y, S
+
+
+def silu_mul(g, u) -> np.ndarray:
+    """silu(g) * u element by element, float64 (same shape as g)."""
+    g = np.ascontiguousarray(g, dtype=np.float64)
+    u = np.ascontiguousarray(u, dtype=np.float64)
+    assert g.shape == u.shape
+    y = np.empty_like(g)
+    load().oracle_silu_mul(_ptr(g), _ptr(u), g.size, _ptr(y))
+    return y
