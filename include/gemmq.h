@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 3
+#define GEMMQ_ABI_VERSION 4
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q4_K 12
@@ -167,6 +167,30 @@ int gemmq_gemm_group(int fmt, int count, const void *const *W, float *const *Y, 
 int gemmq_linear_group(int fmt, int count, const void *const *W, float *const *Y,
                        const int64_t *N, const float *X, void *Xq, int64_t M, int64_t K,
                        int path, void *stream);
+
+/*
+ * The MLP's gated up-projection in one call: quantize X to q8_K into Xq, then
+ *   Y[m, n] = silu(G[m, n]) * U[m, n],   G = Wg x, U = Wu x,
+ * where G and U are exactly the values gemmq_linear_group(fmt, 2, {Wg, Wu}, ...)
+ * computes (same bits), and the product is taken in f32 as e = expf(-g),
+ * s = g / (1 + e) (correctly rounded division), y = s * u.  This is the silu_mul
+ * step the pages run right after the gate/up matmuls (molayo article, status row
+ * "src/"), moved into the matmul's output: one output matrix instead of two.  At
+ * decode shapes it is one launch (quantizer fused, as in gemmq_linear_group).
+ *   Wg, Wu  device, gemmq_weight_bytes(fmt, N, K) bytes each, alignment as in
+ *           gemmq_gemm; the gate and the up matrix, N rows each.
+ *   X, Xq   as in gemmq_linear_group (Xq receives the q8_K blocks of X).
+ *   Y       device, f32 [M, N], 4-byte aligned; overwritten.
+ *   fmt, M, K, path, stream  as in gemmq_gemm_ex; N == 0 still quantizes X.
+ * Accuracy: with g, u within the matmul bound of gemmq_gemm, |y - silu(g*) u*|
+ * is at most 1.1 |u| dg + |silu(g)| du plus a few f32 roundings of y (g*, u*
+ * exact; dg, du the matmul bounds), and, from the f32 range, |g u| 2^-126 +
+ * 2^-149 (exp(-g) overflows for g < -88.72, where y is +-0).
+ * Errors: those of gemmq_linear_group for the two matrices; nothing is launched
+ * on an error.
+ */
+int gemmq_linear_silu_mul(int fmt, const void *Wg, const void *Wu, const float *X, void *Xq,
+                          float *Y, int64_t M, int64_t N, int64_t K, int path, void *stream);
 
 /* gemmq_linear_group for one matrix with GEMMQ_PATH_AUTO. */
 int gemmq_linear(int fmt, const void *W, const float *X, void *Xq, float *Y, int64_t M, int64_t N,

@@ -30,6 +30,7 @@ from ._lib import (  # noqa: F401
     linear,
     linear_group,
     linear_group_ptr,
+    linear_silu_mul,
     q8K_bytes,
     quantize_q8K,
     quantize_q8K_ptr,

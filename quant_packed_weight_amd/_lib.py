@@ -18,7 +18,7 @@ Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 
@@ -40,6 +40,7 @@ EXPORTS = {
     "gemmq_linear_group": (_I, [_I, _I, ctypes.POINTER(_P), ctypes.POINTER(_P),
                                 ctypes.POINTER(_I64), _P, _P, _I64, _I64, _I, _P]),
     "gemmq_linear": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "gemmq_linear_silu_mul": (_I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
 }
 
@@ -254,3 +255,26 @@ def linear(fmt, w, x, N, path=PATH_AUTO, stream=None):
     """y = W x for f32 activations x [M, K] (quantized to q8_K on the device)."""
     outs, _ = linear_group(fmt, [w], x, [N], path=path, stream=stream)
     return outs[0]
+
+
+def linear_silu_mul(fmt, wg, wu, x, N, xq=None, out=None, path=PATH_AUTO, stream=None):
+    """silu(Wg x) * (Wu x) for f32 activations x [M, K] (gemmq_linear_silu_mul):
+    returns (f32 [M, N], xq) with xq the q8_K blocks of x."""
+    torch = _torch()
+    M, K = x.shape
+    for w in (wg, wu):
+        if w.numel() < weight_bytes(fmt, N, K):
+            raise ValueError("buffer smaller than the stated shape")
+    if xq is None:
+        xq = torch.empty((M, (K // QK) * Q8K_BYTES), dtype=torch.uint8, device=x.device)
+    elif xq.numel() < q8K_bytes(M, K):
+        raise ValueError("xq too small")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    elif out.numel() < M * N:
+        raise ValueError("out too small")
+    _check(lib().gemmq_linear_silu_mul(fmt, _dev(wg, "wg", torch.uint8), _dev(wu, "wu", torch.uint8),
+                                       _dev(x, "x", torch.float32), _dev(xq, "xq", torch.uint8),
+                                       _dev(out, "out", torch.float32), M, N, K, path,
+                                       _stream(stream)), "gemmq_linear_silu_mul")
+    return out, xq

@@ -193,6 +193,39 @@ int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y
   return launched(gemmq::launch_gemm(fmt, g, xq, M, K, st));
 }
 
+int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* X, void* Xq,
+                          float* Y, int64_t M, int64_t N, int64_t K, int path, void* stream) {
+  int rc = check_weights(fmt, Wg, N, K);
+  if (rc == GEMMQ_OK) rc = check_weights(fmt, Wu, N, K);
+  if (rc != GEMMQ_OK) return rc;
+  if (M < 0) return GEMMQ_E_INVALID_ARG;
+  if (M > kMaxRows || 2 * N > kMaxRows) return GEMMQ_E_SHAPE;
+  if (path != GEMMQ_PATH_AUTO && path != GEMMQ_PATH_GEMV && path != GEMMQ_PATH_GEMM)
+    return GEMMQ_E_INVALID_ARG;
+  if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
+  if (M == 0) return GEMMQ_OK;
+  if (!X || !Xq || (N > 0 && !Y)) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(X, 16) || !aligned(Xq, 4) || (N > 0 && !aligned(Y, 4))) return GEMMQ_E_ALIGNMENT;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  gemmq::Group g{};
+  g.count = 2;
+  g.W[0] = static_cast<const uint8_t*>(Wg);
+  g.W[1] = static_cast<const uint8_t*>(Wu);
+  g.Y[0] = g.Y[1] = Y;
+  g.N[0] = g.N[1] = N;
+  uint8_t* xq = static_cast<uint8_t*>(Xq);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool gemv = use_gemv(path, M);
+  clear_pending();
+  if (N > 0 && gemv && gemmq::gemv_fusable(M, K))
+    return launched(gemmq::launch_gemv_silu(fmt, g, nullptr, X, xq, (int)M, K, st));
+  rc = launched(gemmq::launch_quantize_q8K(X, xq, M, K, st));
+  if (rc != GEMMQ_OK || N == 0) return rc;
+  if (gemv) return launched(gemmq::launch_gemv_silu(fmt, g, xq, nullptr, nullptr, (int)M, K, st));
+  return launched(gemmq::launch_gemm_silu(fmt, g, xq, M, K, st));
+}
+
 int gemmq_linear(int fmt, const void* W, const float* X, void* Xq, float* Y, int64_t M, int64_t N,
                  int64_t K, void* stream) {
   return gemmq_linear_group(fmt, 1, &W, &Y, &N, X, Xq, M, K, GEMMQ_PATH_AUTO, stream);

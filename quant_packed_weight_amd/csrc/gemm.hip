@@ -122,11 +122,30 @@ __device__ __forceinline__ void store_x(uint8_t* st, const XRegs& r) {
   if (part == 0) reinterpret_cast<uint32_t*>(st + kOffDx)[row] = r.d;
 }
 
-// Columns past N load a copy of column N-1 (never stored).
-__device__ __forceinline__ const uint8_t* w_row(const uint8_t* __restrict__ W, int64_t n0,
+// Columns past N load a copy of column N-1 (never stored).  SILU: N counts the
+// interleaved gate (even) and up (odd) rows; the up matrix is Wu.
+template <bool SILU>
+__device__ __forceinline__ const uint8_t* w_row(const uint8_t* __restrict__ W,
+                                                const uint8_t* __restrict__ Wu, int64_t n0,
                                                 int64_t N, int nb) {
-  const int64_t n = n0 + (threadIdx.x >> 2);
-  return W + (n < N ? n : N - 1) * nb * kQ6KBytes;
+  int64_t n = n0 + (threadIdx.x >> 2);
+  if constexpr (SILU) {
+    if (n >= N) n = N - 2 + (n & 1);
+    return ((n & 1) ? Wu : W) + (n >> 1) * nb * kQ6KBytes;
+  } else {
+    return W + (n < N ? n : N - 1) * nb * kQ6KBytes;
+  }
+}
+
+// y = silu(g) * u (the same f32 steps as the GEMV's): e = exp(-g), g / (1 + e), * u
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// the value of lane ^ 1 (quad permute [1,0,3,2]); every lane must be active
+__device__ __forceinline__ float pair_partner(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF,
+                                                            0xF, true));
 }
 
 // ------------------------------------------------- q6_K weight tile
@@ -250,6 +269,7 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
 }
 
 // ------------------------------------------------- the q6_K kernel
+template <bool SILU>
 __global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
                                                           const uint8_t* __restrict__ Xq, int64_t M,
                                                           int nb) {
@@ -275,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
     for (int r = 0; r < 16; ++r) y[mt][r] = 0.0f;
 
   const uint8_t* xrow = x_row(Xq, m0, M, nb);
-  const uint8_t* wrow = w_row(W, n0, N, nb);
+  const uint8_t* wrow = w_row<SILU>(W, gt.W[1], n0, N, nb);
   XRegs xr;
   W6Regs wr;
   load_x(xr, xrow, 0);
@@ -293,7 +313,18 @@ __global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
   }
 
   const int64_t col = n0 + bcol;
-  if (col < N) {
+  if constexpr (SILU) {
+    // lanes 2k / 2k+1 hold gate / up of output col / 2 for the same rows
+    const int64_t n = col >> 1, Nout = N >> 1;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float u = pair_partner(y[mt][r]);
+        const int64_t row = m0 + wm * 64 + 32 * mt + 8 * (r >> 2) + 4 * hsel + (r & 3);
+        if ((i & 1) == 0 && n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(y[mt][r], u);
+      }
+  } else if (col < N) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -522,7 +553,11 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
   q4s_epilogue<16>(acca1, accb1, am1, dx, dcol, mcol, y[1], 0);
 }
 
-template <int SPLIT>
+// SILU: the tile's 128 weight rows are gate rows 64t..64t+63 then up rows
+// 64t..64t+63 (two buffer descriptors; load groups 0..8 and 9..17 split exactly
+// at row 64), and lane i of wave w unpacks gate row 16w + i/2 for even i, the up
+// row for odd i, so each MFMA column pair holds (gate, up) of one output.
+template <int SPLIT, bool SILU>
 __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
     const GroupTiles gt, const uint8_t* __restrict__ Xq, int64_t M, int nb) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -549,9 +584,13 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
   // the workgroup's activation rows and weight rows as two buffers: rows past
   // M or N read as zero (their outputs are never stored)
   const int64_t mrows = M - m0 < q4s::kBM ? M - m0 : q4s::kBM;
-  const int64_t nrows = N - n0 < q4s::kBN ? N - n0 : q4s::kBN;
   const rsrc_t xr = make_rsrc(Xq + m0 * xstride, (uint32_t)(mrows * xstride));
-  const rsrc_t wr = make_rsrc(W + n0 * wstride, (uint32_t)(nrows * wstride));
+  // SILU: outputs o0..o0+63 of Nout; wr covers the gate rows, wr2 the up rows
+  const int64_t Nout = SILU ? N >> 1 : N, o0 = SILU ? (int64_t)tile * (q4s::kBN / 2) : n0;
+  const int64_t orows = SILU ? (Nout - o0 < q4s::kBN / 2 ? Nout - o0 : q4s::kBN / 2)
+                             : (N - n0 < q4s::kBN ? N - n0 : q4s::kBN);
+  const rsrc_t wr = make_rsrc(W + o0 * wstride, (uint32_t)(orows * wstride));
+  const rsrc_t wr2 = SILU ? make_rsrc(gt.W[1] + o0 * wstride, (uint32_t)(orows * wstride)) : wr;
   // this group's half of every stage
   const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)lds) +
                         (uint32_t)kg * q4s::kStage;
@@ -570,8 +609,10 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
   uint32_t vw[5];
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
-    const uint32_t c = 64u * (uint32_t)(wave + 4 * j) + (uint32_t)lane;
-    vw[j] = (c / 9u) * wstride + 16u * (c % 9u);
+    const uint32_t u = (uint32_t)(wave + 4 * j);
+    const uint32_t c = 64u * u + (uint32_t)lane;
+    const uint32_t row = c / 9u - (SILU && u >= 9u ? 64u : 0u);  // up rows from wr2's base
+    vw[j] = row * wstride + 16u * (c % 9u);
   }
 
   // part p (0..15) of the loads of super-block b into stage `slot`: value rows
@@ -591,9 +632,10 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
     } else if (p == 10) {
       if (wave == 0) dma4(xr, vdx, xb, st + q4s::kOffDx);
     } else if (p < 15) {
-      dma16(wr, vw[p - 11], wb, st + q4s::kOffW + 1024 * (wave + 4 * (p - 11)));
+      const int u = wave + 4 * (p - 11);
+      dma16(SILU && u >= 9 ? wr2 : wr, vw[p - 11], wb, st + q4s::kOffW + 1024 * u);
     } else {
-      if (wave < 2) dma16(wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
+      if (wave < 2) dma16(SILU ? wr2 : wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
     }
   };
   float y[2][16];
@@ -601,6 +643,8 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r) y[t][r] = 0.0f;
+  // the LDS weight row this lane unpacks (its MFMA column)
+  const int wrow_l = SILU ? ((i & 1) ? 64 : 0) + 16 * wave + (i >> 1) : 32 * wave + i;
 
   // Step s: group kg works on super-block b0 + s.  Every step issues one stage
   // of loads -- past the group's last block they re-read a valid block into a
@@ -619,7 +663,7 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
     const int nxt = slot == 0 ? q4s::kS - 1 : slot - 1;
     const int bn = blk(s + q4s::kS - 1);
     if (b0 + s < bend)
-      q4s_compute(ldsg + slot * kStride, 32 * wave + i, y, i, h,
+      q4s_compute(ldsg + slot * kStride, wrow_l, y, i, h,
                   [&](int p) { issue(bn, nxt, p); });
     else  // the second group's idle last step (odd nb): only its loads
 #pragma unroll
@@ -646,43 +690,65 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) y[t][r] += red[(16 * t + r) * 64];
   }
-  const int64_t col = n0 + 32 * wave + i;
-  if (col < N) {
+  if constexpr (SILU) {
+    // lanes 2k / 2k+1 hold gate / up of output o0 + 16 wave + k for the same rows
+    const int64_t n = o0 + 16 * wave + (i >> 1);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
+        const float u = pair_partner(y[t][r]);
         const int64_t row = m0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < M) Y[row * N + col] = y[t][r];
+        if ((i & 1) == 0 && n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(y[t][r], u);
       }
+  } else {
+    const int64_t col = n0 + 32 * wave + i;
+    if (col < N) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row < M) Y[row * N + col] = y[t][r];
+        }
+    }
   }
 }
 
 }  // namespace
 
-int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
-                hipStream_t st) {
-  const int64_t nb = K / kQK;
-  if (nb > 0x7fffffffLL) return -1;
-  // the dynamic LDS limit is a per-device attribute of each kernel
+namespace {
+
+// the dynamic LDS limit is a per-device attribute of each kernel
+template <bool SILU>
+bool set_lds_limits() {
   static std::atomic<int> attr_done[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   if (attr_done[dev].load(std::memory_order_acquire) == 0) {
-    if (hipFuncSetAttribute((const void*)gemm_q6k_kernel,
+    if (hipFuncSetAttribute((const void*)gemm_q6k_kernel<SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_q4k_kernel<1>,
+        hipFuncSetAttribute((const void*)gemm_q4k_kernel<1, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             q4s::lds_bytes<1>()) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_q4k_kernel<2>,
+        hipFuncSetAttribute((const void*)gemm_q4k_kernel<2, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             q4s::lds_bytes<2>()) != hipSuccess)
-      return -1;
+      return false;
     attr_done[dev].store(1, std::memory_order_release);
   }
+  return true;
+}
+
+template <bool SILU>
+int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
+               hipStream_t st) {
+  const int64_t nb = K / kQK;
+  if (nb > 0x7fffffffLL) return -1;
+  if (!set_lds_limits<SILU>()) return -1;
   GroupTiles gt;
   const int64_t bn = fmt == 12 ? q4s::kBN : kBN, bm = fmt == 12 ? q4s::kBM : kBM;
-  if (!make_tiles(grp, bn, gt)) return -1;
+  if (!(SILU ? make_pair_tiles(grp, bn, gt) : make_tiles(grp, bn, gt))) return -1;
   const uint32_t gx = gt.start[kMaxGroup];
   const int64_t gy = (M + bm - 1) / bm;
   if (gy > 65535) return -1;
@@ -691,15 +757,28 @@ int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t
   if (fmt == 12) {
     // long rows run split over K (the choice depends on K only)
     if (nb >= 32)
-      hipLaunchKernelGGL(gemm_q4k_kernel<2>, grid, dim3(512), q4s::lds_bytes<2>(), st, gt, Xq, M,
-                         (int)nb);
+      hipLaunchKernelGGL((gemm_q4k_kernel<2, SILU>), grid, dim3(512), q4s::lds_bytes<2>(), st, gt,
+                         Xq, M, (int)nb);
     else
-      hipLaunchKernelGGL(gemm_q4k_kernel<1>, grid, dim3(256), q4s::lds_bytes<1>(), st, gt, Xq, M,
-                         (int)nb);
+      hipLaunchKernelGGL((gemm_q4k_kernel<1, SILU>), grid, dim3(256), q4s::lds_bytes<1>(), st, gt,
+                         Xq, M, (int)nb);
   } else {
-    hipLaunchKernelGGL(gemm_q6k_kernel, grid, dim3(256), kLds, st, gt, Xq, M, (int)nb);
+    hipLaunchKernelGGL(gemm_q6k_kernel<SILU>, grid, dim3(256), kLds, st, gt, Xq, M, (int)nb);
   }
   return 0;
+}
+
+}  // namespace
+
+int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
+                hipStream_t st) {
+  return launch_any<false>(fmt, grp, Xq, M, K, st);
+}
+
+int launch_gemm_silu(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
+                     hipStream_t st) {
+  if (grp.count != 2 || grp.N[0] != grp.N[1]) return -1;
+  return launch_any<true>(fmt, grp, Xq, M, K, st);
 }
 
 }  // namespace gemmq

@@ -222,13 +222,24 @@ __device__ __forceinline__ int dot16(const uint32_t* w, const u32x4& x, int s) {
 }
 
 // ---------------------------------------------------------------- kernel
+// SiLU-gated product (SILU): y = silu(g) * u from the two outputs g, u of one
+// row of the gate and the up matrix, in f32: e = exp(-g) (the device expf),
+// s = g / (1 + e) correctly rounded, y = s * u.
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
 // FMT: 12 q4_K, 14 q6_K.  MT activation rows computed (>= M).  IT rounds of 16
 // blocks loaded together.  P rows per round.  KS waves share one row (P = 1):
 // wave w takes rounds w, w + KS, ... and the KS partial sums meet in LDS, added
 // in wave order.  R rows per wave (P = 1), computed side by side on the same
 // activation fragments.  The grid is the concatenation of every grouped
 // matrix's tiles (one tile = P R rows, one workgroup of KS waves).
-template <int FMT, int MT, int IT, int P, int KS, int R, int RG, bool FUSED>
+// SILU: the group is one virtual matrix of 2N rows whose row 2n is gate row n
+// (gt.W[0]) and row 2n+1 up row n (gt.W[1]); P R is even, so a wave's rows come
+// in (gate, up) pairs computed exactly as in two plain calls, and the pair's
+// outputs meet in LDS for y[m][n] = silu(g) * u (Y has N columns).
+template <int FMT, int MT, int IT, int P, int KS, int R, int RG, bool FUSED, bool SILU>
 __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
                                                             uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ X, int nb,
@@ -244,6 +255,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
   static_assert(KS == 1 || P == 1, "split rows only when one row fills a round");
   static_assert(R == 1 || P == 1, "several rows per wave only when one row fills a round");
   static_assert(!FUSED || IT == 1, "the fused form takes one round per wave");
+  static_assert(!SILU || (P * R) % 2 == 0, "gate/up rows come in pairs");
   constexpr int V = R * MT;  // outputs of a wave: value r * MT + m is row r, activation row m
   const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)) : 0;
   const int w = wv % KS, rg = wv / KS;  // K share and row group of this wave
@@ -259,8 +271,13 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     int64_t n = n0 + prow + r;
-    if (n >= N) n = N - 1;  // tail rows: a valid row, never stored
-    wrow[r] = W + n * nb * BB;
+    if constexpr (SILU) {
+      if (n >= N) n = N - 2 + (n & 1);  // tail pairs: a valid pair, never stored
+      wrow[r] = ((n & 1) ? gt.W[1] : W) + (n >> 1) * nb * BB;
+    } else {
+      if (n >= N) n = N - 1;  // tail rows: a valid row, never stored
+      wrow[r] = W + n * nb * BB;
+    }
   }
 
   // per-lane constants
@@ -451,6 +468,14 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
 
   // ---- 3. lane reduction and store
   const int64_t nn0 = n0 + prow;
+  // SILU: the wave's finished values by (row slot prow R + r, m), then combined
+  __shared__ float sv[SILU ? NW : 1][SILU ? P * R * MT : 1];
+  auto put = [&](int64_t nn, int slot, int m, float v) {
+    if constexpr (SILU)
+      sv[wv][slot * MT + m] = v;
+    else if (m < M && nn < N)
+      Y[(int64_t)m * N + nn] = v;
+  };
   if constexpr (KS > 1) {
     // lanes of the xor tree hold the wave's partial of value vidx; the KS
     // partials of each value are added in wave order by wave 0
@@ -467,9 +492,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
       float t = red[rg][0][j];
 #pragma unroll
       for (int k = 1; k < KS; ++k) t += red[rg][k][j];
-      const int m = j % MT;
-      const int64_t nn = nn0 + j / MT;
-      if (m < M && nn < N) Y[(int64_t)m * N + nn] = t;
+      put(nn0 + j / MT, j / MT, j % MT, t);
     }
   } else if constexpr (V <= SEG) {
     float v[V];
@@ -478,17 +501,31 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     seg_reduce<V, SEG>(v, lane);
     if (holder<V, SEG>(lane)) {
       const int j = vidx<V, SEG>(lane);
-      const int m = j % MT;
-      const int64_t nn = nn0 + j / MT;
-      if (m < M && nn < N) Y[(int64_t)m * N + nn] = v[0];
+      put(nn0 + j / MT, prow * R + j / MT, j % MT, v[0]);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < V; ++j) {
       const float v = seg_all<SEG>(acc[j]);
-      const int m = j % MT;
-      const int64_t nn = nn0 + j / MT;
-      if ((lane & (SEG - 1)) == 0 && m < M && nn < N) Y[(int64_t)m * N + nn] = v;
+      if ((lane & (SEG - 1)) == 0) put(nn0 + j / MT, prow * R + j / MT, j % MT, v);
+    }
+  }
+  if constexpr (SILU) {
+    // the slots were written by other lanes of this wave (for split rows by
+    // wave 0 of the row group, which alone reads them): a wave's LDS accesses
+    // complete in order, the fence keeps the compiler from reordering them
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (KS == 1 || w == 0) {
+      constexpr int NO = (P * R / 2) * MT;  // (gate, up) pairs x activation rows
+      static_assert(NO <= 64, "one output per lane");
+      const int64_t Nout = N >> 1;
+      if (lane < NO) {
+        const int pr = lane / MT, m = lane % MT;
+        const float g = sv[wv][(2 * pr) * MT + m], u = sv[wv][(2 * pr + 1) * MT + m];
+        const int64_t n = (n0 >> 1) + pr;
+        if (m < M && n < Nout) Y[(int64_t)m * Nout + n] = silu_mul_f32(g, u);
+      }
     }
   }
 }
@@ -503,8 +540,15 @@ constexpr int kQB = 4;
 
 // X == nullptr: the plain form, reading the q8_K blocks at Xq.  Otherwise the
 // fused form: every workgroup quantizes X into its LDS and workgroup 0 also
-// writes the blocks to Xq.
-template <int FMT, int MT, int IT, int P, int KS, int R = 1>
+// writes the blocks to Xq.  SILU: grp holds the gate (0) and up (1) matrices
+// of equal N and one output Y (see the kernel); their tiles cover the 2N
+// interleaved rows (make_pair_tiles).
+template <bool SILU>
+bool group_tiles(const Group& grp, int64_t rows_per_tile, GroupTiles& gt) {
+  return SILU ? make_pair_tiles(grp, rows_per_tile, gt) : make_tiles(grp, rows_per_tile, gt);
+}
+
+template <int FMT, int MT, bool SILU, int IT, int P, int KS, int R = 1>
 int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hipStream_t st) {
   GroupTiles gt;
   if (X) {
@@ -513,21 +557,21 @@ int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hip
       // the kernel quantizes up to min(4, ceil(16 MT / RG)) blocks per wave
       constexpr int QB = (16 * MT + RG - 1) / RG < 4 ? (16 * MT + RG - 1) / RG : 4;
       if (M * nb > kQB * RG || M * nb > QB * RG) return -1;
-      if (!make_tiles(grp, RG * P * R, gt)) return -1;
+      if (!group_tiles<SILU>(grp, RG * P * R, gt)) return -1;
       const uint32_t tiles = gt.start[kMaxGroup];
       if (tiles == 0) return 0;
-      hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true>), dim3(tiles),
+      hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU>), dim3(tiles),
                          dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
       return 0;
     } else {
       return -1;
     }
   }
-  if (!make_tiles(grp, P * R, gt)) return -1;
+  if (!group_tiles<SILU>(grp, P * R, gt)) return -1;
   const uint32_t tiles = gt.start[kMaxGroup];
   if (tiles == 0) return 0;
-  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, 1, false>), dim3(tiles), dim3(64 * KS),
-                     0, st, gt, Xq, (const float*)nullptr, nb, M);
+  hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, 1, false, SILU>), dim3(tiles),
+                     dim3(64 * KS), 0, st, gt, Xq, (const float*)nullptr, nb, M);
   return 0;
 }
 
@@ -537,44 +581,50 @@ int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hip
 // two rows per wave whenever a row fills a round.
 int split_waves(int nb) { return nb <= 16 ? 1 : nb <= 32 ? 2 : nb <= 48 ? 3 : nb <= 64 ? 4 : 0; }
 
-template <int FMT, int MT>
+template <int FMT, int MT, bool SILU>
 int launch_mt(const Group& g, uint8_t* Xq, const float* X, int nb, int M, hipStream_t st) {
-  if (nb == 1) return launch_cfg<FMT, MT, 1, 16, 1>(g, Xq, X, nb, M, st);
-  if (nb == 2) return launch_cfg<FMT, MT, 1, 8, 1>(g, Xq, X, nb, M, st);
-  if (nb == 4) return launch_cfg<FMT, MT, 1, 4, 1>(g, Xq, X, nb, M, st);
-  if (nb == 8) return launch_cfg<FMT, MT, 1, 2, 1>(g, Xq, X, nb, M, st);
-  if (nb <= 16) return launch_cfg<FMT, MT, 1, 1, 1, 2>(g, Xq, X, nb, M, st);
-  if (nb <= 32) return launch_cfg<FMT, MT, 1, 1, 2, 2>(g, Xq, X, nb, M, st);
-  if (nb <= 48) return launch_cfg<FMT, MT, 1, 1, 3, 2>(g, Xq, X, nb, M, st);
-  if (nb <= 64) return launch_cfg<FMT, MT, 1, 1, 4, 2>(g, Xq, X, nb, M, st);
-  return launch_cfg<FMT, MT, 2, 1, 4, 2>(g, Xq, X, nb, M, st);
+  if (nb == 1) return launch_cfg<FMT, MT, SILU, 1, 16, 1>(g, Xq, X, nb, M, st);
+  if (nb == 2) return launch_cfg<FMT, MT, SILU, 1, 8, 1>(g, Xq, X, nb, M, st);
+  if (nb == 4) return launch_cfg<FMT, MT, SILU, 1, 4, 1>(g, Xq, X, nb, M, st);
+  if (nb == 8) return launch_cfg<FMT, MT, SILU, 1, 2, 1>(g, Xq, X, nb, M, st);
+  if (nb <= 16) return launch_cfg<FMT, MT, SILU, 1, 1, 1, 2>(g, Xq, X, nb, M, st);
+  if (nb <= 32) return launch_cfg<FMT, MT, SILU, 1, 1, 2, 2>(g, Xq, X, nb, M, st);
+  if (nb <= 48) return launch_cfg<FMT, MT, SILU, 1, 1, 3, 2>(g, Xq, X, nb, M, st);
+  if (nb <= 64) return launch_cfg<FMT, MT, SILU, 1, 1, 4, 2>(g, Xq, X, nb, M, st);
+  return launch_cfg<FMT, MT, SILU, 2, 1, 4, 2>(g, Xq, X, nb, M, st);
 }
 
-template <int FMT>
+template <int FMT, bool SILU>
 int launch_fmt(const Group& g, uint8_t* Xq, const float* X, int M, int nb, hipStream_t st) {
   switch (M) {
-    case 1: return launch_mt<FMT, 1>(g, Xq, X, nb, M, st);
-    case 2: return launch_mt<FMT, 2>(g, Xq, X, nb, M, st);
+    case 1: return launch_mt<FMT, 1, SILU>(g, Xq, X, nb, M, st);
+    case 2: return launch_mt<FMT, 2, SILU>(g, Xq, X, nb, M, st);
     case 3:
-    case 4: return launch_mt<FMT, 4>(g, Xq, X, nb, M, st);
+    case 4: return launch_mt<FMT, 4, SILU>(g, Xq, X, nb, M, st);
     case 5:
     case 6:
     case 7:
     case 8:
       if (X) return -1;
-      return launch_mt<FMT, 8>(g, Xq, X, nb, M, st);
+      return launch_mt<FMT, 8, SILU>(g, Xq, X, nb, M, st);
     default: return -1;
   }
+}
+
+template <bool SILU>
+int launch_any(int fmt, const Group& g, uint8_t* Xq, const float* X, int M, int64_t K,
+               hipStream_t st) {
+  const int64_t nb = K / kQK;
+  if (nb > 0x7fffffffLL) return -1;
+  return fmt == 12 ? launch_fmt<12, SILU>(g, Xq, X, M, (int)nb, st)
+                   : launch_fmt<14, SILU>(g, Xq, X, M, (int)nb, st);
 }
 
 }  // namespace
 
 int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st) {
-  const int64_t nb = K / kQK;
-  if (nb > 0x7fffffffLL) return -1;
   uint8_t* xq = const_cast<uint8_t*>(Xq);  // read only in the plain form
-  return fmt == 12 ? launch_fmt<12>(g, xq, nullptr, M, (int)nb, st)
-                   : launch_fmt<14>(g, xq, nullptr, M, (int)nb, st);
+  return launch_any<false>(fmt, g, xq, nullptr, M, K, st);
 }
 
 bool gemv_fusable(int64_t M, int64_t K) {
@@ -586,8 +636,17 @@ bool gemv_fusable(int64_t M, int64_t K) {
 int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,
                       hipStream_t st) {
   if (!gemv_fusable(M, K)) return -1;
-  const int nb = (int)(K / kQK);
-  return fmt == 12 ? launch_fmt<12>(g, Xq, X, M, nb, st) : launch_fmt<14>(g, Xq, X, M, nb, st);
+  return launch_any<false>(fmt, g, Xq, X, M, K, st);
+}
+
+int launch_gemv_silu(int fmt, const Group& g, const uint8_t* Xq, const float* X, uint8_t* Xq_out,
+                     int M, int64_t K, hipStream_t st) {
+  if (g.count != 2 || g.N[0] != g.N[1]) return -1;
+  if (X) {
+    if (!gemv_fusable(M, K)) return -1;
+    return launch_any<true>(fmt, g, Xq_out, X, M, K, st);
+  }
+  return launch_any<true>(fmt, g, const_cast<uint8_t*>(Xq), nullptr, M, K, st);
 }
 
 }  // namespace gemmq

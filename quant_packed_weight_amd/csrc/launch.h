@@ -46,6 +46,19 @@ inline bool make_tiles(const Group& g, int64_t rows_per_tile, GroupTiles& t) {
   return true;
 }
 
+// The SiLU-gated pair (gate g.W[0], up g.W[1], equal N, one output g.Y[0]) as one
+// virtual matrix of 2N rows whose row 2n is gate row n and row 2n+1 up row n;
+// the up pointer rides in t.W[1].
+inline bool make_pair_tiles(const Group& g, int64_t rows_per_tile, GroupTiles& t) {
+  Group v{};
+  v.count = 1;
+  v.W[0] = g.W[0];
+  v.Y[0] = g.Y[0];
+  v.N[0] = 2 * g.N[0];
+  if (!make_tiles(v, rows_per_tile, t)) return false;
+  t.W[1] = g.W[1];
+  return true;
+}
 // The matrix that tile `tile` (wave-uniform) belongs to: its weights, output,
 // rows, and the tile's index within it.  Every field is read at a fixed offset
 // and chosen by selects, so the kernel arguments arrive in one round of scalar
@@ -81,6 +94,13 @@ int launch_gemm(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K
 bool gemv_fusable(int64_t M, int64_t K);
 int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,
                       hipStream_t st);
+// SiLU-gated product of a gate and an up matrix (g.W[0], g.W[1], equal N, output
+// g.Y[0] of N columns): y = silu(gate x) * (up x).  X == nullptr reads Xq; else
+// the fused form quantizes X (gemv_fusable) and writes Xq_out.
+int launch_gemv_silu(int fmt, const Group& g, const uint8_t* Xq, const float* X, uint8_t* Xq_out,
+                     int M, int64_t K, hipStream_t st);
+int launch_gemm_silu(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K,
+                     hipStream_t st);
 
 int launch_decode(int fmt, const uint8_t* W, float* Wf, int64_t N, int64_t K, hipStream_t st);
 

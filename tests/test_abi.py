@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_exported(L):
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     assert set(names) == set(gq.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 3
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 4
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -140,6 +140,28 @@ def test_linear_validation(L, args, status):
     wa, ya, na = (P * 1)(W), (P * 1)(Y), (ctypes.c_int64 * 1)(N)
     for path in (0, 1):
         assert L.gemmq_linear_group(fmt, 1, wa, ya, na, X, Xq, M, K, path, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((13, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -2),      # unknown format
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 300, 0), -3),      # K % 256 != 0
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, -1, 1, 256, 0), -1),     # M < 0
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, -1, 256, 0), -1),     # N < 0
+    ((12, None, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -1),        # null gate
+    ((12, FAKE16, None, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -1),        # null up
+    ((12, FAKE16, FAKE16, None, FAKE16, FAKE16, 1, 1, 256, 0), -1),        # null X
+    ((12, FAKE16, FAKE16, FAKE16, None, FAKE16, 1, 1, 256, 0), -1),        # null Xq
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, None, 1, 1, 256, 0), -1),        # null Y
+    ((12, FAKE16, FAKE16 + 8, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -4),  # up alignment
+    ((12, FAKE16, FAKE16, FAKE16 + 4, FAKE16, FAKE16, 1, 1, 256, 0), -4),  # X alignment
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16 + 2, FAKE16, 1, 1, 256, 0), -4),  # Xq alignment
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16 + 1, 1, 1, 256, 0), -4),  # Y alignment
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 9, 1, 256, 1), -3),      # GEMV path, M > 8
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256, 4), -1),      # unknown path
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 0, 5, 256, 0), 0),       # M = 0: empty
+])
+def test_linear_silu_mul_validation(L, args, status):
+    assert L.gemmq_linear_silu_mul(*args, None) == status
 
 
 def test_linear_group_arrays_and_paths(L):

@@ -1,6 +1,6 @@
 """HIP-graph capture of the hot path (quantize + GEMV + GEMM, single and grouped
-launches, and gemmq_linear_group: the fused quantize + GEMV launch and its
-two-launch form), as the benchmark submits it: every replay must equal the eager result
+launches, gemmq_linear_group: the fused quantize + GEMV launch and its
+two-launch form, and gemmq_linear_silu_mul on its fused, GEMV and GEMM routes), as the benchmark submits it: every replay must equal the eager result
 bit for bit, with eager work, synchronisations and changed inputs between the
 replays."""
 import numpy as np
@@ -50,6 +50,17 @@ def test_graph_replays_match_eager():
         Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for N in Ns]
         linears.append((M, K, Ns, Ws, X, Xq, Ys))
 
+    # gemmq_linear_silu_mul: fused (M 1, K 2048), plain GEMV (M 1, K 8192), GEMM (M 40)
+    silus = []
+    for fmt, M, K, N in ((gq.FMT_Q4K, 1, 2048, 300), (gq.FMT_Q6K, 1, 8192, 129),
+                         (gq.FMT_Q4K, 40, 1024, 200)):
+        Wg = torch.from_numpy(synth.make_weights(rng, fmt, N, K)).cuda()
+        Wu = torch.from_numpy(synth.make_weights(rng, fmt, N, K)).cuda()
+        X = torch.from_numpy(synth.make_activations(rng, M, K, True)).cuda()
+        Xq = torch.empty(gq.q8K_bytes(M, K), dtype=torch.uint8, device="cuda")
+        Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        silus.append((fmt, M, N, K, Wg, Wu, X, Xq, Y))
+
     def run(stream):
         st = stream.cuda_stream
         for fmt, M, N, K, W, X, Xq, Y in bufs:
@@ -65,11 +76,16 @@ def test_graph_replays_match_eager():
             assert gq.linear_group_ptr(gq.FMT_Q4K, [w.data_ptr() for w in Ws],
                                        [y.data_ptr() for y in Ys], list(Ns), X.data_ptr(),
                                        Xq.data_ptr(), M, K, gq.PATH_AUTO, st) == 0
+        for fmt, M, N, K, Wg, Wu, X, Xq, Y in silus:
+            assert gq.lib().gemmq_linear_silu_mul(fmt, Wg.data_ptr(), Wu.data_ptr(), X.data_ptr(),
+                                                  Xq.data_ptr(), Y.data_ptr(), M, N, K,
+                                                  gq.PATH_AUTO, st) == 0
 
     def outputs():
         out = [(b[6], b[7]) for b in bufs]
         for M, K, Ns, Ws, X, Xq, Ys in groups + linears:
             out += [(Xq, y) for y in Ys]
+        out += [(b[7], b[8]) for b in silus]
         return out
 
     def eager_ref():
@@ -107,4 +123,6 @@ def test_graph_replays_match_eager():
                 b[5].mul_(-0.5)
             for grp in groups:
                 grp[4].mul_(-0.5)
+            for b in silus:
+                b[6].mul_(-0.5)
             ref = eager_ref()
