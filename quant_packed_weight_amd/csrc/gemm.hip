@@ -148,6 +148,15 @@ __device__ __forceinline__ float pair_partner(float v) {
                                                             0xF, true));
 }
 
+// Lanes 2k (odd = false) and 2k+1 hold the gate and the up output of one column
+// for two rows a, b.  One swap hands the even lane (gate_a, up_a) and the odd
+// lane (gate_b, up_b), so each lane finishes one row of the pair.
+__device__ __forceinline__ void silu_pair(float a, float b, bool odd, float& g, float& u) {
+  const float got = pair_partner(odd ? a : b);  // even lanes get up_a, odd lanes gate_b
+  g = odd ? got : a;
+  u = odd ? b : got;
+}
+
 // ------------------------------------------------- q6_K weight tile
 // thread t: column t/4, part p4 = t%4 -> half hh = p4/2, quarters q = p4%2 (low
 // nibbles of ql bytes 64hh+32q..) and q+2 (their high nibbles).  Plane A gets
@@ -316,13 +325,16 @@ __global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
   if constexpr (SILU) {
     // lanes 2k / 2k+1 hold gate / up of output col / 2 for the same rows
     const int64_t n = col >> 1, Nout = N >> 1;
+    const bool odd = (i & 1) != 0;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float u = pair_partner(y[mt][r]);
-        const int64_t row = m0 + wm * 64 + 32 * mt + 8 * (r >> 2) + 4 * hsel + (r & 3);
-        if ((i & 1) == 0 && n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(y[mt][r], u);
+      for (int r = 0; r < 16; r += 2) {
+        float g, u;
+        silu_pair(y[mt][r], y[mt][r + 1], odd, g, u);
+        const int rr = r + (odd ? 1 : 0);
+        const int64_t row = m0 + wm * 64 + 32 * mt + 8 * (rr >> 2) + 4 * hsel + (rr & 3);
+        if (n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(g, u);
       }
   } else if (col < N) {
 #pragma unroll
@@ -693,13 +705,16 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
   if constexpr (SILU) {
     // lanes 2k / 2k+1 hold gate / up of output o0 + 16 wave + k for the same rows
     const int64_t n = o0 + 16 * wave + (i >> 1);
+    const bool odd = (i & 1) != 0;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float u = pair_partner(y[t][r]);
-        const int64_t row = m0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-        if ((i & 1) == 0 && n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(y[t][r], u);
+      for (int r = 0; r < 16; r += 2) {
+        float g, u;
+        silu_pair(y[t][r], y[t][r + 1], odd, g, u);
+        const int rr = r + (odd ? 1 : 0);
+        const int64_t row = m0 + 32 * t + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        if (n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(g, u);
       }
   } else {
     const int64_t col = n0 + 32 * wave + i;
