@@ -7,7 +7,8 @@
  * library; every format constant below is written out again on purpose.
  *
  * What it computes is the operation the PocketLLM pages call gemm_quant: a linear
- * layer y = W x evaluated directly on ggml K-quant packed weights (q4_K, q6_K) with
+ * layer y = W x evaluated directly on ggml K-quant packed weights (q2_K, q3_K,
+ * q4_K, q5_K, q6_K -- the K-quant rung of the pages' width ladder) with
  * the activations quantized to int8 blocks first (PocketLLM README, "What it runs":
  * the K-quant rung is decoded inside the kernel and never widened; molayo article
  * "PocketLLM: 단일 가속기에서 대규모 언어 모델 실행", status row "src/ -- C++ engine":
@@ -25,6 +26,16 @@
  *         w = d*sc_j*q - dmin*m_j.
  *   q6_K, 210 B per 256 weights: 128 B low nibbles | 64 B 2-bit highs | 16 int8
  *         sub-scales | f16 d.  Sub-block j (16 weights) decodes as w = d*sc_j*(q-32).
+ *   q2_K, 84 B per 256 weights: 16 B sub-block bytes (scale in the low nibble,
+ *         min in the high nibble) | 64 B of 2-bit quants | f16 d | f16 dmin.
+ *         Sub-block j (16 weights) decodes as w = d*sc_j*q - dmin*m_j, q in 0..3.
+ *   q3_K, 110 B per 256 weights: 32 B high-bit mask | 64 B of 2-bit low parts |
+ *         12 B packed 6-bit scales | f16 d.  Sub-block j (16 weights) decodes as
+ *         w = d*(sc_j - 32)*q, q in -4..3 (low part, minus 4 when the high bit is
+ *         clear).
+ *   q5_K, 176 B per 256 weights: f16 d | f16 dmin | 12 B scales and mins packed
+ *         as in q4_K | 32 B high bits | 128 B of 4-bit low parts.  Sub-block j
+ *         (32 weights) decodes as w = d*sc_j*q - dmin*m_j, q in 0..31.
  *   q8_K, 292 B per 256 activations: f32 d | 256 int8 | 16 int16 group sums.
  *
  * Parity status: every function here is pinned by the CPU tests (closed forms,
@@ -37,7 +48,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#define OQ2K_BYTES 84
+#define OQ3K_BYTES 110
 #define OQ4K_BYTES 144
+#define OQ5K_BYTES 176
 #define OQ6K_BYTES 210
 #define OQ8K_BYTES 292
 #define OQK 256
@@ -115,6 +129,106 @@ static int q6k_quant(const uint8_t *ql, const uint8_t *qh, int i)
     return low | (high << 4);
 }
 
+/* q2_K: 2-bit quant of weight i (0..255).  Each 128-weight half h owns 32 bytes;
+ * its 32-weight quarter c takes bits 2c..2c+1 of byte l = i % 32. */
+static int q2k_quant(const uint8_t *qs, int i)
+{
+    int h = i / 128, c = (i % 128) / 32, l = i % 32;
+    return (qs[32 * h + l] >> (2 * c)) & 3;
+}
+
+/* q3_K: quant of weight i in -4..3.  The low two bits are laid out as q2_K's;
+ * the third bit is bit 4h+c of mask byte l (h, c, l as for q2_K), and a clear
+ * bit subtracts 4. */
+static int q3k_quant(const uint8_t *hmask, const uint8_t *qs, int i)
+{
+    int h = i / 128, c = (i % 128) / 32, l = i % 32;
+    int low = (qs[32 * h + l] >> (2 * c)) & 3;
+    int high = (hmask[l] >> (4 * h + c)) & 1;
+    return high ? low : low - 4;
+}
+
+/* q3_K: 6-bit scale of sub-block j (0..15), before the -32 offset.  For
+ * j = 4g + k the low four bits are a nibble of byte k (g = 0: low, g = 2: high)
+ * or of byte 4 + k (g = 1: low, g = 3: high); the top two bits are bits
+ * 2g..2g+1 of byte 8 + k. */
+static int q3k_scale(const uint8_t *s, int j)
+{
+    int g = j / 4, k = j % 4;
+    int low = (s[4 * (g & 1) + k] >> (4 * (g >> 1))) & 15;
+    int high = (s[8 + k] >> (2 * g)) & 3;
+    return low | (high << 4);
+}
+
+/* q5_K: 5-bit quant of weight i (0..255).  The low four bits are laid out as
+ * q4_K's quants; the fifth is bit 2g + (r >= 32) of byte l of the high-bit
+ * array, for 64-weight group g, r = i % 64 and l = r % 32. */
+static int q5k_quant(const uint8_t *qh, const uint8_t *qs, int i)
+{
+    int g = i / 64, r = i % 64, l = r % 32;
+    int high = (qh[l] >> (2 * g + (r >= 32))) & 1;
+    return q4k_quant(qs, i) | (high << 4);
+}
+
+/* Any of the five formats as integers: quants q[256] (offsets applied), the
+ * L-weight sub-blocks' scales sc[] and mins mn[] (0 where the format has none),
+ * d and dmin (0 where none).  Weight i of sub-block j is d*sc_j*q_i - dmin*mn_j.
+ * Returns L (16 or 32), or 0 for an unknown format. */
+static int unpack_block(int fmt, const uint8_t *blk, int *q, int *sc, int *mn, double *d,
+                        double *dmin)
+{
+    switch (fmt) {
+    case 10: /* q2_K */
+        *d = oracle_f16_to_f64(rd_u16(blk + 80));
+        *dmin = oracle_f16_to_f64(rd_u16(blk + 82));
+        for (int j = 0; j < 16; ++j) {
+            sc[j] = blk[j] & 15;
+            mn[j] = blk[j] >> 4;
+        }
+        for (int i = 0; i < OQK; ++i)
+            q[i] = q2k_quant(blk + 16, i);
+        return 16;
+    case 11: /* q3_K */
+        *d = oracle_f16_to_f64(rd_u16(blk + 108));
+        *dmin = 0.0;
+        for (int j = 0; j < 16; ++j) {
+            sc[j] = q3k_scale(blk + 96, j) - 32;
+            mn[j] = 0;
+        }
+        for (int i = 0; i < OQK; ++i)
+            q[i] = q3k_quant(blk, blk + 32, i);
+        return 16;
+    case 12: /* q4_K */
+        *d = oracle_f16_to_f64(rd_u16(blk));
+        *dmin = oracle_f16_to_f64(rd_u16(blk + 2));
+        for (int j = 0; j < 8; ++j)
+            q4k_scale_min(blk + 4, j, &sc[j], &mn[j]);
+        for (int i = 0; i < OQK; ++i)
+            q[i] = q4k_quant(blk + 16, i);
+        return 32;
+    case 13: /* q5_K */
+        *d = oracle_f16_to_f64(rd_u16(blk));
+        *dmin = oracle_f16_to_f64(rd_u16(blk + 2));
+        for (int j = 0; j < 8; ++j)
+            q4k_scale_min(blk + 4, j, &sc[j], &mn[j]);
+        for (int i = 0; i < OQK; ++i)
+            q[i] = q5k_quant(blk + 16, blk + 48, i);
+        return 32;
+    case 14: /* q6_K */
+        *d = oracle_f16_to_f64(rd_u16(blk + 208));
+        *dmin = 0.0;
+        for (int j = 0; j < 16; ++j) {
+            sc[j] = ((const int8_t *)(blk + 192))[j];
+            mn[j] = 0;
+        }
+        for (int i = 0; i < OQK; ++i)
+            q[i] = q6k_quant(blk, blk + 128, i) - 32;
+        return 16;
+    default:
+        return 0;
+    }
+}
+
 /* ---------------------------------------------------------------- decode */
 
 /* q4_K -> f32.  The exact value d*sc*q - dmin*m is formed in long double (each
@@ -149,6 +263,28 @@ void oracle_decode_q6K(const uint8_t *W, int64_t nblocks, float *out)
             out[b * OQK + i] = (float)v;
         }
     }
+}
+
+/* q2_K, q3_K, q5_K -> f32 (fmt 10, 11, 13; also accepts 12 and 14).  The exact
+ * value d*sc*q - dmin*m is formed in long double (q5_K: at most 22 + 17
+ * significant bits, exponents inside the f16 range, so the difference fits a
+ * 64-bit significand; q2_K and q3_K fewer), then rounded once to f32.
+ * Returns 0, or -1 for an unknown format. */
+int oracle_decode(int fmt, const uint8_t *W, int64_t nblocks, float *out)
+{
+    static const int bytes[15] = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 84, 110, 144, 176, 210};
+    if (fmt < 10 || fmt > 14)
+        return -1;
+    int q[OQK], sc[16], mn[16];
+    double d, dmin;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int L = unpack_block(fmt, W + b * bytes[fmt], q, sc, mn, &d, &dmin);
+        for (int i = 0; i < OQK; ++i) {
+            long double v = (long double)d * sc[i / L] * q[i] - (long double)dmin * mn[i / L];
+            out[b * OQK + i] = (float)v;
+        }
+    }
+    return 0;
 }
 
 /* ---------------------------------------------------------------- quantize */
@@ -202,19 +338,69 @@ int oracle_quantize_q8K(const float *X, int64_t M, int64_t K, uint8_t *Xq)
 
 /* ---------------------------------------------------------------- matmul */
 
+#define OFMT_Q2K 10
+#define OFMT_Q3K 11
 #define OFMT_Q4K 12
+#define OFMT_Q5K 13
 #define OFMT_Q6K 14
 
 static int fmt_block_bytes(int fmt)
 {
-    return fmt == OFMT_Q4K ? OQ4K_BYTES : fmt == OFMT_Q6K ? OQ6K_BYTES : 0;
+    switch (fmt) {
+    case OFMT_Q2K: return OQ2K_BYTES;
+    case OFMT_Q3K: return OQ3K_BYTES;
+    case OFMT_Q4K: return OQ4K_BYTES;
+    case OFMT_Q5K: return OQ5K_BYTES;
+    case OFMT_Q6K: return OQ6K_BYTES;
+    default: return 0;
+    }
+}
+
+/* Route A for q2_K, q3_K and q5_K: per super-block, I_sc = sum_j sc_j *
+ * sum_{i in j} q_i * qx_i and I_min = sum_j m_j * sum_{i in j} qx_i as exact
+ * int64, then d_x * (d * I_sc - dmin * I_min) in double. */
+static int gemm_int_other(int fmt, const uint8_t *W, const uint8_t *Xq, int64_t M, int64_t N,
+                          int64_t K, const int64_t *rows, int64_t nrows, double *Y)
+{
+    int wb = fmt_block_bytes(fmt);
+    int64_t nb = K / OQK;
+    int q[OQK], sc[16], mn[16];
+    double d, dmin;
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int64_t n = 0; n < N; ++n)
+            Y[r * N + n] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            int L = unpack_block(fmt, W + (n * nb + b) * wb, q, sc, mn, &d, &dmin);
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t m = rows ? rows[r] : r;
+                const uint8_t *xb = Xq + (m * nb + b) * OQ8K_BYTES;
+                double dx = rd_f32(xb);
+                const int8_t *qx = (const int8_t *)(xb + 4);
+                int64_t isc = 0, imn = 0;
+                for (int j = 0; j < OQK / L; ++j) {
+                    int64_t dot = 0, sx = 0;
+                    for (int i = L * j; i < L * j + L; ++i) {
+                        dot += (int64_t)q[i] * qx[i];
+                        sx += qx[i];
+                    }
+                    isc += sc[j] * dot;
+                    imn += mn[j] * sx;
+                }
+                Y[r * N + n] += dx * (d * (double)isc - dmin * (double)imn);
+            }
+        }
+    }
+    return 0;
 }
 
 /* Route A (integer decomposition).  For every listed activation row m and every
  * weight row n: y = sum over super-blocks b of d_x * (d * I_sc - dmin * I_min) for
  * q4_K, with I_sc = sum_j sc_j * sum_{i in j} q_i * qx_i and
  * I_min = sum_j m_j * sum_{i in j} qx_i, both exact int64; for q6_K
- * y = sum_b d_x * d * sum_j sc_j * sum_{i in j} (q_i - 32) * qx_i.  The block
+ * y = sum_b d_x * d * sum_j sc_j * sum_{i in j} (q_i - 32) * qx_i; for q2_K,
+ * q3_K and q5_K the same sums over their own sub-blocks (16, 16 and 32 weights;
+ * q3_K has no min term) from the integers of unpack_block.  The block
  * terms are combined in double.  This is the exact real sum over k of
  * (unrounded weight) * (d_x * qx), up to double rounding.
  * rows == NULL means all M rows; Y is [nrows, N].  Returns 0 or -1 on bad args. */
@@ -227,6 +413,8 @@ int oracle_gemm_int(int fmt, const uint8_t *W, const uint8_t *Xq, int64_t M, int
     if (!rows)
         nrows = M;
     int64_t nb = K / OQK;
+    if (fmt != OFMT_Q4K && fmt != OFMT_Q6K)
+        return gemm_int_other(fmt, W, Xq, M, N, K, rows, nrows, Y);
     int *q = (int *)malloc(sizeof(int) * (size_t)K); /* weight quants of one row */
     int *sc = (int *)malloc(sizeof(int) * (size_t)(K / 16));
     int *mn = (int *)malloc(sizeof(int) * (size_t)(K / 32));
@@ -319,8 +507,10 @@ int oracle_gemm_dequant(int fmt, const uint8_t *W, const uint8_t *Xq, int64_t M,
     for (int64_t n = 0; n < N; ++n) {
         if (fmt == OFMT_Q4K)
             oracle_decode_q4K(W + n * nb * wb, nb, w);
-        else
+        else if (fmt == OFMT_Q6K)
             oracle_decode_q6K(W + n * nb * wb, nb, w);
+        else
+            oracle_decode(fmt, W + n * nb * wb, nb, w);
         for (int64_t r = 0; r < nrows; ++r) {
             double y = 0.0, s = 0.0;
             for (int64_t k = 0; k < K; ++k) {
@@ -351,4 +541,4 @@ void oracle_silu_mul(const double *g, const double *u, int64_t n, double *y)
 }
 
 /* Version of this oracle's interface, for the test loader. */
-int oracle_version(void) { return 2; }
+int oracle_version(void) { return 3; }

@@ -16,9 +16,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gemmq_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
+FMT_Q2K = 10
+FMT_Q3K = 11
 FMT_Q4K = 12
+FMT_Q5K = 13
 FMT_Q6K = 14
-BLOCK_BYTES = {FMT_Q4K: 144, FMT_Q6K: 210}
+BLOCK_BYTES = {FMT_Q2K: 84, FMT_Q3K: 110, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210}
 Q8K_BYTES = 292
 
 _lib = None
@@ -51,6 +54,8 @@ def load():
             lib.oracle_decode_q4K.restype = None
             lib.oracle_decode_q6K.argtypes = [P, I64, P]
             lib.oracle_decode_q6K.restype = None
+            lib.oracle_decode.argtypes = [ctypes.c_int, P, I64, P]
+            lib.oracle_decode.restype = ctypes.c_int
             lib.oracle_quantize_q8K.argtypes = [P, I64, I64, P]
             lib.oracle_quantize_q8K.restype = ctypes.c_int
             lib.oracle_gemm_int.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, I64, P]
@@ -77,8 +82,12 @@ def decode(fmt: int, W: np.ndarray, N: int, K: int) -> np.ndarray:
     nblk = N * (K // 256)
     assert W.size == nblk * BLOCK_BYTES[fmt]
     out = np.empty((N, K), dtype=np.float32)
-    fn = load().oracle_decode_q4K if fmt == FMT_Q4K else load().oracle_decode_q6K
-    fn(_ptr(W), nblk, _ptr(out))
+    if fmt == FMT_Q4K:
+        load().oracle_decode_q4K(_ptr(W), nblk, _ptr(out))
+    elif fmt == FMT_Q6K:
+        load().oracle_decode_q6K(_ptr(W), nblk, _ptr(out))
+    elif load().oracle_decode(fmt, _ptr(W), nblk, _ptr(out)) != 0:
+        raise ValueError("oracle_decode: unknown format %d" % fmt)
     return out
 
 

@@ -11,6 +11,12 @@ available here; these stand in for them):
         min uniform on 0..63 and every 4-bit quant uniform on 0..15.
   q6_K: low-nibble and high-bit bytes uniform random (quants uniform on 0..63);
         sub-scales uniform on -64..63; d = f16(|N(0,1)| * 1e-3).
+  q2_K, q5_K: as q4_K (uniform scale/min and quant bytes, d and dmin =
+        f16(|N(0,1)| * 2e-3)); q2_K's 4-bit scales and mins and 2-bit quants, q5_K's
+        6-bit scales and mins and 5-bit quants are then uniform.
+  q3_K: uniform mask, quant and scale bytes (6-bit scales uniform on 0..63,
+        i.e. -32..31 after the offset; quants uniform on -4..3);
+        d = f16(|N(0,1)| * 2e-3).
   activations: f32 N(0,1); optionally 4 distinct outlier columns (the same in
         every row) multiplied by 20.
 Draw order per workload: every matrix's weight bytes in list order, then the
@@ -24,10 +30,16 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-FMT_Q4K = 12  # GGUF type ids
+FMT_Q2K = 10  # GGUF type ids
+FMT_Q3K = 11
+FMT_Q4K = 12
+FMT_Q5K = 13
 FMT_Q6K = 14
-BLOCK_BYTES = {FMT_Q4K: 144, FMT_Q6K: 210}
-FMT_NAME = {FMT_Q4K: "q4_K", FMT_Q6K: "q6_K"}
+BLOCK_BYTES = {FMT_Q2K: 84, FMT_Q3K: 110, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210}
+FMT_NAME = {FMT_Q2K: "q2_K", FMT_Q3K: "q3_K", FMT_Q4K: "q4_K", FMT_Q5K: "q5_K",
+            FMT_Q6K: "q6_K"}
+# byte offsets of the f16 factors d and dmin in each block
+_D_OFFS = {FMT_Q2K: (80, 82), FMT_Q3K: (108,), FMT_Q4K: (0, 2), FMT_Q5K: (0, 2)}
 Q8K_BYTES = 292
 QK = 256
 
@@ -109,12 +121,11 @@ def make_weights(rng: np.random.Generator, fmt: int, N: int, K: int,
     nblk = N * (K // QK)
     bb = BLOCK_BYTES[fmt]
     raw = rng.integers(0, 256, size=(nblk, bb), dtype=np.uint8)
-    if fmt == FMT_Q4K:
+    if fmt in _D_OFFS:
         s = 2e-3 if d_scale is None else d_scale
-        d = (np.abs(rng.standard_normal(nblk)) * s).astype(np.float16)
-        dmin = (np.abs(rng.standard_normal(nblk)) * s).astype(np.float16)
-        raw[:, 0:2] = d.view(np.uint8).reshape(nblk, 2)
-        raw[:, 2:4] = dmin.view(np.uint8).reshape(nblk, 2)
+        for o in _D_OFFS[fmt]:
+            f = (np.abs(rng.standard_normal(nblk)) * s).astype(np.float16)
+            raw[:, o:o + 2] = f.view(np.uint8).reshape(nblk, 2)
     elif fmt == FMT_Q6K:
         s = 1e-3 if d_scale is None else d_scale
         sc = rng.integers(-64, 64, size=(nblk, 16)).astype(np.int8)

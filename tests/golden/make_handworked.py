@@ -1,4 +1,4 @@
-"""Writes q4K_handworked.txt and q6K_handworked.txt.
+"""Writes q2K, q3K, q4K, q5K and q6K_handworked.txt.
 
 The pages print no worked decode, so these fixtures are worked by hand from the
 ggml K-quant layout (the reading the oracle follows).  Everything below is the
@@ -62,6 +62,83 @@ def q6_weights():
     return out
 
 
+# ---------------------------------------------------------------- q2_K
+# d = 0.5 (bytes 00 38), dmin = 0.25 (bytes 00 34), stored after the quants.
+# Sub-block byte j holds scale j in its low nibble and min j in its high nibble:
+#   0x30 -> sc 0, m 3    0x81 -> sc 1, m 8    0xD2 -> sc 2, m 13   0x23 -> sc 3, m 2
+#   0x74 -> sc 4, m 7    0xC5 -> sc 5, m 12   0x16 -> sc 6, m 1    0x67 -> sc 7, m 6
+#   0xB8 -> sc 8, m 11   0x09 -> sc 9, m 0    0x5A -> sc 10, m 5   0xAB -> sc 11, m 10
+#   0xFC -> sc 12, m 15  0x4D -> sc 13, m 4   0x9E -> sc 14, m 9   0xEF -> sc 15, m 14
+Q2_SCALE_BYTES = [0x30, 0x81, 0xD2, 0x23, 0x74, 0xC5, 0x16, 0x67,
+                  0xB8, 0x09, 0x5A, 0xAB, 0xFC, 0x4D, 0x9E, 0xEF]
+Q2_SC = list(range(16))
+Q2_M = [3, 8, 13, 2, 7, 12, 1, 6, 11, 0, 5, 10, 15, 4, 9, 14]
+# Quant byte 32h + l repeats E4 39 4E 93 by l % 4.  Bit pairs, low to high:
+#   0xE4 = 11 10 01 00 -> quarters 0..3 get 0, 1, 2, 3
+#   0x39 = 00 11 10 01 -> 1, 2, 3, 0
+#   0x4E = 01 00 11 10 -> 2, 3, 0, 1
+#   0x93 = 10 01 00 11 -> 3, 0, 1, 2
+# so weight 128h + 32c + l has q = (l % 4 + c) % 4.
+Q2_QS = [[0xE4, 0x39, 0x4E, 0x93][l % 4] for h in range(2) for l in range(32)]
+
+
+def q2_weights():
+    out = []
+    for h in range(2):
+        for c in range(4):
+            for l in range(32):
+                j = (128 * h + 32 * c + l) // 16
+                out.append(0.5 * Q2_SC[j] * ((l % 4 + c) % 4) - 0.25 * Q2_M[j])
+    return out
+
+
+# ---------------------------------------------------------------- q3_K
+# Mask byte l is l itself, so weight 128h + 32c + l has its third bit set when
+# bit 4h + c of l is set (never for h = 1, c >= 1, since l < 32).
+# Low parts: the same bytes as the q2_K quants above, low = (l % 4 + c) % 4;
+# q = low where the bit is set, low - 4 where it is clear.
+# Scales (stored values u, sc = u - 32), chosen:
+#   u = 0 63 32 31 1 62 17 48 5 40 33 20 60 3 44 27
+#   low nibbles: 0 F 0 F 1 E 1 0 5 8 1 4 C 3 C B; top two bits: 0 3 2 1 0 3 1 3 0 2 2 1 3 0 2 1
+#   bytes 0..3 = low nibbles of u0..u3 | low nibbles of u8..u11 << 4: 50 8F 10 4F
+#   bytes 4..7 = low nibbles of u4..u7 | low nibbles of u12..u15 << 4: C1 3E C1 B0
+#   byte 8 + k = top(u_k) | top(u_4+k) << 2 | top(u_8+k) << 4 | top(u_12+k) << 6:
+#     k = 0: 0 | 0 | 0 | 3<<6 = C0     k = 1: 3 | 3<<2 | 2<<4 | 0 = 2F
+#     k = 2: 2 | 1<<2 | 2<<4 | 2<<6 = A6   k = 3: 1 | 3<<2 | 1<<4 | 1<<6 = 5D
+# d = 0.5 (bytes 00 38) at the end.
+Q3_SCALE_BYTES = [0x50, 0x8F, 0x10, 0x4F, 0xC1, 0x3E, 0xC1, 0xB0, 0xC0, 0x2F, 0xA6, 0x5D]
+Q3_SC = [u - 32 for u in [0, 63, 32, 31, 1, 62, 17, 48, 5, 40, 33, 20, 60, 3, 44, 27]]
+
+
+def q3_weights():
+    out = []
+    for h in range(2):
+        for c in range(4):
+            for l in range(32):
+                low = (l % 4 + c) % 4
+                q = low if (l >> (4 * h + c)) & 1 else low - 4
+                out.append(0.5 * Q3_SC[(128 * h + 32 * c + l) // 16] * q)
+    return out
+
+
+# ---------------------------------------------------------------- q5_K
+# d = 0.5, dmin = 0.25 and the 12 scale bytes of the q4_K block above (same
+# packing, same hand decode Q4_SC / Q4_M).  High-bit byte l is l itself, so
+# weight 64g + 32t + l gets +16 when bit 2g + t of l is set.  Low nibbles: the
+# q4_K block's quant bytes, low = l % 16 (t = 0) or 15 - l % 16 (t = 1).
+
+
+def q5_weights():
+    out = []
+    for g in range(4):
+        for t in range(2):
+            for l in range(32):
+                low = l % 16 if t == 0 else 15 - l % 16
+                q = low + (16 if (l >> (2 * g + t)) & 1 else 0)
+                out.append(0.5 * Q4_SC[2 * g + t] * q - 0.25 * Q4_M[2 * g + t])
+    return out
+
+
 def write(name, raw, weights, header):
     with open(os.path.join(HERE, name), "w") as f:
         f.write(header)
@@ -80,6 +157,21 @@ def main():
     write("q6K_handworked.txt", q6, q6_weights(),
           "# One q6_K block decoded by hand (see make_handworked.py for the derivation).\n"
           "# d = 0.5, sc = %s\n" % (Q6_SC,))
+    q2 = Q2_SCALE_BYTES + Q2_QS + [0x00, 0x38, 0x00, 0x34]
+    assert len(q2) == 84
+    write("q2K_handworked.txt", q2, q2_weights(),
+          "# One q2_K block decoded by hand (see make_handworked.py for the derivation).\n"
+          "# d = 0.5, dmin = 0.25, sc = %s, m = %s\n" % (Q2_SC, Q2_M))
+    q3 = list(range(32)) + Q2_QS + Q3_SCALE_BYTES + [0x00, 0x38]
+    assert len(q3) == 110
+    write("q3K_handworked.txt", q3, q3_weights(),
+          "# One q3_K block decoded by hand (see make_handworked.py for the derivation).\n"
+          "# d = 0.5, sc = %s\n" % (Q3_SC,))
+    q5 = [0x00, 0x38, 0x00, 0x34] + Q4_SCALE_BYTES + list(range(32)) + Q4_QS
+    assert len(q5) == 176
+    write("q5K_handworked.txt", q5, q5_weights(),
+          "# One q5_K block decoded by hand (see make_handworked.py for the derivation).\n"
+          "# d = 0.5, dmin = 0.25, sc = %s, m = %s\n" % (Q4_SC, Q4_M))
 
 
 if __name__ == "__main__":

@@ -12,35 +12,64 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from packer import pack_q4K, pack_q6K, q8K_fields
+from packer import pack_q2K, pack_q3K, pack_q4K, pack_q5K, pack_q6K, q8K_fields
 from quant_packed_weight_amd import synth
 
-Q4, Q6 = 12, 14
+Q2, Q3, Q4, Q5, Q6 = 10, 11, 12, 13, 14
+FMTS = [Q2, Q3, Q4, Q5, Q6]
+BYTES = {Q2: 84, Q3: 110, Q4: 144, Q5: 176, Q6: 210}
+D_OFFS = {Q2: (80, 82), Q3: (108,), Q4: (0, 2), Q5: (0, 2), Q6: (208,)}
+HAS_MIN = {Q2, Q4, Q5}  # formats whose decode is a difference of two products
 
 
-def _fields_q4K(rng, n):
+def _random_blocks(rng, fmt, n):
+    """n blocks from random logical fields: (raw bytes [n, bytes], weight(b, i))
+    with weight the exact unrounded value as a Fraction."""
     d = (np.abs(rng.standard_normal(n)) * 2e-3).astype(np.float16)
     dmin = (np.abs(rng.standard_normal(n)) * 2e-3).astype(np.float16)
-    return d, dmin, rng.integers(0, 64, (n, 8)), rng.integers(0, 64, (n, 8)), rng.integers(0, 16, (n, 256))
+    F = lambda v: Fraction(float(v))  # noqa: E731
+    if fmt in (Q4, Q5):
+        sc, mn = rng.integers(0, 64, (n, 8)), rng.integers(0, 64, (n, 8))
+        q = rng.integers(0, 16 if fmt == Q4 else 32, (n, 256))
+        raw = (pack_q4K if fmt == Q4 else pack_q5K)(d, dmin, sc, mn, q)
+        return raw, lambda b, i: F(d[b]) * int(sc[b, i // 32]) * int(q[b, i]) - F(dmin[b]) * int(mn[b, i // 32])
+    if fmt == Q2:
+        sc, mn = rng.integers(0, 16, (n, 16)), rng.integers(0, 16, (n, 16))
+        q = rng.integers(0, 4, (n, 256))
+        raw = pack_q2K(d, dmin, sc, mn, q)
+        return raw, lambda b, i: F(d[b]) * int(sc[b, i // 16]) * int(q[b, i]) - F(dmin[b]) * int(mn[b, i // 16])
+    if fmt == Q3:
+        sc, q = rng.integers(-32, 32, (n, 16)), rng.integers(-4, 4, (n, 256))
+        return pack_q3K(d, sc, q), lambda b, i: F(d[b]) * int(sc[b, i // 16]) * int(q[b, i])
+    sc, q = rng.integers(-128, 128, (n, 16)), rng.integers(0, 64, (n, 256))
+    return pack_q6K(d, sc, q), lambda b, i: F(d[b]) * int(sc[b, i // 16]) * (int(q[b, i]) - 32)
 
 
-def _fields_q6K(rng, n):
-    d = (np.abs(rng.standard_normal(n)) * 1e-3).astype(np.float16)
-    return d, rng.integers(-128, 128, (n, 16)), rng.integers(0, 64, (n, 256))
+def _unit_blocks(rng, fmt, n):
+    """n blocks with d = 2^-10, unit scales and zero mins: (raw, integer weights [n, 256])."""
+    d, z = np.full(n, 2.0 ** -10), np.zeros(n)
+    if fmt in (Q4, Q5):
+        q = rng.integers(0, 16 if fmt == Q4 else 32, (n, 256))
+        one, zero = np.ones((n, 8), int), np.zeros((n, 8), int)
+        return (pack_q4K if fmt == Q4 else pack_q5K)(d, z, one, zero, q), q
+    if fmt == Q2:
+        q = rng.integers(0, 4, (n, 256))
+        return pack_q2K(d, z, np.ones((n, 16), int), np.zeros((n, 16), int), q), q
+    if fmt == Q3:
+        q = rng.integers(-4, 4, (n, 256))
+        return pack_q3K(d, np.ones((n, 16), int), q), q
+    q = rng.integers(0, 64, (n, 256))
+    return pack_q6K(d, np.ones((n, 16), int), q), q - 32
 
 
-@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_exact_rational_tiny(orc, fmt):
     # y = sum_k w_k * xhat_k with the unrounded w_k built from the packer's fields
     rng = np.random.default_rng(21 + fmt)
     N, K, M = 3, 512, 2
     nb = K // 256
-    if fmt == Q4:
-        d, dmin, sc, mn, q = _fields_q4K(rng, N * nb)
-        W = pack_q4K(d, dmin, sc, mn, q).reshape(N, -1)
-    else:
-        d, sc, q = _fields_q6K(rng, N * nb)
-        W = pack_q6K(d, sc, q).reshape(N, -1)
+    raw, weight = _random_blocks(rng, fmt, N * nb)
+    W = raw.reshape(N, -1)
     x = rng.standard_normal((M, K)).astype(np.float32)
     xq = orc.quantize_q8K(x)
     dx, qx, _ = q8K_fields(xq)
@@ -53,36 +82,24 @@ def test_exact_rational_tiny(orc, fmt):
                 blk = n * nb + b
                 fdx = Fraction(float(dx[m * nb + b]))
                 for i in range(256):
-                    if fmt == Q4:
-                        j = i // 32
-                        w = (Fraction(float(d[blk])) * int(sc[blk, j]) * int(q[blk, i])
-                             - Fraction(float(dmin[blk])) * int(mn[blk, j]))
-                    else:
-                        w = Fraction(float(d[blk])) * int(sc[blk, i // 16]) * (int(q[blk, i]) - 32)
-                    exact += w * fdx * int(qx[m * nb + b, i])
+                    exact += weight(blk, i) * fdx * int(qx[m * nb + b, i])
             s = S[m, n]
             assert abs(Fraction(float(ya[m, n])) - exact) <= Fraction(1e-15) * Fraction(s)
-            # the decode-then-dot route rounds each q4_K weight once to f32
-            bound = (2.0 ** -24 if fmt == Q4 else 0.0) * s + 1e-15 * s
+            # the decode-then-dot route rounds each weight with a min term once to f32
+            bound = (2.0 ** -24 if fmt in HAS_MIN else 0.0) * s + 1e-15 * s
             assert abs(Fraction(float(yb[m, n])) - exact) <= Fraction(bound)
 
 
-@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_textbook_integer_gemm(orc, fmt):
     # scales 1, mins 0, d_w = 2^-10 and activations with d_x = 2^-7 exactly:
     # y = 2^-17 * (integer matmul), with no tolerance at all.
     rng = np.random.default_rng(31 + fmt)
     N, K, M = 17, 768, 5
     nb = K // 256
-    if fmt == Q4:
-        qw = rng.integers(0, 16, (N * nb, 256))
-        W = pack_q4K(np.full(N * nb, 2.0 ** -10), np.zeros(N * nb), np.ones((N * nb, 8), int),
-                     np.zeros((N * nb, 8), int), qw).reshape(N, -1)
-        wint = qw.reshape(N, K)
-    else:
-        qw = rng.integers(0, 64, (N * nb, 256))
-        W = pack_q6K(np.full(N * nb, 2.0 ** -10), np.ones((N * nb, 16), int), qw).reshape(N, -1)
-        wint = qw.reshape(N, K) - 32
+    raw, qint = _unit_blocks(rng, fmt, N * nb)
+    W = raw.reshape(N, -1)
+    wint = qint.reshape(N, K)
     k = rng.integers(-127, 128, (M, K))
     k[:, ::256] = 127  # every block has amax = 127 * 2^-7, so d_x = 2^-7 and q_x = k
     x = (k * 2.0 ** -7).astype(np.float32)
@@ -95,7 +112,7 @@ def test_textbook_integer_gemm(orc, fmt):
     assert np.array_equal(yb, want)
 
 
-@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_routes_agree(orc, fmt):
     rng = np.random.default_rng(41 + fmt)
     N, K, M = 64, 2048, 9
@@ -103,12 +120,12 @@ def test_routes_agree(orc, fmt):
     xq = orc.quantize_q8K(synth.make_activations(rng, M, K, True))
     ya = orc.gemm_int(fmt, W, xq, M, N, K)
     yb, S = orc.gemm_dequant(fmt, W, xq, M, N, K)
-    bound = (2.0 ** -23 if fmt == Q4 else 1e-13) * S
+    bound = (2.0 ** -23 if fmt in HAS_MIN else 1e-13) * S
     assert np.all(np.abs(ya - yb) <= bound)
     assert np.all(S > 0)
 
 
-@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_row_subset_bit_identical(orc, fmt):
     rng = np.random.default_rng(51 + fmt)
     N, K, M = 40, 512, 11
@@ -125,7 +142,7 @@ def test_row_subset_bit_identical(orc, fmt):
         assert np.array_equal(one[0], full[m])
 
 
-@pytest.mark.parametrize("fmt", [Q4, Q6])
+@pytest.mark.parametrize("fmt", FMTS)
 def test_power_of_two_linearity(orc, fmt):
     rng = np.random.default_rng(61 + fmt)
     N, K, M = 16, 512, 3
@@ -134,9 +151,8 @@ def test_power_of_two_linearity(orc, fmt):
     xq = orc.quantize_q8K(x)
     y = orc.gemm_int(fmt, W, xq, M, N, K)
     # doubling every f16 scale field doubles y exactly
-    W2 = W.copy().reshape(-1, 144 if fmt == Q4 else 210)
-    offs = (0, 2) if fmt == Q4 else (208,)
-    for o in offs:
+    W2 = W.copy().reshape(-1, BYTES[fmt])
+    for o in D_OFFS[fmt]:
         f = W2[:, o:o + 2].copy().view(np.float16) * np.float16(2)
         W2[:, o:o + 2] = f.view(np.uint8)
     y2 = orc.gemm_int(fmt, W2.reshape(N, -1), xq, M, N, K)
