@@ -3,7 +3,8 @@
  * MI355X (gfx950).
  *
  * The operation is gemm_quant from the PocketLLM pages: a Qwen3 linear layer
- * y = W x evaluated directly on ggml K-quant packed weights, with the weights
+ * y = W x evaluated directly on ggml K-quant packed weights (the K-quant rung
+ * of the pages' width ladder, q2_K through q6_K), with the weights
  * decoded inside the kernel and never widened in device memory (PocketLLM
  * README, "What it runs" and "Roadmap": the K-quant rung is decoded in-kernel,
  * packed, never widened), after the activations have been quantized to int8
@@ -32,8 +33,16 @@
  *
  * Block formats (little-endian; the pages name the ggml formats but print no
  * layout, so these are the public ggml layouts):
+ *  q2_K   84 B / 256 weights: 16 B of 4-bit scale (low nibble) and min (high
+ *        nibble) per sub-block | 64 B of 2-bit quants | f16 d | f16 dmin;
+ *        sub-block j (16 weights): w = d*sc_j*q - dmin*m_j, q in 0..3.
+ *  q3_K  110 B / 256 weights: 32 B high-bit mask | 64 B of 2-bit low parts |
+ *        12 B of 6-bit scales | f16 d; sub-block j (16 weights):
+ *        w = d*(sc_j - 32)*q, q = low part, minus 4 where the mask bit is clear.
  *  q4_K  144 B / 256 weights: f16 d | f16 dmin | 12 B of 6-bit scales and mins |
  *        128 B of 4-bit quants; sub-block j (32 weights): w = d*sc_j*q - dmin*m_j.
+ *  q5_K  176 B / 256 weights: q4_K's 16-byte header | 32 B of high bits | 128 B
+ *        of 4-bit low parts laid out as q4_K's quants; w as q4_K, q in 0..31.
  *  q6_K  210 B / 256 weights: 128 B low nibbles | 64 B 2-bit highs | 16 int8
  *        scales | f16 d; sub-block j (16 weights): w = d*sc_j*(q - 32).
  *  q8_K  292 B / 256 activations: f32 d | 256 int8 q | 16 int16 group sums.
@@ -48,13 +57,19 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 4
+#define GEMMQ_ABI_VERSION 5
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
+#define GEMMQ_Q2_K 10
+#define GEMMQ_Q3_K 11
 #define GEMMQ_Q4_K 12
+#define GEMMQ_Q5_K 13
 #define GEMMQ_Q6_K 14
 
+#define GEMMQ_Q2_K_BYTES 84
+#define GEMMQ_Q3_K_BYTES 110
 #define GEMMQ_Q4_K_BYTES 144
+#define GEMMQ_Q5_K_BYTES 176
 #define GEMMQ_Q6_K_BYTES 210
 #define GEMMQ_Q8_K_BYTES 292
 #define GEMMQ_QK 256
@@ -63,7 +78,7 @@ extern "C" {
 /* Status codes. */
 #define GEMMQ_OK 0
 #define GEMMQ_E_INVALID_ARG (-1)        /* null pointer, negative size, bad path id */
-#define GEMMQ_E_UNSUPPORTED_FORMAT (-2) /* fmt is not GEMMQ_Q4_K or GEMMQ_Q6_K */
+#define GEMMQ_E_UNSUPPORTED_FORMAT (-2) /* fmt is not one of GEMMQ_Q2_K .. GEMMQ_Q6_K */
 #define GEMMQ_E_SHAPE (-3)              /* K not a positive multiple of 256, or M too large for the path */
 #define GEMMQ_E_ALIGNMENT (-4)          /* a pointer breaks the alignment stated below */
 #define GEMMQ_E_DEVICE (-5)             /* current device is not gfx950, or no device */
@@ -80,7 +95,8 @@ int gemmq_abi_version(void);
 /* Static string naming a status code; never NULL. */
 const char *gemmq_status_str(int status);
 
-/* Bytes of one super-block of `fmt` (144, 210), or 0 for an unknown format. */
+/* Bytes of one super-block of `fmt` (84, 110, 144, 176, 210), or 0 for an
+ * unknown format. */
 size_t gemmq_block_bytes(int fmt);
 
 /* Bytes of an N x K packed weight matrix: N * K/256 * block_bytes; 0 when fmt is
@@ -108,9 +124,9 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
 /*
  * Y[m, n] = sum_k w[n, k] * d_x[m, k/256] * q_x[m, k]  -- the packed linear layer
  * (steps a2..a5: in-kernel unpack, GEMV for M <= 8, MFMA GEMM otherwise).
- *   fmt  GEMMQ_Q4_K or GEMMQ_Q6_K.
- *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K,
- *        4-byte aligned for q6_K.
+ *   fmt  GEMMQ_Q2_K, GEMMQ_Q3_K, GEMMQ_Q4_K, GEMMQ_Q5_K or GEMMQ_Q6_K.
+ *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K
+ *        and q5_K, 4-byte aligned for q2_K, q3_K and q6_K.
  *   Xq   device, gemmq_q8K_bytes(M, K) bytes from gemmq_quantize_q8K (or any
  *        valid q8_K blocks: |q| <= 127 and sums equal to the sums of q),
  *        4-byte aligned.
@@ -201,8 +217,8 @@ int gemmq_linear(int fmt, const void *W, const float *X, void *Xq, float *Y, int
  * (step a2) the matmul kernels use.  Never used on the compute path.
  *   W   device, gemmq_weight_bytes(fmt, N, K) bytes, alignment as in gemmq_gemm.
  *   Wf  device, f32 [N, K], 16-byte aligned; overwritten.
- * q4_K weights are the single f32 rounding of d*sc*q - dmin*m; q6_K weights are
- * exact.  Errors as gemmq_gemm.
+ * q2_K, q4_K and q5_K weights are the single f32 rounding of d*sc*q - dmin*m;
+ * q3_K and q6_K weights are exact.  Errors as gemmq_gemm.
  */
 int gemmq_decode(int fmt, const void *W, float *Wf, int64_t N, int64_t K, void *stream);
 

@@ -9,7 +9,10 @@ from ._lib import (  # noqa: F401
     ABI_VERSION,
     BLOCK_BYTES,
     EXPORTS,
+    FMT_Q2K,
+    FMT_Q3K,
     FMT_Q4K,
+    FMT_Q5K,
     FMT_Q6K,
     LIB_PATH,
     MAX_GROUP,

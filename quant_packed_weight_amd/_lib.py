@@ -11,14 +11,17 @@ import ctypes
 import os
 import threading
 
+FMT_Q2K = 10
+FMT_Q3K = 11
 FMT_Q4K = 12
+FMT_Q5K = 13
 FMT_Q6K = 14
-BLOCK_BYTES = {FMT_Q4K: 144, FMT_Q6K: 210}
+BLOCK_BYTES = {FMT_Q2K: 84, FMT_Q3K: 110, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210}
 Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 

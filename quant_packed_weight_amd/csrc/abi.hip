@@ -34,8 +34,20 @@ int check_device() {
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 int fmt_bytes(int fmt) {
-  return fmt == GEMMQ_Q4_K ? GEMMQ_Q4_K_BYTES : fmt == GEMMQ_Q6_K ? GEMMQ_Q6_K_BYTES : 0;
+  switch (fmt) {
+    case GEMMQ_Q2_K: return GEMMQ_Q2_K_BYTES;
+    case GEMMQ_Q3_K: return GEMMQ_Q3_K_BYTES;
+    case GEMMQ_Q4_K: return GEMMQ_Q4_K_BYTES;
+    case GEMMQ_Q5_K: return GEMMQ_Q5_K_BYTES;
+    case GEMMQ_Q6_K: return GEMMQ_Q6_K_BYTES;
+    default: return 0;
+  }
 }
+
+// Weight base alignment: blocks of 144 and 176 bytes keep every block 16-byte
+// aligned (the kernels load them with aligned 16-byte loads); the others only
+// need dword alignment of the base.
+uintptr_t fmt_align(int fmt) { return fmt == GEMMQ_Q4_K || fmt == GEMMQ_Q5_K ? 16 : 4; }
 
 // Launch outcome.  The thread's pending HIP error is cleared just before each
 // launch (see clear_pending), so an error read here belongs to our launch.
@@ -55,7 +67,7 @@ int check_weights(int fmt, const void* W, int64_t N, int64_t K) {
   if (N < 0) return GEMMQ_E_INVALID_ARG;
   if (K <= 0 || K % GEMMQ_QK != 0 || K > kMaxK || N > kMaxRows) return GEMMQ_E_SHAPE;
   if (N > 0 && !W) return GEMMQ_E_INVALID_ARG;
-  if (W && !aligned(W, fmt == GEMMQ_Q4_K ? 16 : 4)) return GEMMQ_E_ALIGNMENT;
+  if (W && !aligned(W, fmt_align(fmt))) return GEMMQ_E_ALIGNMENT;
   return GEMMQ_OK;
 }
 

@@ -12,23 +12,27 @@
 //    in 0..105: two int8 planes whose MFMA sums, combined as 8*A + B, give
 //    I_sc = sum_j sc_j * dot_j for a whole 256-weight super-block in int32.
 //    For q6_K, v = sc*(q-32) in -4064..4096 splits as 128*hi + lo with
-//    lo = v & 127 and hi = v >> 7 in -32..32.
-//  * The q4_K min term I_min = sum_g m_{g/2} * bsum_g is a K = 16 contraction
-//    of the activation group sums (|bsum| <= 2032) with the mins (<= 63): both
-//    are exact in f16 and every partial sum is below 2^24, so one
-//    v_mfma_f32_32x32x16_f16 gives it exactly, already in f32.
+//    lo = v & 127 and hi = v >> 7 in -32..32; q5_K's v = sc*q (0..1953) splits
+//    the same way; q2_K's v = sc*q (0..45) is one plane; q3_K's v = sc*q
+//    (-124..128) is one plane as -v (-128..124) with d negated.
+//  * The min term I_min = sum_g m_g * bsum_g (q4_K and q5_K: m_g the min of the
+//    32-weight sub-block holding group g; q2_K: of the group itself) is a
+//    K = 16 contraction of the activation group sums (|bsum| <= 2032) with the
+//    mins (<= 63): both are exact in f16 and every partial sum is below 2^24,
+//    so one v_mfma_f32_32x32x16_f16 gives it exactly, already in f32.
 //  * One f32 epilogue per super-block and output:
-//    y += d_x * (d * I_sc - dmin * I_min)   (q6_K: y += d_x * d * I_sc).
+//    y += d_x * (d * I_sc - dmin * I_min)   (q3_K, q6_K: y += d_x * d * I_sc).
 //
 // Two kernels:
 //  * q4_K (gemm_q4k_kernel, further below): activation and raw weight tiles
 //    stream through LDS stages filled by direct buffer->LDS loads; each wave
 //    unpacks its own 32 weight rows and computes a 64 x 32 tile; wave
 //    priorities by phase keep the two waves of a SIMD out of step.
-//  * q6_K (gemm_q6k_kernel): a 256-thread workgroup computes a 128 (M) x 64
-//    (N) tile, each of its four waves a 64 x 32 sub-tile.  Per super-block the
-//    workgroup stages the activation tile (int8 values, d_x) and the weight
-//    tile -- unpacked once into the two int8 planes -- in LDS;
+//  * q2_K, q3_K, q5_K, q6_K (gemm_plane_kernel): a 256-thread workgroup
+//    computes a 128 (M) x 64 (N) tile, each of its four waves a 64 x 32
+//    sub-tile.  Per super-block the workgroup stages the activation tile (int8
+//    values, d_x, and for q2_K/q5_K the group sums) and the weight tile --
+//    unpacked once into its int8 planes (and mins) -- in LDS;
 //    the global loads of super-block b+1 are issued before the MFMAs of
 //    super-block b and held in registers; one 69 KB stage lets two workgroups
 //    share a CU.
@@ -64,6 +68,13 @@ constexpr int kOffDx = kOffPb + kBN * kRow;  // [kBM] f32 d_x
 constexpr int kOffD = kOffDx + kBM * 4;      // [kBN] f32 d
 constexpr int kStage = kOffD + kBN * 4;
 constexpr int kLds = kStage;  // one stage: two workgroups fit in a CU's 160 KB
+// formats with a min term (q2_K, q5_K) also stage dmin, the activation group
+// sums and the weight mins, both as f16 over the 16 groups of 16
+constexpr int kOffDm = kStage;               // [kBN] f32 dmin
+constexpr int kOffBs = kOffDm + kBN * 4;     // [kBM][16] f16 group sums
+constexpr int kOffMn = kOffBs + kBM * 32;    // [kBN][16] f16 mins (per group of 16)
+constexpr int kLdsMin = kOffMn + kBN * 32;   // still two workgroups per CU
+static_assert(2 * kLdsMin <= 160 * 1024, "two workgroups per CU");
 
 // bytes of w (each <= 15) times a (<= 7): per 16-bit half the product stays below
 // 2^16 and no byte carries into the next.
@@ -90,12 +101,15 @@ __device__ __forceinline__ uint32_t i16x2_to_h2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// ------------------------------------------------- activation tile (q6_K kernel)
-// thread t: row t/2, half t%2 of the 256 int8 values; half 0 also d_x (the
-// q6_K route needs no group sums: the -32 offset is in the weight planes).
+// ------------------------------------------------- activation tile (plane kernel)
+// thread t: row t/2, half t%2 of the 256 int8 values; half 0 also d_x.  With
+// MIN (formats with a min term) also sums 8*half..8*half+7 (the other formats
+// need none: q6_K's -32 offset and q3_K's -4 are inside the weight planes).
+template <bool MIN>
 struct XRegs {
   u32x4 q[8];
   uint32_t d;
+  u32x4 s;  // MIN only
 };
 
 // Rows past M load a copy of row M-1: MFMA rows are independent and those
@@ -106,34 +120,40 @@ __device__ __forceinline__ const uint8_t* x_row(const uint8_t* __restrict__ Xq, 
   return Xq + (m < M ? m : M - 1) * nb * kQ8KBytes;
 }
 
-__device__ __forceinline__ void load_x(XRegs& r, const uint8_t* xrow, int b) {
+template <bool MIN>
+__device__ __forceinline__ void load_x(XRegs<MIN>& r, const uint8_t* xrow, int b) {
   const int part = threadIdx.x & 1;
   const uint8_t* xb = xrow + b * kQ8KBytes;
 #pragma unroll
   for (int i = 0; i < 8; ++i) r.q[i] = ld16(xb + 4 + 128 * part + 16 * i);
   r.d = part == 0 ? ld4(xb) : 0u;
+  if constexpr (MIN) r.s = ld16(xb + 260 + 16 * part);
 }
 
-__device__ __forceinline__ void store_x(uint8_t* st, const XRegs& r) {
+template <bool MIN>
+__device__ __forceinline__ void store_x(uint8_t* st, const XRegs<MIN>& r) {
   const int t = threadIdx.x, row = t >> 1, part = t & 1;
   uint8_t* a = st + kOffA + row * kRow + 128 * part;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st16(a + 16 * i, r.q[i].x, r.q[i].y, r.q[i].z, r.q[i].w);
   if (part == 0) reinterpret_cast<uint32_t*>(st + kOffDx)[row] = r.d;
+  if constexpr (MIN)
+    st16(st + kOffBs + row * 32 + 16 * part, i16x2_to_h2(r.s.x), i16x2_to_h2(r.s.y),
+         i16x2_to_h2(r.s.z), i16x2_to_h2(r.s.w));
 }
 
 // Columns past N load a copy of column N-1 (never stored).  SILU: N counts the
 // interleaved gate (even) and up (odd) rows; the up matrix is Wu.
-template <bool SILU>
+template <bool SILU, int BYTES>
 __device__ __forceinline__ const uint8_t* w_row(const uint8_t* __restrict__ W,
                                                 const uint8_t* __restrict__ Wu, int64_t n0,
                                                 int64_t N, int nb) {
   int64_t n = n0 + (threadIdx.x >> 2);
   if constexpr (SILU) {
     if (n >= N) n = N - 2 + (n & 1);
-    return ((n & 1) ? Wu : W) + (n >> 1) * nb * kQ6KBytes;
+    return ((n & 1) ? Wu : W) + (n >> 1) * nb * BYTES;
   } else {
-    return W + (n < N ? n : N - 1) * nb * kQ6KBytes;
+    return W + (n < N ? n : N - 1) * nb * BYTES;
   }
 }
 
@@ -157,17 +177,66 @@ __device__ __forceinline__ void silu_pair(float a, float b, bool odd, float& g, 
   u = odd ? b : got;
 }
 
-// ------------------------------------------------- q6_K weight tile
-// thread t: column t/4, part p4 = t%4 -> half hh = p4/2, quarters q = p4%2 (low
-// nibbles of ql bytes 64hh+32q..) and q+2 (their high nibbles).  Plane A gets
-// hi = v >> 7, plane B gets lo = v & 127, v = sc * (quant - 32).
-struct W6Regs {
+// ------------------------------------------------- weight tiles of the plane kernel
+// Per format: block bytes, int8 planes per weight, and whether a min term
+// (-dmin * sum_g m_g * bsum_g) is added.
+//   q6_K: v = sc*(q-32) in -4064..4096 -> plane A = v >> 7, plane B = v & 127.
+//   q5_K: v = sc*q in 0..1953          -> plane A = v >> 7, plane B = v & 127.
+//   q2_K: v = sc*q in 0..45            -> plane A = v.
+//   q3_K: v = sc*q in -124..128        -> plane A = -v (in -128..124), d negated.
+template <int FMT>
+struct PlaneFmt;
+template <>
+struct PlaneFmt<10> {
+  static constexpr int kBytes = 84, kPlanes = 1;
+  static constexpr bool kMin = true;
+};
+template <>
+struct PlaneFmt<11> {
+  static constexpr int kBytes = 110, kPlanes = 1;
+  static constexpr bool kMin = false;
+};
+template <>
+struct PlaneFmt<13> {
+  static constexpr int kBytes = 176, kPlanes = 2;
+  static constexpr bool kMin = true;
+};
+template <>
+struct PlaneFmt<14> {
+  static constexpr int kBytes = 210, kPlanes = 2;
+  static constexpr bool kMin = false;
+};
+
+// The raw bytes one thread holds for its (column, part) of a super-block.
+//   q6_K: thread t: column t/4, part p4 = t%4 -> half hh = p4/2, quarters
+//   q = p4%2 (low nibbles of ql bytes 64hh+32q..) and q+2 (their high nibbles).
+//   q2_K, q3_K, q5_K: part c = t%4 -> weights 64c..64c+63.
+template <int FMT>
+struct WRegs;
+template <>
+struct WRegs<14> {
   uint32_t ql[8], qh[8];
   uint32_t sc, d;
 };
+template <>
+struct WRegs<13> {
+  uint32_t ql[8], qh[8];  // low nibbles of group c; all 32 high-bit bytes
+  uint32_t h[4];          // d, dmin and the 12 scale bytes
+};
+template <>
+struct WRegs<10> {
+  uint32_t qs[8];  // the 32 quant bytes of half c/2
+  uint32_t sc, dd;  // scale/min bytes 4c..4c+3; d and dmin
+};
+template <>
+struct WRegs<11> {
+  uint32_t qs[8], hm[8];  // low parts of half c/2; all 32 mask bytes
+  uint32_t sc[3], d;      // the 12 scale bytes; d
+};
 
-// 32 bytes at a 2-byte-aligned address: the dword-aligned 36-byte span that
-// covers them (never past p + 34), shifted into place.
+// 32 bytes at a 2-byte-aligned address: the 36 bytes from p rounded down to a
+// dword (so at most p + 35 is read; every caller stays inside its block),
+// shifted into place.
 __device__ __forceinline__ void ld32_a2(const uint8_t* p, uint32_t (&o)[8]) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p);
   const uint8_t* base = reinterpret_cast<const uint8_t*>(a & ~uintptr_t(3));
@@ -178,7 +247,7 @@ __device__ __forceinline__ void ld32_a2(const uint8_t* p, uint32_t (&o)[8]) {
   for (int i = 0; i < 8; ++i) o[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
 }
 
-__device__ __forceinline__ void load_w(W6Regs& r, const uint8_t* wrow, int b) {
+__device__ __forceinline__ void load_w(WRegs<14>& r, const uint8_t* wrow, int b) {
   const int p4 = threadIdx.x & 3, hh = p4 >> 1, q = p4 & 1;
   const uint8_t* wb = wrow + b * kQ6KBytes;
   ld32_a2(wb + 64 * hh + 32 * q, r.ql);
@@ -200,7 +269,7 @@ __device__ __forceinline__ uint32_t q6_pack_plane(uint32_t e, uint32_t o, bool h
   return (pe & 0x00ff00ffu) | ((po & 0x00ff00ffu) << 8);
 }
 
-__device__ __forceinline__ void store_w(uint8_t* st, const W6Regs& r) {
+__device__ __forceinline__ void store_w(uint8_t* st, const WRegs<14>& r) {
   const int t = threadIdx.x, col = t >> 2, p4 = t & 3, hh = p4 >> 1, q = p4 & 1;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
@@ -229,11 +298,144 @@ __device__ __forceinline__ void store_w(uint8_t* st, const W6Regs& r) {
   if (p4 == 0) reinterpret_cast<float*>(st + kOffD)[col] = f16_to_f32(r.d);
 }
 
+// q5_K (176-byte blocks, 16-byte aligned)
+__device__ __forceinline__ void load_w(WRegs<13>& r, const uint8_t* wrow, int b) {
+  const int c = threadIdx.x & 3;
+  const uint8_t* wb = wrow + b * 176;
+  const uint4 l0 = ld16a(wb + 48 + 32 * c), l1 = ld16a(wb + 64 + 32 * c);
+  const uint4 h0 = ld16a(wb + 16), h1 = ld16a(wb + 32), hd = ld16a(wb);
+  r.ql[0] = l0.x; r.ql[1] = l0.y; r.ql[2] = l0.z; r.ql[3] = l0.w;
+  r.ql[4] = l1.x; r.ql[5] = l1.y; r.ql[6] = l1.z; r.ql[7] = l1.w;
+  r.qh[0] = h0.x; r.qh[1] = h0.y; r.qh[2] = h0.z; r.qh[3] = h0.w;
+  r.qh[4] = h1.x; r.qh[5] = h1.y; r.qh[6] = h1.z; r.qh[7] = h1.w;
+  r.h[0] = hd.x; r.h[1] = hd.y; r.h[2] = hd.z; r.h[3] = hd.w;
+}
+
+// v = sc * q split into the two planes (v in 0..1953: hi = v >> 7 <= 15)
+__device__ __forceinline__ void planes_u16(uint32_t q, uint32_t sc, uint32_t& hi, uint32_t& lo) {
+  const u16x2 s2 = {(unsigned short)sc, (unsigned short)sc};
+  const uint32_t e = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, q & 0x00ff00ffu) * s2);
+  const uint32_t o =
+      __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, (q >> 8) & 0x00ff00ffu) * s2);
+  hi = ((e >> 7) & 0x00ff00ffu) | (((o >> 7) & 0x00ff00ffu) << 8);
+  lo = (e & 0x007f007fu) | ((o & 0x007f007fu) << 8);
+}
+
+__device__ __forceinline__ uint32_t h2_pair(uint32_t a, uint32_t b) {
+  const h2 v = {(_Float16)(int)a, (_Float16)(int)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ void store_w(uint8_t* st, const WRegs<13>& r) {
+  const int t = threadIdx.x, col = t >> 2, c = t & 3;
+  const Q4KScales sm = q4k_scales(r.h[1], r.h[2], r.h[3]);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {  // sub-block 2c + half
+    const uint32_t sc = byte_of(sm.sc_lo, sm.sc_hi, 2 * c + half);
+    uint32_t hiw[8], low[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t nib = half ? hi_nib(r.ql[k]) : lo_nib(r.ql[k]);
+      const uint32_t q = nib | (((r.qh[k] >> (2 * c + half)) & 0x01010101u) << 4);
+      planes_u16(q, sc, hiw[k], low[k]);
+    }
+    uint8_t* pa = st + kOffPa + col * kRow + 64 * c + 32 * half;
+    uint8_t* pb = st + kOffPb + col * kRow + 64 * c + 32 * half;
+    st16(pa, hiw[0], hiw[1], hiw[2], hiw[3]);
+    st16(pa + 16, hiw[4], hiw[5], hiw[6], hiw[7]);
+    st16(pb, low[0], low[1], low[2], low[3]);
+    st16(pb + 16, low[4], low[5], low[6], low[7]);
+  }
+  // the mins of sub-blocks 2c, 2c+1 cover group sums 4c..4c+3
+  const uint32_t m0 = byte_of(sm.mn_lo, sm.mn_hi, 2 * c), m1 = byte_of(sm.mn_lo, sm.mn_hi, 2 * c + 1);
+  const uint32_t p0 = h2_pair(m0, m0), p1 = h2_pair(m1, m1);
+  *reinterpret_cast<uint2*>(st + kOffMn + col * 32 + 8 * c) = make_uint2(p0, p1);
+  if (c == 0) {
+    reinterpret_cast<float*>(st + kOffD)[col] = f16_to_f32(r.h[0]);
+    reinterpret_cast<float*>(st + kOffDm)[col] = f16_to_f32(r.h[0] >> 16);
+  }
+}
+
+// q2_K (84-byte blocks, 4-byte aligned)
+__device__ __forceinline__ void load_w(WRegs<10>& r, const uint8_t* wrow, int b) {
+  const int c = threadIdx.x & 3;
+  const uint8_t* wb = wrow + b * 84;
+  const u32x4 q0 = ld16(wb + 16 + 32 * (c >> 1)), q1 = ld16(wb + 32 + 32 * (c >> 1));
+  r.qs[0] = q0.x; r.qs[1] = q0.y; r.qs[2] = q0.z; r.qs[3] = q0.w;
+  r.qs[4] = q1.x; r.qs[5] = q1.y; r.qs[6] = q1.z; r.qs[7] = q1.w;
+  r.sc = ld4(wb + 4 * c);
+  r.dd = ld4(wb + 80);
+}
+
+__device__ __forceinline__ void store_w(uint8_t* st, const WRegs<10>& r) {
+  const int t = threadIdx.x, col = t >> 2, c = t & 3;
+  uint8_t* pa = st + kOffPa + col * kRow + 64 * c;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {  // sub-block 4c + g: quarter 2(c&1) + g/2, bytes 16(g&1)..
+    const int sh = 2 * (2 * (c & 1) + (g >> 1));
+    const uint32_t sc = (r.sc >> (8 * g)) & 15u;
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = mul_bytes((r.qs[4 * (g & 1) + k] >> sh) & 0x03030303u, sc);
+    st16(pa + 16 * g, v[0], v[1], v[2], v[3]);
+  }
+  const uint32_t m = (r.sc >> 4) & 0x0f0f0f0fu;  // the four mins, one per byte
+  *reinterpret_cast<uint2*>(st + kOffMn + col * 32 + 8 * c) =
+      make_uint2(h2_pair(m & 0xffu, (m >> 8) & 0xffu), h2_pair((m >> 16) & 0xffu, m >> 24));
+  if (c == 0) {
+    reinterpret_cast<float*>(st + kOffD)[col] = f16_to_f32(r.dd);
+    reinterpret_cast<float*>(st + kOffDm)[col] = f16_to_f32(r.dd >> 16);
+  }
+}
+
+// q3_K (110-byte blocks, 2-byte aligned: every read stays inside the block)
+__device__ __forceinline__ void load_w(WRegs<11>& r, const uint8_t* wrow, int b) {
+  const int c = threadIdx.x & 3;
+  const uint8_t* wb = wrow + b * 110;
+  ld32_a2(wb, r.hm);
+  ld32_a2(wb + 32 + 32 * (c >> 1), r.qs);
+  ld_dwords_a2<3>(wb + 96, r.sc);
+  r.d = ld2(wb + 108);
+}
+
+__device__ __forceinline__ void store_w(uint8_t* st, const WRegs<11>& r) {
+  const int t = threadIdx.x, col = t >> 2, c = t & 3, h = c >> 1;
+  uint8_t* pa = st + kOffPa + col * kRow + 64 * c;
+  // scales 4c..4c+3: low nibbles from byte word c&1 (high nibbles when c >= 2),
+  // top bits 2c..2c+1 of the bytes of word 2
+  const uint32_t lo4 = (r.sc[c & 1] >> (4 * (c >> 1))) & 0x0f0f0f0fu;
+  const uint32_t hi2 = (r.sc[2] >> (2 * c)) & 0x03030303u;
+  const uint32_t u6 = lo4 | (hi2 << 4);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const int qq = 2 * (c & 1) + (g >> 1);
+    const short s = (short)((int)((u6 >> (8 * g)) & 63u) - 32);
+    const i16x2 s2 = {s, s}, four = {4, 4};
+    uint32_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t low = (r.qs[4 * (g & 1) + k] >> (2 * qq)) & 0x03030303u;
+      const uint32_t hb = (r.hm[4 * (g & 1) + k] >> (4 * h + qq)) & 0x01010101u;
+      const uint32_t u = low | (hb << 2);  // q + 4 in 0..7
+      // -sc * q = sc * (4 - (q + 4)), in -128..124
+      const i16x2 e = (four - __builtin_bit_cast(i16x2, u & 0x00ff00ffu)) * s2;
+      const i16x2 o = (four - __builtin_bit_cast(i16x2, (u >> 8) & 0x00ff00ffu)) * s2;
+      v[k] = (__builtin_bit_cast(uint32_t, e) & 0x00ff00ffu) |
+             ((__builtin_bit_cast(uint32_t, o) & 0x00ff00ffu) << 8);
+    }
+    st16(pa + 16 * g, v[0], v[1], v[2], v[3]);
+  }
+  if (c == 0) reinterpret_cast<float*>(st + kOffD)[col] = -f16_to_f32(r.d);
+}
+
 // ------------------------------------------------- one super-block from LDS
 // 32x32 accumulator layout: lane holds column lane%32; register r holds row
 // 8*(r/4) + 4*(lane/32) + r%4.
+template <int FMT>
 __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], int arow0, int bcol,
                                         int hsel) {
+  constexpr int PLANES = PlaneFmt<FMT>::kPlanes;
+  constexpr bool MIN = PlaneFmt<FMT>::kMin;
   // plane A (hi) over the super-block, then acc <<= 7, then plane B (lo) on
   // top: acc = I_sc, exact in int32; two independent chains
   v16i acc[2];
@@ -248,18 +450,31 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
       acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
                         ba, acc[mt]);
   }
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << 7);
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    const int ko = 32 * kc + 16 * hsel;
-    const v4i bb = *reinterpret_cast<const v4i*>(st + kOffPb + bcol * kRow + ko);
+  if constexpr (PLANES == 2) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
-      acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
-                        bb, acc[mt]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << 7);
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const int ko = 32 * kc + 16 * hsel;
+      const v4i bb = *reinterpret_cast<const v4i*>(st + kOffPb + bcol * kRow + ko);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
+                          bb, acc[mt]);
+    }
+  }
+  // the min term: sum_g m_g * bsum_g over the 16 groups, exact in f32
+  v16f accm[2];
+  float dmcol = 0.0f;
+  if constexpr (MIN) {
+    dmcol = reinterpret_cast<const float*>(st + kOffDm)[bcol];
+    const v8h bm = *reinterpret_cast<const v8h*>(st + kOffMn + bcol * 32 + 16 * hsel);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      accm[mt] = mfma_f16(*reinterpret_cast<const v8h*>(st + kOffBs + (arow0 + 32 * mt) * 32 + 16 * hsel),
+                          bm, (v16f){0.0f});
   }
   const float dcol = reinterpret_cast<const float*>(st + kOffD)[bcol];
 #pragma unroll
@@ -272,16 +487,19 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const int r = 4 * q4 + s;
-        y[mt][r] = fmaf(dxs[s], dcol * (float)acc[mt][r], y[mt][r]);
+        float t = dcol * (float)acc[mt][r];
+        if constexpr (MIN) t = fmaf(-dmcol, accm[mt][r], t);
+        y[mt][r] = fmaf(dxs[s], t, y[mt][r]);
       }
     }
 }
 
-// ------------------------------------------------- the q6_K kernel
-template <bool SILU>
-__global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
-                                                          const uint8_t* __restrict__ Xq, int64_t M,
-                                                          int nb) {
+// ------------------------------------------------- the plane kernel (q2_K, q3_K, q5_K, q6_K)
+template <int FMT, bool SILU>
+__global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
+                                                            const uint8_t* __restrict__ Xq,
+                                                            int64_t M, int nb) {
+  constexpr bool MIN = PlaneFmt<FMT>::kMin;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
   const uint8_t* __restrict__ W = tm.W;
@@ -304,9 +522,9 @@ __global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
     for (int r = 0; r < 16; ++r) y[mt][r] = 0.0f;
 
   const uint8_t* xrow = x_row(Xq, m0, M, nb);
-  const uint8_t* wrow = w_row<SILU>(W, gt.W[1], n0, N, nb);
-  XRegs xr;
-  W6Regs wr;
+  const uint8_t* wrow = w_row<SILU, PlaneFmt<FMT>::kBytes>(W, gt.W[1], n0, N, nb);
+  XRegs<MIN> xr;
+  WRegs<FMT> wr;
   load_x(xr, xrow, 0);
   load_w(wr, wrow, 0);
   for (int b = 0; b < nb; ++b) {
@@ -317,7 +535,7 @@ __global__ __launch_bounds__(256, 2) void gemm_q6k_kernel(const GroupTiles gt,
       load_x(xr, xrow, b + 1);
       load_w(wr, wrow, b + 1);
     }
-    compute(lds, y, arow0, bcol, hsel);
+    compute<FMT>(lds, y, arow0, bcol, hsel);
     __syncthreads();
   }
 
@@ -741,8 +959,14 @@ bool set_lds_limits() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   if (attr_done[dev].load(std::memory_order_acquire) == 0) {
-    if (hipFuncSetAttribute((const void*)gemm_q6k_kernel<SILU>,
+    if (hipFuncSetAttribute((const void*)gemm_plane_kernel<14, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
+        hipFuncSetAttribute((const void*)gemm_plane_kernel<11, SILU>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
+        hipFuncSetAttribute((const void*)gemm_plane_kernel<10, SILU>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
+        hipFuncSetAttribute((const void*)gemm_plane_kernel<13, SILU>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_q4k_kernel<1, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             q4s::lds_bytes<1>()) != hipSuccess ||
@@ -778,7 +1002,23 @@ int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t 
       hipLaunchKernelGGL((gemm_q4k_kernel<1, SILU>), grid, dim3(256), q4s::lds_bytes<1>(), st, gt,
                          Xq, M, (int)nb);
   } else {
-    hipLaunchKernelGGL(gemm_q6k_kernel<SILU>, grid, dim3(256), kLds, st, gt, Xq, M, (int)nb);
+    switch (fmt) {
+      case 10:
+        hipLaunchKernelGGL((gemm_plane_kernel<10, SILU>), grid, dim3(256), kLdsMin, st, gt, Xq, M,
+                           (int)nb);
+        break;
+      case 11:
+        hipLaunchKernelGGL((gemm_plane_kernel<11, SILU>), grid, dim3(256), kLds, st, gt, Xq, M,
+                           (int)nb);
+        break;
+      case 13:
+        hipLaunchKernelGGL((gemm_plane_kernel<13, SILU>), grid, dim3(256), kLdsMin, st, gt, Xq, M,
+                           (int)nb);
+        break;
+      default:
+        hipLaunchKernelGGL((gemm_plane_kernel<14, SILU>), grid, dim3(256), kLds, st, gt, Xq, M,
+                           (int)nb);
+    }
   }
   return 0;
 }

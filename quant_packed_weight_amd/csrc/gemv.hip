@@ -10,8 +10,11 @@
 //
 //  * One 64-lane wavefront owns P weight rows and issues every weight load of
 //    them before any arithmetic.  Four lanes share a super-block: q4_K lane g
-//    takes the 32 quant bytes of 64-weight group g (sub-blocks 2g and 2g+1);
-//    q6_K lane (half hh, pair p) takes quarters p and p+2 of half hh.  A round
+//    takes the 32 quant bytes of 64-weight group g (sub-blocks 2g and 2g+1),
+//    q5_K the same plus the 32 high-bit bytes; q2_K and q3_K lane g takes
+//    weights 64g..64g+63 (sub-blocks 4g..4g+3) from the 32 bytes of 2-bit
+//    parts of half g/2 (q3_K also the 32 mask bytes); q6_K lane (half hh,
+//    pair p) takes quarters p and p+2 of half hh.  A round
 //    is 16 consecutive blocks of a row (or, for rows of 16/P blocks, P rows side
 //    by side), so one load instruction of the wave covers 2.3 KiB (q4_K) of
 //    contiguous weight bytes.
@@ -68,8 +71,9 @@ __device__ __forceinline__ void ld36(const uint8_t* p, uint32_t (&o)[9]) {
   o[8] = ld4(p + 32);
 }
 
-// 32 bytes at a 2-byte-aligned address: the dword-aligned 36-byte span that
-// covers them (never past p + 34), shifted into place.
+// 32 bytes at a 2-byte-aligned address: the 36 bytes from p rounded down to a
+// dword (so at most p + 35 is read; every caller stays inside its block),
+// shifted into place.
 __device__ __forceinline__ void ld32_a2(const uint8_t* p, uint32_t (&o)[8]) {
   const uintptr_t a = reinterpret_cast<uintptr_t>(p);
   uint32_t raw[9];
@@ -246,7 +250,8 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
                                                             int M) {
   constexpr int SEG = 64 / P;  // lanes that share a row
   constexpr int BPR = 16 / P;  // blocks of a row per round when P > 1
-  constexpr int BB = FMT == 12 ? kQ4KBytes : kQ6KBytes;
+  constexpr int BB = FMT == 10 ? 84 : FMT == 11 ? 110 : FMT == 12 ? kQ4KBytes : FMT == 13 ? 176
+                                                                                  : kQ6KBytes;
   constexpr int NW = KS * RG;  // waves of the workgroup
   const int lane = lane_id();
   const int G = lane >> 2, c = lane & 3;
@@ -281,13 +286,14 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
   }
 
   // per-lane constants
-  // q4_K lane c = group g: values 64g..64g+63 (sub-blocks 2g, 2g+1), sums 4g..4g+3.
+  // q2_K, q3_K, q4_K, q5_K lane c: values 64c..64c+63, sums 4c..4c+3 (q4_K and
+  //   q5_K: sub-blocks 2c, 2c+1; q2_K and q3_K: sub-blocks 4c..4c+3).
   // q6_K lane c = (hh, p) = (c/2, c%2): quarters p and p+2 of half hh, i.e. values
   //   128hh+32p.. and 128hh+32p+64.., sums 8hh+2p, +1 and 8hh+2p+4, +5.
-  const int qoff = FMT == 12 ? 64 * c : 128 * (c >> 1) + 32 * (c & 1);
-  const int qoff2 = FMT == 12 ? 64 * c + 32 : qoff + 64;
-  const int soff = FMT == 12 ? 8 * c : 2 * (8 * (c >> 1) + 2 * (c & 1));
-  const int soff2 = soff + (FMT == 12 ? 4 : 8);
+  const int qoff = FMT != 14 ? 64 * c : 128 * (c >> 1) + 32 * (c & 1);
+  const int qoff2 = FMT != 14 ? 64 * c + 32 : qoff + 64;
+  const int soff = FMT != 14 ? 8 * c : 2 * (8 * (c >> 1) + 2 * (c & 1));
+  const int soff2 = soff + (FMT != 14 ? 4 : 8);
 
   float acc[V];
 #pragma unroll
@@ -303,8 +309,12 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
       return x_frag(Xq, nb, m, b, qoff, qoff2, soff, soff2);
   };
 
-  uint32_t wq[IT][R][8], wh[IT][R][8];  // q4_K: 32 quant bytes; q6_K: ql and qh bytes
-  uint32_t hd[IT][R][4];  // q4_K: block header; q6_K: [0] scale bytes, [1] d
+  // wq: q4_K quant bytes, q5_K low nibbles, q2_K/q3_K 2-bit bytes of half c/2,
+  //     q6_K ql bytes; wh: q6_K qh bytes, q5_K high bits, q3_K mask (32 bytes each)
+  // hd: q4_K/q5_K block header; q6_K [0] scale bytes, [1] d; q2_K [0] scale/min
+  //     bytes 4c..4c+3, [1] d and dmin; q3_K [0..2] scale bytes, [3] d
+  uint32_t wq[IT][R][8], wh[IT][R][8];
+  uint32_t hd[IT][R][4];
   // ---- 1. every weight load of the IT rounds from block s0 on (lanes past the
   // row's end load its last block when `clamp`, else nothing)
   auto load_round = [&](int s0, bool clamp) {
@@ -316,12 +326,32 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
         if (clamp) b = b < nb ? b : nb - 1;
         if (b < nb) {
           const uint8_t* wb = wrow[r] + b * BB;
-          if constexpr (FMT == 12) {
+          if constexpr (FMT == 12 || FMT == 13) {
+            constexpr int QO = FMT == 12 ? 16 : 48;  // quant (low nibble) bytes
             const uint4 h = ld16a(wb);
-            const uint4 q0 = ld16a(wb + 16 + 32 * c), q1 = ld16a(wb + 32 + 32 * c);
+            const uint4 q0 = ld16a(wb + QO + 32 * c), q1 = ld16a(wb + QO + 16 + 32 * c);
             hd[i][r][0] = h.x; hd[i][r][1] = h.y; hd[i][r][2] = h.z; hd[i][r][3] = h.w;
             wq[i][r][0] = q0.x; wq[i][r][1] = q0.y; wq[i][r][2] = q0.z; wq[i][r][3] = q0.w;
             wq[i][r][4] = q1.x; wq[i][r][5] = q1.y; wq[i][r][6] = q1.z; wq[i][r][7] = q1.w;
+            if constexpr (FMT == 13) {
+              const uint4 h0 = ld16a(wb + 16), h1 = ld16a(wb + 32);
+              wh[i][r][0] = h0.x; wh[i][r][1] = h0.y; wh[i][r][2] = h0.z; wh[i][r][3] = h0.w;
+              wh[i][r][4] = h1.x; wh[i][r][5] = h1.y; wh[i][r][6] = h1.z; wh[i][r][7] = h1.w;
+            }
+          } else if constexpr (FMT == 10) {
+            const u32x4 q0 = ld16(wb + 16 + 32 * (c >> 1)), q1 = ld16(wb + 32 + 32 * (c >> 1));
+            wq[i][r][0] = q0.x; wq[i][r][1] = q0.y; wq[i][r][2] = q0.z; wq[i][r][3] = q0.w;
+            wq[i][r][4] = q1.x; wq[i][r][5] = q1.y; wq[i][r][6] = q1.z; wq[i][r][7] = q1.w;
+            hd[i][r][0] = ld4(wb + 4 * c);
+            hd[i][r][1] = ld4(wb + 80);
+          } else if constexpr (FMT == 11) {
+            // 110-byte blocks are 2-byte aligned; every read stays in the block
+            ld32_a2(wb, wh[i][r]);
+            ld32_a2(wb + 32 + 32 * (c >> 1), wq[i][r]);
+            uint32_t sb[3];
+            ld_dwords_a2<3>(wb + 96, sb);
+            hd[i][r][0] = sb[0]; hd[i][r][1] = sb[1]; hd[i][r][2] = sb[2];
+            hd[i][r][3] = ld2(wb + 108);
           } else {
             const int hh = c >> 1, p = c & 1;
             ld32_a2(wb + 64 * hh + 32 * p, wq[i][r]);
@@ -340,8 +370,9 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     for (int i = 0; i < IT; ++i) {
       const int b = s0 + bl0 + 16 * i;
       if (b >= nb) break;
-      if constexpr (FMT == 12) {
-        // scales and mins of sub-blocks 2c and 2c+1 as byte pairs
+      if constexpr (FMT == 12 || FMT == 13) {
+        // scales and mins of sub-blocks 2c and 2c+1 as byte pairs (q5_K: the
+        // same header; its quants add the high bits 2c and 2c+1 as bit 4)
         int sc0[R], sc1[R];
         uint32_t m0[R], m1[R], lo[R][8], hi[R][8];
         float d[R], dmin[R];
@@ -367,6 +398,10 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
           for (int k = 0; k < 8; ++k) {
             lo[r][k] = lo_nib(wq[i][r][k]);
             hi[r][k] = hi_nib(wq[i][r][k]);
+            if constexpr (FMT == 13) {
+              lo[r][k] |= ((wh[i][r][k] >> (2 * c)) & 0x01010101u) << 4;
+              hi[r][k] |= ((wh[i][r][k] >> (2 * c + 1)) & 0x01010101u) << 4;
+            }
           }
         }
 #pragma unroll
@@ -380,6 +415,68 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
             const int imn = dot2(x.s0, m0[r], dot2(x.s1, m1[r], 0));
             float t = d[r] * (float)isc;
             t = fmaf(-dmin[r], (float)imn, t);
+            acc[r * MT + m] = fmaf(x.d, t, acc[r * MT + m]);
+          }
+        }
+      } else if constexpr (FMT == 10 || FMT == 11) {
+        // sub-blocks 4c + g, g = 0..3, against activation runs a0, a1, b0, b1:
+        // quarter 2(c&1) + g/2 of half c/2, bytes 16(g&1)..16(g&1)+15 of it
+        uint32_t qg[R][4][4];
+        int sg[R][4];
+        uint32_t mp0[R], mp1[R];  // q2_K: mins (4c, 4c+1), (4c+2, 4c+3) as int16 pairs
+        float d[R], dmin[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int qq = 2 * (c & 1) + (g >> 1);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              uint32_t v = (wq[i][r][4 * (g & 1) + k] >> (2 * qq)) & 0x03030303u;
+              if constexpr (FMT == 11)  // q + 4 in 0..7: the mask bit adds 4
+                v |= ((wh[i][r][4 * (g & 1) + k] >> (4 * (c >> 1) + qq)) & 0x01010101u) << 2;
+              qg[r][g][k] = v;
+            }
+          }
+          if constexpr (FMT == 10) {
+            const uint32_t w = hd[i][r][0];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) sg[r][g] = (int)((w >> (8 * g)) & 15u);
+            mp0[r] = ((w >> 4) & 0xfu) | ((w << 4) & 0xf0000u);
+            mp1[r] = ((w >> 20) & 0xfu) | ((w >> 12) & 0xf0000u);
+            d[r] = f16_to_f32(hd[i][r][1]);
+            dmin[r] = f16_to_f32(hd[i][r][1] >> 16);
+          } else {
+            // scales 4c..4c+3: low nibbles from word c&1 (its high nibbles when
+            // c >= 2), top bits 2c..2c+1 of the bytes of word 2; minus 32
+            const uint32_t lo4 = (hd[i][r][c & 1] >> (4 * (c >> 1))) & 0x0f0f0f0fu;
+            const uint32_t u6 = lo4 | (((hd[i][r][2] >> (2 * c)) & 0x03030303u) << 4);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) sg[r][g] = (int)((u6 >> (8 * g)) & 63u) - 32;
+            // the -4 offset against the group sums: -4 * sum_g sc_g * bsum_g
+            mp0[r] = (uint32_t)(sg[r][0] & 0xffff) | ((uint32_t)sg[r][1] << 16);
+            mp1[r] = (uint32_t)(sg[r][2] & 0xffff) | ((uint32_t)sg[r][3] << 16);
+            d[r] = f16_to_f32(hd[i][r][3]);
+            dmin[r] = 0.0f;
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const XFrag x = xfrag(m < M ? m : M - 1, b);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            int isc = __mul24(sg[r][0], dot16(qg[r][0], x.a0, 0)) +
+                      __mul24(sg[r][1], dot16(qg[r][1], x.a1, 0)) +
+                      __mul24(sg[r][2], dot16(qg[r][2], x.b0, 0)) +
+                      __mul24(sg[r][3], dot16(qg[r][3], x.b1, 0));
+            const int isum = dot2(x.s0, mp0[r], dot2(x.s1, mp1[r], 0));
+            float t;
+            if constexpr (FMT == 10) {
+              t = d[r] * (float)isc;
+              t = fmaf(-dmin[r], (float)isum, t);
+            } else {
+              t = d[r] * (float)(isc - 4 * isum);
+            }
             acc[r * MT + m] = fmaf(x.d, t, acc[r * MT + m]);
           }
         }
@@ -616,8 +713,13 @@ int launch_any(int fmt, const Group& g, uint8_t* Xq, const float* X, int M, int6
                hipStream_t st) {
   const int64_t nb = K / kQK;
   if (nb > 0x7fffffffLL) return -1;
-  return fmt == 12 ? launch_fmt<12, SILU>(g, Xq, X, M, (int)nb, st)
-                   : launch_fmt<14, SILU>(g, Xq, X, M, (int)nb, st);
+  switch (fmt) {
+    case 10: return launch_fmt<10, SILU>(g, Xq, X, M, (int)nb, st);
+    case 11: return launch_fmt<11, SILU>(g, Xq, X, M, (int)nb, st);
+    case 12: return launch_fmt<12, SILU>(g, Xq, X, M, (int)nb, st);
+    case 13: return launch_fmt<13, SILU>(g, Xq, X, M, (int)nb, st);
+    default: return launch_fmt<14, SILU>(g, Xq, X, M, (int)nb, st);
+  }
 }
 
 }  // namespace

@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 4
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 5
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -49,7 +49,7 @@ def test_version_and_status_names(L):
 
 
 def test_size_helpers(L):
-    assert gq.block_bytes(12) == 144 and gq.block_bytes(14) == 210 and gq.block_bytes(13) == 0
+    assert [gq.block_bytes(f) for f in range(9, 16)] == [0, 84, 110, 144, 176, 210, 0]
     assert gq.weight_bytes(12, 4096, 4096) == 4096 * 16 * 144
     assert gq.weight_bytes(14, 151936, 2048) == 255252480
     assert gq.weight_bytes(12, 10, 300) == 0 and gq.weight_bytes(12, -1, 256) == 0
@@ -63,7 +63,11 @@ FAKE16 = 0x10000  # never dereferenced: every call below fails validation first
 
 
 @pytest.mark.parametrize("args,status", [
-    ((13, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -2),      # unknown format
+    ((15, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -2),      # unknown format
+    ((9, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -2),       # unknown format
+    ((13, FAKE16 + 4, FAKE16, FAKE16, 1, 1, 256, 0), -4),  # q5_K weights need 16 bytes
+    ((10, FAKE16 + 2, FAKE16, FAKE16, 1, 1, 256, 0), -4),  # q2_K weights need 4 bytes
+    ((11, FAKE16 + 2, FAKE16, FAKE16, 1, 1, 256, 0), -4),  # q3_K weights need 4 bytes
     ((12, FAKE16, FAKE16, FAKE16, 1, 1, 300, 0), -3),      # K % 256 != 0
     ((12, FAKE16, FAKE16, FAKE16, 1, 1, 0, 0), -3),        # K = 0
     ((12, FAKE16, FAKE16, FAKE16, 1, -1, 256, 0), -1),     # N < 0
@@ -114,12 +118,12 @@ def test_group_null_arrays(L):
     assert L.gemmq_gemm_group(12, 1, None, one_p, one_n, FAKE16, 1, 256, 0, None) == -1
     assert L.gemmq_gemm_group(12, 1, one_p, None, one_n, FAKE16, 1, 256, 0, None) == -1
     assert L.gemmq_gemm_group(12, 1, one_p, one_p, None, FAKE16, 1, 256, 0, None) == -1
-    assert L.gemmq_gemm_group(13, 1, one_p, one_p, one_n, FAKE16, 1, 256, 0, None) == -2
+    assert L.gemmq_gemm_group(15, 1, one_p, one_p, one_n, FAKE16, 1, 256, 0, None) == -2
     assert L.gemmq_gemm_group(12, 1, one_p, one_p, one_n, None, 1, 256, 0, None) == -1
 
 
 @pytest.mark.parametrize("args,status", [
-    ((13, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256), -2),      # unknown format
+    ((15, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256), -2),      # unknown format
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 300), -3),      # K % 256 != 0
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, -1, 1, 256), -1),     # M < 0
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, 1, -1, 256), -1),     # N < 0
@@ -143,7 +147,7 @@ def test_linear_validation(L, args, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((13, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -2),      # unknown format
+    ((15, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256, 0), -2),      # unknown format
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 300, 0), -3),      # K % 256 != 0
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, -1, 1, 256, 0), -1),     # M < 0
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, -1, 256, 0), -1),     # N < 0
