@@ -16,5 +16,6 @@ from .oracle import (  # noqa: F401
     gemm_int,
     load,
     quantize_q8K,
+    repack,
     silu_mul,
 )

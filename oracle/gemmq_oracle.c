@@ -540,5 +540,43 @@ void oracle_silu_mul(const double *g, const double *u, int64_t n, double *y)
         y[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
 }
 
+/* Load-time repack of a q3_K or q6_K matrix (the survey's "repack" row, the
+ * GPU counterpart of the pages' q4_K 8-column panels: molayo article, status row
+ * "src/ -- C++ engine"): the same bytes, reordered so that every field of every
+ * block starts on a 16-byte boundary.  The matrix's NB = N*K/256 blocks, in row
+ * order, are split into their fields and each field is stored for all blocks
+ * in a row (structure of arrays):
+ *   q6_K: ql[NB][128] | qh[NB][64] | sc[NB][16] | d[NB][2]
+ *   q3_K: hmask[NB][32] | qs[NB][64] | scales[NB][12] | d[NB][2]
+ * The layout is this library's own (the pages describe panels for q4_K but no
+ * byte layout).  Returns 0, or -1 for another format or bad sizes. */
+int oracle_repack(int fmt, const uint8_t *W, int64_t N, int64_t K, uint8_t *out)
+{
+    static const int f6[] = {128, 64, 16, 2}, f3[] = {32, 64, 12, 2};
+    const int *f;
+    int bb;
+    if (fmt == OFMT_Q6K) {
+        f = f6;
+        bb = OQ6K_BYTES;
+    } else if (fmt == OFMT_Q3K) {
+        f = f3;
+        bb = OQ3K_BYTES;
+    } else {
+        return -1;
+    }
+    if (N < 0 || K <= 0 || K % OQK != 0)
+        return -1;
+    int64_t nb = N * (K / OQK);
+    int64_t dst = 0;
+    int src = 0;
+    for (int k = 0; k < 4; ++k) {
+        for (int64_t i = 0; i < nb; ++i)
+            memcpy(out + dst + i * f[k], W + i * bb + src, (size_t)f[k]);
+        dst += nb * f[k];
+        src += f[k];
+    }
+    return 0;
+}
+
 /* Version of this oracle's interface, for the test loader. */
-int oracle_version(void) { return 3; }
+int oracle_version(void) { return 4; }

@@ -62,6 +62,8 @@ def load():
             lib.oracle_gemm_int.restype = ctypes.c_int
             lib.oracle_gemm_dequant.argtypes = [ctypes.c_int, P, P, I64, I64, I64, P, I64, P, P]
             lib.oracle_gemm_dequant.restype = ctypes.c_int
+            lib.oracle_repack.argtypes = [ctypes.c_int, P, I64, I64, P]
+            lib.oracle_repack.restype = ctypes.c_int
             lib.oracle_silu_mul.argtypes = [P, P, I64, P]
             lib.oracle_silu_mul.restype = None
             _lib = lib
@@ -144,3 +146,13 @@ def silu_mul(g, u) -> np.ndarray:
     y = np.empty_like(g)
     load().oracle_silu_mul(_ptr(g), _ptr(u), g.size, _ptr(y))
     return y
+
+
+def repack(fmt: int, W: np.ndarray, N: int, K: int) -> np.ndarray:
+    """q3_K / q6_K matrix -> its load-time repacked bytes (same size, uint8 [N, row bytes])."""
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    assert W.size == N * (K // 256) * BLOCK_BYTES[fmt]
+    out = np.empty_like(W).reshape(N, -1)
+    if load().oracle_repack(fmt, _ptr(W), N, K, _ptr(out)) != 0:
+        raise ValueError("oracle_repack: format %d has no repacked layout" % fmt)
+    return out
