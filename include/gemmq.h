@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 5
+#define GEMMQ_ABI_VERSION 6
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q2_K 10
@@ -65,6 +65,11 @@ extern "C" {
 #define GEMMQ_Q4_K 12
 #define GEMMQ_Q5_K 13
 #define GEMMQ_Q6_K 14
+
+/* The load-time repacked layouts of q3_K and q6_K (gemmq_repack): the type id
+ * plus 256.  Accepted wherever a weight format is, except gemmq_decode. */
+#define GEMMQ_Q3_K_R (256 + GEMMQ_Q3_K)
+#define GEMMQ_Q6_K_R (256 + GEMMQ_Q6_K)
 
 #define GEMMQ_Q2_K_BYTES 84
 #define GEMMQ_Q3_K_BYTES 110
@@ -78,7 +83,7 @@ extern "C" {
 /* Status codes. */
 #define GEMMQ_OK 0
 #define GEMMQ_E_INVALID_ARG (-1)        /* null pointer, negative size, bad path id */
-#define GEMMQ_E_UNSUPPORTED_FORMAT (-2) /* fmt is not one of GEMMQ_Q2_K .. GEMMQ_Q6_K */
+#define GEMMQ_E_UNSUPPORTED_FORMAT (-2) /* fmt is not one of GEMMQ_Q2_K .. GEMMQ_Q6_K, _R */
 #define GEMMQ_E_SHAPE (-3)              /* K not a positive multiple of 256, or M too large for the path */
 #define GEMMQ_E_ALIGNMENT (-4)          /* a pointer breaks the alignment stated below */
 #define GEMMQ_E_DEVICE (-5)             /* current device is not gfx950, or no device */
@@ -124,9 +129,10 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
 /*
  * Y[m, n] = sum_k w[n, k] * d_x[m, k/256] * q_x[m, k]  -- the packed linear layer
  * (steps a2..a5: in-kernel unpack, GEMV for M <= 8, MFMA GEMM otherwise).
- *   fmt  GEMMQ_Q2_K, GEMMQ_Q3_K, GEMMQ_Q4_K, GEMMQ_Q5_K or GEMMQ_Q6_K.
- *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K
- *        and q5_K, 4-byte aligned for q2_K, q3_K and q6_K.
+ *   fmt  GEMMQ_Q2_K, GEMMQ_Q3_K, GEMMQ_Q4_K, GEMMQ_Q5_K, GEMMQ_Q6_K, or a
+ *        repacked GEMMQ_Q3_K_R / GEMMQ_Q6_K_R (weights from gemmq_repack).
+ *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K,
+ *        q5_K and the repacked layouts, 4-byte aligned for q2_K, q3_K and q6_K.
  *   Xq   device, gemmq_q8K_bytes(M, K) bytes from gemmq_quantize_q8K (or any
  *        valid q8_K blocks: |q| <= 127 and sums equal to the sums of q),
  *        4-byte aligned.
@@ -211,6 +217,27 @@ int gemmq_linear_silu_mul(int fmt, const void *Wg, const void *Wu, const float *
 /* gemmq_linear_group for one matrix with GEMMQ_PATH_AUTO. */
 int gemmq_linear(int fmt, const void *W, const float *X, void *Xq, float *Y, int64_t M, int64_t N,
                  int64_t K, void *stream);
+
+/*
+ * Load-time repack of a q3_K or q6_K matrix into its GEMMQ_Q3_K_R /
+ * GEMMQ_Q6_K_R layout: the same bytes (gemmq_weight_bytes(fmt, N, K)), with the
+ * NB = N*K/256 blocks' fields each stored for all blocks in block order --
+ *   q6_K: ql[NB][128] | qh[NB][64] | sc[NB][16] | d[NB][2]
+ *   q3_K: hmask[NB][32] | qs[NB][64] | scales[NB][12] | d[NB][2]
+ * -- so that every field of 16 or more bytes per block is 16-byte aligned and
+ * the kernels load it without realigning (the 110- and 210-byte blocks
+ * otherwise start on any even address).  The matmul on repacked weights gives
+ * the same bits as on the original ones.  This is the GPU counterpart of the
+ * pages' load-time q4_K 8-column panels (molayo article, status row "src/"),
+ * for the two formats whose block size breaks alignment.  The layout belongs
+ * to a whole matrix: a repacked matrix cannot be sliced by rows.
+ *   fmt  GEMMQ_Q3_K or GEMMQ_Q6_K (the layout of W).
+ *   W    device, 4-byte aligned.   Wr  device, 16-byte aligned, not overlapping W.
+ * Errors: GEMMQ_E_UNSUPPORTED_FORMAT (another fmt), GEMMQ_E_INVALID_ARG (null,
+ *         N < 0, overlap), GEMMQ_E_SHAPE, GEMMQ_E_ALIGNMENT, GEMMQ_E_DEVICE,
+ *         GEMMQ_E_LAUNCH.
+ */
+int gemmq_repack(int fmt, const void *W, void *Wr, int64_t N, int64_t K, void *stream);
 
 /*
  * Diagnostic export: decode packed weights to f32 with the same device unpacker

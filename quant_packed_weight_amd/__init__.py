@@ -11,9 +11,11 @@ from ._lib import (  # noqa: F401
     EXPORTS,
     FMT_Q2K,
     FMT_Q3K,
+    FMT_Q3K_R,
     FMT_Q4K,
     FMT_Q5K,
     FMT_Q6K,
+    FMT_Q6K_R,
     LIB_PATH,
     MAX_GROUP,
     PATH_AUTO,
@@ -36,6 +38,7 @@ from ._lib import (  # noqa: F401
     linear_silu_mul,
     q8K_bytes,
     quantize_q8K,
+    repack,
     quantize_q8K_ptr,
     status_str,
     weight_bytes,

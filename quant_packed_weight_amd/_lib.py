@@ -16,12 +16,15 @@ FMT_Q3K = 11
 FMT_Q4K = 12
 FMT_Q5K = 13
 FMT_Q6K = 14
-BLOCK_BYTES = {FMT_Q2K: 84, FMT_Q3K: 110, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210}
+FMT_Q3K_R = 256 + FMT_Q3K  # repacked layouts (gemmq_repack)
+FMT_Q6K_R = 256 + FMT_Q6K
+BLOCK_BYTES = {FMT_Q2K: 84, FMT_Q3K: 110, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 210,
+               FMT_Q3K_R: 110, FMT_Q6K_R: 210}
 Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 
@@ -45,6 +48,7 @@ EXPORTS = {
     "gemmq_linear": (_I, [_I, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "gemmq_linear_silu_mul": (_I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
+    "gemmq_repack": (_I, [_I, _P, _P, _I64, _I64, _P]),
 }
 
 
@@ -281,3 +285,19 @@ def linear_silu_mul(fmt, wg, wu, x, N, xq=None, out=None, path=PATH_AUTO, stream
                                        _dev(out, "out", torch.float32), M, N, K, path,
                                        _stream(stream)), "gemmq_linear_silu_mul")
     return out, xq
+
+
+def repack(fmt, w, N, K, out=None, stream=None):
+    """q3_K / q6_K weights (uint8 device tensor) -> their repacked layout
+    (gemmq_repack); use the result with FMT_Q3K_R / FMT_Q6K_R."""
+    torch = _torch()
+    nbytes = weight_bytes(fmt, N, K)
+    if w.numel() < nbytes:
+        raise ValueError("buffer smaller than the stated shape")
+    if out is None:
+        out = torch.empty((N, nbytes // max(N, 1)), dtype=torch.uint8, device=w.device)
+    elif out.numel() < nbytes:
+        raise ValueError("out too small")
+    _check(lib().gemmq_repack(fmt, _dev(w, "w", torch.uint8), _dev(out, "out", torch.uint8), N, K,
+                              _stream(stream)), "gemmq_repack")
+    return out

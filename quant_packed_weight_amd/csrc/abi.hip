@@ -40,14 +40,19 @@ int fmt_bytes(int fmt) {
     case GEMMQ_Q4_K: return GEMMQ_Q4_K_BYTES;
     case GEMMQ_Q5_K: return GEMMQ_Q5_K_BYTES;
     case GEMMQ_Q6_K: return GEMMQ_Q6_K_BYTES;
+    case GEMMQ_Q3_K_R: return GEMMQ_Q3_K_BYTES;
+    case GEMMQ_Q6_K_R: return GEMMQ_Q6_K_BYTES;
     default: return 0;
   }
 }
 
 // Weight base alignment: blocks of 144 and 176 bytes keep every block 16-byte
-// aligned (the kernels load them with aligned 16-byte loads); the others only
-// need dword alignment of the base.
-uintptr_t fmt_align(int fmt) { return fmt == GEMMQ_Q4_K || fmt == GEMMQ_Q5_K ? 16 : 4; }
+// aligned, and so do the repacked layouts' field arrays (the kernels load them
+// with aligned 16-byte loads); the others only need dword alignment of the base.
+uintptr_t fmt_align(int fmt) {
+  return fmt == GEMMQ_Q4_K || fmt == GEMMQ_Q5_K || fmt == GEMMQ_Q3_K_R || fmt == GEMMQ_Q6_K_R ? 16
+                                                                                                 : 4;
+}
 
 // Launch outcome.  The thread's pending HIP error is cleared just before each
 // launch (see clear_pending), so an error read here belongs to our launch.
@@ -253,7 +258,26 @@ int gemmq_gemm(int fmt, const void* W, const void* Xq, float* Y, int64_t M, int6
   return gemmq_gemm_ex(fmt, W, Xq, Y, M, N, K, GEMMQ_PATH_AUTO, stream);
 }
 
+int gemmq_repack(int fmt, const void* W, void* Wr, int64_t N, int64_t K, void* stream) {
+  if (fmt != GEMMQ_Q3_K && fmt != GEMMQ_Q6_K) return GEMMQ_E_UNSUPPORTED_FORMAT;
+  const int rc = check_weights(fmt, W, N, K);
+  if (rc != GEMMQ_OK) return rc;
+  if (N == 0) return GEMMQ_OK;
+  if (!Wr) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(Wr, 16)) return GEMMQ_E_ALIGNMENT;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(W), b = reinterpret_cast<uintptr_t>(Wr);
+  const uintptr_t bytes = (uintptr_t)gemmq_weight_bytes(fmt, N, K);
+  if (a < b + bytes && b < a + bytes) return GEMMQ_E_INVALID_ARG;  // out of place only
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  clear_pending();
+  return launched(gemmq::launch_repack(fmt, static_cast<const uint8_t*>(W),
+                                       static_cast<uint8_t*>(Wr), N, K,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 int gemmq_decode(int fmt, const void* W, float* Wf, int64_t N, int64_t K, void* stream) {
+  if (fmt == GEMMQ_Q3_K_R || fmt == GEMMQ_Q6_K_R) return GEMMQ_E_UNSUPPORTED_FORMAT;
   const int rc = check_weights(fmt, W, N, K);
   if (rc != GEMMQ_OK) return rc;
   if (N == 0) return GEMMQ_OK;

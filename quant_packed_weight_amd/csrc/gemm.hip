@@ -207,6 +207,13 @@ struct PlaneFmt<14> {
   static constexpr bool kMin = false;
 };
 
+// The repacked q3_K / q6_K layouts (type id + 256, repack.hip): the same
+// planes from aligned loads.
+template <>
+struct PlaneFmt<256 + 11> : PlaneFmt<11> {};
+template <>
+struct PlaneFmt<256 + 14> : PlaneFmt<14> {};
+
 // The raw bytes one thread holds for its (column, part) of a super-block.
 //   q6_K: thread t: column t/4, part p4 = t%4 -> half hh = p4/2, quarters
 //   q = p4%2 (low nibbles of ql bytes 64hh+32q..) and q+2 (their high nibbles).
@@ -388,6 +395,44 @@ __device__ __forceinline__ void store_w(uint8_t* st, const WRegs<10>& r) {
   }
 }
 
+template <>
+struct WRegs<256 + 11> : WRegs<11> {};
+template <>
+struct WRegs<256 + 14> : WRegs<14> {};
+
+// The repacked layouts: block bi of a matrix of NB blocks at m (16-byte aligned)
+//   q6_K: ql[NB][128] | qh[NB][64] | sc[NB][16] | d[NB][2]
+__device__ __forceinline__ void load_w_rp(WRegs<14>& r, const uint8_t* m, int64_t NB, int64_t bi) {
+  const int p4 = threadIdx.x & 3, hh = p4 >> 1, q = p4 & 1;
+  const uint8_t* lp = m + 128 * bi + 64 * hh + 32 * q;
+  const uint8_t* hp = m + 128 * NB + 64 * bi + 32 * hh;
+  const uint4 l0 = ld16a(lp), l1 = ld16a(lp + 16), h0 = ld16a(hp), h1 = ld16a(hp + 16);
+  r.ql[0] = l0.x; r.ql[1] = l0.y; r.ql[2] = l0.z; r.ql[3] = l0.w;
+  r.ql[4] = l1.x; r.ql[5] = l1.y; r.ql[6] = l1.z; r.ql[7] = l1.w;
+  r.qh[0] = h0.x; r.qh[1] = h0.y; r.qh[2] = h0.z; r.qh[3] = h0.w;
+  r.qh[4] = h1.x; r.qh[5] = h1.y; r.qh[6] = h1.z; r.qh[7] = h1.w;
+  const uint8_t* sp = m + 192 * NB + 16 * bi + 8 * hh + 2 * q;
+  r.sc = (uint32_t)ld2(sp) | ((uint32_t)ld2(sp + 4) << 16);
+  r.d = ld2(m + 208 * NB + 2 * bi);
+}
+
+//   q3_K: hmask[NB][32] | qs[NB][64] | scales[NB][12] | d[NB][2]
+__device__ __forceinline__ void load_w_rp(WRegs<11>& r, const uint8_t* m, int64_t NB, int64_t bi) {
+  const int c = threadIdx.x & 3;
+  const uint8_t* qp = m + 32 * NB + 64 * bi + 32 * (c >> 1);
+  const uint4 h0 = ld16a(m + 32 * bi), h1 = ld16a(m + 32 * bi + 16);
+  const uint4 q0 = ld16a(qp), q1 = ld16a(qp + 16);
+  r.hm[0] = h0.x; r.hm[1] = h0.y; r.hm[2] = h0.z; r.hm[3] = h0.w;
+  r.hm[4] = h1.x; r.hm[5] = h1.y; r.hm[6] = h1.z; r.hm[7] = h1.w;
+  r.qs[0] = q0.x; r.qs[1] = q0.y; r.qs[2] = q0.z; r.qs[3] = q0.w;
+  r.qs[4] = q1.x; r.qs[5] = q1.y; r.qs[6] = q1.z; r.qs[7] = q1.w;
+  const uint8_t* sp = m + 96 * NB + 12 * bi;
+  r.sc[0] = ld4(sp);
+  r.sc[1] = ld4(sp + 4);
+  r.sc[2] = ld4(sp + 8);
+  r.d = ld2(m + 108 * NB + 2 * bi);
+}
+
 // q3_K (110-byte blocks, 2-byte aligned: every read stays inside the block)
 __device__ __forceinline__ void load_w(WRegs<11>& r, const uint8_t* wrow, int b) {
   const int c = threadIdx.x & 3;
@@ -500,6 +545,7 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
                                                             const uint8_t* __restrict__ Xq,
                                                             int64_t M, int nb) {
   constexpr bool MIN = PlaneFmt<FMT>::kMin;
+  constexpr bool RP = FMT > 255;  // repacked layout
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
   const uint8_t* __restrict__ W = tm.W;
@@ -523,17 +569,39 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
 
   const uint8_t* xrow = x_row(Xq, m0, M, nb);
   const uint8_t* wrow = w_row<SILU, PlaneFmt<FMT>::kBytes>(W, gt.W[1], n0, N, nb);
+  // repacked: this thread's matrix, the index of its row's first block, and
+  // the blocks in that matrix
+  const uint8_t* wmat = W;
+  int64_t wblk = 0;
+  if constexpr (RP) {
+    int64_t n = n0 + (threadIdx.x >> 2);
+    if constexpr (SILU) {
+      if (n >= N) n = N - 2 + (n & 1);
+      wmat = (n & 1) ? gt.W[1] : W;
+      n >>= 1;
+    } else if (n >= N) {
+      n = N - 1;
+    }
+    wblk = n * nb;
+  }
+  const int64_t NB = (SILU ? N >> 1 : N) * nb;
   XRegs<MIN> xr;
   WRegs<FMT> wr;
+  auto loadw = [&](int b) {
+    if constexpr (RP)
+      load_w_rp(wr, wmat, NB, wblk + b);
+    else
+      load_w(wr, wrow, b);
+  };
   load_x(xr, xrow, 0);
-  load_w(wr, wrow, 0);
+  loadw(0);
   for (int b = 0; b < nb; ++b) {
     store_x(lds, xr);
     store_w(lds, wr);
     __syncthreads();
     if (b + 1 < nb) {  // in flight during the MFMAs below
       load_x(xr, xrow, b + 1);
-      load_w(wr, wrow, b + 1);
+      loadw(b + 1);
     }
     compute<FMT>(lds, y, arow0, bcol, hsel);
     __syncthreads();
@@ -963,6 +1031,10 @@ bool set_lds_limits() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_plane_kernel<11, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
+        hipFuncSetAttribute((const void*)gemm_plane_kernel<256 + 11, SILU>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
+        hipFuncSetAttribute((const void*)gemm_plane_kernel<256 + 14, SILU>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_plane_kernel<10, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_plane_kernel<13, SILU>,
@@ -1014,6 +1086,14 @@ int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t 
       case 13:
         hipLaunchKernelGGL((gemm_plane_kernel<13, SILU>), grid, dim3(256), kLdsMin, st, gt, Xq, M,
                            (int)nb);
+        break;
+      case 256 + 11:
+        hipLaunchKernelGGL((gemm_plane_kernel<256 + 11, SILU>), grid, dim3(256), kLds, st, gt, Xq,
+                           M, (int)nb);
+        break;
+      case 256 + 14:
+        hipLaunchKernelGGL((gemm_plane_kernel<256 + 14, SILU>), grid, dim3(256), kLds, st, gt, Xq,
+                           M, (int)nb);
         break;
       default:
         hipLaunchKernelGGL((gemm_plane_kernel<14, SILU>), grid, dim3(256), kLds, st, gt, Xq, M,

@@ -233,7 +233,8 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
-// FMT: 12 q4_K, 14 q6_K.  MT activation rows computed (>= M).  IT rounds of 16
+// FMT: the GGUF type id (10 q2_K .. 14 q6_K), plus 256 for the repacked q3_K /
+// q6_K layout (repack.hip).  MT activation rows computed (>= M).  IT rounds of 16
 // blocks loaded together.  P rows per round.  KS waves share one row (P = 1):
 // wave w takes rounds w, w + KS, ... and the KS partial sums meet in LDS, added
 // in wave order.  R rows per wave (P = 1), computed side by side on the same
@@ -248,9 +249,11 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
                                                             uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ X, int nb,
                                                             int M) {
+  constexpr bool RP = FMT > 255;  // the repacked layout of q3_K / q6_K
+  constexpr int BF = FMT & 255;   // the block format
   constexpr int SEG = 64 / P;  // lanes that share a row
   constexpr int BPR = 16 / P;  // blocks of a row per round when P > 1
-  constexpr int BB = FMT == 10 ? 84 : FMT == 11 ? 110 : FMT == 12 ? kQ4KBytes : FMT == 13 ? 176
+  constexpr int BB = BF == 10 ? 84 : BF == 11 ? 110 : BF == 12 ? kQ4KBytes : BF == 13 ? 176
                                                                                   : kQ6KBytes;
   constexpr int NW = KS * RG;  // waves of the workgroup
   const int lane = lane_id();
@@ -272,28 +275,35 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
   float* __restrict__ Y = tm.Y;
   const int64_t N = tm.N;
   const int64_t n0 = (int64_t)tm.local * (RG * P * R) + rg * (P * R);  // first row of this wave
-  const uint8_t* wrow[R];
+  const uint8_t* wrow[R];  // the row's first block (block layout)
+  const uint8_t* wmat[R];  // repacked: the row's matrix and its first block index
+  int64_t wblk[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     int64_t n = n0 + prow + r;
     if constexpr (SILU) {
       if (n >= N) n = N - 2 + (n & 1);  // tail pairs: a valid pair, never stored
-      wrow[r] = ((n & 1) ? gt.W[1] : W) + (n >> 1) * nb * BB;
+      wmat[r] = (n & 1) ? gt.W[1] : W;
+      wblk[r] = (n >> 1) * nb;
     } else {
       if (n >= N) n = N - 1;  // tail rows: a valid row, never stored
-      wrow[r] = W + n * nb * BB;
+      wmat[r] = W;
+      wblk[r] = n * nb;
     }
+    wrow[r] = wmat[r] + wblk[r] * BB;
   }
+  // repacked: blocks in the matrix (its field arrays are NB entries long)
+  const int64_t NB = (SILU ? N >> 1 : N) * nb;
 
   // per-lane constants
   // q2_K, q3_K, q4_K, q5_K lane c: values 64c..64c+63, sums 4c..4c+3 (q4_K and
   //   q5_K: sub-blocks 2c, 2c+1; q2_K and q3_K: sub-blocks 4c..4c+3).
   // q6_K lane c = (hh, p) = (c/2, c%2): quarters p and p+2 of half hh, i.e. values
   //   128hh+32p.. and 128hh+32p+64.., sums 8hh+2p, +1 and 8hh+2p+4, +5.
-  const int qoff = FMT != 14 ? 64 * c : 128 * (c >> 1) + 32 * (c & 1);
-  const int qoff2 = FMT != 14 ? 64 * c + 32 : qoff + 64;
-  const int soff = FMT != 14 ? 8 * c : 2 * (8 * (c >> 1) + 2 * (c & 1));
-  const int soff2 = soff + (FMT != 14 ? 4 : 8);
+  const int qoff = BF != 14 ? 64 * c : 128 * (c >> 1) + 32 * (c & 1);
+  const int qoff2 = BF != 14 ? 64 * c + 32 : qoff + 64;
+  const int soff = BF != 14 ? 8 * c : 2 * (8 * (c >> 1) + 2 * (c & 1));
+  const int soff2 = soff + (BF != 14 ? 4 : 8);
 
   float acc[V];
 #pragma unroll
@@ -326,25 +336,39 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
         if (clamp) b = b < nb ? b : nb - 1;
         if (b < nb) {
           const uint8_t* wb = wrow[r] + b * BB;
-          if constexpr (FMT == 12 || FMT == 13) {
-            constexpr int QO = FMT == 12 ? 16 : 48;  // quant (low nibble) bytes
+          if constexpr (BF == 12 || BF == 13) {
+            constexpr int QO = BF == 12 ? 16 : 48;  // quant (low nibble) bytes
             const uint4 h = ld16a(wb);
             const uint4 q0 = ld16a(wb + QO + 32 * c), q1 = ld16a(wb + QO + 16 + 32 * c);
             hd[i][r][0] = h.x; hd[i][r][1] = h.y; hd[i][r][2] = h.z; hd[i][r][3] = h.w;
             wq[i][r][0] = q0.x; wq[i][r][1] = q0.y; wq[i][r][2] = q0.z; wq[i][r][3] = q0.w;
             wq[i][r][4] = q1.x; wq[i][r][5] = q1.y; wq[i][r][6] = q1.z; wq[i][r][7] = q1.w;
-            if constexpr (FMT == 13) {
+            if constexpr (BF == 13) {
               const uint4 h0 = ld16a(wb + 16), h1 = ld16a(wb + 32);
               wh[i][r][0] = h0.x; wh[i][r][1] = h0.y; wh[i][r][2] = h0.z; wh[i][r][3] = h0.w;
               wh[i][r][4] = h1.x; wh[i][r][5] = h1.y; wh[i][r][6] = h1.z; wh[i][r][7] = h1.w;
             }
-          } else if constexpr (FMT == 10) {
+          } else if constexpr (BF == 10) {
             const u32x4 q0 = ld16(wb + 16 + 32 * (c >> 1)), q1 = ld16(wb + 32 + 32 * (c >> 1));
             wq[i][r][0] = q0.x; wq[i][r][1] = q0.y; wq[i][r][2] = q0.z; wq[i][r][3] = q0.w;
             wq[i][r][4] = q1.x; wq[i][r][5] = q1.y; wq[i][r][6] = q1.z; wq[i][r][7] = q1.w;
             hd[i][r][0] = ld4(wb + 4 * c);
             hd[i][r][1] = ld4(wb + 80);
-          } else if constexpr (FMT == 11) {
+          } else if constexpr (BF == 11 && RP) {
+            // hmask[NB][32] | qs[NB][64] | scales[NB][12] | d[NB][2]
+            const uint8_t* m = wmat[r];
+            const int64_t bi = wblk[r] + b;
+            const uint4 h0 = ld16a(m + 32 * bi), h1 = ld16a(m + 32 * bi + 16);
+            const uint8_t* qp = m + 32 * NB + 64 * bi + 32 * (c >> 1);
+            const uint4 q0 = ld16a(qp), q1 = ld16a(qp + 16);
+            wh[i][r][0] = h0.x; wh[i][r][1] = h0.y; wh[i][r][2] = h0.z; wh[i][r][3] = h0.w;
+            wh[i][r][4] = h1.x; wh[i][r][5] = h1.y; wh[i][r][6] = h1.z; wh[i][r][7] = h1.w;
+            wq[i][r][0] = q0.x; wq[i][r][1] = q0.y; wq[i][r][2] = q0.z; wq[i][r][3] = q0.w;
+            wq[i][r][4] = q1.x; wq[i][r][5] = q1.y; wq[i][r][6] = q1.z; wq[i][r][7] = q1.w;
+            const uint8_t* sp = m + 96 * NB + 12 * bi;
+            hd[i][r][0] = ld4(sp); hd[i][r][1] = ld4(sp + 4); hd[i][r][2] = ld4(sp + 8);
+            hd[i][r][3] = ld2(m + 108 * NB + 2 * bi);
+          } else if constexpr (BF == 11) {
             // 110-byte blocks are 2-byte aligned; every read stays in the block
             ld32_a2(wb, wh[i][r]);
             ld32_a2(wb + 32 + 32 * (c >> 1), wq[i][r]);
@@ -352,6 +376,21 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
             ld_dwords_a2<3>(wb + 96, sb);
             hd[i][r][0] = sb[0]; hd[i][r][1] = sb[1]; hd[i][r][2] = sb[2];
             hd[i][r][3] = ld2(wb + 108);
+          } else if constexpr (RP) {
+            // q6_K repacked: ql[NB][128] | qh[NB][64] | sc[NB][16] | d[NB][2]
+            const int hh = c >> 1, p = c & 1;
+            const uint8_t* m = wmat[r];
+            const int64_t bi = wblk[r] + b;
+            const uint8_t* lp = m + 128 * bi + 64 * hh + 32 * p;
+            const uint8_t* hp = m + 128 * NB + 64 * bi + 32 * hh;
+            const uint4 l0 = ld16a(lp), l1 = ld16a(lp + 16), h0 = ld16a(hp), h1 = ld16a(hp + 16);
+            wq[i][r][0] = l0.x; wq[i][r][1] = l0.y; wq[i][r][2] = l0.z; wq[i][r][3] = l0.w;
+            wq[i][r][4] = l1.x; wq[i][r][5] = l1.y; wq[i][r][6] = l1.z; wq[i][r][7] = l1.w;
+            wh[i][r][0] = h0.x; wh[i][r][1] = h0.y; wh[i][r][2] = h0.z; wh[i][r][3] = h0.w;
+            wh[i][r][4] = h1.x; wh[i][r][5] = h1.y; wh[i][r][6] = h1.z; wh[i][r][7] = h1.w;
+            const uint8_t* sp = m + 192 * NB + 16 * bi + 8 * hh + 2 * p;
+            hd[i][r][0] = (uint32_t)ld2(sp) | ((uint32_t)ld2(sp + 4) << 16);
+            hd[i][r][1] = ld2(m + 208 * NB + 2 * bi);
           } else {
             const int hh = c >> 1, p = c & 1;
             ld32_a2(wb + 64 * hh + 32 * p, wq[i][r]);
@@ -370,7 +409,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     for (int i = 0; i < IT; ++i) {
       const int b = s0 + bl0 + 16 * i;
       if (b >= nb) break;
-      if constexpr (FMT == 12 || FMT == 13) {
+      if constexpr (BF == 12 || BF == 13) {
         // scales and mins of sub-blocks 2c and 2c+1 as byte pairs (q5_K: the
         // same header; its quants add the high bits 2c and 2c+1 as bit 4)
         int sc0[R], sc1[R];
@@ -398,7 +437,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
           for (int k = 0; k < 8; ++k) {
             lo[r][k] = lo_nib(wq[i][r][k]);
             hi[r][k] = hi_nib(wq[i][r][k]);
-            if constexpr (FMT == 13) {
+            if constexpr (BF == 13) {
               lo[r][k] |= ((wh[i][r][k] >> (2 * c)) & 0x01010101u) << 4;
               hi[r][k] |= ((wh[i][r][k] >> (2 * c + 1)) & 0x01010101u) << 4;
             }
@@ -418,7 +457,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
             acc[r * MT + m] = fmaf(x.d, t, acc[r * MT + m]);
           }
         }
-      } else if constexpr (FMT == 10 || FMT == 11) {
+      } else if constexpr (BF == 10 || BF == 11) {
         // sub-blocks 4c + g, g = 0..3, against activation runs a0, a1, b0, b1:
         // quarter 2(c&1) + g/2 of half c/2, bytes 16(g&1)..16(g&1)+15 of it
         uint32_t qg[R][4][4];
@@ -433,12 +472,12 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
               uint32_t v = (wq[i][r][4 * (g & 1) + k] >> (2 * qq)) & 0x03030303u;
-              if constexpr (FMT == 11)  // q + 4 in 0..7: the mask bit adds 4
+              if constexpr (BF == 11)  // q + 4 in 0..7: the mask bit adds 4
                 v |= ((wh[i][r][4 * (g & 1) + k] >> (4 * (c >> 1) + qq)) & 0x01010101u) << 2;
               qg[r][g][k] = v;
             }
           }
-          if constexpr (FMT == 10) {
+          if constexpr (BF == 10) {
             const uint32_t w = hd[i][r][0];
 #pragma unroll
             for (int g = 0; g < 4; ++g) sg[r][g] = (int)((w >> (8 * g)) & 15u);
@@ -471,7 +510,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
                       __mul24(sg[r][3], dot16(qg[r][3], x.b1, 0));
             const int isum = dot2(x.s0, mp0[r], dot2(x.s1, mp1[r], 0));
             float t;
-            if constexpr (FMT == 10) {
+            if constexpr (BF == 10) {
               t = d[r] * (float)isc;
               t = fmaf(-dmin[r], (float)isum, t);
             } else {
@@ -718,7 +757,10 @@ int launch_any(int fmt, const Group& g, uint8_t* Xq, const float* X, int M, int6
     case 11: return launch_fmt<11, SILU>(g, Xq, X, M, (int)nb, st);
     case 12: return launch_fmt<12, SILU>(g, Xq, X, M, (int)nb, st);
     case 13: return launch_fmt<13, SILU>(g, Xq, X, M, (int)nb, st);
-    default: return launch_fmt<14, SILU>(g, Xq, X, M, (int)nb, st);
+    case 14: return launch_fmt<14, SILU>(g, Xq, X, M, (int)nb, st);
+    case 256 + 11: return launch_fmt<256 + 11, SILU>(g, Xq, X, M, (int)nb, st);
+    case 256 + 14: return launch_fmt<256 + 14, SILU>(g, Xq, X, M, (int)nb, st);
+    default: return -1;
   }
 }
 

@@ -103,5 +103,7 @@ int launch_gemm_silu(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int6
                      hipStream_t st);
 
 int launch_decode(int fmt, const uint8_t* W, float* Wf, int64_t N, int64_t K, hipStream_t st);
+// q3_K (11) / q6_K (14) matrix -> its repacked layout (same size)
+int launch_repack(int fmt, const uint8_t* W, uint8_t* out, int64_t N, int64_t K, hipStream_t st);
 
 }  // namespace gemmq

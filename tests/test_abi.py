@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_exported(L):
     names = _declared()
-    assert len(names) == 13
+    assert len(names) == 14
     assert set(names) == set(gq.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 5
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 6
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -50,6 +50,7 @@ def test_version_and_status_names(L):
 
 def test_size_helpers(L):
     assert [gq.block_bytes(f) for f in range(9, 16)] == [0, 84, 110, 144, 176, 210, 0]
+    assert [gq.block_bytes(256 + f) for f in range(9, 16)] == [0, 0, 110, 0, 0, 210, 0]
     assert gq.weight_bytes(12, 4096, 4096) == 4096 * 16 * 144
     assert gq.weight_bytes(14, 151936, 2048) == 255252480
     assert gq.weight_bytes(12, 10, 300) == 0 and gq.weight_bytes(12, -1, 256) == 0
@@ -223,3 +224,27 @@ def test_product_path_never_imports_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"import\s+oracle|from\s+oracle|liboracle|oracle[./]", text), f
+
+
+@pytest.mark.parametrize("args,status", [
+    ((12, FAKE16, FAKE16 * 4, 1, 256), -2),          # q4_K has no repacked layout
+    ((256 + 14, FAKE16, FAKE16 * 4, 1, 256), -2),    # already repacked
+    ((14, FAKE16, FAKE16 * 4, 1, 300), -3),          # K % 256 != 0
+    ((14, FAKE16, FAKE16 * 4, -1, 256), -1),         # N < 0
+    ((14, None, FAKE16 * 4, 1, 256), -1),            # null W
+    ((14, FAKE16, None, 1, 256), -1),                # null Wr
+    ((14, FAKE16 + 2, FAKE16 * 4, 1, 256), -4),      # W not 4-byte aligned
+    ((14, FAKE16, FAKE16 * 4 + 4, 1, 256), -4),      # Wr not 16-byte aligned
+    ((14, FAKE16, FAKE16 + 16, 1, 256), -1),         # overlapping buffers
+    ((11, FAKE16, FAKE16 * 4, 0, 256), 0),           # N = 0: empty
+])
+def test_repack_validation(L, args, status):
+    assert L.gemmq_repack(*args, None) == status
+
+
+def test_repacked_formats_accepted_except_decode(L):
+    # a repacked format validates like any weight format (16-byte aligned base)
+    # and is refused only by the diagnostic decode
+    assert L.gemmq_gemm(256 + 14, FAKE16 + 4, FAKE16, FAKE16, 1, 1, 256, None) == -4
+    assert L.gemmq_gemm(256 + 11, FAKE16, FAKE16, FAKE16, 1, 1, 300, None) == -3
+    assert L.gemmq_decode(256 + 14, FAKE16, FAKE16, 1, 256, None) == -2
