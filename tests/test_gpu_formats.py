@@ -211,3 +211,17 @@ def test_silu_mul(dev, gq, orc, fmt, M, K, N):
     y = to_host(y).astype(np.float64)
     bound = 8 * 2.0 ** -24 * np.abs(ref) + np.abs(G * U) * 2.0 ** -126 + 2.0 ** -149
     assert (np.abs(y - ref) <= bound).all()
+
+
+@pytest.mark.parametrize("fmt", [Q2, Q3, Q5, 12, 14])
+@pytest.mark.parametrize("path", [1, 2])
+def test_longest_rows(dev, gq, orc, fmt, path):
+    # K at the library's limit (2^24, one row of 65536 super-blocks): the GEMV's
+    # looping four-wave split and the GEMM's K loop (split in two for q4_K)
+    K = 1 << 24
+    M, N = (1, 3) if path == 1 else (9, 2)
+    log("longest rows fmt=%d path=%d M=%d N=%d K=%d" % (fmt, path, M, N, K))
+    rng = np.random.default_rng(fmt + path)
+    W = synth.make_weights(rng, fmt, N, K)
+    xq = orc.quantize_q8K(synth.make_activations(rng, M, K, True))
+    _check(gq, orc, fmt, W, xq, M, N, K, path, "K=2^24")

@@ -19,11 +19,17 @@ def test_graph_replays_match_eager():
 
     device()
     rng = np.random.default_rng(99)
+    # every format, and the repacked layouts (repacked once, before capture)
     cases = [(gq.FMT_Q4K, 1, 640, 1024), (gq.FMT_Q6K, 1, 300, 768),
-             (gq.FMT_Q4K, 40, 200, 512), (gq.FMT_Q6K, 130, 96, 1024)]
+             (gq.FMT_Q4K, 40, 200, 512), (gq.FMT_Q6K, 130, 96, 1024),
+             (gq.FMT_Q2K, 1, 100, 2048), (gq.FMT_Q3K, 3, 70, 512), (gq.FMT_Q5K, 1, 129, 4096),
+             (gq.FMT_Q2K, 33, 64, 512), (gq.FMT_Q3K, 40, 65, 1024), (gq.FMT_Q5K, 64, 100, 768),
+             (gq.FMT_Q6K_R, 1, 200, 3072), (gq.FMT_Q3K_R, 50, 90, 1024)]
     bufs = []
     for fmt, M, N, K in cases:
-        W = torch.from_numpy(synth.make_weights(rng, fmt, N, K)).cuda()
+        W = torch.from_numpy(synth.make_weights(rng, fmt & 255, N, K)).cuda()
+        if fmt > 255:
+            W = gq.repack(fmt & 255, W, N, K)
         X = torch.from_numpy(synth.make_activations(rng, M, K, True)).cuda()
         Xq = torch.empty(gq.q8K_bytes(M, K), dtype=torch.uint8, device="cuda")
         Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
