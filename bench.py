@@ -29,8 +29,9 @@ Output: one JSON line.  `value` is the M=1 weight throughput of the whole step
 `roofline` / `roofline_m512` give the dominant kernels' algorithmic rate from
 HIP events around batches of back-to-back launches against the MI355X peaks
 (HBM 8 TB/s; dense int8 MFMA 5.0 POP/s) and against ceilings measured on the
-same GPU (`ceilings`: a plain 1 GiB device copy, and the vendor library's plain
-int8 GEMM at the largest matrix's shape); `cpu_baseline` times the CPU oracle
+same GPU (`ceilings`: a plain 1 GiB device copy, the library's int8 MFMA-only
+loop with the shader clock it ran at, and the vendor library's plain int8 GEMM
+at the largest matrix's shape); `cpu_baseline` times the CPU oracle
 on a bounded sample, on all host cores and on one.
 """
 from __future__ import annotations
@@ -283,12 +284,34 @@ def profiled_traffic(fam, launches):
 
 def measured_ceilings(wl):
     """Ceilings measured on this GPU beside the datasheet peaks: a plain 1 GiB
-    device-to-device copy (read + write bytes), and a plain int8 GEMM from the
-    vendor library (torch._int_mm, int8 x int8 -> int32, no quantized format) at
-    the largest matrix's shape with M = 512."""
+    device-to-device copy (read + write bytes); the library's int8 MFMA-only
+    loop (gemmq_probe_mfma_i8: independent accumulator chains, no memory
+    traffic), with the shader clock it ran at from its in-kernel counters; and
+    a plain int8 GEMM from the vendor library (torch._int_mm, int8 x int8 ->
+    int32, no quantized format) at the largest matrix's shape with M = 512."""
     import torch
 
+    import quant_packed_weight_amd as gq
+
     out = {}
+    # MFMA-only loop: 2048 workgroups (8 per CU, two waves per SIMD), ~5 ms
+    blocks, iters = 2048, 10000
+    gq.probe_mfma_i8(100, blocks)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _, clocks, nops = gq.probe_mfma_i8(iters, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) * 1e-3
+        cyc, ticks = (int(v) for v in clocks.cpu())
+        if best is None or dt < best[0]:
+            best = (dt, nops, cyc, ticks)
+    dt, nops, cyc, ticks = best
+    out["mfma_i8_TOPs"] = round(nops / dt / 1e12, 1)
+    out["mfma_i8_clock_GHz"] = round(cyc / ticks * 0.1, 3) if ticks > 0 else None
     n = GIB
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
@@ -510,10 +533,14 @@ def main():
         res["roofline_m%d" % M2] = roof(M2)
     c = res["ceilings"] = measured_ceilings(wl)
     c["copy_frac_of_peak"] = round(c["copy_GBs"] / HBM_PEAK_GBS, 4)
+    c["mfma_i8_frac_of_peak"] = round(c["mfma_i8_TOPs"] / INT8_PEAK_TOPS, 4)
     if c.get("int8_gemm_TOPs"):
         c["int8_gemm_frac_of_peak"] = round(c["int8_gemm_TOPs"] / INT8_PEAK_TOPS, 4)
     # the kernels against the measured ceilings as well as the datasheet peaks
     res["roofline"]["frac_of_measured_copy"] = round(res["roofline"]["achieved"] / c["copy_GBs"], 4)
+    if M2:
+        res["roofline_m%d" % M2]["frac_of_measured_mfma"] = round(
+            res["roofline_m%d" % M2]["achieved"] / c["mfma_i8_TOPs"], 4)
     if M2 and c.get("int8_gemm_TOPs"):
         res["roofline_m%d" % M2]["vs_int8_gemm_library"] = round(
             res["roofline_m%d" % M2]["achieved"] / c["int8_gemm_TOPs"], 4)

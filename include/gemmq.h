@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 6
+#define GEMMQ_ABI_VERSION 7
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q2_K 10
@@ -248,6 +248,28 @@ int gemmq_repack(int fmt, const void *W, void *Wr, int64_t N, int64_t K, void *s
  * q3_K and q6_K weights are exact.  Errors as gemmq_gemm.
  */
 int gemmq_decode(int fmt, const void *W, float *Wf, int64_t N, int64_t K, void *stream);
+
+/*
+ * Measurement export: the int8 matrix-core ceiling the matmul kernels are read
+ * against.  Never used on the compute path.  Launches `blocks` workgroups of
+ * four waves; each wave runs `iters` rounds of GEMMQ_PROBE_CHAINS independent
+ * v_mfma_i32_32x32x32_i8 (32 x 32 x 32 int8 multiply-adds each) on register
+ * operands, with no memory traffic, so the time of the launch gives the
+ * sustained dense int8 MFMA rate:
+ *   int8 ops = 2 * 32768 * GEMMQ_PROBE_CHAINS * 4 * blocks * iters.
+ *   iters   >= 1.  blocks in 1..65535.
+ *   out     device, int32 [blocks * 256], 4-byte aligned; each lane's sum of its
+ *           accumulators (keeps the work live; identical in every workgroup).
+ *   clocks  device, uint64 [2], 8-byte aligned: shader-clock cycles
+ *           (s_memtime) and 100 MHz counter ticks (s_memrealtime) across the
+ *           loop of the first wave, so cycles / ticks * 100 MHz is the shader
+ *           clock the loop ran at.
+ * Errors: GEMMQ_E_INVALID_ARG (null pointer, iters < 1, blocks out of range),
+ * GEMMQ_E_ALIGNMENT, GEMMQ_E_DEVICE, GEMMQ_E_LAUNCH.
+ */
+#define GEMMQ_PROBE_CHAINS 4
+int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t *out, uint64_t *clocks,
+                        void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     PATH_AUTO,
     PATH_GEMM,
     PATH_GEMV,
+    PROBE_CHAINS,
     Q8K_BYTES,
     QK,
     GemmqError,
@@ -36,6 +37,7 @@ from ._lib import (  # noqa: F401
     linear_group,
     linear_group_ptr,
     linear_silu_mul,
+    probe_mfma_i8,
     q8K_bytes,
     quantize_q8K,
     repack,

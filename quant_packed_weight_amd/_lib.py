@@ -24,7 +24,8 @@ Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
-ABI_VERSION = 6
+ABI_VERSION = 7
+PROBE_CHAINS = 4  # GEMMQ_PROBE_CHAINS
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 
@@ -49,6 +50,7 @@ EXPORTS = {
     "gemmq_linear_silu_mul": (_I, [_I, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "gemmq_repack": (_I, [_I, _P, _P, _I64, _I64, _P]),
+    "gemmq_probe_mfma_i8": (_I, [_I64, _I64, _P, _P, _P]),
 }
 
 
@@ -301,3 +303,14 @@ def repack(fmt, w, N, K, out=None, stream=None):
     _check(lib().gemmq_repack(fmt, _dev(w, "w", torch.uint8), _dev(out, "out", torch.uint8), N, K,
                               _stream(stream)), "gemmq_repack")
     return out
+
+
+def probe_mfma_i8(iters, blocks, stream=None):
+    """Enqueue the int8 MFMA ceiling loop (gemmq_probe_mfma_i8); returns the
+    (out, clocks) device tensors and the int8 operation count of the launch."""
+    torch = _torch()
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _check(lib().gemmq_probe_mfma_i8(iters, blocks, out.data_ptr(), clocks.data_ptr(),
+                                     _stream(stream)), "gemmq_probe_mfma_i8")
+    return out, clocks, 2 * 32768 * PROBE_CHAINS * 4 * blocks * iters

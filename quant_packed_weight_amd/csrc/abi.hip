@@ -12,6 +12,12 @@
 #include "gemmq.h"
 #include "launch.h"
 
+namespace gemmq {
+// probe.hip: the int8 MFMA ceiling (independent accumulator chains per wave)
+int probe_mfma_chains();
+int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk, hipStream_t st);
+}  // namespace gemmq
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -288,6 +294,18 @@ int gemmq_decode(int fmt, const void* W, float* Wf, int64_t N, int64_t K, void* 
   clear_pending();
   return launched(gemmq::launch_decode(fmt, static_cast<const uint8_t*>(W), Wf, N, K,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clocks,
+                        void* stream) {
+  if (!out || !clocks || iters < 1 || blocks < 1 || blocks > 65535) return GEMMQ_E_INVALID_ARG;
+  if (!aligned(out, 4) || !aligned(clocks, 8)) return GEMMQ_E_ALIGNMENT;
+  if (gemmq::probe_mfma_chains() != GEMMQ_PROBE_CHAINS) return GEMMQ_E_LAUNCH;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  clear_pending();
+  return launched(
+      gemmq::launch_probe_mfma(iters, blocks, out, clocks, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,0 +1,65 @@
+// probe.hip -- a measured ceiling for the matmul kernels: int8 MFMAs with no
+// memory traffic or vector work, and the shader clock they run at.
+//
+// Every wave keeps kChains independent accumulator chains of
+// v_mfma_i32_32x32x32_i8 on register operands, so the matrix cores never wait
+// on a result; the achieved rate is the sustained dense int8 MFMA throughput of
+// the GPU as it is clocked under that load, the denominator against which the
+// GEMM's own rate is best read (the datasheet figure assumes the peak engine
+// clock).  Wave 0 of workgroup 0 reads the shader-clock counter (s_memtime) and
+// the constant 100 MHz counter (s_memrealtime) around its loop, so the host can
+// derive the clock the loop ran at.
+#include "launch.h"
+
+namespace gemmq {
+
+namespace {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kChains = 4;
+
+__global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, int32_t* __restrict__ out,
+                                                         uint64_t* __restrict__ clk) {
+  const int t = (int)threadIdx.x;
+  v4i a = {t, 7 * t + 1, 13 * t + 2, 29 * t + 3};
+  v4i b = {3 * t + 5, 11 * t + 7, 17 * t + 9, 23 * t + 11};
+  asm volatile("" : "+v"(a), "+v"(b));  // operands the compiler cannot fold
+  v16i c[kChains];
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) c[k] = (v16i){0};
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) c[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[k], 0, 0, 0);
+  }
+  // the sum reads every accumulator, so it waits for the last MFMAs
+  int32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kChains; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[k][r];
+  asm volatile("" ::"v"(s));
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  out[(int64_t)blockIdx.x * 256 + t] = s;
+  if (blockIdx.x == 0 && t == 0) {
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
+}
+
+}  // namespace
+
+int probe_mfma_chains() { return kChains; }
+
+int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk,
+                      hipStream_t st) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3((uint32_t)blocks), dim3(256), 0, st, iters, out,
+                     clk);
+  return 0;
+}
+
+}  // namespace gemmq

@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_exported(L):
     names = _declared()
-    assert len(names) == 14
+    assert len(names) == 15
     assert set(names) == set(gq.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 6
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 7
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -248,3 +248,16 @@ def test_repacked_formats_accepted_except_decode(L):
     assert L.gemmq_gemm(256 + 14, FAKE16 + 4, FAKE16, FAKE16, 1, 1, 256, None) == -4
     assert L.gemmq_gemm(256 + 11, FAKE16, FAKE16, FAKE16, 1, 1, 300, None) == -3
     assert L.gemmq_decode(256 + 14, FAKE16, FAKE16, 1, 256, None) == -2
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 1, FAKE16, FAKE16), -1),        # iters < 1
+    ((1, 0, FAKE16, FAKE16), -1),        # no workgroups
+    ((1, 65536, FAKE16, FAKE16), -1),    # too many workgroups
+    ((1, 1, None, FAKE16), -1),
+    ((1, 1, FAKE16, None), -1),
+    ((1, 1, FAKE16 + 2, FAKE16), -4),    # out needs 4 B
+    ((1, 1, FAKE16, FAKE16 + 4), -4),    # clocks need 8 B
+])
+def test_probe_validation(L, args, status):
+    assert L.gemmq_probe_mfma_i8(*args, None) == status
