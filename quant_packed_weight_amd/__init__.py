@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     PATH_AUTO,
     PATH_GEMM,
     PATH_GEMV,
+    PATH_SKINNY,
     PROBE_CHAINS,
     Q8K_BYTES,
     QK,

@@ -22,7 +22,7 @@ BLOCK_BYTES = {FMT_Q2K: 84, FMT_Q3K: 110, FMT_Q4K: 144, FMT_Q5K: 176, FMT_Q6K: 2
                FMT_Q3K_R: 110, FMT_Q6K_R: 210}
 Q8K_BYTES = 292
 QK = 256
-PATH_AUTO, PATH_GEMV, PATH_GEMM = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SKINNY = 0, 1, 2, 3
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
 ABI_VERSION = 7
 PROBE_CHAINS = 4  # GEMMQ_PROBE_CHAINS

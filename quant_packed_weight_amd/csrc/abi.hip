@@ -16,11 +16,18 @@ namespace gemmq {
 // probe.hip: the int8 MFMA ceiling (independent accumulator chains per wave)
 int probe_mfma_chains();
 int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk, hipStream_t st);
+// skinny.hip: the small-M q4_K MFMA kernel
+bool skinny_fits(int fmt, int64_t M);
+int launch_skinny(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
+int launch_skinny_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
+                       hipStream_t st);
 }  // namespace gemmq
 
 namespace {
 
 constexpr int kMaxDevices = 64;
+// activation rows the small-M MFMA kernel takes (automatic choice: from 4)
+constexpr int64_t kSkinnyMinM = 4, kSkinnyMaxM = 16;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 int check_device() {
@@ -148,9 +155,12 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
   }
   if (M < 0) return GEMMQ_E_INVALID_ARG;
   if (M > kMaxRows || rows > kMaxRows) return GEMMQ_E_SHAPE;
-  if (path != GEMMQ_PATH_AUTO && path != GEMMQ_PATH_GEMV && path != GEMMQ_PATH_GEMM)
+  if (path != GEMMQ_PATH_AUTO && path != GEMMQ_PATH_GEMV && path != GEMMQ_PATH_GEMM &&
+      path != GEMMQ_PATH_SKINNY)
     return GEMMQ_E_INVALID_ARG;
   if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
+  if (path == GEMMQ_PATH_SKINNY && fmt != GEMMQ_Q4_K) return GEMMQ_E_UNSUPPORTED_FORMAT;
+  if (path == GEMMQ_PATH_SKINNY && M > kSkinnyMaxM) return GEMMQ_E_SHAPE;
   if (M == 0 || rows == 0) return GEMMQ_OK;
   for (int i = 0; i < count; ++i)
     if (N[i] > 0 && !Y[i]) return GEMMQ_E_INVALID_ARG;
@@ -167,8 +177,21 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
   return GEMMQ_OK;
 }
 
-bool use_gemv(int path, int64_t M) {
-  return path == GEMMQ_PATH_GEMV || (path == GEMMQ_PATH_AUTO && M <= 8);
+// The kernel family a call runs on.  The automatic choice follows the measured
+// crossovers on the Qwen3-8B layer: the decode GEMV up to M = 8 (q4_K: up to
+// M = 3), the small-M MFMA kernel for q4_K at 4 <= M <= 16, the GEMM beyond.
+int pick_path(int fmt, int path, int64_t M) {
+  if (path != GEMMQ_PATH_AUTO) return path;
+  if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) return GEMMQ_PATH_SKINNY;
+  return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
+}
+
+
+int launch_matmul(int fmt, int path, const gemmq::Group& g, const uint8_t* xq, int64_t M,
+                  int64_t K, hipStream_t st) {
+  if (path == GEMMQ_PATH_GEMV) return gemmq::launch_gemv(fmt, g, xq, (int)M, K, st);
+  if (path == GEMMQ_PATH_SKINNY) return gemmq::launch_skinny(fmt, g, xq, (int)M, K, st);
+  return gemmq::launch_gemm(fmt, g, xq, M, K, st);
 }
 
 }  // namespace
@@ -189,8 +212,7 @@ int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
   const uint8_t* xq = static_cast<const uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_pending();
-  if (use_gemv(path, M)) return launched(gemmq::launch_gemv(fmt, g, xq, (int)M, K, st));
-  return launched(gemmq::launch_gemm(fmt, g, xq, M, K, st));
+  return launched(launch_matmul(fmt, pick_path(fmt, path, M), g, xq, M, K, st));
 }
 
 int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y,
@@ -206,14 +228,13 @@ int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y
   if (dv != GEMMQ_OK) return dv;
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool gemv = use_gemv(path, M);
+  const int p = pick_path(fmt, path, M);
   clear_pending();
-  if (rows > 0 && gemv && gemmq::gemv_fusable(M, K))
+  if (rows > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
     return launched(gemmq::launch_gemv_fused(fmt, g, X, xq, (int)M, K, st));
   rc = launched(gemmq::launch_quantize_q8K(X, xq, M, K, st));
   if (rc != GEMMQ_OK || rows == 0) return rc;
-  if (gemv) return launched(gemmq::launch_gemv(fmt, g, xq, (int)M, K, st));
-  return launched(gemmq::launch_gemm(fmt, g, xq, M, K, st));
+  return launched(launch_matmul(fmt, p, g, xq, M, K, st));
 }
 
 int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* X, void* Xq,
@@ -223,9 +244,12 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
   if (rc != GEMMQ_OK) return rc;
   if (M < 0) return GEMMQ_E_INVALID_ARG;
   if (M > kMaxRows || 2 * N > kMaxRows) return GEMMQ_E_SHAPE;
-  if (path != GEMMQ_PATH_AUTO && path != GEMMQ_PATH_GEMV && path != GEMMQ_PATH_GEMM)
+  if (path != GEMMQ_PATH_AUTO && path != GEMMQ_PATH_GEMV && path != GEMMQ_PATH_GEMM &&
+      path != GEMMQ_PATH_SKINNY)
     return GEMMQ_E_INVALID_ARG;
   if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
+  if (path == GEMMQ_PATH_SKINNY && fmt != GEMMQ_Q4_K) return GEMMQ_E_UNSUPPORTED_FORMAT;
+  if (path == GEMMQ_PATH_SKINNY && M > kSkinnyMaxM) return GEMMQ_E_SHAPE;
   if (M == 0) return GEMMQ_OK;
   if (!X || !Xq || (N > 0 && !Y)) return GEMMQ_E_INVALID_ARG;
   if (!aligned(X, 16) || !aligned(Xq, 4) || (N > 0 && !aligned(Y, 4))) return GEMMQ_E_ALIGNMENT;
@@ -239,13 +263,16 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
   g.N[0] = g.N[1] = N;
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool gemv = use_gemv(path, M);
+  const int p = pick_path(fmt, path, M);  // the path gemmq_linear_group takes
   clear_pending();
-  if (N > 0 && gemv && gemmq::gemv_fusable(M, K))
+  if (N > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
     return launched(gemmq::launch_gemv_silu(fmt, g, nullptr, X, xq, (int)M, K, st));
   rc = launched(gemmq::launch_quantize_q8K(X, xq, M, K, st));
   if (rc != GEMMQ_OK || N == 0) return rc;
-  if (gemv) return launched(gemmq::launch_gemv_silu(fmt, g, xq, nullptr, nullptr, (int)M, K, st));
+  if (p == GEMMQ_PATH_GEMV)
+    return launched(gemmq::launch_gemv_silu(fmt, g, xq, nullptr, nullptr, (int)M, K, st));
+  if (p == GEMMQ_PATH_SKINNY)
+    return launched(gemmq::launch_skinny_silu(fmt, g, xq, (int)M, K, st));
   return launched(gemmq::launch_gemm_silu(fmt, g, xq, M, K, st));
 }
 

@@ -1,7 +1,7 @@
 """GPU: the gated up-projection silu(Wg x) * (Wu x) in one call
 (gemmq_linear_silu_mul), on every route: the fused quantize + GEMV launch, the
-plain GEMV (long rows, M up to 8), the MFMA GEMM with and without the split K
-loop, ragged tiles, and N = 0.
+plain GEMV (long rows, M up to 8), the small-M MFMA kernel (q4_K, M 4..16),
+the MFMA GEMM with and without the split K loop, ragged tiles, and N = 0.
 
 Three checks per case:
   * the q8_K bytes equal the oracle's quantizer, bit for bit;
@@ -67,7 +67,10 @@ CASES = [
     (5, 1024, 100, 0, 1.0),      # M > 4: two launches
     (8, 4096, 257, 1, 1.0),      # GEMV forced at its largest M
     (2, 8192, 129, 1, 1.0),
-    (9, 1024, 65, 0, 1.0),       # automatic path takes the GEMM from M = 9
+    (9, 1024, 65, 0, 1.0),       # automatic path: q4_K small-M MFMA kernel, q6_K GEMM
+    (8, 4096, 257, 0, 1.0),      # q4_K: small-M MFMA kernel (eight waves a row)
+    (16, 12288, 70, 0, 2.0),     # q4_K: small-M MFMA kernel, two super-blocks a wave
+    (5, 256, 1, 0, 1.0),         # q4_K: small-M MFMA kernel, one output column
     (40, 1024, 300, 0, 2.0),     # ragged last tile
     (130, 4096, 200, 0, 1.0),    # several row tiles of M
     (40, 8192, 129, 0, 1.0),     # split K loop
