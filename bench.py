@@ -6,7 +6,8 @@ for each activation width K, quantize X to q8_K, then run every matrix of the
 layer through the packed matmul.  The default workload is the Qwen3-8B-shaped
 layer (q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 12288x4096, down
 4096x12288, all q4_K; 108,527,616 weight bytes), run at M = 1 (decode GEMV,
-weight GB/s) and M = 512 (prefill GEMM, int8 TOP/s).
+weight GB/s), M = 512 (prefill GEMM, int8 TOP/s) and M = 8 (batched decode on
+the small-M MFMA kernel, weight GB/s, reported as `batched_decode_m8`).
 
 Each matrix reads the activation of its place in the layer (q/k/v the attention
 input, o the attention output, gate/up the MLP input, down the MLP activation),
@@ -58,7 +59,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qwen3-8b-q4K")
-    p.add_argument("--m", type=int, nargs="+", default=[1, 512],
+    p.add_argument("--m", type=int, nargs="+", default=[1, 512, 8],
                    help="activation rows; the first is the headline (value), the second secondary")
     p.add_argument("--copies", type=int, default=0, help="rotating weight copies (0: auto, >=1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -477,7 +478,8 @@ def main():
         n_l = len(per)
         tot_t = sum(dt for _, dt, _ in per.values())
         fused = [k for k, (_, _, f) in per.items() if f]
-        kname = "gemv_kernel" if M <= 8 else "gemm_q4k_kernel"
+        kname = ("gemv_kernel" if M <= 3 else "skinny_q4k_kernel" if M <= 16
+                 else "gemm_q4k_kernel")
         if fused:
             kname += " (quantizer fused into: %s)" % ", ".join(fused)
         if M <= 8:
@@ -531,6 +533,15 @@ def main():
         res["secondary"] = {"metric": "int8 TOP/s at M=%d" % M2,
                             "value": round(ops[M2] / t[M2] / 1e12, 1), "unit": "TOP/s"}
         res["roofline_m%d" % M2] = roof(M2)
+    for M in Ms[2:]:
+        # further M (batched decode): the pass's weight throughput and its launches
+        per = rates[M]
+        res["batched_decode_m%d" % M] = {
+            "M": M, "value": round(wbytes / t[M] / 1e9, 1), "unit": "GB/s",
+            "us_per_pass": round(t[M] * 1e6, 2),
+            "int8_TOPs": round(ops[M] / t[M] / 1e12, 2),
+            "per_launch_GBs": {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
+                               for k, (ms, dt, _) in per.items()}}
     c = res["ceilings"] = measured_ceilings(wl)
     c["copy_frac_of_peak"] = round(c["copy_GBs"] / HBM_PEAK_GBS, 4)
     c["mfma_i8_frac_of_peak"] = round(c["mfma_i8_TOPs"] / INT8_PEAK_TOPS, 4)
