@@ -7,7 +7,8 @@ layer through the packed matmul.  The default workload is the Qwen3-8B-shaped
 layer (q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 12288x4096, down
 4096x12288, all q4_K; 108,527,616 weight bytes), run at M = 1 (decode GEMV,
 weight GB/s), M = 512 (prefill GEMM, int8 TOP/s) and M = 8 (batched decode on
-the small-M MFMA kernel, weight GB/s, reported as `batched_decode_m8`).
+the small-M MFMA kernel, weight GB/s, reported as `batched_decode_m8`) and
+M = 2048 (prefill, reported as `prefill_m2048`).
 
 Each matrix reads the activation of its place in the layer (q/k/v the attention
 input, o the attention output, gate/up the MLP input, down the MLP activation),
@@ -59,7 +60,7 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="qwen3-8b-q4K")
-    p.add_argument("--m", type=int, nargs="+", default=[1, 512, 8],
+    p.add_argument("--m", type=int, nargs="+", default=[1, 512, 8, 2048],
                    help="activation rows; the first is the headline (value), the second secondary")
     p.add_argument("--copies", type=int, default=0, help="rotating weight copies (0: auto, >=1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -534,14 +535,19 @@ def main():
                             "value": round(ops[M2] / t[M2] / 1e12, 1), "unit": "TOP/s"}
         res["roofline_m%d" % M2] = roof(M2)
     for M in Ms[2:]:
-        # further M (batched decode): the pass's weight throughput and its launches
+        # the rest of the M sweep: batched decode (weight GB/s) or prefill (int8 TOP/s)
         per = rates[M]
-        res["batched_decode_m%d" % M] = {
-            "M": M, "value": round(wbytes / t[M] / 1e9, 1), "unit": "GB/s",
-            "us_per_pass": round(t[M] * 1e6, 2),
-            "int8_TOPs": round(ops[M] / t[M] / 1e12, 2),
-            "per_launch_GBs": {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
-                               for k, (ms, dt, _) in per.items()}}
+        rec = {"M": M, "us_per_pass": round(t[M] * 1e6, 2),
+               "weight_GBs": round(wbytes / t[M] / 1e9, 1),
+               "int8_TOPs": round(ops[M] / t[M] / 1e12, 2)}
+        if M <= 16:
+            rec["per_launch_GBs"] = {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
+                                     for k, (ms, dt, _) in per.items()}
+            res["batched_decode_m%d" % M] = rec
+        else:
+            rec["per_launch_TOPs"] = {k: round(sum(2 * M * m.N * m.K for m in ms) / dt / 1e12, 1)
+                                      for k, (ms, dt, _) in per.items()}
+            res["prefill_m%d" % M] = rec
     c = res["ceilings"] = measured_ceilings(wl)
     c["copy_frac_of_peak"] = round(c["copy_GBs"] / HBM_PEAK_GBS, 4)
     c["mfma_i8_frac_of_peak"] = round(c["mfma_i8_TOPs"] / INT8_PEAK_TOPS, 4)
