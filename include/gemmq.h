@@ -93,7 +93,7 @@ extern "C" {
 #define GEMMQ_PATH_AUTO 0 /* M <= 8: decode GEMV, else the MFMA GEMM */
 #define GEMMQ_PATH_GEMV 1 /* decode GEMV, M in 1..8 only */
 #define GEMMQ_PATH_GEMM 2 /* MFMA GEMM, any M */
-#define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernel: q4_K only, M in 1..16 */
+#define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernel: q4_K only, M in 1..32 */
 
 /* ABI version (GEMMQ_ABI_VERSION of the library that was loaded). */
 int gemmq_abi_version(void);
@@ -148,11 +148,11 @@ int gemmq_gemm(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int6
                int64_t K, void *stream);
 
 /* gemmq_gemm with an explicit path (GEMMQ_PATH_*).  GEMMQ_PATH_GEMV with M > 8
- * and GEMMQ_PATH_SKINNY with M > 16 return GEMMQ_E_SHAPE; GEMMQ_PATH_SKINNY with
+ * and GEMMQ_PATH_SKINNY with M > 32 return GEMMQ_E_SHAPE; GEMMQ_PATH_SKINNY with
  * a format other than GEMMQ_Q4_K returns GEMMQ_E_UNSUPPORTED_FORMAT.  Same
  * arguments, layout and errors otherwise.  GEMMQ_PATH_SKINNY is the batched
- * decode kernel: every activation row in one 16 x 16 x 64 int8 MFMA tile, the
- * super-blocks of a row split over the waves of a workgroup by K alone. */
+ * decode kernel: the activation rows in one or two 16 x 16 x 64 int8 MFMA tiles,
+ * the super-blocks of a row split over the waves of a workgroup by K alone. */
 int gemmq_gemm_ex(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int64_t N,
                   int64_t K, int path, void *stream);
 

@@ -1,9 +1,11 @@
 // skinny.hip -- q4_K packed matmul on int8 MFMA for a few activation rows
-// (batched decode, M <= 16; the automatic path takes it for 4 <= M <= 16).
+// (batched decode and short prefills, M <= 32; the automatic path takes it for
+// 4 <= M <= 32).
 //
 // At these M the GEMV's dot products run once per activation row and turn the
 // vector ALU into the bound, while the 64-row GEMM tile wastes most of its
-// matrix work.  Here one v_mfma_i32_16x16x64_i8 serves all (up to 16) rows:
+// matrix work.  Here one v_mfma_i32_16x16x64_i8 serves 16 rows, and a wave
+// holds one or two such row tiles (M <= 16 or M <= 32) on the same weight planes:
 //
 //  * workgroup = one 16-column tile (16 weight rows) of one matrix; its KS
 //    waves split the row's super-blocks in contiguous parts (KS and the parts
@@ -43,9 +45,6 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 // 16 waves, one workgroup per CU, left the loads of one workgroup exposed; 4
 // waves made the 48-super-block rows too long per wave).
 constexpr int kMaxKS = 8;
-// 16-column tiles per wave (two, sharing the activation loads, measured slower:
-// 165 VGPRs, three waves per SIMD)
-constexpr int kCT = 1;
 
 // bytes of w (each <= 15) times a (<= 7), byte by byte (no carries)
 __device__ __forceinline__ uint32_t mul_bytes(uint32_t w, uint32_t a) {
@@ -60,86 +59,94 @@ __device__ __forceinline__ uint32_t i16x2_to_h2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// What one lane reads for one super-block.
+// What one lane reads for one super-block: its weight column's bytes, and for
+// each of the MT 16-row tiles, activation row 16 mt + n's bytes.
+template <int MT>
 struct SkRegs {
-  uint4 hd[kCT];    // its column's header: d, dmin | scales
-  uint4 q[kCT][4];  // quant bytes of groups 0..3
-  u32x4 xa[4];  // activation row n's values of groups 0..3, K-quarter c
-  uint2 bs;     // activation row n's group sums 4c .. 4c+3
-  uint32_t dx;  // activation row n's d
+  uint4 hd;         // the column's header: d, dmin | scales
+  uint4 q[4];       // quant bytes of groups 0..3
+  u32x4 xa[MT][4];  // activation values of groups 0..3, K-quarter c
+  uint2 bs[MT];     // activation group sums 4c .. 4c+3
+  uint32_t dx[MT];  // activation d
 };
 
-__device__ __forceinline__ void sk_load(SkRegs& r, const uint8_t* const (&wrow)[kCT],
-                                        const uint8_t* xrow, int b, int c, bool xok) {
+template <int MT>
+__device__ __forceinline__ void sk_load(SkRegs<MT>& r, const uint8_t* wrow,
+                                        const uint8_t* const (&xrow)[MT], int b, int c,
+                                        const bool (&xok)[MT]) {
+  const uint8_t* wb = wrow + (int64_t)b * kQ4KBytes;
+  r.hd = ld16a(wb);
 #pragma unroll
-  for (int t = 0; t < kCT; ++t) {
-    const uint8_t* wb = wrow[t] + (int64_t)b * kQ4KBytes;
-    r.hd[t] = ld16a(wb);
+  for (int g = 0; g < 4; ++g) r.q[g] = ld16a(wb + 16 + 32 * g + 16 * (c & 1));
 #pragma unroll
-    for (int g = 0; g < 4; ++g) r.q[t][g] = ld16a(wb + 16 + 32 * g + 16 * (c & 1));
-  }
-  const uint8_t* xb = xrow + (int64_t)b * kQ8KBytes;
-  if (xok) {
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint8_t* xb = xrow[mt] + (int64_t)b * kQ8KBytes;
+    if (xok[mt]) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) r.xa[g] = ld16(xb + 4 + 64 * g + 16 * c);
-    r.bs = ld8(xb + 260 + 8 * c);
-    r.dx = ld4(xb);
-  } else {  // rows past M: zero operands, nothing loaded
+      for (int g = 0; g < 4; ++g) r.xa[mt][g] = ld16(xb + 4 + 64 * g + 16 * c);
+      r.bs[mt] = ld8(xb + 260 + 8 * c);
+      r.dx[mt] = ld4(xb);
+    } else {  // rows past M: zero operands, nothing loaded
 #pragma unroll
-    for (int g = 0; g < 4; ++g) r.xa[g] = u32x4{0u, 0u, 0u, 0u};
-    r.bs = make_uint2(0u, 0u);
-    r.dx = 0u;
+      for (int g = 0; g < 4; ++g) r.xa[mt][g] = u32x4{0u, 0u, 0u, 0u};
+      r.bs[mt] = make_uint2(0u, 0u);
+      r.dx[mt] = 0u;
+    }
   }
 }
 
-__device__ __forceinline__ void sk_compute(const SkRegs& r, int lane, int c,
-                                           float (&y)[kCT][4]) {
-  const int hb = c >> 1;              // high nibbles (second sub-block of each group)
+// One super-block: the planes are unpacked once and serve every row tile.
+template <int MT>
+__device__ __forceinline__ void sk_compute(const SkRegs<MT>& r, int c, float (&y)[MT][4]) {
+  const Q4KScales s = q4k_scales(r.hd.y, r.hd.z, r.hd.w);
+  const int hb = c >> 1;  // high nibbles (second sub-block of each group)
   const uint32_t sh = 4u * (uint32_t)hb;
-  float dxs[4];
+  v4i acca[MT], accb[MT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)  // output register i holds row 4c + i; its d_x sits in lane 4c + i
-    dxs[i] = __builtin_bit_cast(float, __shfl((int)r.dx, 4 * c + i, 64));
-  const uint32_t bh[2] = {i16x2_to_h2(r.bs.x), i16x2_to_h2(r.bs.y)};
-  const v4h sfrag = __builtin_bit_cast(v4h, bh);
+  for (int mt = 0; mt < MT; ++mt) acca[mt] = accb[mt] = (v4i){0, 0, 0, 0};
 #pragma unroll
-  for (int t = 0; t < kCT; ++t) {
-    const Q4KScales s = q4k_scales(r.hd[t].y, r.hd[t].z, r.hd[t].w);
-    v4i acca = (v4i){0, 0, 0, 0}, accb = (v4i){0, 0, 0, 0};
+  for (int g = 0; g < 4; ++g) {
+    // scale of sub-block 2g + hb: byte 2(g & 1) + hb of sc_lo (g < 2) or sc_hi
+    const uint32_t sc = ((g < 2 ? s.sc_lo : s.sc_hi) >> (8 * (2 * (g & 1) + hb))) & 0x3fu;
+    const uint32_t a = sc >> 3, bb = sc & 7u;
+    const uint32_t w4[4] = {r.q[g].x, r.q[g].y, r.q[g].z, r.q[g].w};
+    v4i pa, pb;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // scale of sub-block 2g + hb: byte 2(g & 1) + hb of sc_lo (g < 2) or sc_hi
-      const uint32_t sc = ((g < 2 ? s.sc_lo : s.sc_hi) >> (8 * (2 * (g & 1) + hb))) & 0x3fu;
-      const uint32_t a = sc >> 3, bb = sc & 7u;
-      const uint32_t w4[4] = {r.q[t][g].x, r.q[t][g].y, r.q[t][g].z, r.q[t][g].w};
-      v4i pa, pb;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t nib = (w4[k] >> sh) & 0x0f0f0f0fu;
-        pa[k] = (int)mul_bytes(nib, a);
-        pb[k] = (int)mul_bytes(nib, bb);
-      }
-      const v4i xa = {(int)r.xa[g].x, (int)r.xa[g].y, (int)r.xa[g].z, (int)r.xa[g].w};
-      acca = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, pa, acca, 0, 0, 0);
-      accb = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, pb, accb, 0, 0, 0);
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t nib = (w4[k] >> sh) & 0x0f0f0f0fu;
+      pa[k] = (int)mul_bytes(nib, a);
+      pb[k] = (int)mul_bytes(nib, bb);
     }
-    // min term: lane (n, c) carries group sums 4c..4c+3 of row n against the mins
-    // of sub-blocks 2c, 2c, 2c+1, 2c+1 of column n
-    const uint32_t mw = (c < 2 ? s.mn_lo : s.mn_hi) >> (16 * (c & 1));
-    const _Float16 m0 = (_Float16)(float)(mw & 0xffu), m1 = (_Float16)(float)((mw >> 8) & 0xffu);
-    const v4h mfrag = {m0, m0, m1, m1};
-    const v4f am = __builtin_amdgcn_mfma_f32_16x16x16f16(sfrag, mfrag,
-                                                         (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-    const float dcol = f16_to_f32(r.hd[t].x), mcol = f16_to_f32(r.hd[t].x >> 16);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int isc = (int)(((uint32_t)acca[i] << 3) + (uint32_t)accb[i]);
-      float tt = dcol * (float)isc;
-      tt = fmaf(-mcol, am[i], tt);
-      y[t][i] = fmaf(dxs[i], tt, y[t][i]);
+    for (int mt = 0; mt < MT; ++mt) {
+      const v4i xa = {(int)r.xa[mt][g].x, (int)r.xa[mt][g].y, (int)r.xa[mt][g].z,
+                      (int)r.xa[mt][g].w};
+      acca[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, pa, acca[mt], 0, 0, 0);
+      accb[mt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa, pb, accb[mt], 0, 0, 0);
     }
   }
-  (void)lane;
+  // min term: lane (n, c) carries group sums 4c..4c+3 of row n against the mins
+  // of sub-blocks 2c, 2c, 2c+1, 2c+1 of column n
+  const uint32_t mw = (c < 2 ? s.mn_lo : s.mn_hi) >> (16 * (c & 1));
+  const _Float16 m0 = (_Float16)(float)(mw & 0xffu), m1 = (_Float16)(float)((mw >> 8) & 0xffu);
+  const v4h mfrag = {m0, m0, m1, m1};
+  const float dcol = f16_to_f32(r.hd.x), mcol = f16_to_f32(r.hd.x >> 16);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint32_t bh[2] = {i16x2_to_h2(r.bs[mt].x), i16x2_to_h2(r.bs[mt].y)};
+    const v4h sfrag = __builtin_bit_cast(v4h, bh);
+    const v4f am = __builtin_amdgcn_mfma_f32_16x16x16f16(sfrag, mfrag,
+                                                         (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    // output register i holds row 16 mt + 4c + i; its d_x sits in lane 4c + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float dx = __builtin_bit_cast(float, __shfl((int)r.dx[mt], 4 * c + i, 64));
+      const int isc = (int)(((uint32_t)acca[mt][i] << 3) + (uint32_t)accb[mt][i]);
+      float tt = dcol * (float)isc;
+      tt = fmaf(-mcol, am[i], tt);
+      y[mt][i] = fmaf(dx, tt, y[mt][i]);
+    }
+  }
 }
 
 // y = silu(g) * u in f32, the same steps as the GEMV's and the GEMM's:
@@ -151,74 +158,77 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
 // SILU: the tiles cover the gate/up pair as one virtual matrix of 2N rows, row
 // 2p = gate row p (gt.W[0]) and row 2p+1 = up row p (gt.W[1]); lanes n and n^1
 // hold one output column's gate and up, and the even lane writes
-// silu(gate) * up to column p of the single output.
-template <bool SILU>
+// silu(gate) * up to column p of the single output.  MT: 16-row tiles of
+// activation rows per wave (M <= 16 MT).
+template <bool SILU, int MT>
 __global__ __launch_bounds__(64 * kMaxKS) void skinny_q4k_kernel(const GroupTiles gt,
                                                                   const uint8_t* __restrict__ Xq,
                                                                   int M, int nb, int bpw) {
-  __shared__ float red[kMaxKS][kCT][4][64];
+  __shared__ float red[kMaxKS][MT][4][64];
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int ks = (int)(blockDim.x >> 6);
   const int lane = lane_id(), n = lane & 15, c = lane >> 4;
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
   const int64_t N = tm.N;  // SILU: 2 x the output columns
-  int64_t col[kCT];
-  const uint8_t* wrow[kCT];
+  const int64_t col = (int64_t)tm.local * 16 + n;
+  const int64_t colc = col < N ? col : N - 1;
+  const uint8_t* wrow;
+  if constexpr (SILU)
+    wrow = ((colc & 1) ? gt.W[1] : tm.W) + (colc >> 1) * nb * kQ4KBytes;
+  else
+    wrow = tm.W + colc * nb * kQ4KBytes;
+  bool xok[MT];
+  const uint8_t* xrow[MT];
 #pragma unroll
-  for (int t = 0; t < kCT; ++t) {
-    col[t] = (int64_t)tm.local * (16 * kCT) + 16 * t + n;
-    const int64_t colc = col[t] < N ? col[t] : N - 1;
-    if constexpr (SILU)
-      wrow[t] = ((colc & 1) ? gt.W[1] : tm.W) + (colc >> 1) * nb * kQ4KBytes;
-    else
-      wrow[t] = tm.W + colc * nb * kQ4KBytes;
+  for (int mt = 0; mt < MT; ++mt) {
+    const int row = 16 * mt + n;
+    xok[mt] = row < M;
+    xrow[mt] = Xq + (int64_t)(xok[mt] ? row : M - 1) * nb * kQ8KBytes;
   }
-  const bool xok = n < M;
-  const uint8_t* xrow = Xq + (int64_t)(xok ? n : M - 1) * nb * kQ8KBytes;
   const int b0 = wave * bpw, b1 = b0 + bpw < nb ? b0 + bpw : nb;
 
-  float y[kCT][4];
+  float y[MT][4];
 #pragma unroll
-  for (int t = 0; t < kCT; ++t)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[t][i] = 0.f;
+    for (int i = 0; i < 4; ++i) y[mt][i] = 0.f;
   for (int b = b0; b < b1; ++b) {
-    SkRegs cur;
-    sk_load(cur, wrow, xrow, b, c, xok);
-    sk_compute(cur, lane, c, y);
+    SkRegs<MT> cur;
+    sk_load<MT>(cur, wrow, xrow, b, c, xok);
+    sk_compute<MT>(cur, c, y);
   }
   if (ks > 1) {
 #pragma unroll
-    for (int t = 0; t < kCT; ++t)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][t][i][lane] = y[t][i];
+      for (int i = 0; i < 4; ++i) red[wave][mt][i][lane] = y[mt][i];
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
-    for (int t = 0; t < kCT; ++t)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = red[0][t][i][lane];
-        for (int w = 1; w < ks; ++w) v += red[w][t][i][lane];
-        y[t][i] = v;
+        float v = red[0][mt][i][lane];
+        for (int w = 1; w < ks; ++w) v += red[w][mt][i][lane];
+        y[mt][i] = v;
       }
   }
 #pragma unroll
-  for (int t = 0; t < kCT; ++t) {
+  for (int mt = 0; mt < MT; ++mt) {
     if constexpr (SILU) {
-      const int64_t Nout = N >> 1, p = col[t] >> 1;
+      const int64_t Nout = N >> 1, p = col >> 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float up = __shfl_xor(y[t][i], 1, 64);  // every lane takes part
-        const int row = 4 * c + i;
+        const float up = __shfl_xor(y[mt][i], 1, 64);  // every lane takes part
+        const int row = 16 * mt + 4 * c + i;
         if ((n & 1) == 0 && p < Nout && row < M)
-          tm.Y[(int64_t)row * Nout + p] = silu_mul_f32(y[t][i], up);
+          tm.Y[(int64_t)row * Nout + p] = silu_mul_f32(y[mt][i], up);
       }
-    } else if (col[t] < N) {
+    } else if (col < N) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 4 * c + i;
-        if (row < M) tm.Y[(int64_t)row * N + col[t]] = y[t][i];
+        const int row = 16 * mt + 4 * c + i;
+        if (row < M) tm.Y[(int64_t)row * N + col] = y[mt][i];
       }
     }
   }
@@ -233,7 +243,7 @@ void skinny_split(int nb, int& ks, int& bpw) {
   ks = (nb + bpw - 1) / bpw;
 }
 
-bool skinny_fits(int fmt, int64_t M) { return fmt == 12 && M >= 1 && M <= 16; }
+bool skinny_fits(int fmt, int64_t M) { return fmt == 12 && M >= 1 && M <= 32; }
 
 template <bool SILU>
 int launch_skinny_any(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
@@ -243,13 +253,17 @@ int launch_skinny_any(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t
   if (nb64 < 1 || nb64 > 0x7fffffffLL) return -1;
   const int nb = (int)nb64;
   GroupTiles gt;
-  if (!(SILU ? make_pair_tiles(g, 16 * kCT, gt) : make_tiles(g, 16 * kCT, gt))) return -1;
+  if (!(SILU ? make_pair_tiles(g, 16, gt) : make_tiles(g, 16, gt))) return -1;
   const uint32_t tiles = gt.start[kMaxGroup];
   if (tiles == 0) return 0;
   int ks, bpw;
   skinny_split(nb, ks, bpw);
-  hipLaunchKernelGGL(skinny_q4k_kernel<SILU>, dim3(tiles), dim3(64 * ks), 0, st, gt, Xq, M, nb,
-                     bpw);
+  if (M <= 16)
+    hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 1>), dim3(tiles), dim3(64 * ks), 0, st, gt, Xq, M,
+                       nb, bpw);
+  else
+    hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 2>), dim3(tiles), dim3(64 * ks), 0, st, gt, Xq, M,
+                       nb, bpw);
   return 0;
 }
 

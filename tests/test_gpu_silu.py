@@ -1,6 +1,6 @@
 """GPU: the gated up-projection silu(Wg x) * (Wu x) in one call
 (gemmq_linear_silu_mul), on every route: the fused quantize + GEMV launch, the
-plain GEMV (long rows, M up to 8), the small-M MFMA kernel (q4_K, M 4..16),
+plain GEMV (long rows, M up to 8), the small-M MFMA kernel (q4_K, M 4..32),
 the MFMA GEMM with and without the split K loop, ragged tiles, and N = 0.
 
 Three checks per case:
@@ -68,6 +68,7 @@ CASES = [
     (8, 4096, 257, 1, 1.0),      # GEMV forced at its largest M
     (2, 8192, 129, 1, 1.0),
     (9, 1024, 65, 0, 1.0),       # automatic path: q4_K small-M MFMA kernel, q6_K GEMM
+    (30, 2048, 40, 0, 1.0),      # q4_K: small-M MFMA kernel, two row tiles a wave
     (8, 4096, 257, 0, 1.0),      # q4_K: small-M MFMA kernel (eight waves a row)
     (16, 12288, 70, 0, 2.0),     # q4_K: small-M MFMA kernel, two super-blocks a wave
     (5, 256, 1, 0, 1.0),         # q4_K: small-M MFMA kernel, one output column

@@ -3,7 +3,8 @@ the CPU oracle, element by element within 1e-5 * sum_k|w_k * xhat_k| + 1e-6.
 
 Bit identity inside the path: the split of a row's super-blocks over the waves
 depends on K only and MFMA rows are independent, so an output does not depend on
-M or on which other rows are in the call.  Shapes cover row lengths that give
+M or on which other rows are in the call -- also across the one-tile (M <= 16)
+and two-tile (17 <= M <= 32) forms.  Shapes cover row lengths that give
 one to eight waves per workgroup and several super-blocks per wave, N tails
 (columns past N in a 16-column tile), M past 4-row output groups, and blocks
 with extreme scales and values.
@@ -46,7 +47,7 @@ def _check(gq, orc, W, xq, M, N, K, where):
     return y
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16, 17, 24, 32])
 @pytest.mark.parametrize("N,K", [(1, 256), (15, 512), (17, 768), (100, 1024), (33, 2304),
                                  (40, 4096), (16, 8192), (21, 12288), (7, 20480)])
 def test_skinny_parity(dev, gq, orc, M, N, K):
@@ -58,11 +59,12 @@ def test_skinny_parity(dev, gq, orc, M, N, K):
 @pytest.mark.parametrize("K", [1024, 4608, 12288])
 def test_skinny_rows_independent_of_call(dev, gq, orc, K):
     log("skinny row-subset K=%d" % K)
-    M, N = 16, 70
+    M, N = 32, 70
     W, _, xq = _case(orc, M, N, K, seed=K + 1)
     Wd = to_dev(W)
     full = _check(gq, orc, W, xq, M, N, K, "skinny full")
-    for a, b in [(0, 1), (3, 4), (0, 8), (5, 16), (15, 16), (2, 13)]:
+    for a, b in [(0, 1), (3, 4), (0, 8), (5, 16), (15, 16), (2, 13), (0, 17), (16, 32),
+                 (7, 31), (31, 32)]:
         part = to_host(gq.gemm(Q4, Wd, to_dev(xq[a:b]), b - a, N, K, path=gq.PATH_SKINNY))
         assert np.array_equal(part.view(np.uint32), full[a:b].view(np.uint32)), (a, b)
 
@@ -72,7 +74,7 @@ def test_skinny_extreme_blocks(dev, gq, orc):
     # and negative values, activations at +-amax
     log("skinny extreme blocks")
     rng = np.random.default_rng(99)
-    M, N, K = 16, 48, 2048
+    M, N, K = 32, 48, 2048
     nb = K // 256
     W = synth.make_weights(rng, Q4, N, K).reshape(N * nb, 144).copy()
     d = np.array([65504.0, 6.0e-8, -3.5, 1.0], dtype=np.float16)
@@ -91,7 +93,7 @@ def test_skinny_extreme_blocks(dev, gq, orc):
     _check(gq, orc, W, xq, M, N, K, "skinny extreme")
 
 
-@pytest.mark.parametrize("M", [4, 9, 16])
+@pytest.mark.parametrize("M", [4, 9, 16, 25])
 def test_skinny_group_and_linear(dev, gq, orc, M):
     # a group launch (q/k/v-like) equals single calls; gemmq_linear_group takes
     # the same path automatically at these M and gives the same bits
@@ -118,7 +120,7 @@ def test_skinny_group_and_linear(dev, gq, orc, M):
     assert_within(to_host(outs[0]), yo, S, "skinny group")
 
 
-@pytest.mark.parametrize("M", [4, 8, 16])
+@pytest.mark.parametrize("M", [4, 8, 16, 32])
 def test_skinny_silu_route(dev, gq, M):
     # gemmq_linear_silu_mul on this path: the automatic choice and the forced
     # path agree bit for bit, and equal silu(G) * U of this path's own G, U to
