@@ -141,3 +141,13 @@ def test_skinny_silu_route(dev, gq, M):
     yd = g / (1.0 + np.exp(-np.clip(g, -700, 700))) * u
     err = np.abs(to_host(y).astype(np.float64) - yd)
     assert (err <= 8 * 2.0 ** -24 * np.abs(yd) + np.abs(g * u) * 2.0 ** -126 + 2.0 ** -149).all()
+
+
+def test_skinny_longest_rows(dev, gq, orc):
+    # K at the library's limit (2^24, one row of 65536 super-blocks): eight waves
+    # of 8192 super-blocks each, one and two row tiles
+    K = 1 << 24
+    for M, N in ((5, 3), (17, 2)):
+        log("skinny longest rows M=%d N=%d" % (M, N))
+        W, _, xq = _case(orc, M, N, K, seed=M + N)
+        _check(gq, orc, W, xq, M, N, K, "skinny K=2^24")
