@@ -448,7 +448,8 @@ __device__ __forceinline__ void store_w(uint8_t* st, const WRegs<11>& r) {
   uint8_t* pa = st + kOffPa + col * kRow + 64 * c;
   // scales 4c..4c+3: low nibbles from byte word c&1 (high nibbles when c >= 2),
   // top bits 2c..2c+1 of the bytes of word 2
-  const uint32_t lo4 = (r.sc[c & 1] >> (4 * (c >> 1))) & 0x0f0f0f0fu;
+  // (a select, not r.sc[c & 1]: a runtime index would put the array in scratch)
+  const uint32_t lo4 = (((c & 1) ? r.sc[1] : r.sc[0]) >> (4 * (c >> 1))) & 0x0f0f0f0fu;
   const uint32_t hi2 = (r.sc[2] >> (2 * c)) & 0x03030303u;
   const uint32_t u6 = lo4 | (hi2 << 4);
 #pragma unroll
