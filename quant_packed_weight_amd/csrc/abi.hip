@@ -17,7 +17,6 @@ namespace gemmq {
 int probe_mfma_chains();
 int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk, hipStream_t st);
 // skinny.hip: the small-M q4_K MFMA kernel
-bool skinny_fits(int fmt, int64_t M);
 int launch_skinny(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 int launch_skinny_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
                        hipStream_t st);
@@ -185,7 +184,6 @@ int pick_path(int fmt, int path, int64_t M) {
   if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) return GEMMQ_PATH_SKINNY;
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }
-
 
 int launch_matmul(int fmt, int path, const gemmq::Group& g, const uint8_t* xq, int64_t M,
                   int64_t K, hipStream_t st) {

@@ -2,10 +2,14 @@
 // (batched decode and short prefills, M <= 32; the automatic path takes it for
 // 4 <= M <= 32).
 //
-// At these M the GEMV's dot products run once per activation row and turn the
-// vector ALU into the bound, while the 64-row GEMM tile wastes most of its
-// matrix work.  Here one v_mfma_i32_16x16x64_i8 serves 16 rows, and a wave
-// holds one or two such row tiles (M <= 16 or M <= 32) on the same weight planes:
+// The pages' CPU kernel walks each packed weight row once per tile of 8
+// activation rows (molayo article "PocketLLM: 단일 가속기에서 대규모 언어 모델
+// 실행", status row "src/ -- C++ engine").  On gfx950, at these M the GEMV's dot
+// products run once per activation row and turn the vector ALU into the bound,
+// while the 64-row GEMM tile wastes most of its matrix work.  Here one
+// v_mfma_i32_16x16x64_i8 serves 16 rows, and a wave holds one or two such row
+// tiles (M <= 16 or M <= 32) on the same weight planes, so each weight byte is
+// read and unpacked once for all the rows:
 //
 //  * workgroup = one 16-column tile (16 weight rows) of one matrix; its KS
 //    waves split the row's super-blocks in contiguous parts (KS and the parts
@@ -41,9 +45,9 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-// At most 8 waves per workgroup (measured on the Qwen3-8B layer at M = 4..16:
-// 16 waves, one workgroup per CU, left the loads of one workgroup exposed; 4
-// waves made the 48-super-block rows too long per wave).
+// At most 8 waves per workgroup (measured on the Qwen3-8B layer: 16 waves, one
+// workgroup per CU, left a workgroup's loads exposed; 4 waves were slower at
+// M = 4..8 and 1-4% faster at M = 16..32).
 constexpr int kMaxKS = 8;
 
 // bytes of w (each <= 15) times a (<= 7), byte by byte (no carries)
