@@ -14,11 +14,15 @@
 //  * workgroup = one 16-column tile (16 weight rows) of one matrix; its KS
 //    waves split the row's super-blocks in contiguous parts (KS and the parts
 //    depend on K only, so an output's summation order never depends on M);
-//  * lane (n, c), n = lane % 16, c = lane / 16, holds weight column n and
-//    K-quarter c of every 64-wide MFMA step: for the 64-weight group g of a
-//    super-block that is 16 quant bytes at qs[32g + 16 (c & 1)], low nibbles
-//    for c < 2, high nibbles for c >= 2 (sub-block 2g + c / 2), and activation
-//    row n's int8 values 64g + 16c .. 64g + 16c + 15;
+//  * lane (n, c), n = lane % 16, c = lane / 16, holds weight column n and the
+//    64-weight group c of the super-block: its 32 quant bytes qs[32c..32c+31]
+//    (two 16-byte loads, no byte loaded twice in the wave) and activation row
+//    n's int8 values 64c .. 64c + 63; MFMA step g takes the lane's weights
+//    64c + 16g .. +15 (low nibbles of bytes 16 (g & 1) .. +15 for g < 2, high
+//    nibbles for g >= 2; sub-block 2c + g / 2) against the same activations --
+//    A and B in the same K order, so the instruction's own K layout does not
+//    matter (one 16-byte quant load per MFMA step per lane instead, measured
+//    8-12% slower: the wave's load count sets the pace);
 //  * the sub-block scale is folded into the weight operand as in the prefill
 //    GEMM (sc = 8a + b, two int8 planes a*q and b*q, combined as 8A + B in
 //    int32), the min term sum_g m_g * bsum_g is one v_mfma_f32_16x16x16_f16
@@ -68,7 +72,7 @@ __device__ __forceinline__ uint32_t i16x2_to_h2(uint32_t w) {
 template <int MT>
 struct SkRegs {
   uint4 hd;         // the column's header: d, dmin | scales
-  uint4 q[4];       // quant bytes of groups 0..3
+  uint4 q[2];       // quant bytes 32c .. 32c + 31 (group c)
   u32x4 xa[MT][4];  // activation values of groups 0..3, K-quarter c
   uint2 bs[MT];     // activation group sums 4c .. 4c+3
   uint32_t dx[MT];  // activation d
@@ -80,14 +84,14 @@ __device__ __forceinline__ void sk_load(SkRegs<MT>& r, const uint8_t* wrow,
                                         const bool (&xok)[MT]) {
   const uint8_t* wb = wrow + (int64_t)b * kQ4KBytes;
   r.hd = ld16a(wb);
-#pragma unroll
-  for (int g = 0; g < 4; ++g) r.q[g] = ld16a(wb + 16 + 32 * g + 16 * (c & 1));
+  r.q[0] = ld16a(wb + 16 + 32 * c);
+  r.q[1] = ld16a(wb + 32 + 32 * c);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const uint8_t* xb = xrow[mt] + (int64_t)b * kQ8KBytes;
     if (xok[mt]) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) r.xa[mt][g] = ld16(xb + 4 + 64 * g + 16 * c);
+      for (int g = 0; g < 4; ++g) r.xa[mt][g] = ld16(xb + 4 + 64 * c + 16 * g);
       r.bs[mt] = ld8(xb + 260 + 8 * c);
       r.dx[mt] = ld4(xb);
     } else {  // rows past M: zero operands, nothing loaded
@@ -103,21 +107,23 @@ __device__ __forceinline__ void sk_load(SkRegs<MT>& r, const uint8_t* wrow,
 template <int MT>
 __device__ __forceinline__ void sk_compute(const SkRegs<MT>& r, int c, float (&y)[MT][4]) {
   const Q4KScales s = q4k_scales(r.hd.y, r.hd.z, r.hd.w);
-  const int hb = c >> 1;  // high nibbles (second sub-block of each group)
-  const uint32_t sh = 4u * (uint32_t)hb;
   v4i acca[MT], accb[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acca[mt] = accb[mt] = (v4i){0, 0, 0, 0};
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    // scale of sub-block 2g + hb: byte 2(g & 1) + hb of sc_lo (g < 2) or sc_hi
-    const uint32_t sc = ((g < 2 ? s.sc_lo : s.sc_hi) >> (8 * (2 * (g & 1) + hb))) & 0x3fu;
+    // step g, quarter c: weights 64c + 16g .. +15 = nibble half g >> 1 of quant
+    // bytes 32c + 16 (g & 1) .. +15, sub-block 2c + (g >> 1)
+    const int j = 2 * c + (g >> 1);
+    const uint32_t sc = ((j < 4 ? s.sc_lo : s.sc_hi) >> (8 * (j & 3))) & 0x3fu;
+    const uint4 qg = r.q[g & 1];
+    const uint32_t shg = 4u * (uint32_t)(g >> 1);
     const uint32_t a = sc >> 3, bb = sc & 7u;
-    const uint32_t w4[4] = {r.q[g].x, r.q[g].y, r.q[g].z, r.q[g].w};
+    const uint32_t w4[4] = {qg.x, qg.y, qg.z, qg.w};
     v4i pa, pb;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t nib = (w4[k] >> sh) & 0x0f0f0f0fu;
+      const uint32_t nib = (w4[k] >> shg) & 0x0f0f0f0fu;
       pa[k] = (int)mul_bytes(nib, a);
       pb[k] = (int)mul_bytes(nib, bb);
     }
