@@ -25,8 +25,8 @@ int launch_skinny_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_
 namespace {
 
 constexpr int kMaxDevices = 64;
-// activation rows the small-M MFMA kernel takes (automatic choice: from 4)
-constexpr int64_t kSkinnyMinM = 4, kSkinnyMaxM = 32;
+// activation rows the small-M MFMA kernel takes (automatic choice: from 3)
+constexpr int64_t kSkinnyMinM = 3, kSkinnyMaxM = 32;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 int check_device() {
@@ -178,7 +178,7 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
 
 // The kernel family a call runs on.  The automatic choice follows the measured
 // crossovers on the Qwen3-8B layer: the decode GEMV up to M = 8 (q4_K: up to
-// M = 3), the small-M MFMA kernel for q4_K at 4 <= M <= 32, the GEMM beyond.
+// M = 2), the small-M MFMA kernel for q4_K at 3 <= M <= 32, the GEMM beyond.
 int pick_path(int fmt, int path, int64_t M) {
   if (path != GEMMQ_PATH_AUTO) return path;
   if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) return GEMMQ_PATH_SKINNY;

@@ -1,6 +1,6 @@
 // skinny.hip -- q4_K packed matmul on int8 MFMA for a few activation rows
 // (batched decode and short prefills, M <= 32; the automatic path takes it for
-// 4 <= M <= 32).
+// 3 <= M <= 32).
 //
 // The pages' CPU kernel walks each packed weight row once per tile of 8
 // activation rows (molayo article "PocketLLM: 단일 가속기에서 대규모 언어 모델
@@ -28,7 +28,7 @@
 //    int32), the min term sum_g m_g * bsum_g is one v_mfma_f32_16x16x16_f16
 //    (integers below 2^24 throughout, so exact), and the epilogue per
 //    super-block is y += d_x * (d * I_sc - dmin * I_min) in f32;
-//  * each wave loads one super-block at a time straight into registers (70
+//  * each wave loads one super-block at a time straight into registers (68
 //    VGPRs, seven waves per SIMD: more waves in flight measured faster than
 //    holding the next super-block's loads during the arithmetic);
 //  * the waves' partial sums are added in LDS in wave order;

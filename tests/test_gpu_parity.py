@@ -202,14 +202,14 @@ def test_adversarial_blocks(dev, gq, orc, fmt, path):
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
 def test_auto_dispatch_and_linear(dev, gq, orc, fmt):
-    # automatic path: GEMV up to M = 8 (q4_K: up to 3), the small-M MFMA kernel
-    # for q4_K at 4 <= M <= 32, the GEMM beyond
+    # automatic path: GEMV up to M = 8 (q4_K: up to 2), the small-M MFMA kernel
+    # for q4_K at 3 <= M <= 32, the GEMM beyond
     log("dispatch fmt=%d" % fmt)
     N, K = 96, 512
-    for M in (1, 3, 4, 8, 9, 16, 17, 32, 33, 64):
+    for M in (1, 2, 3, 4, 8, 9, 16, 17, 32, 33, 64):
         W, x, xq = _case(orc, fmt, M, N, K, seed=M + fmt)
         auto = to_host(gq.gemm(fmt, to_dev(W), to_dev(xq), M, N, K))
-        if fmt == Q4 and 4 <= M <= 32:
+        if fmt == Q4 and 3 <= M <= 32:
             path = gq.PATH_SKINNY
         else:
             path = gq.PATH_GEMV if M <= 8 else gq.PATH_GEMM
