@@ -227,6 +227,9 @@ def test_empty_calls_touch_nothing(dev, gq):
     xq = torch.zeros(4 * 292, dtype=torch.uint8, device="cuda:0")
     assert gq.gemm_ptr(Q4, w.data_ptr(), xq.data_ptr(), y.data_ptr(), 0, 4, 256) == 0
     assert gq.gemm_ptr(Q4, w.data_ptr(), xq.data_ptr(), y.data_ptr(), 4, 0, 256) == 0
+    for path in (gq.PATH_GEMV, gq.PATH_SKINNY, gq.PATH_GEMM):
+        assert gq.gemm_ptr(Q4, w.data_ptr(), xq.data_ptr(), y.data_ptr(), 0, 4, 256, path) == 0
+        assert gq.gemm_ptr(Q4, w.data_ptr(), xq.data_ptr(), y.data_ptr(), 4, 0, 256, path) == 0
     assert gq.quantize_q8K_ptr(y.data_ptr(), xq.data_ptr(), 0, 256) == 0
     torch.cuda.synchronize()
     assert bool((y == 7.0).all())
