@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 7
+#define GEMMQ_ABI_VERSION 8
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q2_K 10
@@ -90,10 +90,10 @@ extern "C" {
 #define GEMMQ_E_LAUNCH (-6)             /* the HIP runtime rejected a launch */
 
 /* Paths for gemmq_gemm_ex. */
-#define GEMMQ_PATH_AUTO 0 /* decode GEMV (M <= 8; q4_K M <= 2), small-M MFMA (q4_K 3..32), GEMM */
+#define GEMMQ_PATH_AUTO 0 /* decode GEMV (M <= 8; q4_K M <= 2), small-M MFMA (q4_K 3..64, see below), GEMM */
 #define GEMMQ_PATH_GEMV 1 /* decode GEMV, M in 1..8 only */
 #define GEMMQ_PATH_GEMM 2 /* MFMA GEMM, any M */
-#define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernel: q4_K only, M in 1..32 */
+#define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernel: q4_K only, M in 1..64 */
 
 /* ABI version (GEMMQ_ABI_VERSION of the library that was loaded). */
 int gemmq_abi_version(void);
@@ -131,7 +131,9 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
  * Y[m, n] = sum_k w[n, k] * d_x[m, k/256] * q_x[m, k]  -- the packed linear layer
  * (steps a2..a5: in-kernel unpack; the path chosen by GEMMQ_PATH_AUTO: the decode
  * GEMV for M <= 8 -- for q4_K M <= 2 --, the small-M MFMA kernel for q4_K at
- * 3 <= M <= 32, the MFMA GEMM otherwise).
+ * 3 <= M <= 64 when M <= 16 or when the launch's output columns times ceil(M/16)
+ * are at most 20480, the MFMA GEMM otherwise; the choice is made once per launch,
+ * from M and the sum of the N of the matrices it serves).
  *   fmt  GEMMQ_Q2_K, GEMMQ_Q3_K, GEMMQ_Q4_K, GEMMQ_Q5_K, GEMMQ_Q6_K, or a
  *        repacked GEMMQ_Q3_K_R / GEMMQ_Q6_K_R (weights from gemmq_repack).
  *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K,
@@ -150,10 +152,10 @@ int gemmq_gemm(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int6
                int64_t K, void *stream);
 
 /* gemmq_gemm with an explicit path (GEMMQ_PATH_*).  GEMMQ_PATH_GEMV with M > 8
- * and GEMMQ_PATH_SKINNY with M > 32 return GEMMQ_E_SHAPE; GEMMQ_PATH_SKINNY with
+ * and GEMMQ_PATH_SKINNY with M > 64 return GEMMQ_E_SHAPE; GEMMQ_PATH_SKINNY with
  * a format other than GEMMQ_Q4_K returns GEMMQ_E_UNSUPPORTED_FORMAT.  Same
  * arguments, layout and errors otherwise.  GEMMQ_PATH_SKINNY is the batched
- * decode kernel: the activation rows in one or two 16 x 16 x 64 int8 MFMA tiles,
+ * decode kernel: the activation rows in one to four 16 x 16 x 64 int8 MFMA tiles,
  * the super-blocks of a row split over the waves of a workgroup by K alone. */
 int gemmq_gemm_ex(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int64_t N,
                   int64_t K, int path, void *stream);
@@ -161,8 +163,9 @@ int gemmq_gemm_ex(int fmt, const void *W, const void *Xq, float *Y, int64_t M, i
 /*
  * Several weight matrices of one format that read the same activations, in one
  * launch: for g < count, Y[g] = W[g] applied to Xq exactly as
- * gemmq_gemm_ex(fmt, W[g], Xq, Y[g], M, N[g], K, path, stream) computes it (the
- * same bits).  Sharing one input is what a transformer layer's q/k/v
+ * gemmq_gemm_ex(fmt, W[g], Xq, Y[g], M, N[g], K, p, stream) computes it (the
+ * same bits), where p is `path`, or for GEMMQ_PATH_AUTO the path chosen for the
+ * whole launch (from M and N[0] + ... + N[count-1], as gemmq_gemm describes).  Sharing one input is what a transformer layer's q/k/v
  * projections and its gate/up projections do; one launch instead of several
  * removes the per-launch cost that dominates at small M.
  *   count  1..4.

@@ -24,7 +24,7 @@ Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SKINNY = 0, 1, 2, 3
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
-ABI_VERSION = 7
+ABI_VERSION = 8
 PROBE_CHAINS = 4  # GEMMQ_PROBE_CHAINS
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")

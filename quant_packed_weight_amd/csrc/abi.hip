@@ -26,7 +26,10 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 // activation rows the small-M MFMA kernel takes (automatic choice: from 3)
-constexpr int64_t kSkinnyMinM = 3, kSkinnyMaxM = 32;
+constexpr int64_t kSkinnyMinM = 3, kSkinnyMaxM = 64;
+// automatic choice past one 16-row tile: the small-M kernel while the launch's
+// output columns times its 16-row tiles stay within this bound
+constexpr int64_t kSkinnyColTiles = 20480;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 int check_device() {
@@ -176,12 +179,20 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
   return GEMMQ_OK;
 }
 
-// The kernel family a call runs on.  The automatic choice follows the measured
-// crossovers on the Qwen3-8B layer: the decode GEMV up to M = 8 (q4_K: up to
-// M = 2), the small-M MFMA kernel for q4_K at 3 <= M <= 32, the GEMM beyond.
-int pick_path(int fmt, int path, int64_t M) {
+// The kernel family a launch of M activation rows and `cols` output columns (all
+// matrices of the launch together) runs on.  The automatic choice follows the
+// measured crossovers on the Qwen3-8B layer: the decode GEMV up to M = 8 (q4_K: up
+// to M = 2); for q4_K at 3 <= M <= 64 the small-M MFMA kernel, always for one
+// 16-row tile and for t > 1 tiles while cols * t <= kSkinnyColTiles (its time grows
+// with cols * t, while the GEMM at these M runs one 64-row tile per column tile
+// and costs about the same at any cols below a chip's worth of workgroups); the
+// GEMM beyond.
+int pick_path(int fmt, int path, int64_t M, int64_t cols) {
   if (path != GEMMQ_PATH_AUTO) return path;
-  if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) return GEMMQ_PATH_SKINNY;
+  if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) {
+    const int64_t t = (M + 15) / 16;
+    if (t == 1 || cols * t <= kSkinnyColTiles) return GEMMQ_PATH_SKINNY;
+  }
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }
 
@@ -210,7 +221,7 @@ int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
   const uint8_t* xq = static_cast<const uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_pending();
-  return launched(launch_matmul(fmt, pick_path(fmt, path, M), g, xq, M, K, st));
+  return launched(launch_matmul(fmt, pick_path(fmt, path, M, rows), g, xq, M, K, st));
 }
 
 int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y,
@@ -226,7 +237,7 @@ int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y
   if (dv != GEMMQ_OK) return dv;
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int p = pick_path(fmt, path, M);
+  const int p = pick_path(fmt, path, M, rows);
   clear_pending();
   if (rows > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
     return launched(gemmq::launch_gemv_fused(fmt, g, X, xq, (int)M, K, st));
@@ -261,7 +272,7 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
   g.N[0] = g.N[1] = N;
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int p = pick_path(fmt, path, M);  // the path gemmq_linear_group takes
+  const int p = pick_path(fmt, path, M, 2 * N);  // as gemmq_linear_group on {Wg, Wu}
   clear_pending();
   if (N > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
     return launched(gemmq::launch_gemv_silu(fmt, g, nullptr, X, xq, (int)M, K, st));

@@ -1,14 +1,14 @@
 // skinny.hip -- q4_K packed matmul on int8 MFMA for a few activation rows
-// (batched decode and short prefills, M <= 32; the automatic path takes it for
-// 3 <= M <= 32).
+// (batched decode and short prefills, M <= 64; the automatic path takes it for
+// 3 <= M <= 16, and up to M = 64 for launches with few enough output columns).
 //
 // The pages' CPU kernel walks each packed weight row once per tile of 8
 // activation rows (molayo article "PocketLLM: 단일 가속기에서 대규모 언어 모델
 // 실행", status row "src/ -- C++ engine").  On gfx950, at these M the GEMV's dot
 // products run once per activation row and turn the vector ALU into the bound,
 // while the 64-row GEMM tile wastes most of its matrix work.  Here one
-// v_mfma_i32_16x16x64_i8 serves 16 rows, and a wave holds one or two such row
-// tiles (M <= 16 or M <= 32) on the same weight planes, so each weight byte is
+// v_mfma_i32_16x16x64_i8 serves 16 rows, and a wave holds one to four such row
+// tiles (M <= 16, 32, 48, 64) on the same weight planes, so each weight byte is
 // read and unpacked once for all the rows:
 //
 //  * workgroup = one 16-column tile (16 weight rows) of one matrix; its KS
@@ -253,7 +253,7 @@ void skinny_split(int nb, int& ks, int& bpw) {
   ks = (nb + bpw - 1) / bpw;
 }
 
-bool skinny_fits(int fmt, int64_t M) { return fmt == 12 && M >= 1 && M <= 32; }
+bool skinny_fits(int fmt, int64_t M) { return fmt == 12 && M >= 1 && M <= 64; }
 
 template <bool SILU>
 int launch_skinny_any(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
@@ -268,12 +268,14 @@ int launch_skinny_any(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t
   if (tiles == 0) return 0;
   int ks, bpw;
   skinny_split(nb, ks, bpw);
-  if (M <= 16)
-    hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 1>), dim3(tiles), dim3(64 * ks), 0, st, gt, Xq, M,
-                       nb, bpw);
-  else
-    hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 2>), dim3(tiles), dim3(64 * ks), 0, st, gt, Xq, M,
-                       nb, bpw);
+  // 68-69 / 101-104 / 134-137 / 167-170 VGPRs for one to four row tiles, no scratch
+  const dim3 grid(tiles), block(64 * ks);
+  switch ((M + 15) / 16) {
+    case 1: hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 1>), grid, block, 0, st, gt, Xq, M, nb, bpw); break;
+    case 2: hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 2>), grid, block, 0, st, gt, Xq, M, nb, bpw); break;
+    case 3: hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 3>), grid, block, 0, st, gt, Xq, M, nb, bpw); break;
+    default: hipLaunchKernelGGL((skinny_q4k_kernel<SILU, 4>), grid, block, 0, st, gt, Xq, M, nb, bpw); break;
+  }
   return 0;
 }
 

@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 7
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 8
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -82,7 +82,7 @@ FAKE16 = 0x10000  # never dereferenced: every call below fails validation first
     ((12, FAKE16, FAKE16, FAKE16 + 1, 1, 1, 256, 0), -4),  # Y needs 4 B
     ((12, FAKE16, FAKE16, FAKE16, 1, 1, 256, 7), -1),      # unknown path
     ((12, FAKE16, FAKE16, FAKE16, 9, 1, 256, 1), -3),      # GEMV path with M > 8
-    ((12, FAKE16, FAKE16, FAKE16, 33, 1, 256, 3), -3),     # small-M MFMA path with M > 32
+    ((12, FAKE16, FAKE16, FAKE16, 65, 1, 256, 3), -3),     # small-M MFMA path with M > 64
     ((14, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),      # small-M MFMA path: q4_K only
     ((13, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),
     ((12, FAKE16, FAKE16, FAKE16, 0, 5, 256, 0), 0),       # M = 0: empty, nothing touched
@@ -104,7 +104,7 @@ def test_gemm_validation(L, args, status):
     (2, [FAKE16, FAKE16 + 8], [FAKE16, FAKE16], [1, 1], 1, 0, -4),    # W alignment
     (2, [FAKE16, FAKE16], [FAKE16, FAKE16 + 2], [1, 1], 1, 0, -4),    # Y alignment
     (3, [FAKE16] * 3, [FAKE16] * 3, [1] * 3, 9, 1, -3),               # GEMV path, M > 8
-    (3, [FAKE16] * 3, [FAKE16] * 3, [1] * 3, 33, 3, -3),              # small-M path, M > 32
+    (3, [FAKE16] * 3, [FAKE16] * 3, [1] * 3, 65, 3, -3),              # small-M path, M > 64
     (3, [FAKE16] * 3, [FAKE16] * 3, [1] * 3, 1, 5, -1),               # unknown path
     (2, [FAKE16, None], [FAKE16, None], [4, 0], 0, 0, 0),             # M = 0: empty
     (2, [None, None], [None, None], [0, 0], 3, 0, 0),                 # all N = 0: empty
@@ -168,7 +168,7 @@ def test_linear_validation(L, args, status):
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 9, 1, 256, 1), -3),      # GEMV path, M > 8
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256, 4), -1),      # unknown path
     ((14, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),      # small-M path: q4_K only
-    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 33, 1, 256, 3), -3),     # small-M path, M > 32
+    ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 65, 1, 256, 3), -3),     # small-M path, M > 64
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 0, 5, 256, 0), 0),       # M = 0: empty
 ])
 def test_linear_silu_mul_validation(L, args, status):
@@ -186,7 +186,7 @@ def test_linear_group_arrays_and_paths(L):
     assert L.gemmq_linear_group(12, 1, one_p, one_p, None, *args, 0, None) == -1
     assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, *args, 4, None) == -1
     assert L.gemmq_linear_group(14, 1, one_p, one_p, one_n, *args, 3, None) == -2
-    assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, FAKE16, FAKE16, 33, 256, 3,
+    assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, FAKE16, FAKE16, 65, 256, 3,
                                 None) == -3
     assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, FAKE16, FAKE16, 9, 256, 1,
                                 None) == -3

@@ -25,6 +25,7 @@ def test_graph_replays_match_eager():
              (gq.FMT_Q2K, 1, 100, 2048), (gq.FMT_Q3K, 3, 70, 512), (gq.FMT_Q5K, 1, 129, 4096),
              (gq.FMT_Q2K, 33, 64, 512), (gq.FMT_Q3K, 40, 65, 1024), (gq.FMT_Q5K, 64, 100, 768),
              (gq.FMT_Q6K_R, 1, 200, 3072), (gq.FMT_Q3K_R, 50, 90, 1024),
+             (gq.FMT_Q4K, 80, 96, 512),  # q4_K GEMM
              (gq.FMT_Q4K, 8, 333, 4096), (gq.FMT_Q4K, 27, 70, 12288)]  # small-M MFMA kernel
     bufs = []
     for fmt, M, N, K in cases:
@@ -38,7 +39,7 @@ def test_graph_replays_match_eager():
 
     # grouped launches: two matrices sharing one input, GEMV and GEMM
     groups = []
-    for M in (1, 12, 40):
+    for M in (1, 12, 40, 70):
         K, Ns = 1024, (300, 77)
         Ws = [torch.from_numpy(synth.make_weights(rng, gq.FMT_Q4K, N, K)).cuda() for N in Ns]
         X = torch.from_numpy(synth.make_activations(rng, M, K, True)).cuda()
@@ -47,9 +48,9 @@ def test_graph_replays_match_eager():
         groups.append((M, K, Ns, Ws, X, Xq, Ys))
 
     # gemmq_linear_group: fused at (M 1, K 4096) and (M 2, K 1024), two launches
-    # at (M 1, K 12288) and (M 40, K 1024)
+    # at (M 1, K 12288), (M 40, K 1024: small-M MFMA), (M 70: GEMM)
     linears = []
-    for M, K in ((1, 4096), (2, 1024), (1, 12288), (40, 1024), (8, 4096)):
+    for M, K in ((1, 4096), (2, 1024), (1, 12288), (40, 1024), (8, 4096), (70, 1024)):
         Ns = (260, 33)
         Ws = [torch.from_numpy(synth.make_weights(rng, gq.FMT_Q4K, N, K)).cuda() for N in Ns]
         X = torch.from_numpy(synth.make_activations(rng, M, K, True)).cuda()
@@ -57,10 +58,12 @@ def test_graph_replays_match_eager():
         Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for N in Ns]
         linears.append((M, K, Ns, Ws, X, Xq, Ys))
 
-    # gemmq_linear_silu_mul: fused (M 1, K 2048), plain GEMV (M 1, K 8192), GEMM (M 40)
+    # gemmq_linear_silu_mul: fused (M 1, K 2048), plain GEMV (M 1, K 8192), GEMM
+    # (M 70), small-M MFMA (M 40 and 20)
     silus = []
     for fmt, M, K, N in ((gq.FMT_Q4K, 1, 2048, 300), (gq.FMT_Q6K, 1, 8192, 129),
-                         (gq.FMT_Q4K, 40, 1024, 200), (gq.FMT_Q4K, 20, 3072, 90)):
+                         (gq.FMT_Q4K, 70, 1024, 200), (gq.FMT_Q4K, 40, 1024, 200),
+                         (gq.FMT_Q4K, 20, 3072, 90)):
         Wg = torch.from_numpy(synth.make_weights(rng, fmt, N, K)).cuda()
         Wu = torch.from_numpy(synth.make_weights(rng, fmt, N, K)).cuda()
         X = torch.from_numpy(synth.make_activations(rng, M, K, True)).cuda()

@@ -72,9 +72,13 @@ CASES = [
     (8, 4096, 257, 0, 1.0),      # q4_K: small-M MFMA kernel (eight waves a row)
     (16, 12288, 70, 0, 2.0),     # q4_K: small-M MFMA kernel, two super-blocks a wave
     (5, 256, 1, 0, 1.0),         # q4_K: small-M MFMA kernel, one output column
-    (40, 1024, 300, 0, 2.0),     # ragged last tile
+    (40, 1024, 300, 0, 2.0),     # q4_K: small-M MFMA kernel, three row tiles; q6_K: GEMM
+    (64, 2048, 77, 0, 1.0),      # q4_K: small-M MFMA kernel, four row tiles
+    (20, 1024, 11000, 0, 1.0),   # q4_K: 2 x 11000 columns in two row tiles -> GEMM
+    (40, 1024, 300, 2, 2.0),     # GEMM forced: ragged last tile
+    (70, 1024, 300, 0, 1.0),     # GEMM: ragged last tile
     (130, 4096, 200, 0, 1.0),    # several row tiles of M
-    (40, 8192, 129, 0, 1.0),     # split K loop
+    (70, 8192, 129, 0, 1.0),     # split K loop
     (17, 256, 1, 0, 1.0),        # one output column
     (1, 1024, 200, 2, 1.0),      # GEMM forced at M = 1
     (40, 1024, 0, 0, 1.0),

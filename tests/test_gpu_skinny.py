@@ -3,8 +3,8 @@ the CPU oracle, element by element within 1e-5 * sum_k|w_k * xhat_k| + 1e-6.
 
 Bit identity inside the path: the split of a row's super-blocks over the waves
 depends on K only and MFMA rows are independent, so an output does not depend on
-M or on which other rows are in the call -- also across the one-tile (M <= 16)
-and two-tile (17 <= M <= 32) forms.  Shapes cover row lengths that give
+M or on which other rows are in the call -- also across the forms with one to
+four 16-row tiles (M <= 16, 32, 48, 64).  Shapes cover row lengths that give
 one to eight waves per workgroup and several super-blocks per wave, N tails
 (columns past N in a 16-column tile), M past 4-row output groups, and blocks
 with extreme scales and values.
@@ -47,7 +47,7 @@ def _check(gq, orc, W, xq, M, N, K, where):
     return y
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16, 17, 24, 32])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8, 11, 16, 17, 24, 32, 33, 40, 48, 49, 64])
 @pytest.mark.parametrize("N,K", [(1, 256), (15, 512), (17, 768), (100, 1024), (33, 2304),
                                  (40, 4096), (16, 8192), (21, 12288), (7, 20480)])
 def test_skinny_parity(dev, gq, orc, M, N, K):
@@ -59,22 +59,23 @@ def test_skinny_parity(dev, gq, orc, M, N, K):
 @pytest.mark.parametrize("K", [1024, 4608, 12288])
 def test_skinny_rows_independent_of_call(dev, gq, orc, K):
     log("skinny row-subset K=%d" % K)
-    M, N = 32, 70
+    M, N = 64, 70
     W, _, xq = _case(orc, M, N, K, seed=K + 1)
     Wd = to_dev(W)
     full = _check(gq, orc, W, xq, M, N, K, "skinny full")
     for a, b in [(0, 1), (3, 4), (0, 8), (5, 16), (15, 16), (2, 13), (0, 17), (16, 32),
-                 (7, 31), (31, 32)]:
+                 (7, 31), (31, 32), (0, 33), (10, 50), (40, 64), (63, 64), (1, 49)]:
         part = to_host(gq.gemm(Q4, Wd, to_dev(xq[a:b]), b - a, N, K, path=gq.PATH_SKINNY))
         assert np.array_equal(part.view(np.uint32), full[a:b].view(np.uint32)), (a, b)
 
 
-def test_skinny_extreme_blocks(dev, gq, orc):
+@pytest.mark.parametrize("M", [32, 64])
+def test_skinny_extreme_blocks(dev, gq, orc, M):
     # every scale and min at 63, quants at 0 or 15, f16 d / dmin at large, tiny
     # and negative values, activations at +-amax
-    log("skinny extreme blocks")
+    log("skinny extreme blocks M=%d" % M)
     rng = np.random.default_rng(99)
-    M, N, K = 32, 48, 2048
+    N, K = 48, 2048
     nb = K // 256
     W = synth.make_weights(rng, Q4, N, K).reshape(N * nb, 144).copy()
     d = np.array([65504.0, 6.0e-8, -3.5, 1.0], dtype=np.float16)
@@ -93,7 +94,7 @@ def test_skinny_extreme_blocks(dev, gq, orc):
     _check(gq, orc, W, xq, M, N, K, "skinny extreme")
 
 
-@pytest.mark.parametrize("M", [3, 9, 16, 25])
+@pytest.mark.parametrize("M", [3, 9, 16, 25, 41, 60])
 def test_skinny_group_and_linear(dev, gq, orc, M):
     # a group launch (q/k/v-like) equals single calls; gemmq_linear_group takes
     # the same path automatically at these M and gives the same bits
@@ -120,7 +121,7 @@ def test_skinny_group_and_linear(dev, gq, orc, M):
     assert_within(to_host(outs[0]), yo, S, "skinny group")
 
 
-@pytest.mark.parametrize("M", [4, 8, 16, 32])
+@pytest.mark.parametrize("M", [4, 8, 16, 32, 47, 64])
 def test_skinny_silu_route(dev, gq, M):
     # gemmq_linear_silu_mul on this path: the automatic choice and the forced
     # path agree bit for bit, and equal silu(G) * U of this path's own G, U to
@@ -145,9 +146,9 @@ def test_skinny_silu_route(dev, gq, M):
 
 def test_skinny_longest_rows(dev, gq, orc):
     # K at the library's limit (2^24, one row of 65536 super-blocks): eight waves
-    # of 8192 super-blocks each, one and two row tiles
+    # of 8192 super-blocks each, one to four row tiles
     K = 1 << 24
-    for M, N in ((5, 3), (17, 2)):
+    for M, N in ((5, 3), (17, 2), (40, 1), (50, 1)):
         log("skinny longest rows M=%d N=%d" % (M, N))
         W, _, xq = _case(orc, M, N, K, seed=M + N)
         _check(gq, orc, W, xq, M, N, K, "skinny K=2^24")
