@@ -90,7 +90,7 @@ extern "C" {
 #define GEMMQ_E_LAUNCH (-6)             /* the HIP runtime rejected a launch */
 
 /* Paths for gemmq_gemm_ex. */
-#define GEMMQ_PATH_AUTO 0 /* decode GEMV (M <= 8; q4_K M <= 2), small-M MFMA (q4_K 3..64, see below), GEMM */
+#define GEMMQ_PATH_AUTO 0 /* decode GEMV (M <= 8; q4_K M <= 2), small-M MFMA (q4_K 3..64), GEMM; see gemmq_gemm */
 #define GEMMQ_PATH_GEMV 1 /* decode GEMV, M in 1..8 only */
 #define GEMMQ_PATH_GEMM 2 /* MFMA GEMM, any M */
 #define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernel: q4_K only, M in 1..64 */
@@ -132,8 +132,9 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
  * (steps a2..a5: in-kernel unpack; the path chosen by GEMMQ_PATH_AUTO: the decode
  * GEMV for M <= 8 -- for q4_K M <= 2 --, the small-M MFMA kernel for q4_K at
  * 3 <= M <= 64 when M <= 16 or when the launch's output columns times ceil(M/16)
- * are at most 20480, the MFMA GEMM otherwise; the choice is made once per launch,
- * from M and the sum of the N of the matrices it serves).
+ * are at most 20480, the MFMA GEMM otherwise -- also for q6_K and q6_K_R at
+ * 5 <= M <= 8 when the launch has at least 16384 output columns; the choice is
+ * made once per launch, from M and the sum of the N of the matrices it serves).
  *   fmt  GEMMQ_Q2_K, GEMMQ_Q3_K, GEMMQ_Q4_K, GEMMQ_Q5_K, GEMMQ_Q6_K, or a
  *        repacked GEMMQ_Q3_K_R / GEMMQ_Q6_K_R (weights from gemmq_repack).
  *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K,

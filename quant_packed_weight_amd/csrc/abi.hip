@@ -30,6 +30,9 @@ constexpr int64_t kSkinnyMinM = 3, kSkinnyMaxM = 64;
 // automatic choice past one 16-row tile: the small-M kernel while the launch's
 // output columns times its 16-row tiles stay within this bound
 constexpr int64_t kSkinnyColTiles = 20480;
+// q6_K at 5 <= M <= 8: the GEMM (64-column tiles) from this many output columns,
+// one tile per CU, where the GEMV's per-row dot products cost more than the GEMM
+constexpr int64_t kQ6GemmCols = 16384;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 int check_device() {
@@ -186,13 +189,16 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
 // 16-row tile and for t > 1 tiles while cols * t <= kSkinnyColTiles (its time grows
 // with cols * t, while the GEMM at these M runs one 64-row tile per column tile
 // and costs about the same at any cols below a chip's worth of workgroups); the
-// GEMM beyond.
+// GEMM beyond.  q6_K (either layout) at 5 <= M <= 8 takes the GEMM once the
+// launch has kQ6GemmCols columns.
 int pick_path(int fmt, int path, int64_t M, int64_t cols) {
   if (path != GEMMQ_PATH_AUTO) return path;
   if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) {
     const int64_t t = (M + 15) / 16;
     if (t == 1 || cols * t <= kSkinnyColTiles) return GEMMQ_PATH_SKINNY;
   }
+  if ((fmt == GEMMQ_Q6_K || fmt == GEMMQ_Q6_K_R) && M >= 5 && M <= 8 && cols >= kQ6GemmCols)
+    return GEMMQ_PATH_GEMM;
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }
 

@@ -203,21 +203,24 @@ def test_adversarial_blocks(dev, gq, orc, fmt, path):
 def _expected_path(gq, fmt, M, cols):
     # GEMV up to M = 8 (q4_K: up to 2); the small-M MFMA kernel for q4_K at
     # 3 <= M <= 64 with one 16-row tile, or with t tiles while cols * t <= 20480;
-    # the GEMM otherwise
+    # q6_K at 5 <= M <= 8 on the GEMM from 16384 columns; the GEMM otherwise
     t = (M + 15) // 16
     if fmt == Q4 and 3 <= M <= 64 and (t == 1 or cols * t <= 20480):
         return gq.PATH_SKINNY
+    if fmt == Q6 and 5 <= M <= 8 and cols >= 16384:
+        return gq.PATH_GEMM
     return gq.PATH_GEMV if M <= 8 else gq.PATH_GEMM
 
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
-@pytest.mark.parametrize("N", [96, 7000])
+@pytest.mark.parametrize("N", [96, 7000, 16383, 16384])
 def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
     # the automatic path takes the expected kernel family (the same bits as that
-    # path forced); N = 7000 crosses the column bound between t = 2 and t = 3
+    # path forced); N = 7000 crosses the q4_K column bound between t = 2 and
+    # t = 3, N = 16384 the q6_K one at M = 5..8
     log("dispatch fmt=%d N=%d" % (fmt, N))
     K = 512 if N < 1000 else 256
-    for M in (1, 2, 3, 4, 8, 9, 16, 17, 32, 33, 48, 49, 64, 65):
+    for M in (1, 2, 3, 4, 5, 6, 8, 9, 16, 17, 32, 33, 48, 49, 64, 65):
         W, x, xq = _case(orc, fmt, M, N, K, seed=M + fmt)
         auto = to_host(gq.gemm(fmt, to_dev(W), to_dev(xq), M, N, K))
         path = _expected_path(gq, fmt, M, N)

@@ -75,6 +75,7 @@ CASES = [
     (40, 1024, 300, 0, 2.0),     # q4_K: small-M MFMA kernel, three row tiles; q6_K: GEMM
     (64, 2048, 77, 0, 1.0),      # q4_K: small-M MFMA kernel, four row tiles
     (20, 1024, 11000, 0, 1.0),   # q4_K: 2 x 11000 columns in two row tiles -> GEMM
+    (6, 1024, 8200, 0, 1.0),     # q6_K: 2 x 8200 columns at M = 6 -> GEMM
     (40, 1024, 300, 2, 2.0),     # GEMM forced: ragged last tile
     (70, 1024, 300, 0, 1.0),     # GEMM: ragged last tile
     (130, 4096, 200, 0, 1.0),    # several row tiles of M
