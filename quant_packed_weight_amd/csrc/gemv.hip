@@ -123,6 +123,18 @@ __device__ __forceinline__ void seg_step(float (&v)[V], int& cnt, int lane) {
   }
 }
 
+// Whether a wave compiled for MT activation rows computes row m of a call with
+// M rows: rows up to MT/2 always (the MT-row form serves MT/2 < M <= MT), the
+// others while m < M.  Skipped rows keep a zero partial that is never stored;
+// the reduction over the MT-row layout is the same, so the bits of the real
+// rows do not depend on the skip.  The eight-row form computes every row (the
+// wave-uniform branches measured 10-60% slower there at any M, while the
+// four-row form gained up to 30% at M = 3 and up to 14% at M = 4).
+template <int MT>
+__device__ __forceinline__ bool row_live(int m, int M) {
+  return MT > 4 || m <= MT / 2 || m < M;
+}
+
 // Reduce-scatter over segments of SEG lanes (V <= SEG, a power of two): lane l
 // ends with the total of value vidx<V, SEG>(l) in v[0].
 template <int V, int SEG>
@@ -445,6 +457,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+          if (!row_live<MT>(m, M)) break;  // wave-uniform: rows past M are not computed
           const XFrag x = xfrag(m < M ? m : M - 1, b);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
@@ -501,6 +514,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+          if (!row_live<MT>(m, M)) break;  // wave-uniform: rows past M are not computed
           const XFrag x = xfrag(m < M ? m : M - 1, b);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
@@ -542,6 +556,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
         }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
+          if (!row_live<MT>(m, M)) break;  // wave-uniform: rows past M are not computed
           const XFrag x = xfrag(m < M ? m : M - 1, b);
 #pragma unroll
           for (int r = 0; r < R; ++r) {
