@@ -230,6 +230,27 @@ def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
         assert np.array_equal(lin.view(np.uint32), auto.view(np.uint32)), M
 
 
+@pytest.mark.parametrize("N", [16383, 16384])
+def test_auto_dispatch_q6K_repacked(dev, gq, orc, N):
+    # the repacked q6_K layout follows the q6_K choice: at M = 5..8 the GEMM from
+    # 16384 columns, the GEMV below; both equal the original layout's bits
+    import torch
+
+    K = 512
+    for M in (4, 5, 8):
+        log("dispatch q6_K_R N=%d M=%d" % (N, M))
+        W, x, xq = _case(orc, Q6, M, N, K, seed=100 + M)
+        Wd, xqd = to_dev(W), to_dev(xq)
+        Wr = gq.repack(Q6, Wd, N, K)
+        auto = to_host(gq.gemm(gq.FMT_Q6K_R, Wr, xqd, M, N, K))
+        path = _expected_path(gq, Q6, M, N)
+        forced = to_host(gq.gemm(gq.FMT_Q6K_R, Wr, xqd, M, N, K, path=path))
+        plain = to_host(gq.gemm(Q6, Wd, xqd, M, N, K, path=path))
+        assert np.array_equal(auto.view(np.uint32), forced.view(np.uint32)), M
+        assert np.array_equal(auto.view(np.uint32), plain.view(np.uint32)), M
+        torch.cuda.synchronize()
+
+
 def test_empty_calls_touch_nothing(dev, gq):
     import torch
 
