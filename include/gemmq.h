@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 8
+#define GEMMQ_ABI_VERSION 9
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q2_K 10
@@ -80,36 +80,49 @@ extern "C" {
 #define GEMMQ_QK 256
 #define GEMMQ_MAX_GROUP 4 /* matrices per gemmq_gemm_group call */
 
-/* Status codes. */
 #define GEMMQ_OK 0
-#define GEMMQ_E_INVALID_ARG (-1)        /* null pointer, negative size, bad path id */
-#define GEMMQ_E_UNSUPPORTED_FORMAT (-2) /* fmt is not one of GEMMQ_Q2_K .. GEMMQ_Q6_K, _R */
-#define GEMMQ_E_SHAPE (-3)              /* K not a positive multiple of 256, or M too large for the path */
+/* Status codes.  Formats the library does not implement are refused by name
+ * rather than guessed at, as the pages' engine refuses unimplemented formats
+ * at load (PocketLLM README, "Roadmap" and "Current status"). */
+#define GEMMQ_E_INVALID_ARG (-1)        /* null pointer, negative size, bad path id or count */
+#define GEMMQ_E_UNSUPPORTED_FORMAT (-2) /* fmt is not one of GEMMQ_Q2_K .. GEMMQ_Q6_K, _R
+                                           (or not accepted by the entry point or path) */
+#define GEMMQ_E_SHAPE (-3)              /* K not a positive multiple of 256 up to 2^24, rows
+                                           above 2^31, or M above the path's limit */
 #define GEMMQ_E_ALIGNMENT (-4)          /* a pointer breaks the alignment stated below */
 #define GEMMQ_E_DEVICE (-5)             /* current device is not gfx950, or no device */
-#define GEMMQ_E_LAUNCH (-6)             /* the HIP runtime rejected a launch */
+#define GEMMQ_E_LAUNCH (-6)             /* the HIP runtime rejected a launch or a kernel
+                                           attribute the launch needs */
 
-/* Paths for gemmq_gemm_ex. */
+/* Paths for gemmq_gemm_ex, each with its limit on M (GEMMQ_E_SHAPE beyond). */
 #define GEMMQ_PATH_AUTO 0 /* decode GEMV (M <= 8; q4_K M <= 2), small-M MFMA (q4_K 3..64), GEMM; see gemmq_gemm */
 #define GEMMQ_PATH_GEMV 1 /* decode GEMV, M in 1..8 only */
-#define GEMMQ_PATH_GEMM 2 /* MFMA GEMM, any M */
+#define GEMMQ_PATH_GEMM 2 /* MFMA GEMM, M up to GEMMQ_GEMM_MAX_M */
 #define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernel: q4_K only, M in 1..64 */
+#define GEMMQ_GEMM_MAX_M 4194240 /* 65535 tiles of 64 activation rows */
 
-/* ABI version (GEMMQ_ABI_VERSION of the library that was loaded). */
+/* ABI version (GEMMQ_ABI_VERSION of the library that was loaded): the C core
+ * is a separately versioned library loaded through ctypes, as the pages' engine
+ * core is (PocketLLM README, "Current status").  Never fails. */
 int gemmq_abi_version(void);
 
-/* Static string naming a status code; never NULL. */
+/* Static string naming a status code and the condition behind it (the pages
+ * refuse by name: PocketLLM README, "Roadmap"); never NULL, "GEMMQ_E_UNKNOWN..."
+ * for a value that is not a status. */
 const char *gemmq_status_str(int status);
 
-/* Bytes of one super-block of `fmt` (84, 110, 144, 176, 210), or 0 for an
- * unknown format. */
+/* Bytes of one super-block of `fmt` (84, 110, 144, 176, 210: the K-quant block
+ * sizes of the formats the pages' width ladder names, PocketLLM README "What it
+ * runs"), or 0 for an unknown format. */
 size_t gemmq_block_bytes(int fmt);
 
 /* Bytes of an N x K packed weight matrix: N * K/256 * block_bytes; 0 when fmt is
- * unknown, N or K is negative, or K % 256 != 0. */
+ * unknown, N or K is negative, K % 256 != 0, K > 2^24 or N > 2^31. */
 size_t gemmq_weight_bytes(int fmt, int64_t N, int64_t K);
 
-/* Bytes of M x K activations in q8_K: M * K/256 * 292; 0 on bad sizes. */
+/* Bytes of M x K activations in q8_K (the int8 activation blocks of the pages'
+ * CPU gemm_quant, molayo article, status row "src/"): M * K/256 * 292; 0 on bad
+ * sizes (as gemmq_weight_bytes). */
 size_t gemmq_q8K_bytes(int64_t M, int64_t K);
 
 /*
@@ -128,7 +141,11 @@ size_t gemmq_q8K_bytes(int64_t M, int64_t K);
 int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *stream);
 
 /*
- * Y[m, n] = sum_k w[n, k] * d_x[m, k/256] * q_x[m, k]  -- the packed linear layer
+ * Y[m, n] = sum_k w[n, k] * d_x[m, k/256] * q_x[m, k]  -- the packed linear layer,
+ * the pages' gemm_quant operator (PocketLLM README, "Current status": the kernel
+ * layer declares gemm_quant; molayo article, status row "src/": the packed dot
+ * walks each weight row once per tile of activation rows, and the reordered f32
+ * sums are held to a 1e-5 scaled relative bound)
  * (steps a2..a5: in-kernel unpack; the path chosen by GEMMQ_PATH_AUTO: the decode
  * GEMV for M <= 8 -- for q4_K M <= 2 --, the small-M MFMA kernel for q4_K at
  * 3 <= M <= 64 when M <= 16 or when the launch's output columns times ceil(M/16)
@@ -152,8 +169,9 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
 int gemmq_gemm(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int64_t N,
                int64_t K, void *stream);
 
-/* gemmq_gemm with an explicit path (GEMMQ_PATH_*).  GEMMQ_PATH_GEMV with M > 8
- * and GEMMQ_PATH_SKINNY with M > 64 return GEMMQ_E_SHAPE; GEMMQ_PATH_SKINNY with
+/* gemmq_gemm with an explicit path (GEMMQ_PATH_*).  GEMMQ_PATH_GEMV with M > 8,
+ * GEMMQ_PATH_SKINNY with M > 64 and GEMMQ_PATH_GEMM (also when chosen by
+ * GEMMQ_PATH_AUTO) with M > GEMMQ_GEMM_MAX_M return GEMMQ_E_SHAPE; GEMMQ_PATH_SKINNY with
  * a format other than GEMMQ_Q4_K returns GEMMQ_E_UNSUPPORTED_FORMAT.  Same
  * arguments, layout and errors otherwise.  GEMMQ_PATH_SKINNY is the batched
  * decode kernel: the activation rows in one to four 16 x 16 x 64 int8 MFMA tiles,
@@ -195,7 +213,8 @@ int gemmq_gemm_group(int fmt, int count, const void *const *W, float *const *Y, 
  *   fmt, count, W, Y, N, M, K, path, stream  as in gemmq_gemm_group; all N[g]
  *          == 0 still quantizes X.
  * Errors: those of gemmq_quantize_q8K and gemmq_gemm_group; nothing is launched
- * on an error.
+ * on an error (the matmul's limits are checked before the quantizer is
+ * enqueued, so Xq is untouched when the call fails).
  */
 int gemmq_linear_group(int fmt, int count, const void *const *W, float *const *Y,
                        const int64_t *N, const float *X, void *Xq, int64_t M, int64_t K,
@@ -252,7 +271,9 @@ int gemmq_repack(int fmt, const void *W, void *Wr, int64_t N, int64_t K, void *s
 
 /*
  * Diagnostic export: decode packed weights to f32 with the same device unpacker
- * (step a2) the matmul kernels use.  Never used on the compute path.
+ * (step a2) the matmul kernels use: the weights the pages decode inside the
+ * kernel and never widen (PocketLLM README, "What it runs"), widened here only
+ * for inspection.  Never used on the compute path.
  *   W   device, gemmq_weight_bytes(fmt, N, K) bytes, alignment as in gemmq_gemm.
  *   Wf  device, f32 [N, K], 16-byte aligned; overwritten.
  * q2_K, q4_K and q5_K weights are the single f32 rounding of d*sc*q - dmin*m;
@@ -262,23 +283,25 @@ int gemmq_decode(int fmt, const void *W, float *Wf, int64_t N, int64_t K, void *
 
 /*
  * Measurement export: the int8 matrix-core ceiling the matmul kernels are read
- * against.  Never used on the compute path.  Launches `blocks` workgroups of
+ * against (the pages state no GPU figure for this operator; this measures the
+ * device's own).  Never used on the compute path.  Launches `blocks` workgroups of
  * four waves; each wave runs `iters` rounds of GEMMQ_PROBE_CHAINS independent
  * v_mfma_i32_32x32x32_i8 (32 x 32 x 32 int8 multiply-adds each) on register
  * operands, with no memory traffic, so the time of the launch gives the
  * sustained dense int8 MFMA rate:
  *   int8 ops = 2 * 32768 * GEMMQ_PROBE_CHAINS * 4 * blocks * iters.
- *   iters   >= 1.  blocks in 1..65535.
+ *   iters   1..GEMMQ_PROBE_MAX_ITERS.  blocks in 1..65535.
  *   out     device, int32 [blocks * 256], 4-byte aligned; each lane's sum of its
  *           accumulators (keeps the work live; identical in every workgroup).
  *   clocks  device, uint64 [2], 8-byte aligned: shader-clock cycles
  *           (s_memtime) and 100 MHz counter ticks (s_memrealtime) across the
  *           loop of the first wave, so cycles / ticks * 100 MHz is the shader
  *           clock the loop ran at.
- * Errors: GEMMQ_E_INVALID_ARG (null pointer, iters < 1, blocks out of range),
+ * Errors: GEMMQ_E_INVALID_ARG (null pointer, iters or blocks out of range),
  * GEMMQ_E_ALIGNMENT, GEMMQ_E_DEVICE, GEMMQ_E_LAUNCH.
  */
 #define GEMMQ_PROBE_CHAINS 4
+#define GEMMQ_PROBE_MAX_ITERS 1000000
 int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t *out, uint64_t *clocks,
                         void *stream);
 

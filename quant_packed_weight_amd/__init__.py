@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     FMT_Q5K,
     FMT_Q6K,
     FMT_Q6K_R,
+    GEMM_MAX_M,
     LIB_PATH,
     MAX_GROUP,
     PATH_AUTO,
@@ -23,6 +24,7 @@ from ._lib import (  # noqa: F401
     PATH_GEMV,
     PATH_SKINNY,
     PROBE_CHAINS,
+    PROBE_MAX_ITERS,
     Q8K_BYTES,
     QK,
     GemmqError,

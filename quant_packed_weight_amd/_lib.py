@@ -24,8 +24,10 @@ Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SKINNY = 0, 1, 2, 3
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
-ABI_VERSION = 8
+ABI_VERSION = 9
 PROBE_CHAINS = 4  # GEMMQ_PROBE_CHAINS
+PROBE_MAX_ITERS = 1000000  # GEMMQ_PROBE_MAX_ITERS
+GEMM_MAX_M = 4194240  # GEMMQ_GEMM_MAX_M
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 
@@ -229,6 +231,8 @@ def decode(fmt, w, N, K, out=None, stream=None):
         raise ValueError("w smaller than the stated shape")
     if out is None:
         out = torch.empty((N, K), dtype=torch.float32, device=w.device)
+    elif out.numel() < N * K:
+        raise ValueError("out too small")
     _check(lib().gemmq_decode(fmt, _dev(w, "w", torch.uint8), _dev(out, "out", torch.float32),
                               N, K, _stream(stream)), "gemmq_decode")
     return out

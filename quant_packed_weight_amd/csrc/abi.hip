@@ -72,10 +72,15 @@ uintptr_t fmt_align(int fmt) {
                                                                                                  : 4;
 }
 
-// Launch outcome.  The thread's pending HIP error is cleared just before each
-// launch (see clear_pending), so an error read here belongs to our launch.
+// Launcher outcome: -1 means the shape does not fit the kernel's launch
+// geometry, -2 that the runtime refused a per-device kernel attribute; the
+// callers check both before enqueuing anything (shape_matmul, prepare_matmul),
+// so here they only guard the launchers' own checks.  The thread's pending HIP error is
+// cleared just before each launch (see clear_pending), so an error read here
+// belongs to our launch.
 int launched(int rc) {
-  if (rc != 0) return GEMMQ_E_SHAPE;
+  if (rc == -1) return GEMMQ_E_SHAPE;
+  if (rc != 0) return GEMMQ_E_LAUNCH;
   return hipGetLastError() == hipSuccess ? GEMMQ_OK : GEMMQ_E_LAUNCH;
 }
 
@@ -105,10 +110,13 @@ const char* gemmq_status_str(int status) {
     case GEMMQ_OK: return "GEMMQ_OK";
     case GEMMQ_E_INVALID_ARG: return "GEMMQ_E_INVALID_ARG: null pointer, negative size or bad path";
     case GEMMQ_E_UNSUPPORTED_FORMAT:
-      return "GEMMQ_E_UNSUPPORTED_FORMAT: only q4_K (12) and q6_K (14) are implemented";
+      return "GEMMQ_E_UNSUPPORTED_FORMAT: the weight format must be q2_K (10), q3_K (11), q4_K "
+             "(12), q5_K (13), q6_K (14) or a repacked q3_K / q6_K (267, 270; gemmq_decode and "
+             "gemmq_repack take the plain ones only), and the small-M path takes q4_K only";
     case GEMMQ_E_SHAPE:
-      return "GEMMQ_E_SHAPE: K must be a positive multiple of 256 within limits, and the GEMV "
-             "path takes M <= 8";
+      return "GEMMQ_E_SHAPE: K must be a positive multiple of 256 up to 2^24, rows up to 2^31; "
+             "the GEMV path takes M <= 8, the small-M path M <= 64, the GEMM path M <= "
+             "4194240";
     case GEMMQ_E_ALIGNMENT: return "GEMMQ_E_ALIGNMENT: a pointer breaks the documented alignment";
     case GEMMQ_E_DEVICE: return "GEMMQ_E_DEVICE: the current HIP device is not a gfx950";
     case GEMMQ_E_LAUNCH: return "GEMMQ_E_LAUNCH: the HIP runtime rejected a kernel launch";
@@ -202,6 +210,19 @@ int pick_path(int fmt, int path, int64_t M, int64_t cols) {
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }
 
+// What a matmul launch on `path` could refuse is checked before anything is
+// enqueued, so a group or linear call never leaves the quantizer's output
+// written and then refuses its matmul.  Only the GEMM has limits of its own:
+// its grid's M-tiles (a shape check, made with the argument checks) and the
+// per-device dynamic LDS limit of its kernels (made once the device is known).
+int shape_matmul(int fmt, int path, int64_t M, int64_t K) {
+  return path != GEMMQ_PATH_GEMM || gemmq::gemm_fits(fmt, M, K) ? GEMMQ_OK : GEMMQ_E_SHAPE;
+}
+
+int prepare_matmul(int path, bool silu) {
+  return path != GEMMQ_PATH_GEMM || gemmq::prepare_gemm(silu) == 0 ? GEMMQ_OK : GEMMQ_E_LAUNCH;
+}
+
 int launch_matmul(int fmt, int path, const gemmq::Group& g, const uint8_t* xq, int64_t M,
                   int64_t K, hipStream_t st) {
   if (path == GEMMQ_PATH_GEMV) return gemmq::launch_gemv(fmt, g, xq, (int)M, K, st);
@@ -222,12 +243,17 @@ int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
   if (rc != GEMMQ_OK || M == 0 || rows == 0) return rc;
   if (!Xq) return GEMMQ_E_INVALID_ARG;
   if (!aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
+  const int p = pick_path(fmt, path, M, rows);
+  rc = shape_matmul(fmt, p, M, K);
+  if (rc != GEMMQ_OK) return rc;
   const int dv = check_device();
   if (dv != GEMMQ_OK) return dv;
+  rc = prepare_matmul(p, false);
+  if (rc != GEMMQ_OK) return rc;
   const uint8_t* xq = static_cast<const uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_pending();
-  return launched(launch_matmul(fmt, pick_path(fmt, path, M, rows), g, xq, M, K, st));
+  return launched(launch_matmul(fmt, p, g, xq, M, K, st));
 }
 
 int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y,
@@ -239,11 +265,13 @@ int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y
   if (rc != GEMMQ_OK || M == 0) return rc;
   if (!X || !Xq) return GEMMQ_E_INVALID_ARG;
   if (!aligned(X, 16) || !aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
+  const int p = pick_path(fmt, path, M, rows);
+  if (rows > 0 && (rc = shape_matmul(fmt, p, M, K)) != GEMMQ_OK) return rc;
   const int dv = check_device();
   if (dv != GEMMQ_OK) return dv;
+  if (rows > 0 && (rc = prepare_matmul(p, false)) != GEMMQ_OK) return rc;
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int p = pick_path(fmt, path, M, rows);
   clear_pending();
   if (rows > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
     return launched(gemmq::launch_gemv_fused(fmt, g, X, xq, (int)M, K, st));
@@ -268,8 +296,11 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
   if (M == 0) return GEMMQ_OK;
   if (!X || !Xq || (N > 0 && !Y)) return GEMMQ_E_INVALID_ARG;
   if (!aligned(X, 16) || !aligned(Xq, 4) || (N > 0 && !aligned(Y, 4))) return GEMMQ_E_ALIGNMENT;
+  const int p = pick_path(fmt, path, M, 2 * N);  // as gemmq_linear_group on {Wg, Wu}
+  if (N > 0 && (rc = shape_matmul(fmt, p, M, K)) != GEMMQ_OK) return rc;
   const int dv = check_device();
   if (dv != GEMMQ_OK) return dv;
+  if (N > 0 && (rc = prepare_matmul(p, true)) != GEMMQ_OK) return rc;
   gemmq::Group g{};
   g.count = 2;
   g.W[0] = static_cast<const uint8_t*>(Wg);
@@ -278,7 +309,6 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
   g.N[0] = g.N[1] = N;
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int p = pick_path(fmt, path, M, 2 * N);  // as gemmq_linear_group on {Wg, Wu}
   clear_pending();
   if (N > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
     return launched(gemmq::launch_gemv_silu(fmt, g, nullptr, X, xq, (int)M, K, st));
@@ -340,7 +370,11 @@ int gemmq_decode(int fmt, const void* W, float* Wf, int64_t N, int64_t K, void* 
 
 int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clocks,
                         void* stream) {
-  if (!out || !clocks || iters < 1 || blocks < 1 || blocks > 65535) return GEMMQ_E_INVALID_ARG;
+  // the iteration cap keeps a mistaken argument from occupying the GPU for
+  // long (10^6 rounds of 2048 workgroups run for about a second)
+  if (!out || !clocks || iters < 1 || iters > GEMMQ_PROBE_MAX_ITERS || blocks < 1 ||
+      blocks > 65535)
+    return GEMMQ_E_INVALID_ARG;
   if (!aligned(out, 4) || !aligned(clocks, 8)) return GEMMQ_E_ALIGNMENT;
   if (gemmq::probe_mfma_chains() != GEMMQ_PROBE_CHAINS) return GEMMQ_E_LAUNCH;
   const int dv = check_device();

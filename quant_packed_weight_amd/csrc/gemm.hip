@@ -1056,14 +1056,13 @@ template <bool SILU>
 int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
                hipStream_t st) {
   const int64_t nb = K / kQK;
-  if (nb > 0x7fffffffLL) return -1;
-  if (!set_lds_limits<SILU>()) return -1;
+  if (!gemm_fits(fmt, M, K)) return -1;
+  if (!set_lds_limits<SILU>()) return -2;
   GroupTiles gt;
   const int64_t bn = fmt == 12 ? q4s::kBN : kBN, bm = fmt == 12 ? q4s::kBM : kBM;
   if (!(SILU ? make_pair_tiles(grp, bn, gt) : make_tiles(grp, bn, gt))) return -1;
   const uint32_t gx = gt.start[kMaxGroup];
   const int64_t gy = (M + bm - 1) / bm;
-  if (gy > 65535) return -1;
   if (gx == 0) return 0;
   const dim3 grid(gx, (uint32_t)gy);
   if (fmt == 12) {
@@ -1105,6 +1104,18 @@ int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t 
 }
 
 }  // namespace
+
+// One limit for every format: 65535 tiles of 64 activation rows, the grid's
+// second dimension at the q4_K kernel's tile (the plane kernel's 128-row tiles
+// would take twice as many).
+bool gemm_fits(int fmt, int64_t M, int64_t K) {
+  (void)fmt;
+  return K / kQK <= 0x7fffffffLL && M <= 65535LL * 64;
+}
+
+int prepare_gemm(bool silu) {
+  return (silu ? set_lds_limits<true>() : set_lds_limits<false>()) ? 0 : -2;
+}
 
 int launch_gemm(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
                 hipStream_t st) {

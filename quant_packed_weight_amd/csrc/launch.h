@@ -1,6 +1,7 @@
 // launch.h -- internal launchers behind the C ABI (abi.hip).  Each launcher
-// assumes its arguments were validated by the ABI layer and returns 0, or -1
-// when the problem does not fit the launch geometry.
+// assumes its arguments were validated by the ABI layer and returns 0, -1 when
+// the problem does not fit the launch geometry, or -2 when the runtime refused
+// a per-device kernel attribute the launch needs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -88,6 +89,12 @@ int launch_quantize_q8K(const float* X, uint8_t* Xq, int64_t M, int64_t K, hipSt
 int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 
 int launch_gemm(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K, hipStream_t st);
+// Checked before anything is enqueued, so that a call is refused whole:
+// whether M rows of K fit the GEMM's grid (a pure function of its arguments),
+// and the per-device set-up of its kernels (raising their dynamic LDS limit:
+// 0, or -2 when the runtime refuses).
+bool gemm_fits(int fmt, int64_t M, int64_t K);
+int prepare_gemm(bool silu);
 // The fused decode form: quantize X (M x K f32) and run the GEMV in one launch,
 // each workgroup quantizing into its own LDS; Xq receives the q8_K blocks.
 // Taken when gemv_fusable(M, K): M <= 4 and M K / 256 small enough (see gemv.hip).

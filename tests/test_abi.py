@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 8
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 9
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -87,6 +87,9 @@ FAKE16 = 0x10000  # never dereferenced: every call below fails validation first
     ((13, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),
     ((12, FAKE16, FAKE16, FAKE16, 0, 5, 256, 0), 0),       # M = 0: empty, nothing touched
     ((12, FAKE16, FAKE16, FAKE16, 5, 0, 256, 0), 0),       # N = 0: empty
+    ((12, FAKE16, FAKE16, FAKE16, gq.GEMM_MAX_M + 1, 1, 256, 2), -3),  # GEMM grid limit
+    ((12, FAKE16, FAKE16, FAKE16, gq.GEMM_MAX_M + 1, 1, 256, 0), -3),  # the same, chosen
+    ((14, FAKE16, FAKE16, FAKE16, gq.GEMM_MAX_M + 1, 1, 256, 0), -3),
 ])
 def test_gemm_validation(L, args, status):
     fmt, W, Xq, Y, M, N, K, path = args
@@ -175,6 +178,24 @@ def test_linear_silu_mul_validation(L, args, status):
     assert L.gemmq_linear_silu_mul(*args, None) == status
 
 
+@pytest.mark.parametrize("fmt", [12, 14, 10])
+def test_linear_refused_before_the_quantizer(L, fmt):
+    # a matmul that cannot be launched (M past the GEMM's grid) is refused before
+    # the quantizer is enqueued: the call returns the shape error while X and Xq
+    # are still untouched (no device is needed to reach this status: the check
+    # precedes the device check, and nothing with these pointers is enqueued)
+    P = ctypes.c_void_p
+    wa, ya, na = (P * 1)(FAKE16), (P * 1)(FAKE16), (ctypes.c_int64 * 1)(1)
+    M = gq.GEMM_MAX_M + 1
+    for path in (0, 2):
+        assert L.gemmq_linear_group(fmt, 1, wa, ya, na, FAKE16, FAKE16, M, 256, path, None) == -3
+        assert L.gemmq_linear_silu_mul(fmt, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, M, 1, 256,
+                                       path, None) == -3
+    # with no matrix rows the call only quantizes, and that has no such limit
+    na0 = (ctypes.c_int64 * 1)(0)
+    assert L.gemmq_linear_group(fmt, 1, wa, ya, na0, FAKE16, FAKE16, M, 256, 0, None) == -5
+
+
 def test_linear_group_arrays_and_paths(L):
     P = ctypes.c_void_p
     one_p, one_n = (P * 1)(FAKE16), (ctypes.c_int64 * 1)(1)
@@ -217,6 +238,32 @@ def test_quantize_validation(L, args, status):
 ])
 def test_decode_validation(L, args, status):
     assert L.gemmq_decode(*args, None) == status
+
+
+def test_binding_checks_out_sizes(L):
+    # the torch wrappers refuse an undersized output before any launch (no GPU
+    # here: fake device tensors are never handed to the library)
+    class FakeDev:
+        is_cuda = True
+
+        def __init__(self, n, dtype):
+            import torch
+            self.dtype, self._n = dtype, n
+            self.shape = (n,)
+
+        def numel(self):
+            return self._n
+
+        def is_contiguous(self):
+            return True
+
+        def data_ptr(self):
+            raise AssertionError("reached the library")
+
+    import torch
+    w = FakeDev(144 * 4, torch.uint8)
+    with pytest.raises(ValueError):
+        gq.decode(12, w, 2, 512, out=FakeDev(2 * 512 - 1, torch.float32))
 
 
 def test_binding_raises_named_error(L):
@@ -267,6 +314,7 @@ def test_repacked_formats_accepted_except_decode(L):
     ((1, 1, FAKE16, None), -1),
     ((1, 1, FAKE16 + 2, FAKE16), -4),    # out needs 4 B
     ((1, 1, FAKE16, FAKE16 + 4), -4),    # clocks need 8 B
+    ((gq.PROBE_MAX_ITERS + 1, 1, FAKE16, FAKE16), -1),  # past the iteration cap
 ])
 def test_probe_validation(L, args, status):
     assert L.gemmq_probe_mfma_i8(*args, None) == status
