@@ -24,10 +24,7 @@
 //    y += d_x * (d * I_sc - dmin * I_min)   (q3_K, q6_K: y += d_x * d * I_sc).
 //
 // Two kernels:
-//  * q4_K (gemm_q4k_kernel, further below): activation and raw weight tiles
-//    stream through LDS stages filled by direct buffer->LDS loads; each wave
-//    unpacks its own 32 weight rows and computes a 64 x 32 tile; wave
-//    priorities by phase keep the two waves of a SIMD out of step.
+//  * q4_K: gemm_q4k_kernel in gemm_q4k.hip (launched from here).
 //  * q2_K, q3_K, q5_K, q6_K (gemm_plane_kernel): a 256-thread workgroup
 //    computes a 128 (M) x 64 (N) tile, each of its four waves a 64 x 32
 //    sub-tile.  Per super-block the workgroup stages the activation tile (int8
@@ -42,23 +39,17 @@
 #include <atomic>
 
 #include "device.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace gemmq {
 
 namespace {
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
+using namespace gk;
 
 constexpr int kBM = 128;        // activation rows per workgroup
 constexpr int kBN = 64;         // weight rows (output columns) per workgroup
-constexpr int kRow = 256 + 16;  // LDS stride of one int8 K-row (padded against bank conflicts)
 
 // LDS map of one stage (bytes)
 constexpr int kOffA = 0;                     // [kBM][kRow] activation int8
@@ -75,31 +66,6 @@ constexpr int kOffBs = kOffDm + kBN * 4;     // [kBM][16] f16 group sums
 constexpr int kOffMn = kOffBs + kBM * 32;    // [kBN][16] f16 mins (per group of 16)
 constexpr int kLdsMin = kOffMn + kBN * 32;   // still two workgroups per CU
 static_assert(2 * kLdsMin <= 160 * 1024, "two workgroups per CU");
-
-// bytes of w (each <= 15) times a (<= 7): per 16-bit half the product stays below
-// 2^16 and no byte carries into the next.
-__device__ __forceinline__ uint32_t mul_bytes(uint32_t w, uint32_t a) {
-  const u16x2 v = __builtin_bit_cast(u16x2, w);
-  const u16x2 s = {(unsigned short)a, (unsigned short)a};
-  return __builtin_bit_cast(uint32_t, v * s);
-}
-
-__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
-  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ void st16(uint8_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  *reinterpret_cast<uint4*>(p) = make_uint4(a, b, c, d);
-}
-
-// two int16 (packed in a dword) -> two f16 (exact: |value| <= 2048)
-__device__ __forceinline__ uint32_t i16x2_to_h2(uint32_t w) {
-  const h2 v = {(_Float16)(short)(w & 0xffffu), (_Float16)(short)(w >> 16)};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // ------------------------------------------------- activation tile (plane kernel)
 // thread t: row t/2, half t%2 of the 256 int8 values; half 0 also d_x.  With
@@ -155,26 +121,6 @@ __device__ __forceinline__ const uint8_t* w_row(const uint8_t* __restrict__ W,
   } else {
     return W + (n < N ? n : N - 1) * nb * BYTES;
   }
-}
-
-// y = silu(g) * u (the same f32 steps as the GEMV's): e = exp(-g), g / (1 + e), * u
-__device__ __forceinline__ float silu_mul_f32(float g, float u) {
-  return g / (1.0f + expf(-g)) * u;
-}
-
-// the value of lane ^ 1 (quad permute [1,0,3,2]); every lane must be active
-__device__ __forceinline__ float pair_partner(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF,
-                                                            0xF, true));
-}
-
-// Lanes 2k (odd = false) and 2k+1 hold the gate and the up output of one column
-// for two rows a, b.  One swap hands the even lane (gate_a, up_a) and the odd
-// lane (gate_b, up_b), so each lane finishes one row of the pair.
-__device__ __forceinline__ void silu_pair(float a, float b, bool odd, float& g, float& u) {
-  const float got = pair_partner(odd ? a : b);  // even lanes get up_a, odd lanes gate_b
-  g = odd ? got : a;
-  u = odd ? b : got;
 }
 
 // ------------------------------------------------- weight tiles of the plane kernel
@@ -634,389 +580,6 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
   }
 }
 
-// ------------------------------------------------- q4_K: streamed tiles
-// The q4_K kernel streams both operands through a ring of LDS stages filled by
-// direct buffer->LDS loads (no registers held for the prefetch, no copy loop):
-//   workgroup = 4 waves, tile 64 (M) x 128 (N); wave w: all 64 rows, weight
-//   columns 32w..32w+31, unpacking its own planes (shared by its two M-tiles);
-//   stage = int8 values [64][272] | group sums [64][16] | d_x [64] |
-//   raw q4_K blocks [128][144] (38 KB); two stages, so two workgroups share a
-//   CU and one computes while the other waits;
-//   the two planes go to two accumulators so every activation fragment is
-//   read from LDS once, three MFMA steps ahead of its use.
-// The next stage's loads are issued a sixteenth at a time, one part per
-// compute chunk, so the load queue never stalls the wave for long.  They are
-// issued from inline assembly: the compiler then neither sees them as LDS
-// writes (it would drain every load before each LDS read) nor tracks them, and
-// the kernel waits on vmcnt itself: a stage's loads are complete once fewer
-// than one stage's worth of later loads is outstanding.
-namespace q4s {
-constexpr int kBM = 64;
-constexpr int kBN = 128;
-constexpr int kS = 2;                       // LDS stages
-constexpr int kOffQ = 0;                    // [kBM][kRow] int8
-constexpr int kOffBs = kBM * kRow;          // [kBM][16] int16 group sums
-constexpr int kOffDx = kOffBs + kBM * 32;   // [kBM] f32 d_x
-constexpr int kOffW = kOffDx + kBM * 4;     // [kBN][144] raw weight blocks
-constexpr int kStage = kOffW + kBN * kQ4KBytes;
-// SPLIT K-groups of four waves per workgroup: 1 (76 KB, two workgroups per CU)
-// or 2 (152.6 KB, one workgroup of eight waves per CU, each group half of the
-// super-blocks); both give two waves per SIMD when the grid fills the CUs, and
-// the split keeps two per SIMD on grids of one workgroup per CU.  It is chosen
-// from K alone (rows of 32 super-blocks or more), so an output's summation
-// order never depends on M.
-template <int SPLIT>
-constexpr int lds_bytes() { return kS * SPLIT * kStage; }
-// loads per stage issued by each wave: 16 value rows + 2 group-sum blocks + 4
-// weight chunks (waves 0 and 1 a fifth, wave 0 also the 64 d_x); waits count
-// the smallest number, which can only wait for more than needed.
-constexpr int kDma = 22;
-constexpr int kWait = kDma * (kS - 2) < 63 ? kDma * (kS - 2) : 63;  // vmcnt field is 6 bits
-}  // namespace q4s
-
-typedef int rsrc_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// Raw buffer descriptor over [base, base + bytes): offsets at or past `bytes`
-// read as zero.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  return (rsrc_t){(int)(uint32_t)a, (int)((a >> 32) & 0xffffu), (int)bytes, 0x00020000};
-}
-
-// 64 lanes x 4 bytes: lane l's dword from buffer byte voff(l) + soff to LDS
-// byte lds + 4 l (lds wave-uniform, through M0).  The s_nop covers the one
-// wait state an M0 write needs before a load into LDS.
-__device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff),
-               "{m0}"(lds)
-               : "memory");
-}
-
-// Same with 16 bytes per lane (16-byte aligned source) to LDS byte lds + 16 l.
-__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs),
-               "s"(soff), "{m0}"(lds)
-               : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// own LDS writes done, then the workgroup barrier; the memory clobber keeps the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// f32 epilogue of accumulator registers r0..r0+n-1 of one 32x32 tile:
-// y += d_x * (d * I_sc - dmin * I_min), I_sc = 8 * A + B from the two plane
-// accumulators; dx[r] is d_x of the register's row.
-template <int n>
-__device__ __forceinline__ void q4s_epilogue(const v16i& acca, const v16i& accb, const v16f& am,
-                                             const float (&dx)[16], float dcol, float mcol,
-                                             float (&y)[16], int r0) {
-#pragma unroll
-  for (int r = r0; r < r0 + n; ++r) {
-    const int isc = (int)(((uint32_t)acca[r] << 3) + (uint32_t)accb[r]);
-    float tt = dcol * (float)isc;
-    tt = fmaf(-mcol, am[r], tt);
-    y[r] = fmaf(dx[r], tt, y[r]);
-  }
-}
-
-// d_x of the 16 rows a lane's accumulator registers hold in the tile whose
-// first row in the stage is row0 - 4h: register r <-> row row0 + 8(r/4) + r%4.
-__device__ __forceinline__ void q4s_load_dx(const uint8_t* st, int row0, float (&dx)[16]) {
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const float4 v = *reinterpret_cast<const float4*>(st + q4s::kOffDx + 4 * (row0 + 8 * q4));
-    dx[4 * q4] = v.x;
-    dx[4 * q4 + 1] = v.y;
-    dx[4 * q4 + 2] = v.z;
-    dx[4 * q4 + 3] = v.w;
-  }
-}
-
-// the two weight planes of MFMA step kc from the lane's raw quant bytes
-__device__ __forceinline__ void q4s_planes(const uint4 (&q)[4], const uint32_t (&aw)[2],
-                                           const uint32_t (&bw)[2], int kc, v4i& pa, v4i& pb) {
-  const uint4 raw = q[kc >> 1];
-  const uint32_t r4[4] = {raw.x, raw.y, raw.z, raw.w};
-  const uint32_t a = (aw[kc >> 2] >> (8 * (kc & 3))) & 0xffu;
-  const uint32_t bb = (bw[kc >> 2] >> (8 * (kc & 3))) & 0xffu;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t nib = (kc & 1) ? hi_nib(r4[k]) : lo_nib(r4[k]);
-    pa[k] = (int)mul_bytes(nib, a);
-    pb[k] = (int)mul_bytes(nib, bb);
-  }
-}
-
-// One super-block for one wave from stage `st`: lane (i, h) holds weight row
-// i of the wave's 32 and K-half h of every 32-wide MFMA step (bytes 16h..16h+15
-// of the sub-block).  The work is laid out in fenced chunks so that vector
-// work sits beside independent matrix work: M-tile 0's MFMAs of step kc run
-// beside the unpacking of step kc+1, M-tile 1's MFMAs beside tile 0's
-// epilogue; tile 1's epilogue closes the super-block.  dma(p), p = 0..15, is
-// called at the head of chunk p: it issues part p of the next stage's loads,
-// so the load queue fills a little at a time instead of stalling the wave.
-template <typename Dma>
-__device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (&y)[2][16], int i,
-                                            int h, Dma&& dma) {
-  using q4s::kOffBs;
-  using q4s::kOffQ;
-  const uint8_t* wb = st + q4s::kOffW + wrow * kQ4KBytes;
-  const uint8_t* a0 = st + kOffQ + i * kRow + 16 * h;  // M-tile 0 fragments, step kc at +32 kc
-  const uint8_t* a1 = a0 + 32 * kRow;                  // M-tile 1
-  // activation fragments are read kAhead chunks before their MFMAs: fragment
-  // f = 0..15 is M-tile f/8, step f%8
-  constexpr int kAhead = 3;
-  v4i af[16];
-  auto read_af = [&](int f) {
-    af[f] = *reinterpret_cast<const v4i*>((f < 8 ? a0 : a1) + 32 * (f & 7));
-  };
-  const uint4 hd = *reinterpret_cast<const uint4*>(wb);
-  uint4 q[4];
-#pragma unroll
-  for (int p = 0; p < 4; ++p) q[p] = *reinterpret_cast<const uint4*>(wb + 16 + 32 * p + 16 * h);
-#pragma unroll
-  for (int f = 0; f < kAhead; ++f) read_af(f);
-  const Q4KScales s = q4k_scales(hd.y, hd.z, hd.w);
-  const uint32_t aw[2] = {(s.sc_lo >> 3) & 0x07070707u, (s.sc_hi >> 3) & 0x07070707u};
-  const uint32_t bw[2] = {s.sc_lo & 0x07070707u, s.sc_hi & 0x07070707u};
-  v4i pa[8], pb[8];
-  q4s_planes(q, aw, bw, 0, pa[0], pb[0]);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // Wave priorities (s_setprio) by phase: of the two waves that share a SIMD
-  // (one from each workgroup on the CU), the one whose matrix work is ahead
-  // gets the issue slots first -- phase A 2, phase B 1, the epilogue-only
-  // phase C 0 -- so MFMAs keep arriving while the other wave's vector work
-  // fills the gaps (measured +6% at M = 512, bit-identical results).
-  // phase A: M-tile 0, unpack one step ahead
-  __builtin_amdgcn_s_setprio(2);
-  v16i acca0 = (v16i){0}, accb0 = (v16i){0};
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    dma(kc);
-    acca0 = mfma_i8(af[kc], pa[kc], acca0);
-    accb0 = mfma_i8(af[kc], pb[kc], accb0);
-    read_af(kc + kAhead);
-    if (kc < 7) q4s_planes(q, aw, bw, kc + 1, pa[kc + 1], pb[kc + 1]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // min-term operands: lane half h carries group sums 8h..8h+7 against m_{(8h+t)/2}
-  const uint32_t mw = h ? s.mn_hi : s.mn_lo;
-  v8h mfrag;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const _Float16 m = (_Float16)(float)((mw >> (8 * k)) & 0xffu);
-    mfrag[2 * k] = m;
-    mfrag[2 * k + 1] = m;
-  }
-  v8h sfrag[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {  // group sums of row 32t+i: int16 -> f16 (exact, |sum| <= 2032)
-    const uint4 braw = *reinterpret_cast<const uint4*>(st + kOffBs + (32 * t + i) * 32 + 16 * h);
-    const uint32_t bh[4] = {i16x2_to_h2(braw.x), i16x2_to_h2(braw.y), i16x2_to_h2(braw.z),
-                            i16x2_to_h2(braw.w)};
-    sfrag[t] = __builtin_bit_cast(v8h, bh);
-  }
-  const float dcol = f16_to_f32(hd.x), mcol = f16_to_f32(hd.x >> 16);
-  float dx[16];
-  q4s_load_dx(st, 4 * h, dx);
-  const v16f am0 = mfma_f16(sfrag[0], mfrag, (v16f){0});
-  __builtin_amdgcn_sched_barrier(0);
-
-  // phase B: M-tile 1 beside tile 0's epilogue, two registers per step
-  __builtin_amdgcn_s_setprio(1);
-  v16i acca1 = (v16i){0}, accb1 = (v16i){0};
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    dma(8 + kc);
-    acca1 = mfma_i8(af[8 + kc], pa[kc], acca1);
-    accb1 = mfma_i8(af[8 + kc], pb[kc], accb1);
-    if (8 + kc + kAhead < 16) read_af(8 + kc + kAhead);
-    q4s_epilogue<2>(acca0, accb0, am0, dx, dcol, mcol, y[0], 2 * kc);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // phase C: tile 1's epilogue
-  __builtin_amdgcn_s_setprio(0);
-  q4s_load_dx(st, 32 + 4 * h, dx);
-  const v16f am1 = mfma_f16(sfrag[1], mfrag, (v16f){0});
-  q4s_epilogue<16>(acca1, accb1, am1, dx, dcol, mcol, y[1], 0);
-}
-
-// SILU: the tile's 128 weight rows are gate rows 64t..64t+63 then up rows
-// 64t..64t+63 (two buffer descriptors; load groups 0..8 and 9..17 split exactly
-// at row 64), and lane i of wave w unpacks gate row 16w + i/2 for even i, the up
-// row for odd i, so each MFMA column pair holds (gate, up) of one output.
-template <int SPLIT, bool SILU>
-__global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k_kernel(
-    const GroupTiles gt, const uint8_t* __restrict__ Xq, int64_t M, int nb) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  // SPLIT groups of four waves: K-group kg takes super-blocks [kg nb0, ...);
-  // in each group wave `wave` owns weight columns 32 wave .. 32 wave + 31
-  const int wave8 = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int kg = SPLIT > 1 ? wave8 >> 2 : 0, wave = wave8 & 3;
-  const int lane = lane_id(), i = lane & 31, h = lane >> 5;
-  // XCD-aware order: workgroup L (x fastest) runs on XCD L % 8, each XCD with
-  // its own L2.  Give XCD x a contiguous block of the (column tile, M-tile)
-  // order with the M-tiles fastest, so the workgroups that read one weight
-  // tile run together on one XCD and fetch it from HBM once.
-  const uint32_t gy = gridDim.y, total = gridDim.x * gy;
-  const uint32_t lin = blockIdx.x + gridDim.x * blockIdx.y;
-  const uint32_t full = total & ~7u;
-  const uint32_t ord = lin < full ? (lin & 7u) * (full >> 3) + (lin >> 3) : lin;
-  const TileMatrix tm = tile_matrix(gt, ord / gy);
-  const uint8_t* __restrict__ W = tm.W;
-  float* __restrict__ Y = tm.Y;
-  const int64_t N = tm.N;
-  const uint32_t tile = tm.local;
-  const int64_t n0 = (int64_t)tile * q4s::kBN, m0 = (int64_t)(ord % gy) * q4s::kBM;
-  const uint32_t xstride = (uint32_t)nb * kQ8KBytes, wstride = (uint32_t)nb * kQ4KBytes;
-  // the workgroup's activation rows and weight rows as two buffers: rows past
-  // M or N read as zero (their outputs are never stored)
-  const int64_t mrows = M - m0 < q4s::kBM ? M - m0 : q4s::kBM;
-  const rsrc_t xr = make_rsrc(Xq + m0 * xstride, (uint32_t)(mrows * xstride));
-  // SILU: outputs o0..o0+63 of Nout; wr covers the gate rows, wr2 the up rows
-  const int64_t Nout = SILU ? N >> 1 : N, o0 = SILU ? (int64_t)tile * (q4s::kBN / 2) : n0;
-  const int64_t orows = SILU ? (Nout - o0 < q4s::kBN / 2 ? Nout - o0 : q4s::kBN / 2)
-                             : (N - n0 < q4s::kBN ? N - n0 : q4s::kBN);
-  const rsrc_t wr = make_rsrc(W + o0 * wstride, (uint32_t)(orows * wstride));
-  const rsrc_t wr2 = SILU ? make_rsrc(gt.W[1] + o0 * wstride, (uint32_t)(orows * wstride)) : wr;
-  // this group's half of every stage
-  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>((lds_void_t*)lds) +
-                        (uint32_t)kg * q4s::kStage;
-  uint8_t* const ldsg = lds + kg * q4s::kStage;
-  constexpr int kStride = SPLIT * q4s::kStage;  // bytes from one stage to the next
-
-  // per-lane source offsets within one super-block column
-  const uint32_t vq = 4 + 4 * lane;  // value bytes of a row: one dword per lane
-  uint32_t vbs[2];                   // group sums: row 8j + lane/8, dword lane%8
-#pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-    vbs[jj] = (uint32_t)(8 * (wave + 4 * jj) + (lane >> 3)) * xstride + 260 + 4 * (lane & 7);
-  const uint32_t vdx = (uint32_t)lane * xstride;  // d_x of row lane
-  // weight load u = wave + 4j (u < 18) covers 16-byte chunks 64u..64u+63 of
-  // the 128 x 9-chunk tile, i.e. row c / 9, chunk c % 9 for c = 64u + lane
-  uint32_t vw[5];
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const uint32_t u = (uint32_t)(wave + 4 * j);
-    const uint32_t c = 64u * u + (uint32_t)lane;
-    const uint32_t row = c / 9u - (SILU && u >= 9u ? 64u : 0u);  // up rows from wr2's base
-    vw[j] = row * wstride + 16u * (c % 9u);
-  }
-
-  // part p (0..15) of the loads of super-block b into stage `slot`: value rows
-  // 2p, 2p+1 (p < 8), the two group-sum blocks (8, 9), d_x (10), the weight
-  // chunks (11..15)
-  auto issue = [&](int b, int slot, int p) {
-    const uint32_t st = lds0 + (uint32_t)slot * kStride;
-    const uint32_t xb = (uint32_t)b * kQ8KBytes, wb = (uint32_t)b * kQ4KBytes;
-    if (p < 8) {
-#pragma unroll
-      for (int j = 2 * p; j < 2 * p + 2; ++j) {
-        const uint32_t r = (uint32_t)(wave + 4 * j);
-        dma4(xr, vq, r * xstride + xb, st + q4s::kOffQ + r * kRow);
-      }
-    } else if (p < 10) {
-      dma4(xr, vbs[p - 8], xb, st + q4s::kOffBs + (wave + 4 * (p - 8)) * 256);
-    } else if (p == 10) {
-      if (wave == 0) dma4(xr, vdx, xb, st + q4s::kOffDx);
-    } else if (p < 15) {
-      const int u = wave + 4 * (p - 11);
-      dma16(SILU && u >= 9 ? wr2 : wr, vw[p - 11], wb, st + q4s::kOffW + 1024 * u);
-    } else {
-      if (wave < 2) dma16(SILU ? wr2 : wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
-    }
-  };
-  float y[2][16];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) y[t][r] = 0.0f;
-  // the LDS weight row this lane unpacks (its MFMA column)
-  const int wrow_l = SILU ? ((i & 1) ? 64 : 0) + 16 * wave + (i >> 1) : 32 * wave + i;
-
-  // Step s: group kg works on super-block b0 + s.  Every step issues one stage
-  // of loads -- past the group's last block they re-read a valid block into a
-  // stage nobody reads -- so the wait count is static.
-  const int nb0 = SPLIT > 1 ? (nb + 1) >> 1 : nb;
-  const int b0 = kg ? nb0 : 0, bend = kg ? nb : nb0;
-  auto blk = [&](int s) { return b0 + s < nb ? b0 + s : nb - 1; };
-#pragma unroll
-  for (int s = 0; s < q4s::kS - 1; ++s)
-#pragma unroll
-    for (int p = 0; p < 16; ++p) issue(blk(s), s, p);
-  int slot = 0;
-  for (int s = 0; s < nb0; ++s) {
-    wait_vm<q4s::kWait>();  // own loads of stage s landed
-    lds_barrier();  // stage s complete everywhere; the stage of s-1 is free
-    const int nxt = slot == 0 ? q4s::kS - 1 : slot - 1;
-    const int bn = blk(s + q4s::kS - 1);
-    if (b0 + s < bend)
-      q4s_compute(ldsg + slot * kStride, wrow_l, y, i, h,
-                  [&](int p) { issue(bn, nxt, p); });
-    else  // the second group's idle last step (odd nb): only its loads
-#pragma unroll
-      for (int p = 0; p < 16; ++p) issue(bn, nxt, p);
-    slot = slot + 1 == q4s::kS ? 0 : slot + 1;
-  }
-  wait_vm<0>();  // no load into LDS outlives the workgroup
-
-  if constexpr (SPLIT > 1) {
-    // the second K-group hands its partial sums to the first through LDS; the
-    // first adds them (its own first) and stores
-    lds_barrier();
-    float* red = reinterpret_cast<float*>(lds) + wave * (32 * 64) + lane;
-    if (kg == 1) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[(16 * t + r) * 64] = y[t][r];
-    }
-    lds_barrier();
-    if (kg == 1) return;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) y[t][r] += red[(16 * t + r) * 64];
-  }
-  if constexpr (SILU) {
-    // lanes 2k / 2k+1 hold gate / up of output o0 + 16 wave + k for the same rows
-    const int64_t n = o0 + 16 * wave + (i >> 1);
-    const bool odd = (i & 1) != 0;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        float g, u;
-        silu_pair(y[t][r], y[t][r + 1], odd, g, u);
-        const int rr = r + (odd ? 1 : 0);
-        const int64_t row = m0 + 32 * t + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        if (n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(g, u);
-      }
-  } else {
-    const int64_t col = n0 + 32 * wave + i;
-    if (col < N) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = m0 + 32 * t + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (row < M) Y[row * N + col] = y[t][r];
-        }
-    }
-  }
-}
-
 }  // namespace
 
 namespace {
@@ -1040,12 +603,7 @@ bool set_lds_limits() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_plane_kernel<13, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_q4k_kernel<1, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            q4s::lds_bytes<1>()) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_q4k_kernel<2, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            q4s::lds_bytes<2>()) != hipSuccess)
+        !q4k_prepare(SILU))
       return false;
     attr_done[dev].store(1, std::memory_order_release);
   }
@@ -1059,21 +617,14 @@ int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t 
   if (!gemm_fits(fmt, M, K)) return -1;
   if (!set_lds_limits<SILU>()) return -2;
   GroupTiles gt;
-  const int64_t bn = fmt == 12 ? q4s::kBN : kBN, bm = fmt == 12 ? q4s::kBM : kBM;
+  const int64_t bn = fmt == 12 ? 128 : kBN;
   if (!(SILU ? make_pair_tiles(grp, bn, gt) : make_tiles(grp, bn, gt))) return -1;
+  if (fmt == 12) return launch_gemm_q4k(gt, SILU, Xq, M, K, st);
   const uint32_t gx = gt.start[kMaxGroup];
-  const int64_t gy = (M + bm - 1) / bm;
+  const int64_t gy = (M + kBM - 1) / kBM;
   if (gx == 0) return 0;
   const dim3 grid(gx, (uint32_t)gy);
-  if (fmt == 12) {
-    // long rows run split over K (the choice depends on K only)
-    if (nb >= 32)
-      hipLaunchKernelGGL((gemm_q4k_kernel<2, SILU>), grid, dim3(512), q4s::lds_bytes<2>(), st, gt,
-                         Xq, M, (int)nb);
-    else
-      hipLaunchKernelGGL((gemm_q4k_kernel<1, SILU>), grid, dim3(256), q4s::lds_bytes<1>(), st, gt,
-                         Xq, M, (int)nb);
-  } else {
+  {
     switch (fmt) {
       case 10:
         hipLaunchKernelGGL((gemm_plane_kernel<10, SILU>), grid, dim3(256), kLdsMin, st, gt, Xq, M,

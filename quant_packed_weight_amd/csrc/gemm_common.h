@@ -1,0 +1,135 @@
+// gemm_common.h -- pieces the two prefill GEMM kernels share (gemm.hip: the
+// plane kernel for q2_K, q3_K, q5_K, q6_K; gemm_q4k.hip: the q4_K kernel):
+// matrix-core wrappers, the plane-byte multiply, buffer descriptors and
+// direct buffer->LDS loads, and the SiLU-gated output pair.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gemmq {
+namespace gk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kRow = 256 + 16;  // LDS stride of one int8 K-row (padded against bank conflicts)
+
+// bytes of w (each <= 15) times a (<= 7): per 16-bit half the product stays below
+// 2^16 and no byte carries into the next.
+__device__ __forceinline__ uint32_t mul_bytes(uint32_t w, uint32_t a) {
+  const u16x2 v = __builtin_bit_cast(u16x2, w);
+  const u16x2 s = {(unsigned short)a, (unsigned short)a};
+  return __builtin_bit_cast(uint32_t, v * s);
+}
+
+// bytes of w times the factor already replicated into both 16-bit halves of f
+__device__ __forceinline__ uint32_t mul_bytes2(uint32_t w, uint32_t f) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) * __builtin_bit_cast(u16x2, f));
+}
+
+__device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void st16(uint8_t* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(a, b, c, d);
+}
+
+// two int16 (packed in a dword) -> two f16 (exact: |value| <= 2048)
+__device__ __forceinline__ uint32_t i16x2_to_h2(uint32_t w) {
+  const h2 v = {(_Float16)(short)(w & 0xffffu), (_Float16)(short)(w >> 16)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+typedef int rsrc_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Raw buffer descriptor over [base, base + bytes): offsets at or past `bytes`
+// read as zero.  Both arguments must be wave-uniform; the components are
+// taken through readfirstlane so that the descriptor lives in scalar
+// registers (the inline-asm loads below require it there, and under register
+// pressure the compiler may otherwise compute it with vector instructions).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return (rsrc_t){__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                  __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu)),
+                  __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
+}
+
+// 64 lanes x 4 bytes: lane l's dword from buffer byte voff(l) + soff to LDS
+// byte lds + 4 l (lds wave-uniform, through M0).  The s_nop covers the one
+// wait state an M0 write needs before a load into LDS.  Issued from inline
+// assembly: through the builtin the compiler treats such a load as an LDS
+// write of unknown alias and drains every load before each LDS read, so the
+// kernels count these loads themselves (wait_vm).
+__device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff),
+               "{m0}"(lds)
+               : "memory");
+}
+
+// Same with 16 bytes per lane (16-byte aligned source) to LDS byte lds + 16 l.
+__device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs),
+               "s"(soff), "{m0}"(lds)
+               : "memory");
+}
+
+// a * b + c in scalar registers, computed where it is used: the kernels issue
+// dozens of row loads per stage, and offsets the compiler hoisted out of the
+// loop would each hold a scalar register for the whole kernel.
+__device__ __forceinline__ uint32_t smad(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm volatile("s_mul_i32 %0, %1, %2\n\ts_add_u32 %0, %0, %3" : "=&s"(r) : "s"(a), "s"(b), "s"(c)
+               : "scc");
+  return r;
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone.  Through the builtin,
+// not inline asm: the compiler's own wait insertion then knows every vector
+// load issued before this point is complete, and does not add a wait of its
+// own (which would also wait for loads issued after this point) before the
+// first use of a register loaded earlier.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// own LDS writes done, then the workgroup barrier; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// y = silu(g) * u (the same f32 steps as the GEMV's): e = exp(-g), g / (1 + e), * u
+__device__ __forceinline__ float silu_mul_f32(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// the value of lane ^ 1 (quad permute [1,0,3,2]); every lane must be active
+__device__ __forceinline__ float pair_partner(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF,
+                                                            0xF, true));
+}
+
+// Lanes 2k (odd = false) and 2k+1 hold the gate and the up output of one column
+// for two rows a, b.  One swap hands the even lane (gate_a, up_a) and the odd
+// lane (gate_b, up_b), so each lane finishes one row of the pair.
+__device__ __forceinline__ void silu_pair(float a, float b, bool odd, float& g, float& u) {
+  const float got = pair_partner(odd ? a : b);  // even lanes get up_a, odd lanes gate_b
+  g = odd ? got : a;
+  u = odd ? b : got;
+}
+
+}  // namespace gk
+}  // namespace gemmq

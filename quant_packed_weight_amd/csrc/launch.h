@@ -95,6 +95,11 @@ int launch_gemm(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K
 // 0, or -2 when the runtime refuses).
 bool gemm_fits(int fmt, int64_t M, int64_t K);
 int prepare_gemm(bool silu);
+// gemm_q4k.hip: the q4_K GEMM over the 128-row weight tiles of `gt` (its LDS
+// limits raised once per device by q4k_prepare; 0 or -1 as the launchers).
+bool q4k_prepare(bool silu);
+int launch_gemm_q4k(const GroupTiles& gt, bool silu, const uint8_t* Xq, int64_t M, int64_t K,
+                    hipStream_t st);
 // The fused decode form: quantize X (M x K f32) and run the GEMV in one launch,
 // each workgroup quantizing into its own LDS; Xq receives the q8_K blocks.
 // Taken when gemv_fusable(M, K): M <= 4 and M K / 256 small enough (see gemv.hip).
