@@ -45,41 +45,50 @@ def gq():
     return quant_packed_weight_amd
 
 
-def exact_weights(rng, fmt, N, K):
+def exact_weights(rng, fmt, N, K, quiet=None):
     """Packed weights with power-of-two d/dmin and full-range fields; returns
     (raw [N, row bytes], mag [N, K]) where mag bounds, per weight, every integer
-    product a kernel forms from it (times its power-of-two scale)."""
+    product a kernel forms from it (times its power-of-two scale).  `quiet`:
+    positions within each block (one per block) whose quant makes sc*q zero in
+    every row (q = 0; q6_K: q = 32)."""
     base = fmt & 255
     n = N * (K // 256)
+
+    def hush(q, zero):
+        if quiet is not None:
+            q.reshape(N, K // 256, 256)[:, np.arange(K // 256), quiet] = zero
+        return q
+
     d = 2.0 ** -rng.integers(10, 12, n)
     dmin = 2.0 ** -rng.integers(10, 12, n)
     if base in (Q4, Q5):
         sc, mn = rng.integers(0, 64, (n, 8)), rng.integers(0, 64, (n, 8))
-        q = rng.integers(0, 16 if base == Q4 else 32, (n, 256))
+        q = hush(rng.integers(0, 16 if base == Q4 else 32, (n, 256)), 0)
         raw = (pack_q4K if base == Q4 else pack_q5K)(d, dmin, sc, mn, q)
         mag = d[:, None] * np.repeat(sc, 32, 1) * q + dmin[:, None] * np.repeat(mn, 32, 1)
     elif base == Q2:
         sc, mn = rng.integers(0, 16, (n, 16)), rng.integers(0, 16, (n, 16))
-        q = rng.integers(0, 4, (n, 256))
+        q = hush(rng.integers(0, 4, (n, 256)), 0)
         raw = pack_q2K(d, dmin, sc, mn, q)
         mag = d[:, None] * np.repeat(sc, 16, 1) * q + dmin[:, None] * np.repeat(mn, 16, 1)
     elif base == Q3:
-        sc, q = rng.integers(-32, 32, (n, 16)), rng.integers(-4, 4, (n, 256))
+        sc, q = rng.integers(-32, 32, (n, 16)), hush(rng.integers(-4, 4, (n, 256)), 0)
         raw = pack_q3K(d, sc, q)
         # the -4 of a clear mask bit is folded in int32 (exact), so the f32
         # terms are subset sums of the weights' own products
         mag = d[:, None] * np.abs(np.repeat(sc, 16, 1) * q)
     else:
-        sc, q = rng.integers(-128, 128, (n, 16)), rng.integers(0, 64, (n, 256))
+        sc, q = rng.integers(-128, 128, (n, 16)), hush(rng.integers(0, 64, (n, 256)), 32)
         raw = pack_q6K(d, sc, q)
         # the -32 offset is folded in int32 (exact), as for q3_K
         mag = d[:, None] * np.abs(np.repeat(sc, 16, 1) * (q - 32))
     return raw.reshape(N, -1), mag.reshape(N, K)
 
 
-def exact_acts(rng, M, K, mag, spike=False):
+def exact_acts(rng, M, K, mag, spike=None):
     """q8_K fields (dx [M, nb], qx [M, K] int) whose every output stays within
-    LIMIT for the weight magnitudes `mag`; spike: one +-127 per block."""
+    LIMIT for the weight magnitudes `mag`; spike: per block, the position (as
+    given to exact_weights' `quiet`) that holds a +-127 in every row."""
     nb = K // 256
     dx = 2.0 ** -rng.integers(7, 9, (M, nb))
     u = rng.random((M, K))
@@ -87,10 +96,8 @@ def exact_acts(rng, M, K, mag, spike=False):
     qx = np.where(u > 0.97, rng.integers(8, 127, (M, K)), qx)
     qx = qx * rng.choice([-1, 1], (M, K))
     spikes = None
-    if spike:
-        # each block's +-127 where the weights are smallest
-        low = mag.max(0).reshape(nb, 256).argmin(1) + 256 * np.arange(nb)
-        spikes = np.repeat(low[None, :], M, 0)
+    if spike is not None:
+        spikes = np.repeat((np.asarray(spike) + 256 * np.arange(nb))[None, :], M, 0)
         np.put_along_axis(qx, spikes, rng.choice([-127, 127], (M, nb)), axis=1)
     dxk = np.repeat(dx, 256, 1)
     for m in range(M):
@@ -99,7 +106,7 @@ def exact_acts(rng, M, K, mag, spike=False):
             if B <= LIMIT:
                 break
             nz = np.flatnonzero(qx[m])
-            if spike:
+            if spike is not None:
                 nz = np.setdiff1d(nz, spikes[m])
             assert nz.size, "the spikes alone pass the bound; use a shorter K"
             qx[m, rng.choice(nz, (nz.size + 1) // 2, replace=False)] = 0
@@ -198,9 +205,10 @@ def test_exact_linear(dev, gq, orc, fmt, M, K):
     log("exact linear fmt=%d M=%d K=%d" % (fmt, M, K))
     rng = np.random.default_rng(5000 + fmt + M + K)
     Ns = [64, 33]
-    mats = [exact_weights(rng, fmt, N, K) for N in Ns]
+    quiet = rng.integers(0, 256, K // 256)
+    mats = [exact_weights(rng, fmt, N, K, quiet) for N in Ns]
     mag = np.concatenate([m for _, m in mats])
-    dx, qx = exact_acts(rng, M, K, mag, spike=True)
+    dx, qx = exact_acts(rng, M, K, mag, spike=quiet)
     x = (qx * np.repeat(dx, 256, 1)).astype(np.float32)
     xq_want = q8K_bytes(dx, qx)
     assert np.array_equal(orc.quantize_q8K(x), xq_want)
