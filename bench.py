@@ -27,14 +27,21 @@ are submitted as eager launches on one stream; --graph instead captures one pass
 per weight copy in a HIP graph and times the replays (slower on this stack).
 
 Output: one JSON line.  `value` is the M=1 weight throughput of the whole step
-(quantizer launches included); `secondary` the M=512 int8 throughput;
-`roofline` / `roofline_m512` give the dominant kernels' algorithmic rate from
-HIP events around batches of back-to-back launches against the MI355X peaks
-(HBM 8 TB/s; dense int8 MFMA 5.0 POP/s) and against ceilings measured on the
-same GPU (`ceilings`: a plain 1 GiB device copy, the library's int8 MFMA-only
-loop with the shader clock it ran at, and the vendor library's plain int8 GEMM
-at the largest matrix's shape); `cpu_baseline` times the CPU oracle
-on a bounded sample, on all host cores and on one.
+(quantizer launches included); `secondary` the M=512 int8 throughput, with the
+matmul kernels' own rate beside it; `roofline` / `roofline_m512` give the
+dominant kernels' algorithmic rate against the MI355X peaks (HBM 8 TB/s; dense
+int8 MFMA 5.0 POP/s), each launch timed by HIP events on its stream around a
+batch of back-to-back copies of it that rotate over >= 1 GiB of weights, and,
+where the committed rocprofv3 runs of this benchmark still match the kernel
+sources, the same launches' kernel-trace durations and HBM bytes
+(profiles/kernel_profile.json); `quantizer` times the standalone q8_K
+quantizer at the prefill widths; `ceilings` are measured on the same GPU: the
+library's read-only stream over 2 GiB, a plain 1 GiB device copy, the
+library's int8 MFMA-only loop with the shader clock it ran at, and the vendor
+library's plain int8 GEMM at the largest matrix's shape.  `cpu_baseline` times
+the CPU oracle on a bounded sample: the benchmarked workload on the physical
+cores this process may use and on one, the other workloads of the set on one,
+and the oracle quantizer alone on 512 x 1024.
 """
 from __future__ import annotations
 
@@ -52,6 +59,11 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, TOP/s
 GIB = 1 << 30
+
+
+def progress(msg):
+    """A progress line on stderr (the JSON result is the only line on stdout)."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
 
 
 def parse():
@@ -119,6 +131,7 @@ class Layer:
 
         P, I64 = ctypes.c_void_p, ctypes.c_int64
         self.lib = gq.lib()
+        self.rot = {}  # per-launch rotating weight copies (launch_weights)
         self.args = {}
         for M in Ms:
             for r in range(copies):
@@ -231,62 +244,153 @@ def fused_launch(M, K):
     return 1 <= M <= 4 and 1 <= nb <= 16 and M * nb <= 32
 
 
+def launch_weights(layer, ms, copies):
+    """Weight copies that one launch rotates through when it is timed on its
+    own: the layer's copies, then clones of this launch's matrices until the
+    copies hold at least 1 GiB, so that every launch of the batch streams its
+    weights from HBM (a small launch cycling through the layer's copies alone
+    would find them in the 256 MB last-level cache)."""
+    n = sum(m.nbytes for m in ms)
+    want = max(copies, math.ceil(GIB / max(n, 1)))
+    ws = [layer.w[r] for r in range(copies)]
+    for _ in range(copies, want):
+        ws.append({m.name: layer.w[0][m.name].clone() for m in ms})
+    return ws
+
+
 def kernel_rates(layer, M, steps, copies, stream):
     """Average duration of each matmul launch of the pass: two HIP events on the
-    launch stream around a batch of back-to-back copies of that launch (weight
-    copies rotated).  Where the pass runs a group as one fused quantize + GEMV
-    launch, that launch is timed; otherwise the matmul launch alone, its
-    activation quantized once beforehand."""
+    launch stream around a batch of back-to-back copies of that launch, rotating
+    over at least 1 GiB of weight copies (launch_weights).  Where the pass runs
+    a group as one fused quantize + GEMV launch, that launch is timed; otherwise
+    the matmul launch alone, its activation quantized once beforehand."""
+    import ctypes
+
     import torch
 
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
     st = stream.cuda_stream
+    lib = layer.lib
     for ms in layer.launches:
         layer.quantize(ms[0].inp, ms[0].K, M, st)
     per = {}
-    n = max(steps, copies)
     for ms in layer.launches:
+        key = launch_name(ms)
+        if key not in layer.rot:
+            layer.rot[key] = launch_weights(layer, ms, copies)
+        ws = layer.rot[key]
         fused = layer.fuse and fused_launch(M, ms[0].K)
-        call = layer.linear if fused else layer.launch
-        for r in range(copies):  # warm the launch path
-            call(ms, M, r, st)
+        n = len(ms)
+        m0 = ms[0]
+        ya = (P * n)(*[layer.y[(M, m.name)].data_ptr() for m in ms])
+        na = (I64 * n)(*[m.N for m in ms])
+        xq = layer.xq[(M, m0.inp)].data_ptr()
+        calls = []
+        for w in ws:
+            wa = (P * n)(*[w[m.name].data_ptr() for m in ms])
+            if fused:
+                calls.append((lib.gemmq_linear_group,
+                              (m0.fmt, n, wa, ya, na, layer.x[(M, m0.inp)].data_ptr(), xq, M,
+                               m0.K, layer.gq.PATH_AUTO, st)))
+            else:
+                calls.append((lib.gemmq_gemm_group,
+                              (m0.fmt, n, wa, ya, na, xq, M, m0.K, layer.gq.PATH_AUTO, st)))
+        reps = max(steps, len(calls))
+        for f, args in calls[:3]:  # warm the launch path
+            if f(*args):
+                raise layer.gq.GemmqError(-1, key)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for r in range(n):
-            call(ms, M, r % copies, st)
+        for i in range(reps):
+            f, args = calls[i % len(calls)]
+            rc = f(*args)
+            if rc:
+                raise layer.gq.GemmqError(rc, key)
         e1.record(stream)
         torch.cuda.synchronize()
-        per[launch_name(ms)] = (ms, e0.elapsed_time(e1) * 1e-3 / n, fused)
+        per[key] = (ms, e0.elapsed_time(e1) * 1e-3 / reps, fused)
     return per
 
 
-def profiled_traffic(fam, launches):
-    """HBM bytes per launch of kernel family `fam` ("gemv" / "gemm") over the
-    pass's launches, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-    (profiles/traffic.json, FETCH scaled by the cold-copy factor).  None when
-    the kernel sources changed since those counters were taken."""
+def quantizer_rates(layer, M, steps, stream):
+    """Average duration of the standalone q8_K quantizer launch for each
+    activation of the pass at M rows, timed like kernel_rates over at least
+    1 GiB of rotating activation copies (so the f32 input streams from HBM).
+    Algorithmic bytes: the f32 input read plus the q8_K output written."""
+    import torch
+
+    st = stream.cuda_stream
+    out = {}
+    for inp, K in layer.wl.inputs():
+        x = layer.x[(M, inp)]
+        xq = layer.xq[(M, inp)]
+        nbytes = M * K * 4 + layer.gq.q8K_bytes(M, K)
+        nx = max(1, math.ceil(GIB / (M * K * 4)))
+        xs = [x] + [x.clone() for _ in range(nx - 1)]
+        reps = max(steps, nx)
+        for i in range(3):  # warm the launch path
+            layer.lib.gemmq_quantize_q8K(xs[i % nx].data_ptr(), xq.data_ptr(), M, K, st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            rc = layer.lib.gemmq_quantize_q8K(xs[i % nx].data_ptr(), xq.data_ptr(), M, K, st)
+            if rc:
+                raise layer.gq.GemmqError(rc, "quantize " + inp)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) * 1e-3 / reps
+        del xs
+        out["%s %dx%d" % (inp, M, K)] = {
+            "us": round(dt * 1e6, 2), "algo_bytes": nbytes,
+            "GBs": round(nbytes / dt / 1e9, 1), "frac": round(nbytes / dt / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
+
+
+def profiled(workload, M, launches):
+    """Per-launch figures of this workload at M rows from the committed
+    rocprofv3 runs of this benchmark (profiles/kernel_profile.json): the
+    kernel-trace average duration (us) and, when the counter runs were taken,
+    the HBM bytes read and written (FETCH_SIZE scaled by a cold device copy's
+    reading, WRITE_SIZE), per launch.  None when the sources of the kernels
+    profiled changed since, or the runs do not cover these launches."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(ROOT, "profiles", "kernel_profile.json")
     try:
         with open(path) as f:
-            t = json.load(f)[fam]
+            t = json.load(f)
+        rec = t["runs"]["%s M=%d" % (workload, M)]
     except (OSError, KeyError, ValueError):
         return None
     h = hashlib.sha256()
-    for src in t.get("sources", []):
-        with open(os.path.join(ROOT, "quant_packed_weight_amd", "csrc", src), "rb") as f:
-            h.update(f.read())
-    per = t.get("per_launch", {})
+    for src in rec.get("sources", []):
+        try:
+            with open(os.path.join(ROOT, "quant_packed_weight_amd", "csrc", src), "rb") as f:
+                h.update(f.read())
+        except OSError:
+            return None
+    per = rec.get("per_launch", {})
     names = [launch_name(ms) for ms in launches]
-    if h.hexdigest() != t.get("source_sha256") or any(n not in per for n in names):
+    if h.hexdigest() != rec.get("source_sha256") or any(n not in per for n in names):
         return None
-    tot = sum(per[n]["read_bytes"] + per[n]["write_bytes"] for n in names)
-    return round(tot / len(names))
+    return {"per_launch": {n: per[n] for n in names}, "summary": t.get("summary")}
+
+
+def kernel_label(M):
+    """The kernel the automatic path runs for an all-q4_K layer at M rows (the
+    library's path choice, restated here only to label the record)."""
+    if M <= 2:
+        return "gemv_kernel"
+    if M <= 64:
+        return "skinny_q4k_kernel"
+    return "gemm_q4k4_kernel" if M >= 1024 else "gemm_q4k2_kernel"
 
 
 def measured_ceilings(wl):
-    """Ceilings measured on this GPU beside the datasheet peaks: a plain 1 GiB
-    device-to-device copy (read + write bytes); the library's int8 MFMA-only
+    """Ceilings measured on this GPU beside the datasheet peaks: the library's
+    read-only stream over 2 GiB (gemmq_probe_read, the GEMV's bound: it only
+    reads weights); a plain 1 GiB device-to-device copy (read + write bytes);
+    the library's int8 MFMA-only
     loop (gemmq_probe_mfma_i8: independent accumulator chains, no memory
     traffic), with the shader clock it ran at from its in-kernel counters; and
     a plain int8 GEMM from the vendor library (torch._int_mm, int8 x int8 ->
@@ -314,6 +418,23 @@ def measured_ceilings(wl):
     dt, nops, cyc, ticks = best
     out["mfma_i8_TOPs"] = round(nops / dt / 1e12, 1)
     out["mfma_i8_clock_GHz"] = round(cyc / ticks * 0.1, 3) if ticks > 0 else None
+    # read-only stream (gemmq_probe_read) over 2 GiB: each launch reads more
+    # than the last-level cache holds, so every byte comes from HBM
+    n = 2 * GIB
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    gq.probe_read(src)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gq.probe_read(src)
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) * 1e-3
+        best = dt if best is None else min(best, dt)
+    out["read_GBs"] = round(n / best / 1e9, 1)
+    del src
     n = GIB
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
@@ -398,14 +519,104 @@ def _oracle_rate(wl, gen, M1, M2, seconds, threads):
     return res
 
 
+def host_cores():
+    """Logical CPUs of the host, those this process may run on, and the
+    physical cores behind the latter (from the sysfs CPU topology)."""
+    aff = sorted(os.sched_getaffinity(0))
+    phys = set()
+    for c in aff:
+        base = "/sys/devices/system/cpu/cpu%d/topology/" % c
+        try:
+            with open(base + "physical_package_id") as f:
+                pkg = f.read().strip()
+            with open(base + "core_id") as f:
+                core = f.read().strip()
+            phys.add((pkg, core))
+        except OSError:
+            phys.add(("?", str(c)))
+    return {"host_logical_cpus": os.cpu_count(), "affinity_logical_cpus": len(aff),
+            "affinity_physical_cores": len(phys)}
+
+
+def _oracle_workload(name, seconds, rows_cap):
+    """One core: a workload of the survey's set through the oracle (quantize +
+    integer-route matmul of every matrix), whole passes repeated for about
+    `seconds`, or for M > 64 a seeded sample of at most `rows_cap` rows
+    (first and last included), extrapolated per multiply-accumulate."""
+    import numpy as np
+
+    import oracle
+    from quant_packed_weight_amd import synth
+
+    g = synth.generate(name)
+    wl = g.workload
+    out = {}
+    for M in wl.Ms:
+        rows = sample_rows(M, rows_cap) if M > 64 else None
+        nr = M if rows is None else len(rows)
+        passes, t0 = 0, time.perf_counter()
+        while True:
+            for inp, _ in wl.inputs():
+                x = g.activations[(M, inp)]
+                xq = oracle.quantize_q8K(x if rows is None else np.ascontiguousarray(x[rows]))
+                for m in wl.matrices:
+                    if m.inp == inp:
+                        oracle.gemm_int(m.fmt, g.weights[m.name], xq, nr, m.N, m.K)
+            passes += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or rows is not None:
+                break
+        mac = sum(nr * m.N * m.K for m in wl.matrices)
+        wb = sum(m.nbytes for m in wl.matrices)
+        rec = {"seconds": round(el, 3), "passes": passes, "GMACs": round(mac * passes / el / 1e9, 3)}
+        if rows is None:
+            rec["us_per_pass"] = round(el / passes * 1e6, 1)
+            rec["weight_GBs"] = round(wb * passes / el / 1e9, 4)
+        else:
+            full = sum(M * m.N * m.K for m in wl.matrices)
+            rec["sample"] = "%d of %d rows, extrapolated per MAC" % (nr, M)
+            rec["ms_per_pass_extrapolated"] = round(el * full / mac * 1e3, 1)
+        out["M=%d" % M] = rec
+    del g
+    return out
+
+
+def _oracle_quantizer(M, K, seconds, threads):
+    """The oracle's q8_K quantizer on an M x K f32 activation, rows split over
+    `threads` host threads (the C call releases the GIL): microseconds per call."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+
+    x = np.random.default_rng(512).standard_normal((M, K), dtype=np.float32)
+    step = -(-M // threads)
+    parts = [np.ascontiguousarray(x[r:r + step]) for r in range(0, M, step)]
+    with ThreadPoolExecutor(threads) as pool:
+        list(pool.map(oracle.quantize_q8K, parts))
+        n, t0 = 0, time.perf_counter()
+        while True:
+            list(pool.map(oracle.quantize_q8K, parts))
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return el / n * 1e6
+
+
 def cpu_baseline(wl, gen, M1, M2, seconds):
-    """The oracle on a bounded sample of the same workload, on all of this host's
-    cores (the row-parallel thin driver above) and on one core."""
-    cores = len(os.sched_getaffinity(0))
+    """The oracle on a bounded sample of the benchmarked workload, on the
+    physical cores this process may use (the row-parallel thin driver above)
+    and on one core; the other workloads of the set on one core; and the
+    oracle's quantizer alone on a 512 x 1024 activation."""
+    hc = host_cores()
+    cores = max(1, hc["affinity_physical_cores"])
     wbytes = sum(m.nbytes for m in wl.matrices)
     nrows = len(sample_rows(M2)) if M2 else 0
     ops2 = sum(2 * nrows * m.N * m.K for m in wl.matrices)
     out = {"kind": "oracle", "cores": cores}
+    out.update(hc)
     for label, threads in (("", cores), ("_1core", 1)):
         r = _oracle_rate(wl, gen, M1, M2, seconds / 4, threads)
         passes, el = r["m1"]
@@ -413,8 +624,8 @@ def cpu_baseline(wl, gen, M1, M2, seconds):
         if not label:
             out["unit"] = "GB/s"
             out["sample"] = ("%d full pass(es) of the %d-matrix layer at M=%d (quantize + "
-                             "integer-route matmul, each matrix's rows split over %d threads), "
-                             "%.1f s; the same with 1 thread in value_1core"
+                             "integer-route matmul, each matrix's rows split over %d threads, one "
+                             "per physical core), %.1f s; the same with 1 thread in value_1core"
                              % (passes, len(wl.matrices), M1, threads, el))
         if M2:
             out["value_m%d%s" % (M2, label)] = ops2 / r["m2"] / 1e12
@@ -423,6 +634,17 @@ def cpu_baseline(wl, gen, M1, M2, seconds):
                 out["sample_m%d" % M2] = ("%d seeded rows of M=%d (first and last included) "
                                           "through all %d matrices, %.1f s (1 thread: value_m%d_1core)"
                                           % (nrows, M2, len(wl.matrices), r["m2"], M2))
+    from quant_packed_weight_amd import synth
+
+    others = {}
+    for name in synth.WORKLOADS:
+        if name != wl.name:
+            others[name] = _oracle_workload(name, seconds / 40, 8 if "1.7b" in name else 32)
+    out["workloads_1core"] = others
+    out["quantizer_512x1024_us"] = {
+        "1core": round(_oracle_quantizer(512, 1024, seconds / 20, 1), 1),
+        "%dcores" % cores: round(_oracle_quantizer(512, 1024, seconds / 20, cores), 1),
+        "pages_context": "1087 us -> 55.6 us on a 44-core host (another machine)"}
     return out
 
 
@@ -462,8 +684,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst, flush
 
-    t_eager = {M: time_passes(layer, M, a.steps, a.warmup, copies, stream) for M in Ms}
-    rates = {M: kernel_rates(layer, M, a.steps, copies, stream) for M in Ms}
+    t_eager, rates = {}, {}
+    for M in Ms:
+        t_eager[M] = time_passes(layer, M, a.steps, a.warmup, copies, stream)
+        progress("M=%d: %.1f us per pass" % (M, t_eager[M] * 1e6))
+    for M in Ms:
+        rates[M] = kernel_rates(layer, M, a.steps, copies, stream)
+        progress("M=%d: launches timed" % M)
     if not a.graph:
         t = t_eager
     else:
@@ -474,40 +701,62 @@ def main():
     M2 = Ms[1] if len(Ms) > 1 else None
     ops = {M: sum(2 * M * m.N * m.K for m in wl.matrices) for M in Ms}
 
+    def traffic(prof):
+        """HBM bytes (read + written) per launch, averaged over the pass's launches."""
+        if not prof or any("read_bytes" not in v for v in prof["per_launch"].values()):
+            return None
+        pl = prof["per_launch"].values()
+        return round(sum(v["read_bytes"] + v["write_bytes"] for v in pl) / len(pl))
+
     def roof(M):
         per = rates[M]
         n_l = len(per)
         tot_t = sum(dt for _, dt, _ in per.values())
         fused = [k for k, (_, _, f) in per.items() if f]
-        # the automatic path's kernel for the all-q4_K layer (the small-M kernel
-        # at 17..64 rows on some launches only)
-        kname = ("gemv_kernel" if M <= 2 else "skinny_q4k_kernel" if M <= 16
-                 else "gemm_q4k_kernel")
+        kname = kernel_label(M)
         if fused:
             kname += " (quantizer fused into: %s)" % ", ".join(fused)
+        prof = profiled(a.workload, M, layer.launches)
         if M <= 8:
             algo = sum(sum(m.nbytes for m in ms) for ms, _, _ in per.values())
             ach = algo / tot_t / 1e9
-            return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4),
-                    "traffic": (profiled_traffic("gemv", layer.launches)
-                                if a.workload == "qwen3-8b-q4K" and M == 1 else None),
-                    "algo_bytes_per_launch": round(algo / n_l),
-                    "kernel": kname, "launches_per_pass": n_l,
-                    "avg_launch_us": round(tot_t / n_l * 1e6, 2),
-                    "per_launch_GBs": {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
-                                       for k, (ms, dt, _) in per.items()}}
-        algo = sum(sum(2 * M * m.N * m.K for m in ms) for ms, _, _ in per.values())
-        ach = algo / tot_t / 1e12
-        return {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS,
-                "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
-                "traffic": (profiled_traffic("gemm", layer.launches)
-                            if a.workload == "qwen3-8b-q4K" and M == 512 else None),
-                "algo_ops_per_launch": round(algo / n_l),
-                "kernel": kname, "launches_per_pass": n_l,
-                "avg_launch_us": round(tot_t / n_l * 1e6, 2),
-                "per_launch_TOPs": {k: round(sum(2 * M * m.N * m.K for m in ms) / dt / 1e12, 1)
+            r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(ach / HBM_PEAK_GBS, 4),
+                 "traffic": traffic(prof),
+                 "algo_bytes_per_launch": round(algo / n_l),
+                 "kernel": kname, "launches_per_pass": n_l,
+                 "avg_launch_us": round(tot_t / n_l * 1e6, 3),
+                 "per_launch_us": {k: round(dt * 1e6, 3) for k, (_, dt, _) in per.items()},
+                 "per_launch_GBs": {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
                                     for k, (ms, dt, _) in per.items()}}
+        else:
+            algo = sum(sum(2 * M * m.N * m.K for m in ms) for ms, _, _ in per.values())
+            ach = algo / tot_t / 1e12
+            r = {"bound": "mfma", "achieved": round(ach, 1), "peak": INT8_PEAK_TOPS,
+                 "unit": "TOP/s", "frac": round(ach / INT8_PEAK_TOPS, 4),
+                 "traffic": traffic(prof),
+                 "algo_ops_per_launch": round(algo / n_l),
+                 "kernel": kname, "launches_per_pass": n_l,
+                 "avg_launch_us": round(tot_t / n_l * 1e6, 3),
+                 "per_launch_us": {k: round(dt * 1e6, 3) for k, (_, dt, _) in per.items()},
+                 "per_launch_TOPs": {k: round(sum(2 * M * m.N * m.K for m in ms) / dt / 1e12, 1)
+                                     for k, (ms, dt, _) in per.items()}}
+        r["timing"] = ("HIP events on the launch stream around %d+ back-to-back launches of "
+                       "each launch, over >= 1 GiB of rotating weight copies" % a.steps)
+        if prof:
+            # the same launches' durations in the committed rocprofv3 kernel trace
+            pl = prof["per_launch"]
+            p_t = sum(v["us"] for v in pl.values()) * 1e-6
+            p_ach = algo / p_t / (1e9 if M <= 8 else 1e12)
+            r["rocprof"] = {"avg_launch_us": round(p_t / n_l * 1e6, 3),
+                            "achieved": round(p_ach, 1),
+                            "frac": round(p_ach / r["peak"], 4),
+                            "events_over_rocprof_time": round(tot_t / p_t, 4),
+                            "per_launch_us": {k: v["us"] for k, v in pl.items()},
+                            "source": prof["summary"]}
+        else:
+            r["rocprof"] = None
+        return r
 
     value = wbytes / t[M1] / 1e9 if M1 <= 8 else ops[M1] / t[M1] / 1e12
     res = {
@@ -533,38 +782,73 @@ def main():
         "roofline": roof(M1),
     }
     if M2:
+        k_t = sum(dt for _, dt, _ in rates[M2].values())
         res["secondary"] = {"metric": "int8 TOP/s at M=%d" % M2,
-                            "value": round(ops[M2] / t[M2] / 1e12, 1), "unit": "TOP/s"}
+                            "value": round(ops[M2] / t[M2] / 1e12, 1), "unit": "TOP/s",
+                            "frac": round(ops[M2] / t[M2] / 1e12 / INT8_PEAK_TOPS, 4),
+                            "matmul_kernels_only_TOPs": round(ops[M2] / k_t / 1e12, 1),
+                            "pass_over_matmul_kernels": round(t[M2] / k_t, 4)}
         res["roofline_m%d" % M2] = roof(M2)
     for M in Ms[2:]:
         # the rest of the M sweep: batched decode (weight GB/s) or prefill (int8 TOP/s)
         per = rates[M]
-        rec = {"M": M, "us_per_pass": round(t[M] * 1e6, 2),
+        k_t = sum(dt for _, dt, _ in per.values())
+        rec = {"M": M, "kernel": kernel_label(M), "us_per_pass": round(t[M] * 1e6, 2),
                "weight_GBs": round(wbytes / t[M] / 1e9, 1),
-               "int8_TOPs": round(ops[M] / t[M] / 1e12, 2)}
+               "int8_TOPs": round(ops[M] / t[M] / 1e12, 2),
+               "matmul_kernels_us": round(k_t * 1e6, 2)}
+        rec["per_launch_us"] = {k: round(dt * 1e6, 3) for k, (_, dt, _) in per.items()}
         if M <= 16:
             rec["per_launch_GBs"] = {k: round(sum(m.nbytes for m in ms) / dt / 1e9, 1)
                                      for k, (ms, dt, _) in per.items()}
+            rec["matmul_kernels_frac_of_hbm_peak"] = round(wbytes / k_t / 1e9 / HBM_PEAK_GBS, 4)
             res["batched_decode_m%d" % M] = rec
         else:
             rec["per_launch_TOPs"] = {k: round(sum(2 * M * m.N * m.K for m in ms) / dt / 1e12, 1)
                                       for k, (ms, dt, _) in per.items()}
+            rec["matmul_kernels_frac_of_int8_peak"] = round(ops[M] / k_t / 1e12 / INT8_PEAK_TOPS, 4)
             res["prefill_m%d" % M] = rec
+    # the standalone activation quantizer at the prefill widths (at M <= 4 with
+    # rows of <= 16 blocks it runs fused into the GEMV workgroups instead)
+    qrec = {}
+    for M in Ms:
+        if M > 8:
+            q = quantizer_rates(layer, M, a.steps, stream)
+            tb = sum(v["algo_bytes"] for v in q.values())
+            tt = sum(v["us"] for v in q.values()) * 1e-6
+            qrec["M=%d" % M] = {"per_launch": q, "GBs": round(tb / tt / 1e9, 1),
+                                "frac": round(tb / tt / 1e9 / HBM_PEAK_GBS, 4)}
+    if qrec:
+        qrec["kernel"] = "quantize_q8K_kernel"
+        qrec["bound"] = "hbm"
+        qrec["algo_bytes"] = "M*K*4 (f32 read) + M*(K/256)*292 (q8_K written)"
+        qrec["timing"] = ("HIP events around back-to-back launches over >= 1 GiB of rotating "
+                          "input copies")
+        res["quantizer"] = qrec
+    progress("quantizer timed")
     c = res["ceilings"] = measured_ceilings(wl)
+    progress("ceilings measured")
+    c["read_frac_of_peak"] = round(c["read_GBs"] / HBM_PEAK_GBS, 4)
     c["copy_frac_of_peak"] = round(c["copy_GBs"] / HBM_PEAK_GBS, 4)
     c["mfma_i8_frac_of_peak"] = round(c["mfma_i8_TOPs"] / INT8_PEAK_TOPS, 4)
     if c.get("int8_gemm_TOPs"):
         c["int8_gemm_frac_of_peak"] = round(c["int8_gemm_TOPs"] / INT8_PEAK_TOPS, 4)
     # the kernels against the measured ceilings as well as the datasheet peaks
-    res["roofline"]["frac_of_measured_copy"] = round(res["roofline"]["achieved"] / c["copy_GBs"], 4)
-    if M2:
-        res["roofline_m%d" % M2]["frac_of_measured_mfma"] = round(
-            res["roofline_m%d" % M2]["achieved"] / c["mfma_i8_TOPs"], 4)
-    if M2 and c.get("int8_gemm_TOPs"):
-        res["roofline_m%d" % M2]["vs_int8_gemm_library"] = round(
-            res["roofline_m%d" % M2]["achieved"] / c["int8_gemm_TOPs"], 4)
+    for key in ["roofline"] + (["roofline_m%d" % M2] if M2 else []):
+        r = res[key]
+        if r["bound"] == "hbm":
+            r["frac_of_measured_read"] = round(r["achieved"] / c["read_GBs"], 4)
+            r["per_launch_frac_of_measured_read"] = {
+                k: round(v / c["read_GBs"], 4) for k, v in r["per_launch_GBs"].items()}
+            r["per_launch_frac_of_peak"] = {
+                k: round(v / HBM_PEAK_GBS, 4) for k, v in r["per_launch_GBs"].items()}
+        else:
+            r["frac_of_measured_mfma"] = round(r["achieved"] / c["mfma_i8_TOPs"], 4)
+            if c.get("int8_gemm_TOPs"):
+                r["vs_int8_gemm_library"] = round(r["achieved"] / c["int8_gemm_TOPs"], 4)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, gen, M1, M2, a.cpu_seconds)
+        progress("oracle timed")
     print(json.dumps(res), flush=True)
 
 

@@ -305,6 +305,21 @@ int gemmq_decode(int fmt, const void *W, float *Wf, int64_t N, int64_t K, void *
 int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t *out, uint64_t *clocks,
                         void *stream);
 
+/*
+ * Measurement export: the read-only device-memory ceiling the decode GEMV is
+ * read against (the GEMV streams each packed weight once and writes next to
+ * nothing).  Never used on the compute path.  Reads `bytes` from `src` with
+ * GEMMQ_PROBE_READ_WORDS waves, every lane keeping eight 16-byte loads in
+ * flight, and stores one XOR fold per wave, so the launch time gives the
+ * sustained read rate: bytes / time.
+ *   src    device, `bytes` bytes, 16-byte aligned; bytes a positive multiple of
+ *          16, at most 2^40.  Contents are arbitrary.
+ *   out    device, uint32 [GEMMQ_PROBE_READ_WORDS], 4-byte aligned; overwritten.
+ * Errors: GEMMQ_E_INVALID_ARG, GEMMQ_E_ALIGNMENT, GEMMQ_E_DEVICE, GEMMQ_E_LAUNCH.
+ */
+#define GEMMQ_PROBE_READ_WORDS 2048
+int gemmq_probe_read(const void *src, int64_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,6 +25,7 @@ from ._lib import (  # noqa: F401
     PATH_SKINNY,
     PROBE_CHAINS,
     PROBE_MAX_ITERS,
+    PROBE_READ_WORDS,
     Q8K_BYTES,
     QK,
     GemmqError,
@@ -41,6 +42,7 @@ from ._lib import (  # noqa: F401
     linear_group_ptr,
     linear_silu_mul,
     probe_mfma_i8,
+    probe_read,
     q8K_bytes,
     quantize_q8K,
     repack,

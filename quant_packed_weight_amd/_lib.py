@@ -28,6 +28,7 @@ ABI_VERSION = 9
 PROBE_CHAINS = 4  # GEMMQ_PROBE_CHAINS
 PROBE_MAX_ITERS = 1000000  # GEMMQ_PROBE_MAX_ITERS
 GEMM_MAX_M = 4194240  # GEMMQ_GEMM_MAX_M
+PROBE_READ_WORDS = 2048  # GEMMQ_PROBE_READ_WORDS
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgemmq.so")
 
@@ -53,6 +54,7 @@ EXPORTS = {
     "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "gemmq_repack": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "gemmq_probe_mfma_i8": (_I, [_I64, _I64, _P, _P, _P]),
+    "gemmq_probe_read": (_I, [_P, _I64, _P, _P]),
 }
 
 
@@ -318,3 +320,16 @@ def probe_mfma_i8(iters, blocks, stream=None):
     _check(lib().gemmq_probe_mfma_i8(iters, blocks, out.data_ptr(), clocks.data_ptr(),
                                      _stream(stream)), "gemmq_probe_mfma_i8")
     return out, clocks, 2 * 32768 * PROBE_CHAINS * 4 * blocks * iters
+
+
+def probe_read(src, stream=None):
+    """Enqueue the read-only stream over the device tensor `src`
+    (gemmq_probe_read); returns the per-wave fold tensor."""
+    torch = _torch()
+    out = torch.empty(PROBE_READ_WORDS, dtype=torch.int32, device=src.device)
+    nbytes = src.numel() * src.element_size()
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    _check(lib().gemmq_probe_read(src.data_ptr(), nbytes - nbytes % 16, out.data_ptr(),
+                                  _stream(stream)), "gemmq_probe_read")
+    return out

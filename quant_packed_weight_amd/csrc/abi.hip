@@ -16,6 +16,8 @@ namespace gemmq {
 // probe.hip: the int8 MFMA ceiling (independent accumulator chains per wave)
 int probe_mfma_chains();
 int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk, hipStream_t st);
+int probe_read_waves();
+int launch_probe_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t st);
 // skinny.hip: the small-M q4_K MFMA kernel
 int launch_skinny(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 int launch_skinny_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
@@ -382,6 +384,17 @@ int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t* out, uint64_t* c
   clear_pending();
   return launched(
       gemmq::launch_probe_mfma(iters, blocks, out, clocks, static_cast<hipStream_t>(stream)));
+}
+
+int gemmq_probe_read(const void* src, int64_t bytes, uint32_t* out, void* stream) {
+  if (!src || !out || bytes < 16 || bytes % 16 != 0 || bytes > ((int64_t)1 << 40))
+    return GEMMQ_E_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(out, 4)) return GEMMQ_E_ALIGNMENT;
+  if (gemmq::probe_read_waves() != GEMMQ_PROBE_READ_WORDS) return GEMMQ_E_LAUNCH;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  clear_pending();
+  return launched(gemmq::launch_probe_read(src, bytes, out, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

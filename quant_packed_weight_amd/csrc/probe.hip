@@ -1,5 +1,6 @@
-// probe.hip -- a measured ceiling for the matmul kernels: int8 MFMAs with no
-// memory traffic or vector work, and the shader clock they run at.
+// probe.hip -- measured ceilings for the matmul kernels: int8 MFMAs with no
+// memory traffic or vector work, and the shader clock they run at; and a plain
+// read-only stream of device memory (the GEMV's bound).
 //
 // Every wave keeps kChains independent accumulator chains of
 // v_mfma_i32_32x32x32_i8 on register operands, so the matrix cores never wait
@@ -51,9 +52,47 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, int32_t*
   }
 }
 
+// Read-only stream: 2048 waves (256 workgroups of eight), each lane folding 16
+// bytes per load with eight loads issued before any is used, in a grid-stride
+// loop over the buffer; every wave stores the XOR of what it read, so no load
+// can be dropped.  The time of the launch gives the sustained read rate of
+// device memory with nothing else in the way.
+constexpr int kReadWaves = 2048;
+constexpr int kReadUnroll = 8;
+
+__global__ __launch_bounds__(512) void read_probe_kernel(const uint4* __restrict__ src,
+                                                         int64_t nvec, uint32_t* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t a = 0;
+  for (; i + (kReadUnroll - 1) * stride < nvec; i += kReadUnroll * stride) {
+    uint4 v[kReadUnroll];
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) v[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < kReadUnroll; ++k) a ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
+  }
+  for (; i < nvec; i += stride) {
+    const uint4 v = src[i];
+    a ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  // fold the wave (xor over the lanes) and store one word per wave
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) a ^= (uint32_t)__shfl_xor((int)a, m, 64);
+  if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = a;
+}
+
 }  // namespace
 
 int probe_mfma_chains() { return kChains; }
+
+int probe_read_waves() { return kReadWaves; }
+
+int launch_probe_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t st) {
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kReadWaves / 8), dim3(512), 0, st,
+                     static_cast<const uint4*>(src), bytes / 16, out);
+  return 0;
+}
 
 int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk,
                       hipStream_t st) {

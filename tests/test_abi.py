@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_exported(L):
     names = _declared()
-    assert len(names) == 15
+    assert len(names) == 16
     assert set(names) == set(gq.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -318,3 +318,16 @@ def test_repacked_formats_accepted_except_decode(L):
 ])
 def test_probe_validation(L, args, status):
     assert L.gemmq_probe_mfma_i8(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, 1024, FAKE16), -1),
+    ((FAKE16, 1024, None), -1),
+    ((FAKE16, 0, FAKE16), -1),            # nothing to read
+    ((FAKE16, 1000, FAKE16), -1),         # not a multiple of 16
+    ((FAKE16, (1 << 40) + 16, FAKE16), -1),
+    ((FAKE16 + 8, 1024, FAKE16), -4),     # src needs 16 B
+    ((FAKE16, 1024, FAKE16 + 2), -4),     # out needs 4 B
+])
+def test_probe_read_validation(L, args, status):
+    assert L.gemmq_probe_read(*args, None) == status

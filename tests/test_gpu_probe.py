@@ -62,3 +62,22 @@ def test_probe_clock_plausible():
     ghz = cyc / ticks * 0.1
     log("probe shader clock %.3f GHz" % ghz)
     assert 0.3 < ghz < 3.5
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 48, 10 * (1 << 20) + 16 * 7, 64 << 20])
+def test_read_probe_reads_every_word_once(nbytes):
+    # the XOR of every wave's fold is the XOR of every 32-bit word of the buffer
+    # exactly when each 16-byte word is read once
+    import torch
+
+    import quant_packed_weight_amd as gq
+
+    log("read probe %d bytes" % nbytes)
+    rng = np.random.default_rng(nbytes)
+    host = rng.integers(0, 2 ** 32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(host.view(np.int32)).to("cuda:0")
+    out = gq.probe_read(src)
+    torch.cuda.synchronize()
+    folds = out.cpu().numpy().view(np.uint32)
+    assert folds.size == gq.PROBE_READ_WORDS
+    assert np.bitwise_xor.reduce(folds) == np.bitwise_xor.reduce(host)
