@@ -95,10 +95,10 @@ extern "C" {
                                            attribute the launch needs */
 
 /* Paths for gemmq_gemm_ex, each with its limit on M (GEMMQ_E_SHAPE beyond). */
-#define GEMMQ_PATH_AUTO 0 /* decode GEMV (M <= 8; q4_K M <= 2), small-M MFMA (q4_K 3..64), GEMM; see gemmq_gemm */
+#define GEMMQ_PATH_AUTO 0 /* decode GEMV (M <= 8; q4_K M <= 2), small-M MFMA (q4_K 3..64; q6_K 3..16), GEMM; see gemmq_gemm */
 #define GEMMQ_PATH_GEMV 1 /* decode GEMV, M in 1..8 only */
 #define GEMMQ_PATH_GEMM 2 /* MFMA GEMM, M up to GEMMQ_GEMM_MAX_M */
-#define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernel: q4_K only, M in 1..64 */
+#define GEMMQ_PATH_SKINNY 3 /* small-M MFMA kernels: q4_K M in 1..64; q6_K and q6_K_R M in 1..16 */
 #define GEMMQ_GEMM_MAX_M 4194240 /* 65535 tiles of 64 activation rows */
 
 /* ABI version (GEMMQ_ABI_VERSION of the library that was loaded): the C core
@@ -149,9 +149,10 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
  * (steps a2..a5: in-kernel unpack; the path chosen by GEMMQ_PATH_AUTO: the decode
  * GEMV for M <= 8 -- for q4_K M <= 2 --, the small-M MFMA kernel for q4_K at
  * 3 <= M <= 64 when M <= 16 or when the launch's output columns times ceil(M/16)
- * are at most 20480, the MFMA GEMM otherwise -- also for q6_K and q6_K_R at
- * 5 <= M <= 8 when the launch has at least 16384 output columns; the choice is
- * made once per launch, from M and the sum of the N of the matrices it serves).
+ * are at most 20480, and for q6_K and q6_K_R at 9 <= M <= 16 and at 3 <= M <= 8
+ * when the launch has at least 16384 output columns, the MFMA GEMM otherwise;
+ * the choice is made once per launch, from M and the sum of the N of the
+ * matrices it serves).
  *   fmt  GEMMQ_Q2_K, GEMMQ_Q3_K, GEMMQ_Q4_K, GEMMQ_Q5_K, GEMMQ_Q6_K, or a
  *        repacked GEMMQ_Q3_K_R / GEMMQ_Q6_K_R (weights from gemmq_repack).
  *   W    device, gemmq_weight_bytes(fmt, N, K) bytes; 16-byte aligned for q4_K,
@@ -170,12 +171,15 @@ int gemmq_gemm(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int6
                int64_t K, void *stream);
 
 /* gemmq_gemm with an explicit path (GEMMQ_PATH_*).  GEMMQ_PATH_GEMV with M > 8,
- * GEMMQ_PATH_SKINNY with M > 64 and GEMMQ_PATH_GEMM (also when chosen by
- * GEMMQ_PATH_AUTO) with M > GEMMQ_GEMM_MAX_M return GEMMQ_E_SHAPE; GEMMQ_PATH_SKINNY with
- * a format other than GEMMQ_Q4_K returns GEMMQ_E_UNSUPPORTED_FORMAT.  Same
- * arguments, layout and errors otherwise.  GEMMQ_PATH_SKINNY is the batched
- * decode kernel: the activation rows in one to four 16 x 16 x 64 int8 MFMA tiles,
- * the super-blocks of a row split over the waves of a workgroup by K alone. */
+ * GEMMQ_PATH_SKINNY with M > 64 (q6_K and q6_K_R: M > 16) and GEMMQ_PATH_GEMM (also
+ * when chosen by GEMMQ_PATH_AUTO) with M > GEMMQ_GEMM_MAX_M return GEMMQ_E_SHAPE;
+ * GEMMQ_PATH_SKINNY with a format other than GEMMQ_Q4_K, GEMMQ_Q6_K and GEMMQ_Q6_K_R
+ * returns GEMMQ_E_UNSUPPORTED_FORMAT.  Same arguments, layout and errors
+ * otherwise.  GEMMQ_PATH_SKINNY is the batched decode kernel (the pages keep
+ * q6_K on a row path of its own: molayo article, status row "src/"): q4_K
+ * holds the activation rows in one to four 16 x 16 x 64 int8 MFMA tiles, q6_K
+ * in one 32 x 32 x 16 tile per 16-weight sub-block; either splits the
+ * super-blocks of a row over the waves of a workgroup by K alone. */
 int gemmq_gemm_ex(int fmt, const void *W, const void *Xq, float *Y, int64_t M, int64_t N,
                   int64_t K, int path, void *stream);
 

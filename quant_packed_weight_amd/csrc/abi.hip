@@ -18,7 +18,8 @@ int probe_mfma_chains();
 int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk, hipStream_t st);
 int probe_read_waves();
 int launch_probe_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t st);
-// skinny.hip: the small-M q4_K MFMA kernel
+// skinny.hip / skinny_q6k.hip: the small-M MFMA kernels (q4_K; q6_K and its
+// repacked layout)
 int launch_skinny(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 int launch_skinny_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
                        hipStream_t st);
@@ -27,15 +28,26 @@ int launch_skinny_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_
 namespace {
 
 constexpr int kMaxDevices = 64;
-// activation rows the small-M MFMA kernel takes (automatic choice: from 3)
-constexpr int64_t kSkinnyMinM = 3, kSkinnyMaxM = 64;
+// activation rows the small-M MFMA kernels take: q4_K up to 64, q6_K up to 16
+// (automatic choice: from 3)
+constexpr int64_t kSkinnyMinM = 3, kSkinnyMaxM = 64, kSkinnyQ6MaxM = 16;
 // automatic choice past one 16-row tile: the small-M kernel while the launch's
 // output columns times its 16-row tiles stay within this bound
 constexpr int64_t kSkinnyColTiles = 20480;
-// q6_K at 5 <= M <= 8: the GEMM (64-column tiles) from this many output columns,
-// one tile per CU, where the GEMV's per-row dot products cost more than the GEMM
-constexpr int64_t kQ6GemmCols = 16384;
+// q6_K (either layout): the automatic choice takes the small-M kernel at
+// 9 <= M <= 16, and at 3 <= M <= 8 from this many output columns (below them
+// its 32-column workgroups are too few to fill the chip and the GEMV is faster:
+// measured on the Qwen3-1.7B shapes, v 1024 and down 2048 columns against the
+// 151936-column head)
+constexpr int64_t kSkinnyQ6Cols = 16384;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+// the largest M the small-M kernel takes in this format (0: not available)
+int64_t skinny_max_m(int fmt) {
+  if (fmt == GEMMQ_Q4_K) return kSkinnyMaxM;
+  if (fmt == GEMMQ_Q6_K || fmt == GEMMQ_Q6_K_R) return kSkinnyQ6MaxM;
+  return 0;
+}
 
 int check_device() {
   int dev = -1;
@@ -174,8 +186,8 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
       path != GEMMQ_PATH_SKINNY)
     return GEMMQ_E_INVALID_ARG;
   if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
-  if (path == GEMMQ_PATH_SKINNY && fmt != GEMMQ_Q4_K) return GEMMQ_E_UNSUPPORTED_FORMAT;
-  if (path == GEMMQ_PATH_SKINNY && M > kSkinnyMaxM) return GEMMQ_E_SHAPE;
+  if (path == GEMMQ_PATH_SKINNY && skinny_max_m(fmt) == 0) return GEMMQ_E_UNSUPPORTED_FORMAT;
+  if (path == GEMMQ_PATH_SKINNY && M > skinny_max_m(fmt)) return GEMMQ_E_SHAPE;
   if (M == 0 || rows == 0) return GEMMQ_OK;
   for (int i = 0; i < count; ++i)
     if (N[i] > 0 && !Y[i]) return GEMMQ_E_INVALID_ARG;
@@ -199,16 +211,17 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
 // 16-row tile and for t > 1 tiles while cols * t <= kSkinnyColTiles (its time grows
 // with cols * t, while the GEMM at these M runs one 64-row tile per column tile
 // and costs about the same at any cols below a chip's worth of workgroups); the
-// GEMM beyond.  q6_K (either layout) at 5 <= M <= 8 takes the GEMM once the
-// launch has kQ6GemmCols columns.
+// GEMM beyond.  q6_K (either layout) takes its small-M kernel at 9 <= M <= 16,
+// and at 3 <= M <= 8 once the launch has kSkinnyQ6Cols columns.
 int pick_path(int fmt, int path, int64_t M, int64_t cols) {
   if (path != GEMMQ_PATH_AUTO) return path;
   if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) {
     const int64_t t = (M + 15) / 16;
     if (t == 1 || cols * t <= kSkinnyColTiles) return GEMMQ_PATH_SKINNY;
   }
-  if ((fmt == GEMMQ_Q6_K || fmt == GEMMQ_Q6_K_R) && M >= 5 && M <= 8 && cols >= kQ6GemmCols)
-    return GEMMQ_PATH_GEMM;
+  if ((fmt == GEMMQ_Q6_K || fmt == GEMMQ_Q6_K_R) && M >= kSkinnyMinM && M <= kSkinnyQ6MaxM &&
+      (M > 8 || cols >= kSkinnyQ6Cols))
+    return GEMMQ_PATH_SKINNY;
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }
 
@@ -293,8 +306,8 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
       path != GEMMQ_PATH_SKINNY)
     return GEMMQ_E_INVALID_ARG;
   if (path == GEMMQ_PATH_GEMV && M > 8) return GEMMQ_E_SHAPE;
-  if (path == GEMMQ_PATH_SKINNY && fmt != GEMMQ_Q4_K) return GEMMQ_E_UNSUPPORTED_FORMAT;
-  if (path == GEMMQ_PATH_SKINNY && M > kSkinnyMaxM) return GEMMQ_E_SHAPE;
+  if (path == GEMMQ_PATH_SKINNY && skinny_max_m(fmt) == 0) return GEMMQ_E_UNSUPPORTED_FORMAT;
+  if (path == GEMMQ_PATH_SKINNY && M > skinny_max_m(fmt)) return GEMMQ_E_SHAPE;
   if (M == 0) return GEMMQ_OK;
   if (!X || !Xq || (N > 0 && !Y)) return GEMMQ_E_INVALID_ARG;
   if (!aligned(X, 16) || !aligned(Xq, 4) || (N > 0 && !aligned(Y, 4))) return GEMMQ_E_ALIGNMENT;

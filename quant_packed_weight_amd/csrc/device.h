@@ -81,9 +81,10 @@ __device__ __forceinline__ uint32_t q6k_quad(uint32_t qlw, uint32_t qhw, int c) 
 // span that covers them (n+1 dwords, never past `p + 4n + 2`) and shifts.
 template <int n>
 __device__ __forceinline__ void ld_dwords_a2(const uint8_t* p, uint32_t (&out)[n]) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint32_t* base = reinterpret_cast<const uint32_t*>(a & ~uintptr_t(3));
-  const uint32_t sh = (uint32_t)(a & 3u);  // 0 or 2
+  // the pointer is stepped back rather than rebuilt from an integer, so that
+  // the loads keep the global address space (not flat loads)
+  const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 3u);  // 0 or 2
+  const uint32_t* base = reinterpret_cast<const uint32_t*>(p - sh);
   uint32_t raw[n + 1];
 #pragma unroll
   for (int i = 0; i < n; ++i) raw[i] = base[i];

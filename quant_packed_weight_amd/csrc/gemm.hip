@@ -191,11 +191,11 @@ struct WRegs<11> {
 // dword (so at most p + 35 is read; every caller stays inside its block),
 // shifted into place.
 __device__ __forceinline__ void ld32_a2(const uint8_t* p, uint32_t (&o)[8]) {
-  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(a & ~uintptr_t(3));
+  // stepped back from p (not rebuilt from an integer): global, not flat, loads
+  const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(p) & 3u);
+  const uint8_t* base = p - sh;
   const u32x4 x0 = ld16(base), x1 = ld16(base + 16);
   const uint32_t raw[9] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w, ld4(base + 32)};
-  const uint32_t sh = (uint32_t)(a & 3u);
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = __builtin_amdgcn_alignbyte(raw[i + 1], raw[i], sh);
 }

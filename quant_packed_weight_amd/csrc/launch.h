@@ -86,6 +86,13 @@ __device__ __forceinline__ TileMatrix tile_matrix(const GroupTiles& t, uint32_t 
 
 int launch_quantize_q8K(const float* X, uint8_t* Xq, int64_t M, int64_t K, hipStream_t st);
 
+// skinny_q6k.hip: the small-M q6_K MFMA kernel (q6_K and its repacked layout,
+// M <= 16); 0, or -1 when the arguments do not fit it
+int launch_skinny_q6k(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
+                      hipStream_t st);
+int launch_skinny_q6k_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
+                           hipStream_t st);
+
 int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 
 int launch_gemm(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K, hipStream_t st);

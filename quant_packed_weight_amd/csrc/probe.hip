@@ -52,29 +52,28 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, int32_t*
   }
 }
 
-// Read-only stream: 2048 waves (256 workgroups of eight), each lane folding 16
-// bytes per load with eight loads issued before any is used, in a grid-stride
-// loop over the buffer; every wave stores the XOR of what it read, so no load
-// can be dropped.  The time of the launch gives the sustained read rate of
-// device memory with nothing else in the way.
+// Read-only stream: 2048 waves (256 workgroups of eight), each lane reading 16
+// bytes per load in a grid-stride loop with eight loads issued before any is
+// used (loads past the end are switched off, so a buffer smaller than eight
+// strides is still read in one round); every wave stores the XOR of what it
+// read, so no load can be dropped.  The time of the launch gives the sustained
+// read rate of device memory with nothing else in the way, and on a buffer the
+// size of one matmul's weights, the time a plain stream of those bytes takes.
 constexpr int kReadWaves = 2048;
 constexpr int kReadUnroll = 8;
 
 __global__ __launch_bounds__(512) void read_probe_kernel(const uint4* __restrict__ src,
                                                          int64_t nvec, uint32_t* __restrict__ out) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t a = 0;
-  for (; i + (kReadUnroll - 1) * stride < nvec; i += kReadUnroll * stride) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
+       i += kReadUnroll * stride) {
     uint4 v[kReadUnroll];
 #pragma unroll
-    for (int k = 0; k < kReadUnroll; ++k) v[k] = src[i + k * stride];
+    for (int k = 0; k < kReadUnroll; ++k)
+      v[k] = i + k * stride < nvec ? src[i + k * stride] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int k = 0; k < kReadUnroll; ++k) a ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
-  }
-  for (; i < nvec; i += stride) {
-    const uint4 v = src[i];
-    a ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   // fold the wave (xor over the lanes) and store one word per wave
 #pragma unroll

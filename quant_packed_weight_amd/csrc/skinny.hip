@@ -1,4 +1,5 @@
 // skinny.hip -- q4_K packed matmul on int8 MFMA for a few activation rows
+// (q6_K's counterpart is skinny_q6k.hip; the launchers here route it there)
 // (batched decode and short prefills, M <= 64; the automatic path takes it for
 // 3 <= M <= 16, and up to M = 64 for launches with few enough output columns).
 //
@@ -280,11 +281,13 @@ int launch_skinny_any(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t
 }
 
 int launch_skinny(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st) {
+  if (fmt == 14 || fmt == 256 + 14) return launch_skinny_q6k(fmt, g, Xq, M, K, st);
   return launch_skinny_any<false>(fmt, g, Xq, M, K, st);
 }
 
 int launch_skinny_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
                        hipStream_t st) {
+  if (fmt == 14 || fmt == 256 + 14) return launch_skinny_q6k_silu(fmt, g, Xq, M, K, st);
   if (g.count != 2 || g.N[0] != g.N[1]) return -1;
   return launch_skinny_any<true>(fmt, g, Xq, M, K, st);
 }

@@ -83,8 +83,11 @@ FAKE16 = 0x10000  # never dereferenced: every call below fails validation first
     ((12, FAKE16, FAKE16, FAKE16, 1, 1, 256, 7), -1),      # unknown path
     ((12, FAKE16, FAKE16, FAKE16, 9, 1, 256, 1), -3),      # GEMV path with M > 8
     ((12, FAKE16, FAKE16, FAKE16, 65, 1, 256, 3), -3),     # small-M MFMA path with M > 64
-    ((14, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),      # small-M MFMA path: q4_K only
-    ((13, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),
+    ((14, FAKE16, FAKE16, FAKE16, 17, 1, 256, 3), -3),     # small-M MFMA path: q6_K M <= 16
+    ((270, FAKE16, FAKE16, FAKE16, 17, 1, 256, 3), -3),
+    ((13, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),      # small-M MFMA path: q4_K, q6_K only
+    ((10, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),
+    ((11, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),
     ((12, FAKE16, FAKE16, FAKE16, 0, 5, 256, 0), 0),       # M = 0: empty, nothing touched
     ((12, FAKE16, FAKE16, FAKE16, 5, 0, 256, 0), 0),       # N = 0: empty
     ((12, FAKE16, FAKE16, FAKE16, gq.GEMM_MAX_M + 1, 1, 256, 2), -3),  # GEMM grid limit
@@ -170,7 +173,8 @@ def test_linear_validation(L, args, status):
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16 + 1, 1, 1, 256, 0), -4),  # Y alignment
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 9, 1, 256, 1), -3),      # GEMV path, M > 8
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 1, 1, 256, 4), -1),      # unknown path
-    ((14, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),      # small-M path: q4_K only
+    ((13, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 4, 1, 256, 3), -2),      # small-M path: q4_K, q6_K
+    ((14, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 17, 1, 256, 3), -3),     # small-M q6_K, M > 16
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 65, 1, 256, 3), -3),     # small-M path, M > 64
     ((12, FAKE16, FAKE16, FAKE16, FAKE16, FAKE16, 0, 5, 256, 0), 0),       # M = 0: empty
 ])
@@ -206,7 +210,7 @@ def test_linear_group_arrays_and_paths(L):
     assert L.gemmq_linear_group(12, 1, one_p, None, one_n, *args, 0, None) == -1
     assert L.gemmq_linear_group(12, 1, one_p, one_p, None, *args, 0, None) == -1
     assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, *args, 4, None) == -1
-    assert L.gemmq_linear_group(14, 1, one_p, one_p, one_n, *args, 3, None) == -2
+    assert L.gemmq_linear_group(13, 1, one_p, one_p, one_n, *args, 3, None) == -2
     assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, FAKE16, FAKE16, 65, 256, 3,
                                 None) == -3
     assert L.gemmq_linear_group(12, 1, one_p, one_p, one_n, FAKE16, FAKE16, 9, 256, 1,

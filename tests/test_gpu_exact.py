@@ -171,6 +171,14 @@ def test_exact_small_m(dev, gq, orc, M, N, K):
     run_case(gq, orc, Q4, M, N, K, PATH_SKINNY, seed=2000 + 131 * M + N + K)
 
 
+@pytest.mark.parametrize("fmt", [Q6, R + Q6])
+@pytest.mark.parametrize("M", [1, 3, 8, 9, 16])
+@pytest.mark.parametrize("N,K", [(37, 256), (70, 2304), (33, 4096), (40, 12288)])
+def test_exact_small_m_q6K(dev, gq, orc, fmt, M, N, K):
+    log("exact small-M q6_K fmt=%d M=%d N=%d K=%d" % (fmt, M, N, K))
+    run_case(gq, orc, fmt, M, N, K, PATH_SKINNY, seed=2500 + fmt + 131 * M + N + K)
+
+
 @pytest.mark.parametrize("fmt", ALL)
 @pytest.mark.parametrize("M", [9, 70, 130])
 @pytest.mark.parametrize("N,K", [(37, 256), (130, 1024), (200, 8192), (65, 12288)])

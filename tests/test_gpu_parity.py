@@ -201,14 +201,15 @@ def test_adversarial_blocks(dev, gq, orc, fmt, path):
 
 
 def _expected_path(gq, fmt, M, cols):
-    # GEMV up to M = 8 (q4_K: up to 2); the small-M MFMA kernel for q4_K at
-    # 3 <= M <= 64 with one 16-row tile, or with t tiles while cols * t <= 20480;
-    # q6_K at 5 <= M <= 8 on the GEMM from 16384 columns; the GEMM otherwise
+    # GEMV up to M = 8 (q4_K: up to 2); the small-M MFMA kernels for q4_K at
+    # 3 <= M <= 64 with one 16-row tile, or with t tiles while cols * t <= 20480,
+    # and for q6_K at 9 <= M <= 16, or at 3 <= M <= 8 from 16384 columns; the
+    # GEMM otherwise
     t = (M + 15) // 16
     if fmt == Q4 and 3 <= M <= 64 and (t == 1 or cols * t <= 20480):
         return gq.PATH_SKINNY
-    if fmt == Q6 and 5 <= M <= 8 and cols >= 16384:
-        return gq.PATH_GEMM
+    if fmt == Q6 and 3 <= M <= 16 and (M > 8 or cols >= 16384):
+        return gq.PATH_SKINNY
     return gq.PATH_GEMV if M <= 8 else gq.PATH_GEMM
 
 
@@ -217,7 +218,7 @@ def _expected_path(gq, fmt, M, cols):
 def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
     # the automatic path takes the expected kernel family (the same bits as that
     # path forced); N = 7000 crosses the q4_K column bound between t = 2 and
-    # t = 3, N = 16384 the q6_K one at M = 5..8
+    # t = 3, N = 16384 the q6_K one at M = 3..8
     log("dispatch fmt=%d N=%d" % (fmt, N))
     K = 512 if N < 1000 else 256
     for M in (1, 2, 3, 4, 5, 6, 8, 9, 16, 17, 32, 33, 48, 49, 64, 65):
@@ -232,12 +233,13 @@ def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
 
 @pytest.mark.parametrize("N", [16383, 16384])
 def test_auto_dispatch_q6K_repacked(dev, gq, orc, N):
-    # the repacked q6_K layout follows the q6_K choice: at M = 5..8 the GEMM from
-    # 16384 columns, the GEMV below; both equal the original layout's bits
+    # the repacked q6_K layout follows the q6_K choice (the small-M kernel at
+    # M = 9..16 and at 3..8 from 16384 columns, the GEMV below, the GEMM beyond)
+    # with the original layout's bits
     import torch
 
     K = 512
-    for M in (4, 5, 8):
+    for M in (2, 4, 5, 8, 16, 17):
         log("dispatch q6_K_R N=%d M=%d" % (N, M))
         W, x, xq = _case(orc, Q6, M, N, K, seed=100 + M)
         Wd, xqd = to_dev(W), to_dev(xq)
