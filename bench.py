@@ -76,6 +76,8 @@ def parse():
                    help="activation rows; the first is the headline (value), the second secondary")
     p.add_argument("--copies", type=int, default=0, help="rotating weight copies (0: auto, >=1 GiB)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-other-workloads", action="store_true",
+                   help="skip the short timing of the set's other workloads")
     p.add_argument("--graph", action="store_true",
                    help="time HIP-graph replays of each pass instead of eager launches")
     p.add_argument("--cpu-seconds", type=float, default=20.0)
@@ -373,7 +375,7 @@ def profiled(workload, M, launches):
     names = [launch_name(ms) for ms in launches]
     if h.hexdigest() != rec.get("source_sha256") or any(n not in per for n in names):
         return None
-    return {"per_launch": {n: per[n] for n in names}, "summary": t.get("summary")}
+    return {"per_launch": {n: per[n] for n in names}, "summary": rec.get("summary")}
 
 
 def kernel_label(M):
@@ -386,7 +388,7 @@ def kernel_label(M):
     return "gemm_q4k4_kernel" if M >= 1024 else "gemm_q4k2_kernel"
 
 
-def measured_ceilings(wl):
+def measured_ceilings(wl, sizes=None):
     """Ceilings measured on this GPU beside the datasheet peaks: the library's
     read-only stream over 2 GiB (gemmq_probe_read, the GEMV's bound: it only
     reads weights); a plain 1 GiB device-to-device copy (read + write bytes);
@@ -434,6 +436,26 @@ def measured_ceilings(wl):
         dt = e0.elapsed_time(e1) * 1e-3
         best = dt if best is None else min(best, dt)
     out["read_GBs"] = round(n / best / 1e9, 1)
+    # the same stream over as many bytes as each launch's weights, rotating
+    # over slices of the 2 GiB buffer (cold): what a plain read of those bytes
+    # takes, fixed launch costs included
+    same = {}
+    for name, nbytes in (sizes or {}).items():
+        al = -(-nbytes // 256) * 256
+        slices = [src[o:o + nbytes - nbytes % 16] for o in range(0, n - al + 1, al)]
+        reps = max(50, len(slices))
+        for v in slices[:3]:
+            gq.probe_read(v)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            gq.probe_read(slices[i % len(slices)])
+        e1.record()
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) * 1e-3 / reps
+        same[name] = {"bytes": nbytes, "us": round(dt * 1e6, 3), "GBs": round(nbytes / dt / 1e9, 1)}
+    if same:
+        out["read_same_bytes"] = same
     del src
     n = GIB
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
@@ -517,6 +539,39 @@ def _oracle_rate(wl, gen, M1, M2, seconds, threads):
             run_all(pool, xq, len(rows))
             res["m2"] = time.perf_counter() - t0
     return res
+
+
+def other_workloads(main_name, steps, warmup):
+    """The set's other workloads (a single q4_K matrix at M = 8, the Qwen3-0.6B
+    layer at M = 1 and 512, the Qwen3-1.7B layer with its q6_K head at M = 1
+    and 512), each pass timed as the main workload's (eager launches over
+    >= 1 GiB of rotating weight copies): microseconds per pass, weight GB/s and
+    int8 TOP/s, and the path each launch takes."""
+    import torch
+
+    from quant_packed_weight_amd import synth
+
+    out = {}
+    for name, wl in synth.WORKLOADS.items():
+        if name == main_name:
+            continue
+        gen = synth.generate(name)
+        wbytes = sum(m.nbytes for m in wl.matrices)
+        copies = max(1, math.ceil(GIB / wbytes))
+        layer = Layer(wl, gen, list(wl.Ms), copies)
+        stream = torch.cuda.current_stream()
+        rec = {"weight_bytes": wbytes, "launches": [launch_name(ms) for ms in layer.launches]}
+        for M in wl.Ms:
+            t = time_passes(layer, M, steps, warmup, copies, stream)
+            ops = sum(2 * M * m.N * m.K for m in wl.matrices)
+            rec["M=%d" % M] = {"us_per_pass": round(t * 1e6, 2),
+                               "weight_GBs": round(wbytes / t / 1e9, 1),
+                               "int8_TOPs": round(ops / t / 1e12, 2)}
+        out[name] = rec
+        del layer, gen
+        torch.cuda.empty_cache()
+        progress("%s timed" % name)
+    return out
 
 
 def host_cores():
@@ -664,9 +719,8 @@ def main():
     torch.cuda.set_device(0)
     wl = synth.WORKLOADS[a.workload]
     Ms = [M for M in a.m]
-    gen = synth.generate(a.workload, Ms=None if set(Ms) - set(wl.Ms) else set(Ms))
-    if set(Ms) - set(wl.Ms):
-        raise SystemExit("workload %s has M in %s" % (a.workload, wl.Ms))
+    # activation widths beyond the workload's own are drawn after its own
+    gen = synth.generate(a.workload, Ms=set(Ms))
     wbytes = sum(m.nbytes for m in wl.matrices)
     copies = a.copies or max(1, math.ceil(GIB / wbytes))
     layer = Layer(wl, gen, Ms, copies, group=not a.no_group, fuse=not a.no_fuse)
@@ -826,7 +880,8 @@ def main():
                           "input copies")
         res["quantizer"] = qrec
     progress("quantizer timed")
-    c = res["ceilings"] = measured_ceilings(wl)
+    c = res["ceilings"] = measured_ceilings(
+        wl, {launch_name(ms): sum(m.nbytes for m in ms) for ms in layer.launches})
     progress("ceilings measured")
     c["read_frac_of_peak"] = round(c["read_GBs"] / HBM_PEAK_GBS, 4)
     c["copy_frac_of_peak"] = round(c["copy_GBs"] / HBM_PEAK_GBS, 4)
@@ -842,10 +897,19 @@ def main():
                 k: round(v / c["read_GBs"], 4) for k, v in r["per_launch_GBs"].items()}
             r["per_launch_frac_of_peak"] = {
                 k: round(v / HBM_PEAK_GBS, 4) for k, v in r["per_launch_GBs"].items()}
+            rs = c.get("read_same_bytes", {})
+            if all(k in rs for k in r["per_launch_us"]):
+                # against a plain read of each launch's bytes (fixed launch costs in both)
+                r["per_launch_frac_of_same_size_read"] = {
+                    k: round(rs[k]["us"] / v, 4) for k, v in r["per_launch_us"].items()}
+                r["frac_of_same_size_read"] = round(
+                    sum(rs[k]["us"] for k in r["per_launch_us"]) / sum(r["per_launch_us"].values()), 4)
         else:
             r["frac_of_measured_mfma"] = round(r["achieved"] / c["mfma_i8_TOPs"], 4)
             if c.get("int8_gemm_TOPs"):
                 r["vs_int8_gemm_library"] = round(r["achieved"] / c["int8_gemm_TOPs"], 4)
+    if not a.no_other_workloads:
+        res["other_workloads"] = other_workloads(a.workload, a.steps, a.warmup)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, gen, M1, M2, a.cpu_seconds)
         progress("oracle timed")

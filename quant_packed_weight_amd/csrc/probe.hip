@@ -52,33 +52,39 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, int32_t*
   }
 }
 
-// Read-only stream: 2048 waves (256 workgroups of eight), each lane reading 16
-// bytes per load in a grid-stride loop with eight loads issued before any is
-// used (loads past the end are switched off, so a buffer smaller than eight
-// strides is still read in one round); every wave stores the XOR of what it
-// read, so no load can be dropped.  The time of the launch gives the sustained
-// read rate of device memory with nothing else in the way, and on a buffer the
-// size of one matmul's weights, the time a plain stream of those bytes takes.
+// Read-only stream: 2048 waves (256 workgroups of eight), each reading one
+// contiguous span of the buffer (a multiple of 8 KiB, the last one shorter) as
+// a matmul wave reads its weight rows: every load instruction covers 1 KiB,
+// eight of them are issued before any is used (loads past the span's end are
+// switched off, so a buffer smaller than a round is still read in one).  Every
+// wave stores the XOR of what it read, so no load can be dropped.  The time of
+// the launch gives the sustained read rate of device memory with nothing else
+// in the way, and on a buffer the size of one matmul's weights, the time a
+// plain stream of those bytes takes.
 constexpr int kReadWaves = 2048;
 constexpr int kReadUnroll = 8;
 
 __global__ __launch_bounds__(512) void read_probe_kernel(const uint4* __restrict__ src,
                                                          int64_t nvec, uint32_t* __restrict__ out) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  constexpr int64_t kRound = 64 * kReadUnroll;  // 16-byte vectors per wave and round
+  const int lane = (int)(threadIdx.x & 63);
+  const int64_t wid = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int64_t nw = (int64_t)gridDim.x * (blockDim.x >> 6);
+  const int64_t span = ((nvec + nw - 1) / nw + kRound - 1) / kRound * kRound;
+  const int64_t lo = wid * span, hi = lo + span < nvec ? lo + span : nvec;
   uint32_t a = 0;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec;
-       i += kReadUnroll * stride) {
+  for (int64_t i = lo + lane; i < hi; i += kRound) {
     uint4 v[kReadUnroll];
 #pragma unroll
     for (int k = 0; k < kReadUnroll; ++k)
-      v[k] = i + k * stride < nvec ? src[i + k * stride] : make_uint4(0u, 0u, 0u, 0u);
+      v[k] = i + 64 * k < hi ? src[i + 64 * k] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int k = 0; k < kReadUnroll; ++k) a ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
   }
   // fold the wave (xor over the lanes) and store one word per wave
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) a ^= (uint32_t)__shfl_xor((int)a, m, 64);
-  if ((threadIdx.x & 63) == 0) out[(int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6)] = a;
+  if (lane == 0) out[wid] = a;
 }
 
 }  // namespace

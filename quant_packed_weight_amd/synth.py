@@ -154,7 +154,8 @@ class Generated:
 
 def generate(name: str, Ms=None, with_weights: bool = True) -> Generated:
     """Draw a named workload.  ``Ms`` restricts which activation sets are kept,
-    without changing the draw order (the others are drawn and dropped)."""
+    without changing the draw order (the others are drawn and dropped); widths
+    in ``Ms`` that the workload does not list are drawn after its own."""
     wl = WORKLOADS[name]
     rng = np.random.default_rng(wl.seed)
     g = Generated(wl)
@@ -169,4 +170,9 @@ def generate(name: str, Ms=None, with_weights: bool = True) -> Generated:
             x = make_activations(rng, M, K, wl.outliers)
             if Ms is None or M in Ms:
                 g.activations[(M, inp)] = x
+    # activation widths outside the workload's own, drawn after all of those
+    # (so they change none of them), in increasing M
+    for M in sorted(set(Ms or ()) - set(wl.Ms)):
+        for inp, K in wl.inputs():
+            g.activations[(M, inp)] = make_activations(rng, M, K, wl.outliers)
     return g
