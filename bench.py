@@ -440,22 +440,40 @@ def measured_ceilings(wl, sizes=None):
     # over slices of the 2 GiB buffer (cold): what a plain read of those bytes
     # takes, fixed launch costs included
     same = {}
+    lib = gq.lib()
+    fold = torch.empty(gq.PROBE_READ_WORDS, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream().cuda_stream
     for name, nbytes in (sizes or {}).items():
+        # the C call with its arguments built beforehand, as the matmul launches
+        # are timed (the Python wrapper's own cost would exceed the kernel's)
         al = -(-nbytes // 256) * 256
-        slices = [src[o:o + nbytes - nbytes % 16] for o in range(0, n - al + 1, al)]
-        reps = max(50, len(slices))
-        for v in slices[:3]:
-            gq.probe_read(v)
+        nb16 = nbytes - nbytes % 16
+        ptrs = [src.data_ptr() + o for o in range(0, n - al + 1, al)]
+        reps = max(50, len(ptrs))
+        for p in ptrs[:3]:
+            lib.gemmq_probe_read(p, nb16, fold.data_ptr(), st)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(reps):
-            gq.probe_read(slices[i % len(slices)])
+            if lib.gemmq_probe_read(ptrs[i % len(ptrs)], nb16, fold.data_ptr(), st):
+                raise gq.GemmqError(-1, "gemmq_probe_read")
         e1.record()
         torch.cuda.synchronize()
         dt = e0.elapsed_time(e1) * 1e-3 / reps
         same[name] = {"bytes": nbytes, "us": round(dt * 1e6, 3), "GBs": round(nbytes / dt / 1e9, 1)}
     if same:
         out["read_same_bytes"] = same
+    # the same launch on 16 bytes: what any launch of the pass costs at the least
+    # (dispatch, one wave's load round trip, completion), timed back to back
+    for p in [src.data_ptr()] * 3:
+        lib.gemmq_probe_read(p, 16, fold.data_ptr(), st)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(200):
+        lib.gemmq_probe_read(src.data_ptr(), 16, fold.data_ptr(), st)
+    e1.record()
+    torch.cuda.synchronize()
+    out["launch_floor_us"] = round(e0.elapsed_time(e1) * 1e3 / 200, 3)
     del src
     n = GIB
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
