@@ -23,7 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libgemmq.so")
-SOURCES = ["abi.hip", "quantize.hip", "gemv.hip", "gemm.hip", "gemm_q4k.hip", "decode.hip",
+SOURCES = ["abi.hip", "quantize.hip", "gemv.hip", "gemm.hip", "gemm_q4k.hip", "gemm_q6k.hip", "decode.hip",
            "repack.hip", "probe.hip", "skinny.hip", "skinny_q6k.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

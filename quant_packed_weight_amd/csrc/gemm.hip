@@ -23,8 +23,10 @@
 //  * One f32 epilogue per super-block and output:
 //    y += d_x * (d * I_sc - dmin * I_min)   (q3_K, q6_K: y += d_x * d * I_sc).
 //
-// Two kernels:
-//  * q4_K: gemm_q4k_kernel in gemm_q4k.hip (launched from here).
+// Kernels:
+//  * q4_K: the two- and four-tile kernels in gemm_q4k.hip (launched from here).
+//  * q6_K on grids of 2048 workgroups and more: the four-tile kernel in
+//    gemm_q6k.hip (the same integer sums and epilogue, so the same bits).
 //  * q2_K, q3_K, q5_K, q6_K (gemm_plane_kernel): a 256-thread workgroup
 //    computes a 128 (M) x 64 (N) tile, each of its four waves a 64 x 32
 //    sub-tile.  Per super-block the workgroup stages the activation tile (int8
@@ -603,12 +605,19 @@ bool set_lds_limits() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
         hipFuncSetAttribute((const void*)gemm_plane_kernel<13, SILU>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
-        !q4k_prepare(SILU))
+        !q4k_prepare(SILU) || !q6k_prepare(SILU))
       return false;
     attr_done[dev].store(1, std::memory_order_release);
   }
   return true;
 }
+
+// q6_K: the four-tile kernel from this many workgroups (eight per CU; measured
+// on the Qwen3-1.7B shapes: the 151936-row head at M = 512 561.7 against
+// 702.8 us on the plane kernel, at M = 64 -- 1187 workgroups -- 188.6 against
+// 182.6 us, down (2048 x 6144) at M = 2048 -- 256 workgroups -- 111.6 against
+// 103.0 us)
+constexpr int64_t kQ6FourTileWorkgroups = 2048;
 
 template <bool SILU>
 int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t K,
@@ -617,6 +626,15 @@ int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t 
   if (!gemm_fits(fmt, M, K)) return -1;
   if (!set_lds_limits<SILU>()) return -2;
   GroupTiles gt;
+  if (fmt == 14 || fmt == 256 + 14) {
+    // the four-tile q6_K kernel (128 x 128 workgroup tiles) where the launch
+    // has enough of them to fill the chip; the plane kernel's 128 x 64 tiles
+    // below that.  Both give every output the same integer sum and the same
+    // f32 epilogue in the same order, so the choice changes no bits.
+    if (!(SILU ? make_pair_tiles(grp, 128, gt) : make_tiles(grp, 128, gt))) return -1;
+    if ((int64_t)gt.start[kMaxGroup] * ((M + 127) / 128) >= kQ6FourTileWorkgroups)
+      return launch_gemm_q6k(gt, fmt, SILU, Xq, M, K, st);
+  }
   const int64_t bn = fmt == 12 ? 128 : kBN;
   if (!(SILU ? make_pair_tiles(grp, bn, gt) : make_tiles(grp, bn, gt))) return -1;
   if (fmt == 12) return launch_gemm_q4k(gt, SILU, Xq, M, K, st);

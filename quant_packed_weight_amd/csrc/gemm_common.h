@@ -1,7 +1,8 @@
-// gemm_common.h -- pieces the two prefill GEMM kernels share (gemm.hip: the
-// plane kernel for q2_K, q3_K, q5_K, q6_K; gemm_q4k.hip: the q4_K kernel):
-// matrix-core wrappers, the plane-byte multiply, buffer descriptors and
-// direct buffer->LDS loads, and the SiLU-gated output pair.
+// gemm_common.h -- pieces the prefill GEMM kernels share (gemm.hip: the plane
+// kernel for q2_K, q3_K, q5_K; gemm_q4k.hip: the q4_K kernels; gemm_q6k.hip:
+// the q6_K kernel): matrix-core wrappers, the plane-byte multiply, buffer
+// descriptors and direct buffer->LDS loads, the SiLU-gated output pair, and
+// the four-tile kernels' activation stage and epilogue.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -129,6 +130,68 @@ __device__ __forceinline__ void silu_pair(float a, float b, bool odd, float& g, 
   const float got = pair_partner(odd ? a : b);  // even lanes get up_a, odd lanes gate_b
   g = odd ? got : a;
   u = odd ? b : got;
+}
+
+
+// ---- the four-tile kernels' activation stage (q4_K and q6_K, from 1024 rows)
+
+// LDS map of one stage for T 32-row tiles (bytes): the int8 values, the int16
+// group sums and d_x of the workgroup's 32 T activation rows
+template <int T>
+struct TileStage {
+  static constexpr int kBM = 32 * T;                // activation rows per workgroup
+  static constexpr int kBN = 128;                   // weight rows (output columns) per workgroup
+  static constexpr int kOffQ = 0;                   // [kBM][kRow] int8 values
+  static constexpr int kOffBs = kBM * kRow;         // [kBM][16] int16 group sums
+  static constexpr int kOffDx = kOffBs + kBM * 32;  // [kBM] f32 d_x
+  static constexpr int kStage = kOffDx + kBM * 4;
+};
+
+// Value row r = base + R of the activation tile (R a compile-time constant):
+// lane l's dword at buffer byte voff(l) + r * xstride + xb to LDS byte
+// st + r * kRow + 4 l.  The row's offsets are computed inside the asm, where
+// they are used: a stage has 32 T rows, and offsets hoisted out of the loop
+// would each hold a scalar register for the whole kernel.
+template <int R>
+__device__ __forceinline__ void dma_row(rsrc_t rs, uint32_t voff, uint32_t base, uint32_t xstride,
+                                        uint32_t xb, uint32_t st) {
+  uint32_t r, so;
+  asm volatile(
+      "s_add_u32 %0, %4, %7\n\t"
+      "s_mul_i32 %1, %0, %5\n\t"
+      "s_add_u32 %1, %1, %6\n\t"
+      "s_mul_i32 %0, %0, %8\n\t"
+      "s_add_u32 m0, %0, %9\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, %1 offen lds"
+      : "=&s"(r), "=&s"(so)
+      : "v"(voff), "s"(rs), "s"(base), "s"(xstride), "s"(xb), "n"(R), "n"(kRow), "s"(st)
+      : "memory", "m0", "scc");
+}
+
+// group sums of row `row` of the stage, groups 8h..8h+7, as f16 (exact)
+__device__ __forceinline__ v8h stage_bsums(const uint8_t* bsp, int row, int h) {
+  const uint4 braw = *reinterpret_cast<const uint4*>(bsp + row * 32 + 16 * h);
+  const uint32_t bh[4] = {i16x2_to_h2(braw.x), i16x2_to_h2(braw.y), i16x2_to_h2(braw.z),
+                          i16x2_to_h2(braw.w)};
+  return __builtin_bit_cast(v8h, bh);
+}
+
+// The epilogue of one tile: y += d_x * (d * I - dm * C) for accumulator
+// registers 4 q4 + s0 .. 4 q4 + s0 + n - 1, whose rows (8 q4 + 4h + s of the
+// tile) have their d_x in one 16-byte LDS word.  q4_K: I = I_sc, C = I_min,
+// dm = dmin; q6_K: I = sum sc q x, C = sum sc bsum, dm = 32 d.
+template <int n>
+__device__ __forceinline__ void tile_epi(const v16i& acc, const v16f& im, float4 dx, float d,
+                                         float dm, float (&y)[16], int q4, int s0) {
+  const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
+#pragma unroll
+  for (int s = s0; s < s0 + n; ++s) {
+    const int r = 4 * q4 + s;
+    float t = d * (float)acc[r];
+    t = fmaf(-dm, im[r], t);
+    y[r] = fmaf(dxs[s], t, y[r]);
+  }
 }
 
 }  // namespace gk

@@ -401,45 +401,12 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k2_kernel(
 // Four row tiles per wave (128 activation rows per workgroup), from 1024
 // activation rows: the raw weights go straight to registers.
 // ====================================================================
-// LDS map of one stage for T row tiles (bytes)
-template <int T>
-struct Q4Map {
-  static constexpr int kBM = 32 * T;                // activation rows per workgroup
-  static constexpr int kBN = 128;                   // weight rows (output columns) per workgroup
-  static constexpr int kOffQ = 0;                   // [kBM][kRow] int8 values
-  static constexpr int kOffBs = kBM * kRow;         // [kBM][16] int16 group sums
-  static constexpr int kOffDx = kOffBs + kBM * 32;  // [kBM] f32 d_x
-  static constexpr int kStage = kOffDx + kBM * 4;
-};
-
 template <int T, int SPLIT>
 constexpr int q4_lds_bytes() {
-  return 2 * SPLIT * Q4Map<T>::kStage;
+  return 2 * SPLIT * TileStage<T>::kStage;
 }
 static_assert(2 * q4_lds_bytes<4, 1>() <= 160 * 1024, "two T = 4 workgroups per CU");
 static_assert(q4_lds_bytes<4, 2>() <= 160 * 1024, "one split T = 4 workgroup per CU");
-
-// Value row r = base + R of the activation tile (R a compile-time constant):
-// lane l's dword at buffer byte voff(l) + r * xstride + xb to LDS byte
-// st + r * kRow + 4 l.  The row's offsets are computed inside the asm, where
-// they are used: a stage has 32 T rows, and offsets hoisted out of the loop
-// would each hold a scalar register for the whole kernel.
-template <int R>
-__device__ __forceinline__ void dma_row(rsrc_t rs, uint32_t voff, uint32_t base, uint32_t xstride,
-                                        uint32_t xb, uint32_t st) {
-  uint32_t r, so;
-  asm volatile(
-      "s_add_u32 %0, %4, %7\n\t"
-      "s_mul_i32 %1, %0, %5\n\t"
-      "s_add_u32 %1, %1, %6\n\t"
-      "s_mul_i32 %0, %0, %8\n\t"
-      "s_add_u32 m0, %0, %9\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, %1 offen lds"
-      : "=&s"(r), "=&s"(so)
-      : "v"(voff), "s"(rs), "s"(base), "s"(xstride), "s"(xb), "n"(R), "n"(kRow), "s"(st)
-      : "memory", "m0", "scc");
-}
 
 // The raw q4_K bytes lane (i, h) needs of one super-block of its weight row:
 // the 16-byte header (d, dmin, scales) and quant bytes 16h..16h+15 of each of
@@ -490,30 +457,6 @@ __device__ __forceinline__ v4i q4_plane(const v4i& nib, uint32_t f) {
   return p;
 }
 
-// group sums of row `row` of the stage, groups 8h..8h+7, as f16 (exact)
-__device__ __forceinline__ v8h q4_bsums(const uint8_t* bsp, int row, int h) {
-  const uint4 braw = *reinterpret_cast<const uint4*>(bsp + row * 32 + 16 * h);
-  const uint32_t bh[4] = {i16x2_to_h2(braw.x), i16x2_to_h2(braw.y), i16x2_to_h2(braw.z),
-                          i16x2_to_h2(braw.w)};
-  return __builtin_bit_cast(v8h, bh);
-}
-
-// The epilogue of one tile: y += d_x * (d * I_sc - dmin * I_min) for
-// accumulator registers 4 q4 + s0 .. 4 q4 + s0 + n - 1, whose rows
-// (8 q4 + 4h + s of the tile) have their d_x in one 16-byte LDS word.
-template <int n>
-__device__ __forceinline__ void q4_epi(const v16i& acc, const v16f& im, float4 dx, float d,
-                                       float dm, float (&y)[16], int q4, int s0) {
-  const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
-#pragma unroll
-  for (int s = s0; s < s0 + n; ++s) {
-    const int r = 4 * q4 + s;
-    float t = d * (float)acc[r];
-    t = fmaf(-dm, im[r], t);
-    y[r] = fmaf(dxs[s], t, y[r]);
-  }
-}
-
 // One super-block for one wave from stage `st`: lane (i, h) holds weight column
 // i of the wave's 32 and K-half h of every 32-wide MFMA step.  Per tile and
 // step one activation fragment feeds two independent MFMAs (the a-plane and
@@ -530,7 +473,7 @@ __device__ __forceinline__ void q4_epi(const v16i& acc, const v16f& im, float4 d
 template <int T, typename Dma, typename Next>
 __device__ __forceinline__ void q4_compute(const uint8_t* st, const Q4Raw& raw, float (&y)[T][16],
                                            int i, int h, Dma&& dma, Next&& next) {
-  using Map = Q4Map<T>;
+  using Map = TileStage<T>;
   constexpr int kAhead = 3;  // activation fragments read this many steps ahead
   constexpr int kF = 8 * T;
   const uint8_t* abase = st + Map::kOffQ + i * kRow + 16 * h;
@@ -589,7 +532,7 @@ __device__ __forceinline__ void q4_compute(const uint8_t* st, const Q4Raw& raw, 
     for (int kc = 0; kc < 8; ++kc) {
       dma(t, kc);
       if (T > 2 && t > 0 && (kc & 1) && kc < 7) read_dx((kc + 1) >> 1);
-      if (kc == 4) bsf = q4_bsums(st + Map::kOffBs, 32 * t + i, h);
+      if (kc == 4) bsf = stage_bsums(st + Map::kOffBs, 32 * t + i, h);
       aa = mfma_i8(af[8 * t + kc], pa[kc], kc == 0 ? (v16i){0} : aa);
       ab = mfma_i8(af[8 * t + kc], pb[kc], kc == 0 ? (v16i){0} : ab);
       if (8 * t + kc + kAhead < kF) read_af(8 * t + kc + kAhead);
@@ -601,7 +544,7 @@ __device__ __forceinline__ void q4_compute(const uint8_t* st, const Q4Raw& raw, 
         }
       } else {
         // two registers per step
-        q4_epi<2>(pacc, pim, dxv[kc >> 1], dcol, mcol, y[t - 1], kc >> 1, 2 * (kc & 1));
+        tile_epi<2>(pacc, pim, dxv[kc >> 1], dcol, mcol, y[t - 1], kc >> 1, 2 * (kc & 1));
       }
       if (t == (T > 2 ? T - 1 : 0) && kc == 0) next();
       __builtin_amdgcn_sched_barrier(0);
@@ -616,7 +559,7 @@ __device__ __forceinline__ void q4_compute(const uint8_t* st, const Q4Raw& raw, 
   __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4)
-    q4_epi<4>(pacc, pim,
+    tile_epi<4>(pacc, pim,
               *reinterpret_cast<const float4*>(dxp + 4 * (32 * (T - 1) + 8 * q4)), dcol, mcol,
               y[T - 1], q4, 0);
 }
@@ -627,7 +570,7 @@ __device__ __forceinline__ void q4_compute(const uint8_t* st, const Q4Raw& raw, 
 template <int T, int SPLIT, bool SILU>
 __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k4_kernel(
     const GroupTiles gt, const uint8_t* __restrict__ Xq, int64_t M, int nb) {
-  using Map = Q4Map<T>;
+  using Map = TileStage<T>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   // SPLIT groups of four waves: K-group kg takes super-blocks [kg nb0, ...);
   // in each group wave `wave` owns weight columns 32 wave .. 32 wave + 31

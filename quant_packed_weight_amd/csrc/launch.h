@@ -107,6 +107,11 @@ int prepare_gemm(bool silu);
 bool q4k_prepare(bool silu);
 int launch_gemm_q4k(const GroupTiles& gt, bool silu, const uint8_t* Xq, int64_t M, int64_t K,
                     hipStream_t st);
+// gemm_q6k.hip: the q6_K GEMM (fmt 14 or its repacked layout) over the
+// 128-row weight tiles of `gt`, limits raised once per device by q6k_prepare
+bool q6k_prepare(bool silu);
+int launch_gemm_q6k(const GroupTiles& gt, int fmt, bool silu, const uint8_t* Xq, int64_t M,
+                    int64_t K, hipStream_t st);
 // The fused decode form: quantize X (M x K f32) and run the GEMV in one launch,
 // each workgroup quantizing into its own LDS; Xq receives the q8_K blocks.
 // Taken when gemv_fusable(M, K): M <= 4 and M K / 256 small enough (see gemv.hip).
