@@ -85,6 +85,28 @@ __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, u
                : "memory");
 }
 
+// dma4 / dma16 taken only where the wave-uniform flag `take` is nonzero.  The
+// branch is inside the asm: a branch the compiler sees splits the basic block,
+// and work fenced beside the matrix instructions (sched_barrier acts within a
+// block) is then sunk past it.
+__device__ __forceinline__ void dma4_if(uint32_t take, rsrc_t rs, uint32_t voff, uint32_t soff,
+                                        uint32_t lds) {
+  const uint32_t t = __builtin_amdgcn_readfirstlane(take);
+  asm volatile("s_cmp_eq_u32 %4, 0\n\ts_cbranch_scc1 1f\n\ts_nop 0\n\t"
+               "buffer_load_dword %0, %1, %2 offen lds\n1:" ::"v"(voff),
+               "s"(rs), "s"(soff), "{m0}"(lds), "s"(t)
+               : "memory", "scc");
+}
+
+__device__ __forceinline__ void dma16_if(uint32_t take, rsrc_t rs, uint32_t voff, uint32_t soff,
+                                         uint32_t lds) {
+  const uint32_t t = __builtin_amdgcn_readfirstlane(take);
+  asm volatile("s_cmp_eq_u32 %4, 0\n\ts_cbranch_scc1 1f\n\ts_nop 0\n\t"
+               "buffer_load_dwordx4 %0, %1, %2 offen lds\n1:" ::"v"(voff),
+               "s"(rs), "s"(soff), "{m0}"(lds), "s"(t)
+               : "memory", "scc");
+}
+
 // a * b + c in scalar registers, computed where it is used: the kernels issue
 // dozens of row loads per stage, and offsets the compiler hoisted out of the
 // loop would each hold a scalar register for the whole kernel.

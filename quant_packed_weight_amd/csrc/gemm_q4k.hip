@@ -83,10 +83,11 @@ constexpr int kStage = kOffW + kBN * kQ4KBytes;
 // order never depends on M.
 template <int SPLIT>
 constexpr int lds_bytes() { return kS * SPLIT * kStage; }
-// loads per stage issued by each wave: 16 value rows + 2 group-sum blocks + 4
-// weight chunks (waves 0 and 1 a fifth, wave 0 also the 64 d_x); waits count
-// the smallest number, which can only wait for more than needed.
-constexpr int kDma = 22;
+// loads per stage issued by each wave: 4 value loads + 4 weight chunks (wave 0
+// a fifth value load and the 64 d_x, waves 0 and 1 a fifth weight chunk and
+// the group sums); waits count the smallest number, which can only wait for
+// more than needed.
+constexpr int kDma = 8;
 constexpr int kWait = kDma * (kS - 2) < 63 ? kDma * (kS - 2) : 63;  // vmcnt field is 6 bits
 }  // namespace q4s
 
@@ -276,11 +277,20 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k2_kernel(
   constexpr int kStride = SPLIT * q4s::kStage;  // bytes from one stage to the next
 
   // per-lane source offsets within one super-block column
-  const uint32_t vq = 4 + 4 * lane;  // value bytes of a row: one dword per lane
-  uint32_t vbs[2];                   // group sums: row 8j + lane/8, dword lane%8
+  // value rows: the stage's 64 padded rows (17 16-byte units each) are 17
+  // 16-byte loads of 64 units: unit U = 64 j + lane is unit U % 17 of row
+  // U / 17 (unit 16, the padding, reads the first group sums: never used).
+  // Wave w issues j = w + 4 k (k < 4) and wave 0 also j = 16.  The q8_K
+  // values are only 4-byte aligned; the 16-byte loads do not need more.
+  uint32_t vx[5];
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj)
-    vbs[jj] = (uint32_t)(8 * (wave + 4 * jj) + (lane >> 3)) * xstride + 260 + 4 * (lane & 7);
+  for (int k = 0; k < 5; ++k) {
+    const uint32_t U = 64u * (k < 4 ? (uint32_t)(wave + 4 * k) : 16u) + (uint32_t)lane;
+    vx[k] = (U / 17u) * xstride + 4u + 16u * (U % 17u);
+  }
+  // group sums: 64 rows x 32 bytes, two 16-byte loads (waves 0, 1): lane l
+  // takes row 32 w + l / 2, half l % 2
+  const uint32_t vbs = (uint32_t)(32 * wave + (lane >> 1)) * xstride + 260 + 16 * (lane & 1);
   const uint32_t vdx = (uint32_t)lane * xstride;  // d_x of row lane
   // weight load u = wave + 4j (u < 18) covers 16-byte chunks 64u..64u+63 of
   // the 128 x 9-chunk tile, i.e. row c / 9, chunk c % 9 for c = 64u + lane
@@ -293,28 +303,25 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k2_kernel(
     vw[j] = row * wstride + 16u * (c % 9u);
   }
 
-  // part p (0..15) of the loads of super-block b into stage `slot`: value rows
-  // 2p, 2p+1 (p < 8), the two group-sum blocks (8, 9), d_x (10), the weight
-  // chunks (11..15)
+  // part p (0..15) of the loads of super-block b into stage `slot`: value
+  // loads (0..4), the group sums (8), d_x (10), the weight chunks (11..15)
   auto issue = [&](int b, int slot, int p) {
     const uint32_t st = lds0 + (uint32_t)slot * kStride;
     const uint32_t xb = (uint32_t)b * kQ8KBytes, wb = (uint32_t)b * kQ4KBytes;
-    if (p < 8) {
-#pragma unroll
-      for (int j = 2 * p; j < 2 * p + 2; ++j) {
-        const uint32_t r = (uint32_t)(wave + 4 * j);
-        dma4(xr, vq, r * xstride + xb, st + q4s::kOffQ + r * kRow);
-      }
-    } else if (p < 10) {
-      dma4(xr, vbs[p - 8], xb, st + q4s::kOffBs + (wave + 4 * (p - 8)) * 256);
+    if (p < 4) {
+      dma16(xr, vx[p], xb, st + q4s::kOffQ + 1024u * (uint32_t)(wave + 4 * p));
+    } else if (p == 4) {
+      dma16_if(wave == 0, xr, vx[4], xb, st + q4s::kOffQ + 1024u * 16u);
+    } else if (p == 8) {
+      dma16_if(wave < 2, xr, vbs, xb, st + q4s::kOffBs + 1024u * (uint32_t)wave);
     } else if (p == 10) {
-      if (wave == 0) dma4(xr, vdx, xb, st + q4s::kOffDx);
-    } else if (p < 15) {
+      dma4_if(wave == 0, xr, vdx, xb, st + q4s::kOffDx);
+    } else if (p >= 11 && p < 15) {
       const int u = wave + 4 * (p - 11);
       dma16(SILU && u >= 9 ? wr2 : wr, vw[p - 11], wb, st + q4s::kOffW + 1024 * u);
-    } else {
-      if (wave < 2) dma16(SILU ? wr2 : wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
-    }
+    } else if (p == 15) {
+      dma16_if(wave < 2, SILU ? wr2 : wr, vw[4], wb, st + q4s::kOffW + 1024 * (wave + 16));
+    }  // parts 5..7 and 9 load nothing
   };
   float y[2][16];
 #pragma unroll
@@ -614,31 +621,48 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k4_kernel(
   auto stage_off = [&](int slot) __attribute__((always_inline)) { return (uint32_t)((slot * SPLIT + kg) * Map::kStage); };
 
   // per-lane source offsets within one super-block column
-  const uint32_t vq = 4 + 4 * lane;  // value bytes of a row: one dword per lane
-  // group sums: block u = wave + 4t, rows 8u + lane/8 (the 32t rows of tile t
-  // in the scalar offset)
-  const uint32_t vbs = (uint32_t)(8 * wave + (lane >> 3)) * xstride + 260 + 4 * (lane & 7);
+  // value rows: the stage's 32 T padded rows (17 16-byte units each) are
+  // 17 T / 2 16-byte loads of 64 units: unit U = 64 j + lane is unit U % 17 of
+  // row U / 17 (unit 16, the padding, reads the first group sums: never used).
+  // Wave w issues j = w + 4 k, k = 0 .. 17 T / 8 - 1 (the last only where
+  // j < 17 T / 2).  With U0 = 64 w + lane, load k takes U = U0 + 256 k, and
+  // 256 = 15 * 17 + 1: row U0 / 17 + 15 k + e, unit U0 % 17 + k - 17 e, where
+  // e = 1 once U0 % 17 + k reaches 17.  The lane keeps its offset for e = 0
+  // and the first k with e = 1; the 15 k rows and 16 k bytes go into the
+  // scalar offset.
+  constexpr int kVal = 17 * T / 2;  // value loads per stage
+  const uint32_t u0 = 64u * (uint32_t)wave + (uint32_t)lane;
+  const uint32_t vx0 = (u0 / 17u) * xstride + 4u + 16u * (u0 % 17u);
+  const uint32_t kwrap = 17u - u0 % 17u;
+  // group sums: 32 T rows x 32 bytes, one 16-byte load per wave (waves < T):
+  // lane l takes row 32 w + l / 2, half l % 2
+  const uint32_t vbs = (uint32_t)(32 * wave + (lane >> 1)) * xstride + 260 + 16 * (lane & 1);
   const uint32_t vdx = (uint32_t)(64 * wave + lane) * xstride;  // waves < T/2: d_x of 64 rows
-  // The next stage's loads, one per call: tile t's MFMA k issues value row
-  // 32t + wave + 4k (k < 8), the group-sum block of tile t (k = 8) and, from
-  // waves 0..T/2-1 in tile 0, the d_x of 64 rows (k = 9).
-  auto issue = [&](int b, int slot, int t, int k) __attribute__((always_inline)) {
+  // The next stage's loads: value load k (k < 17 T / 8), the group sums
+  // (k = 16) and, from waves 0..T/2-1, the d_x of 64 rows (k = 20).
+  auto issue = [&](int b, int slot, int k) __attribute__((always_inline)) {
     const uint32_t st = lds0 + stage_off(slot);
     const uint32_t xb = (uint32_t)b * kQ8KBytes;
-    if (k < 8) {
+    if (k < (kVal + 3) / 4) {
       static_assert(Map::kOffQ == 0, "value rows at the stage base");
-      dma_row<0>(xr, vq, (uint32_t)wave + 32 * t + 4 * k, xstride, xb, st);
-    } else if (k == 8) {
-      dma4(xr, vbs, smad(32 * t, xstride, xb), st + Map::kOffBs + (wave + 4 * t) * 256);
-    } else if (k == 9 && t == 0 && 2 * wave < T) {
-      dma4(xr, vdx, xb, st + Map::kOffDx + 256 * wave);
+      const uint32_t v = (uint32_t)k < kwrap ? vx0 : vx0 + (xstride - 272u);
+      const uint32_t dst = st + 1024u * (uint32_t)(wave + 4 * k);
+      if (4 * k + 3 < kVal)
+        dma16(xr, v, smad(15u * k, xstride, xb + 16u * k), dst);
+      else
+        dma16_if(wave + 4 * k < kVal, xr, v, smad(15u * k, xstride, xb + 16u * k), dst);
+    } else if (k == 16) {
+      if constexpr (T >= 4)
+        dma16(xr, vbs, xb, st + Map::kOffBs + 1024u * (uint32_t)wave);
+      else
+        dma16_if(wave < T, xr, vbs, xb, st + Map::kOffBs + 1024u * (uint32_t)wave);
+    } else if (k == 20) {
+      dma4_if(2 * wave < T, xr, vdx, xb, st + Map::kOffDx + 256 * wave);
     }
   };
   auto issue_all = [&](int b, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-      for (int k = 0; k < 10; ++k) issue(b, slot, t, k);
+    for (int k = 0; k < 21; ++k) issue(b, slot, k);
   };
 
   float y[T][16];
@@ -666,15 +690,11 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k4_kernel(
     if (b0 + s < bend) {
       q4_compute<T>(lds + stage_off(slot), raw, y, i, h,
                     [&](int t, int k) __attribute__((always_inline)) {
-                      // each tile's loads one tile early (tile 0 takes its own
-                      // and tile 1's), so that none is issued in the last tile
-                      if (t == 0) issue(bn, nxt, 0, k);
-                      if (t + 1 < T) issue(bn, nxt, t + 1, k);
-                      if (k == 6) {
-                        if (t == 0) issue(bn, nxt, 0, 8);
-                        if (t + 1 < T) issue(bn, nxt, t + 1, 8);
-                      }
-                      if (k == 7 && t == 0) issue(bn, nxt, 0, 9);
+                      // spread over all tiles but the last: value loads at
+                      // steps 0, 2, 4 and 6, the group sums and d_x at step 7
+                      if (t + 1 < T && !(k & 1)) issue(bn, nxt, (k >> 1) + 4 * t);
+                      if (t == 0 && k == 7) issue(bn, nxt, 16);
+                      if (t == 0 && k == 5) issue(bn, nxt, 20);
                     },
                     [&]() __attribute__((always_inline)) { q4_load_raw(rawn, wnext, h); });
     } else {  // the second group's idle last step (odd nb): only its loads

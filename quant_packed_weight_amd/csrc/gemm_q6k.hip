@@ -266,24 +266,36 @@ __global__ __launch_bounds__(256, 2) void gemm_q6k4_kernel(
     return (uint32_t)(slot * Map::kStage);
   };
 
-  const uint32_t vq = 4 + 4 * lane;
+  // value rows as 16-byte loads of 64 padded 16-byte units each, offsets as
+  // in the four-tile q4_K kernel: wave w issues loads j = w + 4 k; unit
+  // U = 64 j + lane is unit U % 17 of row U / 17, and with U0 = 64 w + lane
+  // load k is row U0 / 17 + 15 k + e, unit U0 % 17 + k - 17 e (e = 1 from
+  // k = 17 - U0 % 17 on)
+  constexpr int kVal = 17 * kT / 2;  // value loads per stage
+  const uint32_t u0 = 64u * (uint32_t)wave + (uint32_t)lane;
+  const uint32_t vx0 = (u0 / 17u) * xstride + 4u + 16u * (u0 % 17u);
+  const uint32_t kwrap = 17u - u0 % 17u;
   const uint32_t vdx = (uint32_t)(64 * wave + lane) * xstride;  // waves 0, 1: d_x of 64 rows
-  // the next stage's loads, one per call (as in the four-tile q4_K kernel)
-  auto issue = [&](int b, int slot, int t, int k) __attribute__((always_inline)) {
+  // the next stage's loads: value load k (k < 17 T / 8) and, from waves 0 and
+  // 1, the d_x of 64 rows (k = 20)
+  auto issue = [&](int b, int slot, int k) __attribute__((always_inline)) {
     const uint32_t st = lds0 + stage_off(slot);
     const uint32_t xb = (uint32_t)b * kQ8KBytes;
-    if (k < 8) {
+    if (k < (kVal + 3) / 4) {
       static_assert(Map::kOffQ == 0, "value rows at the stage base");
-      dma_row<0>(xr, vq, (uint32_t)wave + 32 * t + 4 * k, xstride, xb, st);
-    } else if (k == 9 && t == 0 && 2 * wave < kT) {
-      dma4(xr, vdx, xb, st + Map::kOffDx + 256 * wave);
+      const uint32_t v = (uint32_t)k < kwrap ? vx0 : vx0 + (xstride - 272u);
+      const uint32_t dst = st + 1024u * (uint32_t)(wave + 4 * k);
+      if (4 * k + 3 < kVal)
+        dma16(xr, v, smad(15u * k, xstride, xb + 16u * k), dst);
+      else
+        dma16_if(wave + 4 * k < kVal, xr, v, smad(15u * k, xstride, xb + 16u * k), dst);
+    } else if (k == 20) {
+      dma4_if(2 * wave < kT, xr, vdx, xb, st + Map::kOffDx + 256 * wave);
     }
   };
   auto issue_all = [&](int b, int slot) __attribute__((always_inline)) {
 #pragma unroll
-    for (int t = 0; t < kT; ++t)
-#pragma unroll
-      for (int k = 0; k < 10; ++k) issue(b, slot, t, k);
+    for (int k = 0; k < 21; ++k) issue(b, slot, k);
   };
 
   float y[kT][16];
@@ -304,9 +316,10 @@ __global__ __launch_bounds__(256, 2) void gemm_q6k4_kernel(
     const int bn = blk(s + 1);
     q6_compute(lds + stage_off(slot), raw, y, i, h,
                [&](int t, int k) __attribute__((always_inline)) {
-                 if (t == 0) issue(bn, nxt, 0, k);
-                 if (t + 1 < kT) issue(bn, nxt, t + 1, k);
-                 if (k == 7 && t == 0) issue(bn, nxt, 0, 9);
+                 // value loads at steps 0, 2, 4 and 6 of all tiles but the
+                 // last, d_x at step 5 of tile 0
+                 if (t + 1 < kT && !(k & 1)) issue(bn, nxt, (k >> 1) + 4 * t);
+                 if (t == 0 && k == 5) issue(bn, nxt, 20);
                },
                [&]() __attribute__((always_inline)) {
                  q6_load_raw<RP>(rawn, mat, blk0 + bn, NB, h);
