@@ -59,6 +59,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0    # MI355X dense int8 MFMA, TOP/s
 GIB = 1 << 30
+NUM_CUS = 256              # MI355X compute units (4 SIMDs each)
 
 
 def progress(msg):
@@ -420,6 +421,34 @@ def measured_ceilings(wl, sizes=None):
     dt, nops, cyc, ticks = best
     out["mfma_i8_TOPs"] = round(nops / dt / 1e12, 1)
     out["mfma_i8_clock_GHz"] = round(cyc / ticks * 0.1, 3) if ticks > 0 else None
+    # the same loop with v independent f32 FMAs after every MFMA
+    # (gemmq_probe_mfma_valu), two waves per SIMD as the GEMMs run: shader
+    # clocks per MFMA and SIMD against v, and what a vector instruction costs
+    # once the MFMA no longer hides it
+    blocks_v, iters_v = 2 * NUM_CUS, 4000
+    per = {}
+    for v in (0, 4, 8, 12, 16):
+        gq.probe_mfma_valu(10, blocks_v, v)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            _, clocks, _ = gq.probe_mfma_valu(iters_v, blocks_v, v)
+            e1.record()
+            torch.cuda.synchronize()
+            dt_v = e0.elapsed_time(e1) * 1e-3
+            cyc_v, ticks_v = (int(x) for x in clocks.cpu())
+            if best is None or dt_v < best[0]:
+                best = (dt_v, cyc_v, ticks_v)
+        dt_v, cyc_v, ticks_v = best
+        ghz = cyc_v / ticks_v * 0.1 if ticks_v > 0 else out["mfma_i8_clock_GHz"]
+        mfma_per_simd = blocks_v * 4 * iters_v * gq.PROBE_CHAINS / (4 * NUM_CUS)
+        per[str(v)] = round(dt_v * ghz * 1e9 / mfma_per_simd, 1)
+    out["mfma_valu_clk_per_mfma"] = per
+    out["mfma_valu_note"] = ("shader clocks per int8 32x32x32 MFMA and SIMD with v independent "
+                             "f32 FMAs after each, two waves per SIMD (gemmq_probe_mfma_valu)")
+    out["valu_clk_per_instr"] = round((per["16"] - per["8"]) / 8, 2)
     # read-only stream (gemmq_probe_read) over 2 GiB: each launch reads more
     # than the last-level cache holds, so every byte comes from HBM
     n = 2 * GIB

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GEMMQ_ABI_VERSION 9
+#define GEMMQ_ABI_VERSION 10
 
 /* Weight formats, numbered as the GGUF tensor type ids. */
 #define GEMMQ_Q2_K 10
@@ -308,6 +308,20 @@ int gemmq_decode(int fmt, const void *W, float *Wf, int64_t N, int64_t K, void *
 #define GEMMQ_PROBE_MAX_ITERS 1000000
 int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t *out, uint64_t *clocks,
                         void *stream);
+
+/*
+ * Measurement export: the loop of gemmq_probe_mfma_i8 with `valu` independent
+ * f32 FMAs (no operand taken from a matrix result) issued after every MFMA,
+ * valu in {0, 4, 8, 12, 16}.  Never used on the compute path.  The launch time
+ * against valu gives the time of one MFMA with that much vector work beside it:
+ * how much vector work a matrix instruction hides and what each vector
+ * instruction costs past that, the terms of the GEMMs' per-super-block budget.
+ * Launched with two waves per SIMD (blocks = 2 x compute units), as the GEMMs
+ * run.  Arguments, outputs, operation count and errors as gemmq_probe_mfma_i8;
+ * any other valu is GEMMQ_E_INVALID_ARG.
+ */
+int gemmq_probe_mfma_valu(int64_t iters, int64_t blocks, int32_t valu, int32_t *out,
+                          uint64_t *clocks, void *stream);
 
 /*
  * Measurement export: the read-only device-memory ceiling the decode GEMV is

@@ -42,6 +42,7 @@ from ._lib import (  # noqa: F401
     linear_group_ptr,
     linear_silu_mul,
     probe_mfma_i8,
+    probe_mfma_valu,
     probe_read,
     q8K_bytes,
     quantize_q8K,

@@ -24,7 +24,7 @@ Q8K_BYTES = 292
 QK = 256
 PATH_AUTO, PATH_GEMV, PATH_GEMM, PATH_SKINNY = 0, 1, 2, 3
 MAX_GROUP = 4  # matrices per gemmq_gemm_group / gemmq_linear_group call
-ABI_VERSION = 9
+ABI_VERSION = 10
 PROBE_CHAINS = 4  # GEMMQ_PROBE_CHAINS
 PROBE_MAX_ITERS = 1000000  # GEMMQ_PROBE_MAX_ITERS
 GEMM_MAX_M = 4194240  # GEMMQ_GEMM_MAX_M
@@ -54,6 +54,7 @@ EXPORTS = {
     "gemmq_decode": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "gemmq_repack": (_I, [_I, _P, _P, _I64, _I64, _P]),
     "gemmq_probe_mfma_i8": (_I, [_I64, _I64, _P, _P, _P]),
+    "gemmq_probe_mfma_valu": (_I, [_I64, _I64, _I, _P, _P, _P]),
     "gemmq_probe_read": (_I, [_P, _I64, _P, _P]),
 }
 
@@ -319,6 +320,18 @@ def probe_mfma_i8(iters, blocks, stream=None):
     clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
     _check(lib().gemmq_probe_mfma_i8(iters, blocks, out.data_ptr(), clocks.data_ptr(),
                                      _stream(stream)), "gemmq_probe_mfma_i8")
+    return out, clocks, 2 * 32768 * PROBE_CHAINS * 4 * blocks * iters
+
+
+def probe_mfma_valu(iters, blocks, valu, stream=None):
+    """Enqueue the int8 MFMA loop with `valu` f32 FMAs after every MFMA
+    (gemmq_probe_mfma_valu); returns (out, clocks) and the int8 operation
+    count of the launch."""
+    torch = _torch()
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    clocks = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _check(lib().gemmq_probe_mfma_valu(iters, blocks, valu, out.data_ptr(), clocks.data_ptr(),
+                                       _stream(stream)), "gemmq_probe_mfma_valu")
     return out, clocks, 2 * 32768 * PROBE_CHAINS * 4 * blocks * iters
 
 

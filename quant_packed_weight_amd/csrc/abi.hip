@@ -16,6 +16,9 @@ namespace gemmq {
 // probe.hip: the int8 MFMA ceiling (independent accumulator chains per wave)
 int probe_mfma_chains();
 int launch_probe_mfma(int64_t iters, int64_t blocks, int32_t* out, uint64_t* clk, hipStream_t st);
+// the same with `valu` (0, 4, 8, 12 or 16) f32 FMAs after every MFMA; -1 otherwise
+int launch_probe_mfma_valu(int64_t iters, int64_t blocks, int valu, int32_t* out, uint64_t* clk,
+                           hipStream_t st);
 int probe_read_waves();
 int launch_probe_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t st);
 // skinny.hip / skinny_q6k.hip: the small-M MFMA kernels (q4_K; q6_K and its
@@ -397,6 +400,20 @@ int gemmq_probe_mfma_i8(int64_t iters, int64_t blocks, int32_t* out, uint64_t* c
   clear_pending();
   return launched(
       gemmq::launch_probe_mfma(iters, blocks, out, clocks, static_cast<hipStream_t>(stream)));
+}
+
+int gemmq_probe_mfma_valu(int64_t iters, int64_t blocks, int32_t valu, int32_t* out,
+                          uint64_t* clocks, void* stream) {
+  if (!out || !clocks || iters < 1 || iters > GEMMQ_PROBE_MAX_ITERS || blocks < 1 ||
+      blocks > 65535 || valu < 0 || valu > 16 || valu % 4 != 0)
+    return GEMMQ_E_INVALID_ARG;
+  if (!aligned(out, 4) || !aligned(clocks, 8)) return GEMMQ_E_ALIGNMENT;
+  if (gemmq::probe_mfma_chains() != GEMMQ_PROBE_CHAINS) return GEMMQ_E_LAUNCH;
+  const int dv = check_device();
+  if (dv != GEMMQ_OK) return dv;
+  clear_pending();
+  return launched(gemmq::launch_probe_mfma_valu(iters, blocks, valu, out, clocks,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 int gemmq_probe_read(const void* src, int64_t bytes, uint32_t* out, void* stream) {

@@ -1,6 +1,7 @@
 // probe.hip -- measured ceilings for the matmul kernels: int8 MFMAs with no
-// memory traffic or vector work, and the shader clock they run at; and a plain
-// read-only stream of device memory (the GEMV's bound).
+// memory traffic or vector work, and the shader clock they run at; the same
+// with a given amount of independent vector work beside every MFMA; and a
+// plain read-only stream of device memory (the GEMV's bound).
 //
 // Every wave keeps kChains independent accumulator chains of
 // v_mfma_i32_32x32x32_i8 on register operands, so the matrix cores never wait
@@ -42,6 +43,63 @@ __global__ __launch_bounds__(256) void mfma_probe_kernel(int64_t iters, int32_t*
   for (int k = 0; k < kChains; ++k)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += c[k][r];
+  asm volatile("" ::"v"(s));
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  out[(int64_t)blockIdx.x * 256 + t] = s;
+  if (blockIdx.x == 0 && t == 0) {
+    clk[0] = t1 - t0;
+    clk[1] = r1 - r0;
+  }
+}
+
+// The same chains with V independent f32 FMAs after every MFMA (no operand
+// comes from a matrix result), the order fixed by scheduling groups: one MFMA,
+// then its V vector instructions.  The time per MFMA against V is what the
+// GEMMs' budget needs: how much vector work one matrix instruction hides, and
+// what a vector instruction costs past that.
+template <int V>
+__global__ __launch_bounds__(256) void mfma_valu_probe_kernel(int64_t iters,
+                                                              int32_t* __restrict__ out,
+                                                              uint64_t* __restrict__ clk) {
+  const int t = (int)threadIdx.x;
+  v4i a = {t, 7 * t + 1, 13 * t + 2, 29 * t + 3};
+  v4i b = {3 * t + 5, 11 * t + 7, 17 * t + 9, 23 * t + 11};
+  asm volatile("" : "+v"(a), "+v"(b));
+  v16i c[kChains];
+#pragma unroll
+  for (int k = 0; k < kChains; ++k) c[k] = (v16i){0};
+  float f[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    f[r] = (float)(t + r);
+    asm volatile("" : "+v"(f[r]));
+  }
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) {
+      c[k] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c[k], 0, 0, 0);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        float& x = f[(k * V + v) & 15];
+        x = fmaf(x, 1.0000001f, 0.5f);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kChains; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      if (V > 0) __builtin_amdgcn_sched_group_barrier(0x002, V, 0);  // then V VALU
+    }
+  }
+  int32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < kChains; ++k)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += c[k][r];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(f[r]));  // the vector work stays live
   asm volatile("" ::"v"(s));
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
   const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
@@ -96,6 +154,20 @@ int probe_read_waves() { return kReadWaves; }
 int launch_probe_read(const void* src, int64_t bytes, uint32_t* out, hipStream_t st) {
   hipLaunchKernelGGL(read_probe_kernel, dim3(kReadWaves / 8), dim3(512), 0, st,
                      static_cast<const uint4*>(src), bytes / 16, out);
+  return 0;
+}
+
+int launch_probe_mfma_valu(int64_t iters, int64_t blocks, int valu, int32_t* out, uint64_t* clk,
+                           hipStream_t st) {
+  const dim3 g((uint32_t)blocks), b(256);
+  switch (valu) {
+    case 0: hipLaunchKernelGGL(mfma_valu_probe_kernel<0>, g, b, 0, st, iters, out, clk); break;
+    case 4: hipLaunchKernelGGL(mfma_valu_probe_kernel<4>, g, b, 0, st, iters, out, clk); break;
+    case 8: hipLaunchKernelGGL(mfma_valu_probe_kernel<8>, g, b, 0, st, iters, out, clk); break;
+    case 12: hipLaunchKernelGGL(mfma_valu_probe_kernel<12>, g, b, 0, st, iters, out, clk); break;
+    case 16: hipLaunchKernelGGL(mfma_valu_probe_kernel<16>, g, b, 0, st, iters, out, clk); break;
+    default: return -1;
+  }
   return 0;
 }
 

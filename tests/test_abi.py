@@ -30,7 +30,7 @@ def L():
 
 def test_every_declared_symbol_exported(L):
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 17
     assert set(names) == set(gq.EXPORTS)
     out = subprocess.run(["nm", "-D", "--defined-only", gq.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -41,7 +41,7 @@ def test_every_declared_symbol_exported(L):
 
 
 def test_version_and_status_names(L):
-    assert L.gemmq_abi_version() == gq.ABI_VERSION == 9
+    assert L.gemmq_abi_version() == gq.ABI_VERSION == 10
     for code, word in [(0, "GEMMQ_OK"), (-1, "INVALID_ARG"), (-2, "UNSUPPORTED_FORMAT"),
                        (-3, "SHAPE"), (-4, "ALIGNMENT"), (-5, "DEVICE"), (-6, "LAUNCH"),
                        (-77, "UNKNOWN")]:
@@ -322,6 +322,22 @@ def test_repacked_formats_accepted_except_decode(L):
 ])
 def test_probe_validation(L, args, status):
     assert L.gemmq_probe_mfma_i8(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 3, FAKE16, FAKE16), -1),      # vector work per MFMA not in {0, 4, 8, 12, 16}
+    ((1, 1, 20, FAKE16, FAKE16), -1),
+    ((1, 1, -4, FAKE16, FAKE16), -1),
+    ((0, 1, 8, FAKE16, FAKE16), -1),      # iters < 1
+    ((1, 65536, 8, FAKE16, FAKE16), -1),  # too many workgroups
+    ((1, 1, 8, None, FAKE16), -1),
+    ((1, 1, 8, FAKE16, None), -1),
+    ((1, 1, 8, FAKE16 + 2, FAKE16), -4),  # out needs 4 B
+    ((1, 1, 8, FAKE16, FAKE16 + 4), -4),  # clocks need 8 B
+    ((gq.PROBE_MAX_ITERS + 1, 1, 8, FAKE16, FAKE16), -1),
+])
+def test_probe_mfma_valu_validation(L, args, status):
+    assert L.gemmq_probe_mfma_valu(*args, None) == status
 
 
 @pytest.mark.parametrize("args,status", [

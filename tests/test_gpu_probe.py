@@ -1,5 +1,6 @@
 """GPU: the int8 MFMA ceiling loop (gemmq_probe_mfma_i8) that the benchmark
-reads the GEMM against.
+reads the GEMM against, the same loop with vector work beside every MFMA
+(gemmq_probe_mfma_valu) and the read-only stream (gemmq_probe_read).
 
 The loop's work is checked exactly, not just timed: summed over the 64 lanes of
 a wave, the accumulators hold chains * iters * sum_{i,j} (A B)[i, j]
@@ -50,6 +51,25 @@ def test_probe_work_is_exact(iters, blocks):
         assert got == wave_sum(w, gq.PROBE_CHAINS, iters), (w, got)
     c = to_host(clocks)
     assert c[0] > 0 and c[1] >= 0
+
+
+@pytest.mark.parametrize("valu", [0, 4, 8, 12, 16])
+def test_probe_mfma_valu_work_is_exact(valu):
+    # the loop with vector work beside the MFMAs (gemmq_probe_mfma_valu) does
+    # the same matrix work on the same operands
+    device()
+    import quant_packed_weight_amd as gq
+
+    iters, blocks = 9, 7
+    log("probe mfma+valu valu=%d iters=%d blocks=%d" % (valu, iters, blocks))
+    out, clocks, ops = gq.probe_mfma_valu(iters, blocks, valu)
+    o = to_host(out).astype(np.int64).reshape(blocks, 4, 64)
+    assert ops == 2 * 32768 * gq.PROBE_CHAINS * 4 * blocks * iters
+    assert (o == o[0]).all()
+    for w in range(4):
+        got = np.uint64(int(o[0, w].sum()) & 0xFFFFFFFF)
+        assert got == wave_sum(w, gq.PROBE_CHAINS, iters), (w, got)
+    assert to_host(clocks)[0] > 0
 
 
 def test_probe_clock_plausible():
