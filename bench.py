@@ -641,7 +641,7 @@ def host_cores():
 
 
 def _oracle_workload(name, seconds, rows_cap):
-    """One core: a workload of the survey's set through the oracle (quantize +
+    """One core: one of the benchmark's workloads through the oracle (quantize +
     integer-route matmul of every matrix), whole passes repeated for about
     `seconds`, or for M > 64 a seeded sample of at most `rows_cap` rows
     (first and last included), extrapolated per multiply-accumulate."""

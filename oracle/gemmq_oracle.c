@@ -540,8 +540,8 @@ void oracle_silu_mul(const double *g, const double *u, int64_t n, double *y)
         y[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
 }
 
-/* Load-time repack of a q3_K or q6_K matrix (the survey's "repack" row, the
- * GPU counterpart of the pages' q4_K 8-column panels: molayo article, status row
+/* Load-time repack of a q3_K or q6_K matrix (the GPU counterpart of the pages'
+ * q4_K 8-column panels, a layout chosen at load time: molayo article, status row
  * "src/ -- C++ engine"): the same bytes, reordered so that every field of every
  * block starts on a 16-byte boundary.  The matrix's NB = N*K/256 blocks, in row
  * order, are split into their fields and each field is stored for all blocks
