@@ -191,12 +191,20 @@ __device__ __forceinline__ void dma_row(rsrc_t rs, uint32_t voff, uint32_t base,
       : "memory", "m0", "scc");
 }
 
-// group sums of row `row` of the stage, groups 8h..8h+7, as f16 (exact)
+// The group sums one wave loaded into a stage (32 rows x 16 int16, its lane l
+// at p + 16 l) rewritten in place as f16 (exact: |sum| <= 2032), by that wave
+// between its wait for its own loads and the stage barrier: each row's sums
+// are converted once per workgroup instead of once per wave that reads them.
+__device__ __forceinline__ void bsums_to_f16(uint8_t* p, int lane) {
+  uint4* q = reinterpret_cast<uint4*>(p + 16 * lane);
+  const uint4 v = *q;
+  *q = make_uint4(i16x2_to_h2(v.x), i16x2_to_h2(v.y), i16x2_to_h2(v.z), i16x2_to_h2(v.w));
+}
+
+// group sums of row `row` of the stage (converted by bsums_to_f16), groups
+// 8h..8h+7
 __device__ __forceinline__ v8h stage_bsums(const uint8_t* bsp, int row, int h) {
-  const uint4 braw = *reinterpret_cast<const uint4*>(bsp + row * 32 + 16 * h);
-  const uint32_t bh[4] = {i16x2_to_h2(braw.x), i16x2_to_h2(braw.y), i16x2_to_h2(braw.z),
-                          i16x2_to_h2(braw.w)};
-  return __builtin_bit_cast(v8h, bh);
+  return *reinterpret_cast<const v8h*>(bsp + row * 32 + 16 * h);
 }
 
 // The epilogue of one tile: y += d_x * (d * I - dm * C) for accumulator

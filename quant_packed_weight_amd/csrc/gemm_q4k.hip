@@ -198,14 +198,9 @@ __device__ __forceinline__ void q4s_compute(const uint8_t* st, int wrow, float (
     mfrag[2 * k] = m;
     mfrag[2 * k + 1] = m;
   }
-  v8h sfrag[2];
+  v8h sfrag[2];  // group sums of row 32t+i, already f16 in the stage
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {  // group sums of row 32t+i: int16 -> f16 (exact, |sum| <= 2032)
-    const uint4 braw = *reinterpret_cast<const uint4*>(st + kOffBs + (32 * t + i) * 32 + 16 * h);
-    const uint32_t bh[4] = {i16x2_to_h2(braw.x), i16x2_to_h2(braw.y), i16x2_to_h2(braw.z),
-                            i16x2_to_h2(braw.w)};
-    sfrag[t] = __builtin_bit_cast(v8h, bh);
-  }
+  for (int t = 0; t < 2; ++t) sfrag[t] = stage_bsums(st + kOffBs, 32 * t + i, h);
   const float dcol = f16_to_f32(hd.x), mcol = f16_to_f32(hd.x >> 16);
   float dx[16];
   q4s_load_dx(st, 4 * h, dx);
@@ -344,6 +339,8 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k2_kernel(
   int slot = 0;
   for (int s = 0; s < nb0; ++s) {
     wait_vm<q4s::kWait>();  // own loads of stage s landed
+    if (wave < 2)  // the group sums this wave loaded, to f16
+      bsums_to_f16(ldsg + slot * kStride + q4s::kOffBs + 1024 * wave, lane);
     lds_barrier();  // stage s complete everywhere; the stage of s-1 is free
     const int nxt = slot == 0 ? q4s::kS - 1 : slot - 1;
     const int bn = blk(s + q4s::kS - 1);
@@ -683,6 +680,8 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k4_kernel(
   int slot = 0;
   for (int s = 0; s < nb0; ++s) {
     wait_vm<0>();   // own loads of stage s and the raw weights landed
+    if (wave < T)  // the group sums this wave loaded, to f16
+      bsums_to_f16(lds + stage_off(slot) + Map::kOffBs + 1024 * wave, lane);
     lds_barrier();  // stage s complete everywhere; the other stage is free
     const int nxt = slot ^ 1;
     const int bn = blk(s + 1);
