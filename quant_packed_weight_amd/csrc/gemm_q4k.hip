@@ -48,8 +48,8 @@ namespace {
 using namespace gk;
 
 // ====================================================================
-// Two row tiles per wave (64 activation rows per workgroup), for launches
-// below 1024 activation rows: the raw weight tile is staged in LDS too.
+// Two row tiles per wave (64 activation rows per workgroup), for launches of
+// fewer rows (use_four_tile below): the raw weight tile is staged in LDS too.
 // ====================================================================
 // The kernel streams both operands through a ring of LDS stages filled by
 // direct buffer->LDS loads (no registers held for the prefetch, no copy loop):
@@ -405,8 +405,9 @@ __global__ __launch_bounds__(256 * SPLIT, 3 - SPLIT) void gemm_q4k2_kernel(
 
 
 // ====================================================================
-// Four row tiles per wave (128 activation rows per workgroup), from 1024
-// activation rows: the raw weights go straight to registers.
+// Four row tiles per wave (128 activation rows per workgroup), for launches
+// of 1024 activation rows and more, and of 576..1023 rows where their grid
+// favours it (use_four_tile below): the raw weights go straight to registers.
 // ====================================================================
 template <int T, int SPLIT>
 constexpr int q4_lds_bytes() {
@@ -804,7 +805,23 @@ void q4_launch2(const GroupTiles& gt, uint32_t gx, int64_t gy, const uint8_t* Xq
 // twice the workgroups and it takes 253 us against 307 us).  Both kernels give
 // every output the same arithmetic in the same order, so the choice changes
 // no bits.
+// The two kernels give the same bits, so the choice between them is by time
+// alone (measured per launch on the Qwen3-8B shapes, M = 512..2048, same
+// process): the four-tile kernel from 1024 rows, never below 576, and in
+// between when its grid, counted in rounds over the workgroups the CUs hold at
+// once (two per CU, one for the split form), costs no more than the two-tile
+// kernel's: rounds of 128 rows at ~1.3x the per-row rate (the split form
+// ~1.2x) against rounds of 64 rows.
 constexpr int64_t kQ4FourTileM = 1024;
+constexpr int64_t kQ4TwoTileM = 576;
+bool use_four_tile(int64_t tiles, int64_t M, bool split) {
+  if (M >= kQ4FourTileM) return true;
+  if (M < kQ4TwoTileM) return false;
+  const int64_t slots = split ? 256 : 512;
+  const int64_t r2 = (tiles * ((M + 63) / 64) + slots - 1) / slots;
+  const int64_t r4 = (tiles * ((M + 127) / 128) + slots - 1) / slots;
+  return r4 * 128 * 10 <= r2 * 64 * (split ? 12 : 13);
+}
 
 }  // namespace
 
@@ -825,7 +842,7 @@ int launch_gemm_q4k(const GroupTiles& gt, bool silu, const uint8_t* Xq, int64_t 
   if (gx == 0) return 0;
   // long rows run split over K (the choice depends on K only)
   const bool split = nb >= 32;
-  if (M >= kQ4FourTileM) {
+  if (use_four_tile(gx, M, split)) {
     const int64_t gy = (M + 127) / 128;
     if (gy > 65535) return -1;
     if (split)

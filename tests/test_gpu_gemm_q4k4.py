@@ -1,5 +1,6 @@
-"""GPU: the four-tile q4_K GEMM (launches of 1024 activation rows and more)
-against the oracle and against the two-tile kernel.
+"""GPU: the four-tile q4_K GEMM (launches of 1024 activation rows and more, and
+of 576..1023 where the grid favours it) against the oracle and against the
+two-tile kernel.
 
 The two kernels form the same int32 sums (sc = 8a + b folded into two int8
 planes, combined as 8A + B), the same f16 min term and the same f32 epilogue in
@@ -45,9 +46,11 @@ def _rows(M, n=16, seed=5):
 
 
 # (N, K, M): ragged rows and columns; one super-block; the K split on 32 (even)
-# and 49 (odd) super-blocks; a full gate/up-sized launch
+# and 49 (odd) super-blocks; a full gate/up-sized launch; a q/k/v-sized launch
+# below 1024 rows that the grid rule gives the four-tile kernel (its 600-row
+# subset takes the two-tile kernel)
 @pytest.mark.parametrize("N,K,M", [(1000, 256, 1100), (130, 8192, 1024), (300, 12544, 1030),
-                                   (24576, 4096, 1024)])
+                                   (24576, 4096, 1024), (6144, 4096, 700)])
 def test_four_tile_equals_two_tile(dev, gq, orc, N, K, M):
     log("q4_K four-tile N=%d K=%d M=%d" % (N, K, M))
     rng = np.random.default_rng(N + K + M)
