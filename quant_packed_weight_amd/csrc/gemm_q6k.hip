@@ -129,10 +129,11 @@ __device__ __forceinline__ uint32_t sc_pair(const uint4& sc, int j) {
 __device__ __forceinline__ void q6_planes(const Q6Raw& r, int kc, uint32_t scp, v4i& hi, v4i& lo) {
   const int hh = kc >> 2, q = kc & 3;
   const uint4 l = r.ql[hh][q & 1], qh = r.qh[hh];
-  const u16x2 s2 = __builtin_bit_cast(u16x2, scp);
-  u16x2 c2 = s2 * (u16x2){0xffe0, 0xffe0};  // -32 sc (mod 2^16)
-  // hidden from the optimizer, which would otherwise factor sc q - 32 sc back
-  // into (q - 32) sc: one v_pk_mad_u16 per lane pair instead of a subtract
+  const u16x2 s1 = __builtin_bit_cast(u16x2, scp);
+  const u16x2 s2 = s1 + s1;                  // 2 sc
+  u16x2 c2 = s1 * (u16x2){0xffc0, 0xffc0};  // -64 sc (mod 2^16)
+  // hidden from the optimizer, which would otherwise factor 2 sc q - 64 sc back
+  // into (q - 32) 2 sc: one v_pk_mad_u16 per lane pair instead of a subtract
   // and a multiply
   asm volatile("" : "+v"(c2));
 #pragma unroll
@@ -142,18 +143,18 @@ __device__ __forceinline__ void q6_planes(const Q6Raw& r, int kc, uint32_t scp, 
     // bits 2q, 2q+1 of each qh byte to bits 4, 5
     const uint32_t hs = q == 0 ? hw << 4 : q == 1 ? hw << 2 : q == 2 ? hw : hw >> 2;
     const uint32_t qd = (hs & 0x30303030u) | (lw & 0x0f0f0f0fu);  // four quants, 0..63
-    // bytes 0, 2 and 1, 3 into 16-bit lanes: v = sc q - 32 sc, |v| <= 4096
+    // bytes 0, 2 and 1, 3 into 16-bit lanes: 2v = 2 sc q - 64 sc, v = sc (q -
+    // 32), |2v| <= 8192
     const uint32_t e0 = __builtin_amdgcn_perm(0u, qd, 0x0c020c00u);
     const uint32_t e1 = __builtin_amdgcn_perm(0u, qd, 0x0c030c01u);
     const u16x2 v0 = __builtin_bit_cast(u16x2, e0) * s2 + c2;
     const u16x2 v1 = __builtin_bit_cast(u16x2, e1) * s2 + c2;
     const uint32_t w0 = __builtin_bit_cast(uint32_t, v0), w1 = __builtin_bit_cast(uint32_t, v1);
-    // lo = v & 127, hi = v >> 7 (arithmetic), bytes gathered back in order
-    lo[k] = (int)(__builtin_amdgcn_perm(w1, w0, 0x06020400u) & 0x7f7f7f7fu);
-    const i16x2 a0 = __builtin_bit_cast(i16x2, w0) >> (i16x2){7, 7};
-    const i16x2 a1 = __builtin_bit_cast(i16x2, w1) >> (i16x2){7, 7};
-    hi[k] = (int)__builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, a1),
-                                       __builtin_bit_cast(uint32_t, a0), 0x06020400u);
+    // 2v = 256 hi + 2 lo with hi = v >> 7 (arithmetic) and lo = v & 127: the
+    // high byte of each 16-bit lane is hi, the low byte 2 lo; bytes gathered
+    // back in quant order
+    hi[k] = (int)__builtin_amdgcn_perm(w1, w0, 0x07030501u);
+    lo[k] = (int)((__builtin_amdgcn_perm(w1, w0, 0x06020400u) >> 1) & 0x7f7f7f7fu);
   }
 }
 
