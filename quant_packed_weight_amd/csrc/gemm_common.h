@@ -66,27 +66,21 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                   __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000};
 }
 
-// 64 lanes x 4 bytes: lane l's dword from buffer byte voff(l) + soff to LDS
-// byte lds + 4 l (lds wave-uniform, through M0).  The s_nop covers the one
-// wait state an M0 write needs before a load into LDS.  Issued from inline
-// assembly: through the builtin the compiler treats such a load as an LDS
-// write of unknown alias and drains every load before each LDS read, so the
-// kernels count these loads themselves (wait_vm).
-__device__ __forceinline__ void dma4(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
-  asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(rs), "s"(soff),
-               "{m0}"(lds)
-               : "memory");
-}
-
-// Same with 16 bytes per lane (16-byte aligned source) to LDS byte lds + 16 l.
+// 64 lanes x 16 bytes: lane l's 16 bytes from buffer byte voff(l) + soff (any
+// 4-byte aligned source) to LDS byte lds + 16 l (lds wave-uniform, through M0).
+// The s_nop covers the one wait state an M0 write needs before a load into
+// LDS.  Issued from inline assembly: through the builtin the compiler treats
+// such a load as an LDS write of unknown alias and drains every load before
+// each LDS read, so the kernels count these loads themselves (wait_vm).
 __device__ __forceinline__ void dma16(rsrc_t rs, uint32_t voff, uint32_t soff, uint32_t lds) {
   asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rs),
                "s"(soff), "{m0}"(lds)
                : "memory");
 }
 
-// dma4 / dma16 taken only where the wave-uniform flag `take` is nonzero.  The
-// branch is inside the asm: a branch the compiler sees splits the basic block,
+// 64 lanes x 4 bytes (lane l's dword to LDS byte lds + 4 l) or 16 bytes as
+// dma16, taken only where the wave-uniform flag `take` is nonzero.  The branch
+// is inside the asm: a branch the compiler sees splits the basic block,
 // and work fenced beside the matrix instructions (sched_barrier acts within a
 // block) is then sunk past it.
 __device__ __forceinline__ void dma4_if(uint32_t take, rsrc_t rs, uint32_t voff, uint32_t soff,
@@ -168,28 +162,6 @@ struct TileStage {
   static constexpr int kOffDx = kOffBs + kBM * 32;  // [kBM] f32 d_x
   static constexpr int kStage = kOffDx + kBM * 4;
 };
-
-// Value row r = base + R of the activation tile (R a compile-time constant):
-// lane l's dword at buffer byte voff(l) + r * xstride + xb to LDS byte
-// st + r * kRow + 4 l.  The row's offsets are computed inside the asm, where
-// they are used: a stage has 32 T rows, and offsets hoisted out of the loop
-// would each hold a scalar register for the whole kernel.
-template <int R>
-__device__ __forceinline__ void dma_row(rsrc_t rs, uint32_t voff, uint32_t base, uint32_t xstride,
-                                        uint32_t xb, uint32_t st) {
-  uint32_t r, so;
-  asm volatile(
-      "s_add_u32 %0, %4, %7\n\t"
-      "s_mul_i32 %1, %0, %5\n\t"
-      "s_add_u32 %1, %1, %6\n\t"
-      "s_mul_i32 %0, %0, %8\n\t"
-      "s_add_u32 m0, %0, %9\n\t"
-      "s_nop 0\n\t"
-      "buffer_load_dword %2, %3, %1 offen lds"
-      : "=&s"(r), "=&s"(so)
-      : "v"(voff), "s"(rs), "s"(base), "s"(xstride), "s"(xb), "n"(R), "n"(kRow), "s"(st)
-      : "memory", "m0", "scc");
-}
 
 // The group sums one wave loaded into a stage (32 rows x 16 int16, its lane l
 // at p + 16 l) rewritten in place as f16 (exact: |sum| <= 2032), by that wave

@@ -28,9 +28,9 @@
 //
 // Workgroup: four waves side by side on 128 weight columns, 32 T activation
 // rows.  The activation values, group sums and d_x stream through two LDS
-// stages filled by direct buffer->LDS loads issued a row at a time beside the
-// matrix work; each wave loads its columns' raw q4_K blocks straight into
-// registers one super-block ahead.  With T = 4 a workgroup holds 79 KB of LDS
+// stages filled by direct buffer->LDS loads of 1 KiB each (16 bytes a lane),
+// issued a few at a time beside the matrix work; each wave loads its columns'
+// raw q4_K blocks straight into registers one super-block ahead.  With T = 4 a workgroup holds 79 KB of LDS
 // and two of them share a CU.  Long rows (32 super-blocks or more) split over
 // two K-groups of four waves in one 512-thread workgroup; the second hands its
 // partial sums to the first through LDS.  The split depends on K only and the
