@@ -211,17 +211,19 @@ __device__ __forceinline__ void load_w(WRegs<14>& r, const uint8_t* wrow, int b)
   r.d = ld2(wb + 208);
 }
 
-// e holds bytes 0 and 2 as int16 lanes, o bytes 1 and 3: pack the plane bytes
-__device__ __forceinline__ uint32_t q6_pack_plane(uint32_t e, uint32_t o, bool hi) {
-  uint32_t pe, po;
-  if (hi) {
-    pe = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, e) >> (i16x2){7, 7});
-    po = __builtin_bit_cast(uint32_t, __builtin_bit_cast(i16x2, o) >> (i16x2){7, 7});
-  } else {
-    pe = e & 0x007f007fu;
-    po = o & 0x007f007fu;
-  }
-  return (pe & 0x00ff00ffu) | ((po & 0x00ff00ffu) << 8);
+// v = s q + c (s = s2 / 2, c = c2 / 2) for the four bytes of q, split into
+// the planes hi = v >> 7 and lo = v & 127, through the doubled product: bytes
+// 0, 2 and 1, 3 of q go to 16-bit lanes, one v_pk_mad_u16 each makes
+// 2v = 256 hi + 2 lo (|2v| < 2^15), whose lanes' high bytes are hi and low
+// bytes 2 lo; both are gathered back in quant order.
+__device__ __forceinline__ void planes_2v(uint32_t q, u16x2 s2, u16x2 c2, uint32_t& hi,
+                                          uint32_t& lo) {
+  const uint32_t e = __builtin_amdgcn_perm(0u, q, 0x0c020c00u);
+  const uint32_t o = __builtin_amdgcn_perm(0u, q, 0x0c030c01u);
+  const uint32_t we = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, e) * s2 + c2);
+  const uint32_t wo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, o) * s2 + c2);
+  hi = __builtin_amdgcn_perm(wo, we, 0x07030501u);
+  lo = (__builtin_amdgcn_perm(wo, we, 0x06020400u) >> 1) & 0x7f7f7f7fu;
 }
 
 __device__ __forceinline__ void store_w(uint8_t* st, const WRegs<14>& r) {
@@ -235,13 +237,11 @@ __device__ __forceinline__ void store_w(uint8_t* st, const WRegs<14>& r) {
     for (int k = 0; k < 8; ++k) {
       const uint32_t quad = q6k_quad(r.ql[k], r.qh[k], quarter);  // 4 quants 0..63
       const int s = (int)(int8_t)((k < 4 ? scp : (scp >> 8)) & 0xffu);
-      const i16x2 sv = {(short)s, (short)s};
-      const i16x2 off = {32, 32};
-      const i16x2 e = (__builtin_bit_cast(i16x2, quad & 0x00ff00ffu) - off) * sv;
-      const i16x2 o = (__builtin_bit_cast(i16x2, (quad >> 8) & 0x00ff00ffu) - off) * sv;
-      const uint32_t eu = __builtin_bit_cast(uint32_t, e), ou = __builtin_bit_cast(uint32_t, o);
-      hiw[k] = q6_pack_plane(eu, ou, true);
-      low[k] = q6_pack_plane(eu, ou, false);
+      // v = s (q - 32): 2v = 2s q - 64 s
+      const u16x2 s2 = {(unsigned short)(2 * s), (unsigned short)(2 * s)};
+      u16x2 c2 = {(unsigned short)(-64 * s), (unsigned short)(-64 * s)};
+      asm volatile("" : "+v"(c2));  // keep the multiply-add (the optimizer would factor it)
+      planes_2v(quad, s2, c2, hiw[k], low[k]);
     }
     uint8_t* pa = st + kOffPa + col * kRow + 128 * hh + 32 * quarter;
     uint8_t* pb = st + kOffPb + col * kRow + 128 * hh + 32 * quarter;
@@ -266,15 +266,6 @@ __device__ __forceinline__ void load_w(WRegs<13>& r, const uint8_t* wrow, int b)
   r.h[0] = hd.x; r.h[1] = hd.y; r.h[2] = hd.z; r.h[3] = hd.w;
 }
 
-// v = sc * q split into the two planes (v in 0..1953: hi = v >> 7 <= 15)
-__device__ __forceinline__ void planes_u16(uint32_t q, uint32_t sc, uint32_t& hi, uint32_t& lo) {
-  const u16x2 s2 = {(unsigned short)sc, (unsigned short)sc};
-  const uint32_t e = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, q & 0x00ff00ffu) * s2);
-  const uint32_t o =
-      __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, (q >> 8) & 0x00ff00ffu) * s2);
-  hi = ((e >> 7) & 0x00ff00ffu) | (((o >> 7) & 0x00ff00ffu) << 8);
-  lo = (e & 0x007f007fu) | ((o & 0x007f007fu) << 8);
-}
 
 __device__ __forceinline__ uint32_t h2_pair(uint32_t a, uint32_t b) {
   const h2 v = {(_Float16)(int)a, (_Float16)(int)b};
@@ -292,7 +283,9 @@ __device__ __forceinline__ void store_w(uint8_t* st, const WRegs<13>& r) {
     for (int k = 0; k < 8; ++k) {
       const uint32_t nib = half ? hi_nib(r.ql[k]) : lo_nib(r.ql[k]);
       const uint32_t q = nib | (((r.qh[k] >> (2 * c + half)) & 0x01010101u) << 4);
-      planes_u16(q, sc, hiw[k], low[k]);
+      // v = sc q in 0..1953 (hi = v >> 7 <= 15)
+      planes_2v(q, (u16x2){(unsigned short)(2 * sc), (unsigned short)(2 * sc)}, (u16x2){0, 0},
+                hiw[k], low[k]);
     }
     uint8_t* pa = st + kOffPa + col * kRow + 64 * c + 32 * half;
     uint8_t* pb = st + kOffPb + col * kRow + 64 * c + 32 * half;
