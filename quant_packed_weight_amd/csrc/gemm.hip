@@ -29,12 +29,14 @@
 //    gemm_q6k.hip (the same integer sums and epilogue, so the same bits).
 //  * q2_K, q3_K, q5_K, q6_K (gemm_plane_kernel): a 256-thread workgroup
 //    computes a 128 (M) x 64 (N) tile, each of its four waves a 64 x 32
-//    sub-tile.  Per super-block the workgroup stages the activation tile (int8
-//    values, d_x, and for q2_K/q5_K the group sums) and the weight tile --
-//    unpacked once into its int8 planes (and mins) -- in LDS;
-//    the global loads of super-block b+1 are issued before the MFMAs of
-//    super-block b and held in registers; one 69 KB stage lets two workgroups
-//    share a CU.
+//    sub-tile, or -- where the 128-row grid would have at most 256 workgroups,
+//    one per CU -- a 64 x 64 tile of 32 x 32 wave sub-tiles, which doubles the
+//    workgroups of small launches.  Per super-block the workgroup stages the
+//    activation tile (int8 values, d_x, and for q2_K/q5_K the group sums) and
+//    the weight tile -- unpacked once into its int8 planes (and mins) -- in
+//    LDS; the global loads of super-block b+1 are issued before the MFMAs of
+//    super-block b and held in registers; one 75 KB stage (56 KB for 64 rows)
+//    lets two workgroups share a CU.
 // In both, every output's arithmetic depends only on its own row and column,
 // so any subset of rows gives identical bits.  The grid's first dimension is
 // the concatenation of every grouped matrix's column tiles.
@@ -50,24 +52,28 @@ namespace {
 
 using namespace gk;
 
-constexpr int kBM = 128;        // activation rows per workgroup
-constexpr int kBN = 64;         // weight rows (output columns) per workgroup
+constexpr int kBN = 64;  // weight rows (output columns) per workgroup
 
-// LDS map of one stage (bytes)
-constexpr int kOffA = 0;                     // [kBM][kRow] activation int8
-constexpr int kOffPa = kOffA + kBM * kRow;   // [kBN][kRow] weight plane A (weight 128)
+// LDS map of one stage (bytes): the weight side at fixed offsets, then the
+// activation side for MT row tiles per wave (64 MT activation rows per
+// workgroup).  Formats with a min term (q2_K, q5_K) also stage dmin, the weight
+// mins and the activation group sums (f16 over the 16 groups of 16); the
+// others leave those regions unused.
+constexpr int kOffPa = 0;                    // [kBN][kRow] weight plane A (weight 128)
 constexpr int kOffPb = kOffPa + kBN * kRow;  // [kBN][kRow] weight plane B
-constexpr int kOffDx = kOffPb + kBN * kRow;  // [kBM] f32 d_x
-constexpr int kOffD = kOffDx + kBM * 4;      // [kBN] f32 d
-constexpr int kStage = kOffD + kBN * 4;
-constexpr int kLds = kStage;  // one stage: two workgroups fit in a CU's 160 KB
-// formats with a min term (q2_K, q5_K) also stage dmin, the activation group
-// sums and the weight mins, both as f16 over the 16 groups of 16
-constexpr int kOffDm = kStage;               // [kBN] f32 dmin
-constexpr int kOffBs = kOffDm + kBN * 4;     // [kBM][16] f16 group sums
-constexpr int kOffMn = kOffBs + kBM * 32;    // [kBN][16] f16 mins (per group of 16)
-constexpr int kLdsMin = kOffMn + kBN * 32;   // still two workgroups per CU
-static_assert(2 * kLdsMin <= 160 * 1024, "two workgroups per CU");
+constexpr int kOffD = kOffPb + kBN * kRow;   // [kBN] f32 d
+constexpr int kOffDm = kOffD + kBN * 4;      // [kBN] f32 dmin
+constexpr int kOffMn = kOffDm + kBN * 4;     // [kBN][16] f16 mins (per group of 16)
+constexpr int kOffX = kOffMn + kBN * 32;     // the activation side
+template <int MT>
+struct PlaneX {
+  static constexpr int kBM = 64 * MT;                   // activation rows per workgroup
+  static constexpr int kOffA = kOffX;                   // [kBM][kRow] activation int8
+  static constexpr int kOffDx = kOffA + kBM * kRow;     // [kBM] f32 d_x
+  static constexpr int kOffBs = kOffDx + kBM * 4;       // [kBM][16] f16 group sums
+  static constexpr int kLds = kOffBs + kBM * 32;        // one stage
+};
+static_assert(2 * PlaneX<2>::kLds <= 160 * 1024, "two workgroups per CU");
 
 // ------------------------------------------------- activation tile (plane kernel)
 // thread t: row t/2, half t%2 of the 256 int8 values; half 0 also d_x.  With
@@ -98,15 +104,16 @@ __device__ __forceinline__ void load_x(XRegs<MIN>& r, const uint8_t* xrow, int b
   if constexpr (MIN) r.s = ld16(xb + 260 + 16 * part);
 }
 
-template <bool MIN>
+template <int MT, bool MIN>
 __device__ __forceinline__ void store_x(uint8_t* st, const XRegs<MIN>& r) {
+  using X = PlaneX<MT>;
   const int t = threadIdx.x, row = t >> 1, part = t & 1;
-  uint8_t* a = st + kOffA + row * kRow + 128 * part;
+  uint8_t* a = st + X::kOffA + row * kRow + 128 * part;
 #pragma unroll
   for (int i = 0; i < 8; ++i) st16(a + 16 * i, r.q[i].x, r.q[i].y, r.q[i].z, r.q[i].w);
-  if (part == 0) reinterpret_cast<uint32_t*>(st + kOffDx)[row] = r.d;
+  if (part == 0) reinterpret_cast<uint32_t*>(st + X::kOffDx)[row] = r.d;
   if constexpr (MIN)
-    st16(st + kOffBs + row * 32 + 16 * part, i16x2_to_h2(r.s.x), i16x2_to_h2(r.s.y),
+    st16(st + X::kOffBs + row * 32 + 16 * part, i16x2_to_h2(r.s.x), i16x2_to_h2(r.s.y),
          i16x2_to_h2(r.s.z), i16x2_to_h2(r.s.w));
 }
 
@@ -418,28 +425,29 @@ __device__ __forceinline__ void store_w(uint8_t* st, const WRegs<11>& r) {
 // ------------------------------------------------- one super-block from LDS
 // 32x32 accumulator layout: lane holds column lane%32; register r holds row
 // 8*(r/4) + 4*(lane/32) + r%4.
-template <int FMT>
-__device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], int arow0, int bcol,
+template <int FMT, int MT>
+__device__ __forceinline__ void compute(const uint8_t* st, float (&y)[MT][16], int arow0, int bcol,
                                         int hsel) {
+  using X = PlaneX<MT>;
   constexpr int PLANES = PlaneFmt<FMT>::kPlanes;
   constexpr bool MIN = PlaneFmt<FMT>::kMin;
   // plane A (hi) over the super-block, then acc <<= 7, then plane B (lo) on
   // top: acc = I_sc, exact in int32; two independent chains
-  v16i acc[2];
+  v16i acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) acc[mt] = (v16i){0};
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (v16i){0};
 #pragma unroll
   for (int kc = 0; kc < 8; ++kc) {
     const int ko = 32 * kc + 16 * hsel;
     const v4i ba = *reinterpret_cast<const v4i*>(st + kOffPa + bcol * kRow + ko);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + X::kOffA + (arow0 + 32 * mt) * kRow + ko),
                         ba, acc[mt]);
   }
   if constexpr (PLANES == 2) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << 7);
 #pragma unroll
@@ -447,29 +455,29 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
       const int ko = 32 * kc + 16 * hsel;
       const v4i bb = *reinterpret_cast<const v4i*>(st + kOffPb + bcol * kRow + ko);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + kOffA + (arow0 + 32 * mt) * kRow + ko),
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + X::kOffA + (arow0 + 32 * mt) * kRow + ko),
                           bb, acc[mt]);
     }
   }
   // the min term: sum_g m_g * bsum_g over the 16 groups, exact in f32
-  v16f accm[2];
+  v16f accm[MT];
   float dmcol = 0.0f;
   if constexpr (MIN) {
     dmcol = reinterpret_cast<const float*>(st + kOffDm)[bcol];
     const v8h bm = *reinterpret_cast<const v8h*>(st + kOffMn + bcol * 32 + 16 * hsel);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      accm[mt] = mfma_f16(*reinterpret_cast<const v8h*>(st + kOffBs + (arow0 + 32 * mt) * 32 + 16 * hsel),
+    for (int mt = 0; mt < MT; ++mt)
+      accm[mt] = mfma_f16(*reinterpret_cast<const v8h*>(st + X::kOffBs + (arow0 + 32 * mt) * 32 + 16 * hsel),
                           bm, (v16f){0.0f});
   }
   const float dcol = reinterpret_cast<const float*>(st + kOffD)[bcol];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const float4 dx = *reinterpret_cast<const float4*>(
-          st + kOffDx + 4 * (arow0 - (arow0 & 31) + 32 * mt + 8 * q4 + 4 * hsel));
+          st + X::kOffDx + 4 * (arow0 - (arow0 & 31) + 32 * mt + 8 * q4 + 4 * hsel));
       const float dxs[4] = {dx.x, dx.y, dx.z, dx.w};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -482,10 +490,14 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[2][16], in
 }
 
 // ------------------------------------------------- the plane kernel (q2_K, q3_K, q5_K, q6_K)
-template <int FMT, bool SILU>
+// MT row tiles per wave: 2 (128 activation rows per workgroup) or 1 (64
+// rows, for launches whose 128-row grid leaves CUs idle); the tile height does
+// not enter any output's arithmetic.
+template <int FMT, bool SILU, int MT>
 __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
                                                             const uint8_t* __restrict__ Xq,
                                                             int64_t M, int nb) {
+  constexpr int kBM = PlaneX<MT>::kBM;
   constexpr bool MIN = PlaneFmt<FMT>::kMin;
   constexpr bool RP = FMT > 255;  // repacked layout
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -500,12 +512,12 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
   const int wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int i = lane & 31, hsel = lane >> 5;
-  const int arow0 = wm * 64 + i;  // LDS row of M-tile 0 (M-tile 1: +32)
+  const int arow0 = wm * 32 * MT + i;  // LDS row of M-tile 0 (M-tile 1: +32)
   const int bcol = wn * 32 + i;   // LDS column of this lane's B fragment
 
-  float y[2][16];
+  float y[MT][16];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) y[mt][r] = 0.0f;
 
@@ -535,17 +547,20 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
     else
       load_w(wr, wrow, b);
   };
-  load_x(xr, xrow, 0);
+  // the activation tile: two threads a row, so with MT = 1 waves 2 and 3 stage
+  // none of it
+  const bool xs = MT == 2 || threadIdx.x < 2 * kBM;
+  if (xs) load_x(xr, xrow, 0);
   loadw(0);
   for (int b = 0; b < nb; ++b) {
-    store_x(lds, xr);
+    if (xs) store_x<MT>(lds, xr);
     store_w(lds, wr);
     __syncthreads();
     if (b + 1 < nb) {  // in flight during the MFMAs below
-      load_x(xr, xrow, b + 1);
+      if (xs) load_x(xr, xrow, b + 1);
       loadw(b + 1);
     }
-    compute<FMT>(lds, y, arow0, bcol, hsel);
+    compute<FMT, MT>(lds, y, arow0, bcol, hsel);
     __syncthreads();
   }
 
@@ -555,21 +570,21 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
     const int64_t n = col >> 1, Nout = N >> 1;
     const bool odd = (i & 1) != 0;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         float g, u;
         silu_pair(y[mt][r], y[mt][r + 1], odd, g, u);
         const int rr = r + (odd ? 1 : 0);
-        const int64_t row = m0 + wm * 64 + 32 * mt + 8 * (rr >> 2) + 4 * hsel + (rr & 3);
+        const int64_t row = m0 + wm * 32 * MT + 32 * mt + 8 * (rr >> 2) + 4 * hsel + (rr & 3);
         if (n < Nout && row < M) Y[row * Nout + n] = silu_mul_f32(g, u);
       }
   } else if (col < N) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + 32 * mt + 8 * (r >> 2) + 4 * hsel + (r & 3);
+        const int64_t row = m0 + wm * 32 * MT + 32 * mt + 8 * (r >> 2) + 4 * hsel + (r & 3);
         if (row < M) Y[row * N + col] = y[mt][r];
       }
   }
@@ -580,30 +595,64 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
 namespace {
 
 // the dynamic LDS limit is a per-device attribute of each kernel
+template <int FMT, bool SILU>
+bool plane_lds() {
+  return hipFuncSetAttribute((const void*)gemm_plane_kernel<FMT, SILU, 1>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             PlaneX<1>::kLds) == hipSuccess &&
+         hipFuncSetAttribute((const void*)gemm_plane_kernel<FMT, SILU, 2>,
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             PlaneX<2>::kLds) == hipSuccess;
+}
+
 template <bool SILU>
 bool set_lds_limits() {
   static std::atomic<int> attr_done[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
   if (attr_done[dev].load(std::memory_order_acquire) == 0) {
-    if (hipFuncSetAttribute((const void*)gemm_plane_kernel<14, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_plane_kernel<11, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_plane_kernel<256 + 11, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_plane_kernel<256 + 14, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLds) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_plane_kernel<10, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
-        hipFuncSetAttribute((const void*)gemm_plane_kernel<13, SILU>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMin) != hipSuccess ||
+    if (!plane_lds<14, SILU>() || !plane_lds<11, SILU>() || !plane_lds<256 + 11, SILU>() ||
+        !plane_lds<256 + 14, SILU>() || !plane_lds<10, SILU>() || !plane_lds<13, SILU>() ||
         !q4k_prepare(SILU) || !q6k_prepare(SILU))
       return false;
     attr_done[dev].store(1, std::memory_order_release);
   }
   return true;
 }
+
+template <bool SILU, int MT>
+int launch_plane(int fmt, const GroupTiles& gt, uint32_t gx, const uint8_t* Xq, int64_t M, int nb,
+                 hipStream_t st) {
+  const int64_t gy = (M + PlaneX<MT>::kBM - 1) / PlaneX<MT>::kBM;
+  if (gy > 65535) return -1;
+  const dim3 grid(gx, (uint32_t)gy), block(256);
+  constexpr int lds = PlaneX<MT>::kLds;
+  switch (fmt) {
+    case 10:
+      hipLaunchKernelGGL((gemm_plane_kernel<10, SILU, MT>), grid, block, lds, st, gt, Xq, M, nb);
+      break;
+    case 11:
+      hipLaunchKernelGGL((gemm_plane_kernel<11, SILU, MT>), grid, block, lds, st, gt, Xq, M, nb);
+      break;
+    case 13:
+      hipLaunchKernelGGL((gemm_plane_kernel<13, SILU, MT>), grid, block, lds, st, gt, Xq, M, nb);
+      break;
+    case 256 + 11:
+      hipLaunchKernelGGL((gemm_plane_kernel<256 + 11, SILU, MT>), grid, block, lds, st, gt, Xq, M,
+                         nb);
+      break;
+    case 256 + 14:
+      hipLaunchKernelGGL((gemm_plane_kernel<256 + 14, SILU, MT>), grid, block, lds, st, gt, Xq, M,
+                         nb);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_plane_kernel<14, SILU, MT>), grid, block, lds, st, gt, Xq, M, nb);
+  }
+  return 0;
+}
+
+// the plane kernel's 64-row tiles up to this many 128-row workgroups
+constexpr int64_t kPlaneSmallGrid = 256;
 
 // q6_K: the four-tile kernel from this many workgroups (eight per CU; measured
 // on the Qwen3-1.7B shapes: the 151936-row head at M = 512 561.7 against
@@ -632,37 +681,14 @@ int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t 
   if (!(SILU ? make_pair_tiles(grp, bn, gt) : make_tiles(grp, bn, gt))) return -1;
   if (fmt == 12) return launch_gemm_q4k(gt, SILU, Xq, M, K, st);
   const uint32_t gx = gt.start[kMaxGroup];
-  const int64_t gy = (M + kBM - 1) / kBM;
   if (gx == 0) return 0;
-  const dim3 grid(gx, (uint32_t)gy);
-  {
-    switch (fmt) {
-      case 10:
-        hipLaunchKernelGGL((gemm_plane_kernel<10, SILU>), grid, dim3(256), kLdsMin, st, gt, Xq, M,
-                           (int)nb);
-        break;
-      case 11:
-        hipLaunchKernelGGL((gemm_plane_kernel<11, SILU>), grid, dim3(256), kLds, st, gt, Xq, M,
-                           (int)nb);
-        break;
-      case 13:
-        hipLaunchKernelGGL((gemm_plane_kernel<13, SILU>), grid, dim3(256), kLdsMin, st, gt, Xq, M,
-                           (int)nb);
-        break;
-      case 256 + 11:
-        hipLaunchKernelGGL((gemm_plane_kernel<256 + 11, SILU>), grid, dim3(256), kLds, st, gt, Xq,
-                           M, (int)nb);
-        break;
-      case 256 + 14:
-        hipLaunchKernelGGL((gemm_plane_kernel<256 + 14, SILU>), grid, dim3(256), kLds, st, gt, Xq,
-                           M, (int)nb);
-        break;
-      default:
-        hipLaunchKernelGGL((gemm_plane_kernel<14, SILU>), grid, dim3(256), kLds, st, gt, Xq, M,
-                           (int)nb);
-    }
-  }
-  return 0;
+  // 64-row tiles where 128-row ones would leave CUs without a workgroup (at
+  // most 256 of them; measured on q5_K and q6_K shapes of the Qwen3 layers at
+  // M = 64..2048, e.g. 2048 x 6144 q6_K at M = 512 81.6 -> 65.4 us, at
+  // M = 2048 -- 512 tiles of 128 rows -- 102.3 against 137.7 us)
+  if ((int64_t)gx * ((M + 127) / 128) <= kPlaneSmallGrid)
+    return launch_plane<SILU, 1>(fmt, gt, gx, Xq, M, (int)nb, st);
+  return launch_plane<SILU, 2>(fmt, gt, gx, Xq, M, (int)nb, st);
 }
 
 }  // namespace

@@ -225,3 +225,43 @@ def test_longest_rows(dev, gq, orc, fmt, path):
     W = synth.make_weights(rng, fmt, N, K)
     xq = orc.quantize_q8K(synth.make_activations(rng, M, K, True))
     _check(gq, orc, fmt, W, xq, M, N, K, path, "K=2^24")
+
+
+# 600 rows x 4200 columns: the plane kernel's 128-row grid has 5 x 66 workgroups
+# (ragged in both), above 256, so the call runs 128-row tiles; its row subsets
+# (1 or 2 row tiles, 66 or 132 workgroups) run the 64-row tiles.  The tile height
+# does not enter any output's arithmetic: the bits agree.
+@pytest.mark.parametrize("fmt", [Q2, Q3, Q5, 14, 256 + Q3, 256 + 14])
+def test_gemm_tile_heights_same_bits(dev, gq, orc, fmt):
+    M, N, K = 600, 4200, 512
+    base = fmt & 255
+    log("gemm tile heights fmt=%d" % fmt)
+    W, _, xq = _case(orc, base, M, N, K, seed=91 + fmt)
+    Wd = to_dev(W)
+    if fmt > 255:
+        Wd = gq.repack(base, Wd, N, K)
+    full = to_host(gq.gemm(fmt, Wd, to_dev(xq), M, N, K, path=gq.PATH_GEMM))
+    for a, b in [(0, 64), (100, 300), (536, 600), (599, 600)]:
+        part = to_host(gq.gemm(fmt, Wd, to_dev(xq[a:b]), b - a, N, K, path=gq.PATH_GEMM))
+        assert np.array_equal(part.view(np.uint32), full[a:b].view(np.uint32)), (a, b)
+    rows = np.array([0, 31, 32, 63, 64, 127, 128, 255, 300, 511, 512, 575, 599])
+    yo = orc.gemm_int(base, W, xq, M, N, K, rows)
+    _, S = orc.gemm_dequant(base, W, xq, M, N, K, rows)
+    assert_within(full[rows], yo, S, "tile heights")
+
+
+@pytest.mark.parametrize("fmt", [Q5, 14])
+def test_silu_tile_heights_same_bits(dev, gq, orc, fmt):
+    # 2100 gate/up pairs: 66 pair tiles of 64 interleaved columns (the last
+    # ragged) over 5 row tiles of 128 for 600 rows; 3-row calls take 64-row tiles
+    M, N, K = 600, 2100, 512
+    log("silu tile heights fmt=%d" % fmt)
+    rng = np.random.default_rng(93 + fmt)
+    x = synth.make_activations(rng, M, K, True)
+    wg = to_dev(synth.make_weights(rng, fmt, N, K))
+    wu = to_dev(synth.make_weights(rng, fmt, N, K))
+    y, _ = gq.linear_silu_mul(fmt, wg, wu, to_dev(x), N, path=gq.PATH_GEMM)
+    y = to_host(y)
+    for a in (0, 130, M - 3):
+        ys, _ = gq.linear_silu_mul(fmt, wg, wu, to_dev(x[a:a + 3]), N, path=gq.PATH_GEMM)
+        assert np.array_equal(to_host(ys).view(np.uint32), y[a:a + 3].view(np.uint32)), a
