@@ -10,9 +10,9 @@
 //
 //  * The sub-block scale is folded into the weight operand: sc = 8a + b with
 //    a, b in 0..7, so sc*q = 8(a*q) + b*q with both products in 0..105.  Per
-//    32-row tile a single int32 accumulator takes the a-plane chain of the
-//    super-block's eight sub-blocks, is shifted left by 3, and takes the
-//    b-plane chain: it then holds I_sc = sum_j sc_j * dot_j exactly.
+//    32-row tile the a-plane and the b-plane chains over the super-block's
+//    eight sub-blocks go to two int32 accumulators A and B (each activation
+//    fragment feeds both), and 8 A + B = I_sc = sum_j sc_j * dot_j exactly.
 //  * The min term I_min = sum_g m_g * bsum_g is one v_mfma_f32_32x32x16_f16
 //    per tile (|bsum| <= 2032 and m <= 63 are exact in f16, every partial sum
 //    is an integer below 2^24).

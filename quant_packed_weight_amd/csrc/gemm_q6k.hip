@@ -9,30 +9,29 @@
 //
 //  * A 32-wide MFMA step is two q6_K sub-blocks, and lane half h supplies the
 //    16 weights of one of them (sub-block 2 kc + h of step kc), so each lane's
-//    operand in a step has one scale.  The scale is folded into the weight:
-//    v = sc * q (q the 6-bit quant, 0..63; sc signed 8-bit) is a 14-bit value,
-//    split as v = 128 hi + lo with lo = v & 127 (0..127) and hi = v >> 7
-//    (-63..62): two int8 planes, two MFMA chains per tile, combined as
-//    128 A_hi + A_lo = sum_j sc_j * dot_j exactly in int32.  The products are
-//    made in 16-bit lanes (two per instruction), then the two planes' bytes
-//    are gathered with v_perm.
-//  * The quants' offset 32 comes out through the activation group sums: one
-//    v_mfma_f32_32x32x16_f16 per tile of the 16 group sums against the 16
-//    scales (both exact in f16, every partial sum an integer below 2^24)
-//    gives C = sum_j sc_j * bsum_j, and the epilogue per super-block and
-//    output is y += d_x * (d * I - 32 d * C) -- the q4_K epilogue with
-//    dmin = 32 d and the mins replaced by the scales.
+//    operand in a step has one scale.  The scale and the quants' offset 32 are
+//    folded into the weight: v = sc * (q - 32) (q the 6-bit quant, sc signed
+//    8-bit; |v| <= 4096) is made doubled in 16-bit lanes, 2v = 2 sc q - 64 sc
+//    (one v_pk_mad_u16 per two weights), and since 2v = 256 hi + 2 lo with
+//    hi = v >> 7 (-32..32) and lo = v & 127, one v_perm gathers the lanes'
+//    high bytes as the hi plane and one more, a shift and a mask give the lo
+//    plane: two int8 planes, two MFMA chains per tile, combined as
+//    128 A_hi + A_lo = sum_j sc_j (dot_j - 32 bsum_j) exactly in int32.  No
+//    min term is left: the epilogue per super-block and output is
+//    y += d_x * (d * I).
 //  * A wave takes 32 weight columns and four 32-row tiles (128 activation
 //    rows), so one unpack of its columns serves four tiles; the unpack runs
 //    beside the first tile's MFMAs, each later tile's MFMAs beside the
-//    previous tile's epilogue.  The activation values, group sums and d_x
-//    stream through two LDS stages (79 KB, two workgroups per CU) filled by
-//    direct buffer->LDS loads; each lane loads its column's raw bytes straight
-//    into registers one super-block ahead -- from the 210-byte blocks (2-byte
+//    previous tile's epilogue.  The activation values and d_x stream through
+//    two LDS stages (79 KB, two workgroups per CU) filled by direct
+//    buffer->LDS loads; each lane loads its column's raw bytes straight into
+//    registers one super-block ahead -- from the 210-byte blocks (2-byte
 //    aligned: dword spans realigned with v_alignbyte) or from the repacked
 //    layout's field arrays.
-//  * Rows of 32 super-blocks or more split over two K-groups of four waves in
-//    one 512-thread workgroup (the choice depends on K only).
+//  * No split over K, as in the plane kernel (gemm.hip): both kernels then
+//    form every output with the same integer sums and the same f32 steps in
+//    the same order, so the choice between them (by grid size) changes no
+//    bits.
 // Every output's arithmetic and summation order depend on its own row and
 // column and on K, never on M: any subset of rows gives identical bits.
 #include "device.h"
