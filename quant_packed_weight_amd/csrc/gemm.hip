@@ -539,29 +539,39 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
     wblk = n * nb;
   }
   const int64_t NB = (SILU ? N >> 1 : N) * nb;
-  XRegs<MIN> xr;
-  WRegs<FMT> wr;
-  auto loadw = [&](int b) {
-    if constexpr (RP)
-      load_w_rp(wr, wmat, NB, wblk + b);
-    else
-      load_w(wr, wrow, b);
-  };
+  // D register sets of loads in flight: super-block b + D is loaded while b is
+  // computed.  The 64-row form (small grids, one workgroup per CU or less)
+  // waits on memory latency at depth 1, and has the registers for a second
+  // set.
+  constexpr int D = MT == 1 ? 2 : 1;
+  XRegs<MIN> xr[D];
+  WRegs<FMT> wr[D];
   // the activation tile: two threads a row, so with MT = 1 waves 2 and 3 stage
   // none of it
   const bool xs = MT == 2 || threadIdx.x < 2 * kBM;
-  if (xs) load_x(xr, xrow, 0);
-  loadw(0);
-  for (int b = 0; b < nb; ++b) {
-    if (xs) store_x<MT>(lds, xr);
-    store_w(lds, wr);
-    __syncthreads();
-    if (b + 1 < nb) {  // in flight during the MFMAs below
-      if (xs) load_x(xr, xrow, b + 1);
-      loadw(b + 1);
+  auto load = [&](int j, int b) {
+    if (xs) load_x(xr[j], xrow, b);
+    if constexpr (RP)
+      load_w_rp(wr[j], wmat, NB, wblk + b);
+    else
+      load_w(wr[j], wrow, b);
+  };
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nb) load(j, j);
+  for (int b0 = 0; b0 < nb; b0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int b = b0 + j;
+      if (b < nb) {
+        if (xs) store_x<MT>(lds, xr[j]);
+        store_w(lds, wr[j]);
+        __syncthreads();
+        if (b + D < nb) load(j, b + D);  // in flight during the MFMAs below
+        compute<FMT, MT>(lds, y, arow0, bcol, hsel);
+        __syncthreads();
+      }
     }
-    compute<FMT, MT>(lds, y, arow0, bcol, hsel);
-    __syncthreads();
   }
 
   const int64_t col = n0 + bcol;
