@@ -431,33 +431,51 @@ __device__ __forceinline__ void compute(const uint8_t* st, float (&y)[MT][16], i
   using X = PlaneX<MT>;
   constexpr int PLANES = PlaneFmt<FMT>::kPlanes;
   constexpr bool MIN = PlaneFmt<FMT>::kMin;
-  // plane A (hi) over the super-block, then acc <<= 7, then plane B (lo) on
-  // top: acc = I_sc, exact in int32; two independent chains
+  // acc = I_sc, exact in int32.  With two row tiles: plane A (hi) over the
+  // super-block, then acc <<= 7, then plane B (lo) on top -- two independent
+  // chains, one per tile.  With one: the planes go to two accumulators, one
+  // activation fragment feeding both, combined as (A << 7) + B -- the same
+  // integer, from two chains of eight instead of one of sixteen.
   v16i acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = (v16i){0};
-#pragma unroll
-  for (int kc = 0; kc < 8; ++kc) {
-    const int ko = 32 * kc + 16 * hsel;
-    const v4i ba = *reinterpret_cast<const v4i*>(st + kOffPa + bcol * kRow + ko);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + X::kOffA + (arow0 + 32 * mt) * kRow + ko),
-                        ba, acc[mt]);
-  }
-  if constexpr (PLANES == 2) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << 7);
+  if constexpr (MT == 1 && PLANES == 2) {
+    v16i accb;
 #pragma unroll
     for (int kc = 0; kc < 8; ++kc) {
       const int ko = 32 * kc + 16 * hsel;
+      const v4i a = *reinterpret_cast<const v4i*>(st + X::kOffA + arow0 * kRow + ko);
+      const v4i ba = *reinterpret_cast<const v4i*>(st + kOffPa + bcol * kRow + ko);
       const v4i bb = *reinterpret_cast<const v4i*>(st + kOffPb + bcol * kRow + ko);
+      acc[0] = mfma_i8(a, ba, kc == 0 ? (v16i){0} : acc[0]);
+      accb = mfma_i8(a, bb, kc == 0 ? (v16i){0} : accb);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[0][r] = (int)(((uint32_t)acc[0][r] << 7) + (uint32_t)accb[r]);
+  } else {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (v16i){0};
+#pragma unroll
+    for (int kc = 0; kc < 8; ++kc) {
+      const int ko = 32 * kc + 16 * hsel;
+      const v4i ba = *reinterpret_cast<const v4i*>(st + kOffPa + bcol * kRow + ko);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + X::kOffA + (arow0 + 32 * mt) * kRow + ko),
-                          bb, acc[mt]);
+                          ba, acc[mt]);
+    }
+    if constexpr (PLANES == 2) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mt][r] = (int)((uint32_t)acc[mt][r] << 7);
+#pragma unroll
+      for (int kc = 0; kc < 8; ++kc) {
+        const int ko = 32 * kc + 16 * hsel;
+        const v4i bb = *reinterpret_cast<const v4i*>(st + kOffPb + bcol * kRow + ko);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          acc[mt] = mfma_i8(*reinterpret_cast<const v4i*>(st + X::kOffA + (arow0 + 32 * mt) * kRow + ko),
+                            bb, acc[mt]);
+      }
     }
   }
   // the min term: sum_g m_g * bsum_g over the 16 groups, exact in f32
