@@ -187,6 +187,27 @@ def test_exact_gemm(dev, gq, orc, fmt, M, N, K):
     run_case(gq, orc, fmt, M, N, K, PATH_GEMM, seed=3000 + 7 * fmt + 131 * M + N + K)
 
 
+@pytest.mark.parametrize("fmt", [Q2, Q3, Q5, Q6, R + Q3, R + Q6])
+def test_exact_gemm_128_row_tiles(dev, gq, orc, fmt):
+    # 600 x 4160: the plane kernel's 128-row grid has 5 x 65 workgroups, more
+    # than the 256 up to which it runs 64-row tiles (the cases above), so this
+    # call takes the 128-row form (q6_K: still below the 2048 workgroups of
+    # 128 x 128 from which its four-tile kernel runs); sampled rows across
+    # every row tile, the ragged last one included
+    M, N, K = 600, 4160, 512
+    log("exact gemm 128-row tiles fmt=%d" % fmt)
+    rng = np.random.default_rng(3500 + fmt)
+    W, mag = exact_weights(rng, fmt, N, K)
+    dx, qx = exact_acts(rng, M, K, mag)
+    xq = q8K_bytes(dx, qx)
+    got = to_host(gq.gemm(fmt, weights_dev(gq, fmt, W, N, K), to_dev(xq), M, N, K, path=PATH_GEMM))
+    rows = np.array([0, 31, 32, 63, 64, 127, 128, 255, 256, 383, 384, 511, 512, 575, 599])
+    want = orc.gemm_int(fmt & 255, W, xq, M, N, K, rows)
+    w32 = want.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), want), "case leaves the exact regime"
+    assert_bits(got[rows], w32, "fmt %d 128-row tiles" % fmt)
+
+
 @pytest.mark.parametrize("fmt", [Q4, Q6, R + Q6, Q2])
 @pytest.mark.parametrize("M", [1, 4, 40, 130])
 def test_exact_group(dev, gq, orc, fmt, M):
