@@ -129,10 +129,10 @@ const char* gemmq_status_str(int status) {
     case GEMMQ_E_UNSUPPORTED_FORMAT:
       return "GEMMQ_E_UNSUPPORTED_FORMAT: the weight format must be q2_K (10), q3_K (11), q4_K "
              "(12), q5_K (13), q6_K (14) or a repacked q3_K / q6_K (267, 270; gemmq_decode and "
-             "gemmq_repack take the plain ones only), and the small-M path takes q4_K only";
+             "gemmq_repack take the plain ones only); the small-M path takes q4_K, q6_K and q6_K_R";
     case GEMMQ_E_SHAPE:
       return "GEMMQ_E_SHAPE: K must be a positive multiple of 256 up to 2^24, rows up to 2^31; "
-             "the GEMV path takes M <= 8, the small-M path M <= 64, the GEMM path M <= "
+             "the GEMV path takes M <= 8, the small-M path M <= 64 (q6_K: 16), the GEMM path M <= "
              "4194240";
     case GEMMQ_E_ALIGNMENT: return "GEMMQ_E_ALIGNMENT: a pointer breaks the documented alignment";
     case GEMMQ_E_DEVICE: return "GEMMQ_E_DEVICE: the current HIP device is not a gfx950";
