@@ -250,7 +250,7 @@ def test_gemm_tile_heights_same_bits(dev, gq, orc, fmt):
     assert_within(full[rows], yo, S, "tile heights")
 
 
-@pytest.mark.parametrize("fmt", [Q5, 14])
+@pytest.mark.parametrize("fmt", [Q2, Q3, Q5, 14])
 def test_silu_tile_heights_same_bits(dev, gq, orc, fmt):
     # 2100 gate/up pairs: 66 pair tiles of 64 interleaved columns (the last
     # ragged) over 5 row tiles of 128 for 600 rows; 3-row calls take 64-row tiles
