@@ -247,6 +247,15 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
+// Blocks each wave of the fused form quantizes: the M nb <= MT nbmax blocks of
+// the activation (nbmax = 16 / P when P rows of 16 / P blocks share a round,
+// else rows of up to 16 blocks) spread over its RG waves, at most four.  Rows
+// of 8 blocks at M = 1, for instance, need one block per wave, not two.
+constexpr int fused_qb(int MT, int P, int RG) {
+  const int n = (MT * (P > 1 ? 16 / P : 16) + RG - 1) / RG;
+  return n < 4 ? n : 4;
+}
+
 // FMT: the GGUF type id (10 q2_K .. 14 q6_K), plus 256 for the repacked q3_K /
 // q6_K layout (repack.hip).  MT activation rows computed (>= M).  IT rounds of 16
 // blocks loaded together.  P rows per round.  KS waves share one row (P = 1):
@@ -579,8 +588,8 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     // activation loads first, weight loads next, so quantizing waits only for
     // the former; every load is unconditional (clamped), so the wait counts
     // are exact
-    // blocks quantized per wave, at most (M nb <= 16 MT when the form is used)
-    constexpr int QB = (16 * MT + NW - 1) / NW < 4 ? (16 * MT + NW - 1) / NW : 4;
+    // blocks quantized per wave, at most
+    constexpr int QB = fused_qb(MT, P, NW);
     const int nq = M * nb;
     float4 xv[QB];
 #pragma unroll
@@ -707,8 +716,8 @@ int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hip
   if (X) {
     if constexpr (IT == 1 && KS == 1 && MT <= 4) {
       constexpr int RG = kRG;
-      // the kernel quantizes up to min(4, ceil(16 MT / RG)) blocks per wave
-      constexpr int QB = (16 * MT + RG - 1) / RG < 4 ? (16 * MT + RG - 1) / RG : 4;
+      // the kernel quantizes up to fused_qb(MT, P, RG) blocks per wave
+      constexpr int QB = fused_qb(MT, P, RG);
       if (M * nb > kQB * RG || M * nb > QB * RG) return -1;
       if (!group_tiles<SILU>(grp, RG * P * R, gt)) return -1;
       const uint32_t tiles = gt.start[kMaxGroup];
