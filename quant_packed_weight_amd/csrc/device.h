@@ -71,10 +71,14 @@ __device__ __forceinline__ uint32_t hi_nib(uint32_t w) { return (w >> 4) & 0x0f0
 // Four 6-bit quants (0..63, one per byte) of quarter c of a 128-weight half:
 // low 4 bits from a ql word (low nibbles for c < 2, high nibbles otherwise), top
 // 2 bits from bits 2c..2c+1 of each byte of the matching qh word.
+// The qh word is rotated right by 2c - 4 (mod 32), which puts bits 2c, 2c+1 of
+// each byte at bits 4, 5 of the same byte; the other bits of the rotation are
+// masked off, so one rotate and one and-or replace a shift, a mask and a
+// shift-or.
 __device__ __forceinline__ uint32_t q6k_quad(uint32_t qlw, uint32_t qhw, int c) {
-  uint32_t low = (c < 2 ? qlw : (qlw >> 4)) & 0x0f0f0f0fu;
-  uint32_t high = (qhw >> (2 * c)) & 0x03030303u;
-  return low | (high << 4);
+  const uint32_t low = (c < 2 ? qlw : (qlw >> 4)) & 0x0f0f0f0fu;
+  const uint32_t high = __builtin_amdgcn_alignbit(qhw, qhw, (uint32_t)(2 * c - 4) & 31u);
+  return (high & 0x30303030u) | low;
 }
 
 // Loads n dwords starting at a 2-byte-aligned address: reads the dword-aligned
