@@ -753,7 +753,7 @@ def cpu_baseline(wl, gen, M1, M2, seconds):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU (the packed linear layer has no "
+        print("bench.py: the packed linear layer runs on one GPU per process (it has no "
               "collective); --gpus %d is not supported" % a.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

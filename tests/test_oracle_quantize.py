@@ -3,7 +3,7 @@
 The quantizer reading: per 256-block, d = amax/127 in f32, q = round-half-even of
 x/d clamped to [-127, 127], sums over groups of 16 (molayo article, status row
 "src/ -- C++ engine": activations are quantized to int8 blocks the way llama.cpp
-does; the formula itself is this build's reading).  The checks are properties the
+does; the formula itself is a reading of that sentence, which names no formula).  The checks are properties the
 definition fixes: the error bound of rounding, the extreme code, exact ties,
 reachability of every code, odd symmetry, power-of-two scale invariance, the group
 sums and the zero block.
