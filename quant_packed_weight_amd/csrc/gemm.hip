@@ -698,7 +698,7 @@ int launch_any(int fmt, const Group& grp, const uint8_t* Xq, int64_t M, int64_t 
   GroupTiles gt;
   if (fmt == 14 || fmt == 256 + 14) {
     // the four-tile q6_K kernel (128 x 128 workgroup tiles) where the launch
-    // has enough of them to fill the chip; the plane kernel's 128 x 64 tiles
+    // has enough of them to fill the chip; the plane kernel's 64-column tiles
     // below that.  Both give every output the same integer sum and the same
     // f32 epilogue in the same order, so the choice changes no bits.
     if (!(SILU ? make_pair_tiles(grp, 128, gt) : make_tiles(grp, 128, gt))) return -1;
