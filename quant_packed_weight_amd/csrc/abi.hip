@@ -291,7 +291,7 @@ int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_pending();
-  if (rows > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
+  if (rows > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fuse_quantizer(M, K, rows))
     return launched(gemmq::launch_gemv_fused(fmt, g, X, xq, (int)M, K, st));
   rc = launched(gemmq::launch_quantize_q8K(X, xq, M, K, st));
   if (rc != GEMMQ_OK || rows == 0) return rc;
@@ -328,7 +328,7 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
   uint8_t* xq = static_cast<uint8_t*>(Xq);
   hipStream_t st = static_cast<hipStream_t>(stream);
   clear_pending();
-  if (N > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fusable(M, K))
+  if (N > 0 && p == GEMMQ_PATH_GEMV && gemmq::gemv_fuse_quantizer(M, K, 2 * N))
     return launched(gemmq::launch_gemv_silu(fmt, g, nullptr, X, xq, (int)M, K, st));
   rc = launched(gemmq::launch_quantize_q8K(X, xq, M, K, st));
   if (rc != GEMMQ_OK || N == 0) return rc;

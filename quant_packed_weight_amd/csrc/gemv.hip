@@ -267,7 +267,8 @@ constexpr int fused_qb(int MT, int P, int RG) {
 // (gt.W[0]) and row 2n+1 up row n (gt.W[1]); P R is even, so a wave's rows come
 // in (gate, up) pairs computed exactly as in two plain calls, and the pair's
 // outputs meet in LDS for y[m][n] = silu(g) * u (Y has N columns).
-template <int FMT, int MT, int IT, int P, int KS, int R, int RG, bool FUSED, bool SILU>
+template <int FMT, int MT, int IT, int P, int KS, int R, int RG, bool FUSED, bool SILU,
+          bool STAGE = false>
 __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
                                                             uint8_t* __restrict__ Xq,
                                                             const float* __restrict__ X, int nb,
@@ -591,32 +592,60 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     // blocks quantized per wave, at most
     constexpr int QB = fused_qb(MT, P, NW);
     const int nq = M * nb;
-    float4 xv[QB];
-#pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      int t = wv + NW * j;
-      t = t < nq ? t : nq - 1;
-      xv[j] = *reinterpret_cast<const float4*>(X + (int64_t)t * kQK + 4 * lane);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the two groups of loads in this order
     const int s0 = 16 * w;
-    load_round(s0, true);
-    __builtin_amdgcn_sched_barrier(0);
-    // every wave quantizes QB blocks without branches (past the last block it
-    // repeats it), so the blocks' reductions interleave; only real blocks are
-    // stored
-    Q8Lane q[QB];
+    if constexpr (!STAGE) {
+      float4 xv[QB];
 #pragma unroll
-    for (int j = 0; j < QB; ++j) q[j] = q8k_block(xv[j]);
+      for (int j = 0; j < QB; ++j) {
+        int t = wv + NW * j;
+        t = t < nq ? t : nq - 1;
+        xv[j] = *reinterpret_cast<const float4*>(X + (int64_t)t * kQK + 4 * lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the two groups of loads in this order
+      load_round(s0, true);
+      __builtin_amdgcn_sched_barrier(0);
+      // every wave quantizes QB blocks without branches (past the last block it
+      // repeats it), so the blocks' reductions interleave; only real blocks are
+      // stored
+      Q8Lane q[QB];
 #pragma unroll
-    for (int j = 0; j < QB; ++j) {
-      const int t = wv + NW * j;
-      if (t < nq) {  // wave-uniform
-        uint8_t* o = xl + t * kXL;
-        *reinterpret_cast<uint32_t*>(o + 4 * lane) = q[j].packed;
-        if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(o + 256 + 2 * (lane >> 2)) = q[j].sums;
-        if (lane == 0) *reinterpret_cast<float*>(o + 288) = q[j].d;
-        if (blockIdx.x == 0) q8k_store(Xq + (int64_t)t * kQ8KBytes, q[j], lane);
+      for (int j = 0; j < QB; ++j) q[j] = q8k_block(xv[j]);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const int t = wv + NW * j;
+        if (t < nq) {  // wave-uniform
+          uint8_t* o = xl + t * kXL;
+          *reinterpret_cast<uint32_t*>(o + 4 * lane) = q[j].packed;
+          if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(o + 256 + 2 * (lane >> 2)) = q[j].sums;
+          if (lane == 0) *reinterpret_cast<float*>(o + 288) = q[j].d;
+          if (blockIdx.x == 0) q8k_store(Xq + (int64_t)t * kQ8KBytes, q[j], lane);
+        }
+      }
+    } else {
+      // the staged form: the q8_K blocks already at Xq, copied into the same
+      // LDS layout (values, the 16 group sums, d)
+      uint32_t cv[QB], cs[QB], cd[QB];
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        int t = wv + NW * j;
+        t = t < nq ? t : nq - 1;
+        const uint8_t* xb = Xq + (int64_t)t * kQ8KBytes;
+        cv[j] = ld4(xb + 4 + 4 * lane);
+        cs[j] = ld4(xb + 260 + 4 * (lane & 7));
+        cd[j] = ld4(xb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      load_round(s0, true);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < QB; ++j) {
+        const int t = wv + NW * j;
+        if (t < nq) {  // wave-uniform
+          uint8_t* o = xl + t * kXL;
+          *reinterpret_cast<uint32_t*>(o + 4 * lane) = cv[j];
+          if (lane < 8) *reinterpret_cast<uint32_t*>(o + 256 + 4 * lane) = cs[j];
+          if (lane == 0) *reinterpret_cast<uint32_t*>(o + 288) = cd[j];
+        }
       }
     }
     __syncthreads();
@@ -711,23 +740,31 @@ bool group_tiles(const Group& grp, int64_t rows_per_tile, GroupTiles& gt) {
 }
 
 template <int FMT, int MT, bool SILU, int IT, int P, int KS, int R = 1>
-int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hipStream_t st) {
+int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, bool stage,
+               hipStream_t st) {
   GroupTiles gt;
-  if (X) {
-    if constexpr (IT == 1 && KS == 1 && MT <= 4) {
-      constexpr int RG = kRG;
-      // the kernel quantizes up to fused_qb(MT, P, RG) blocks per wave
-      constexpr int QB = fused_qb(MT, P, RG);
-      if (M * nb > kQB * RG || M * nb > QB * RG) return -1;
+  // X: the fused form; stage (X null): the same workgroups staging the q8_K
+  // blocks at Xq in LDS, where the shape allows it (else the plain form)
+  if constexpr (IT == 1 && KS == 1 && MT <= 4) {
+    constexpr int RG = kRG;
+    // the kernel quantizes or stages up to fused_qb(MT, P, RG) blocks per wave
+    constexpr int QB = fused_qb(MT, P, RG);
+    const bool fits = M * nb <= kQB * RG && M * nb <= QB * RG;
+    if (X && !fits) return -1;
+    if (X || (stage && fits)) {
       if (!group_tiles<SILU>(grp, RG * P * R, gt)) return -1;
       const uint32_t tiles = gt.start[kMaxGroup];
       if (tiles == 0) return 0;
-      hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU>), dim3(tiles),
-                         dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
+      if (X)
+        hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU>), dim3(tiles),
+                           dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
+      else
+        hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU, true>), dim3(tiles),
+                           dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
       return 0;
-    } else {
-      return -1;
     }
+  } else {
+    if (X) return -1;
   }
   if (!group_tiles<SILU>(grp, P * R, gt)) return -1;
   const uint32_t tiles = gt.start[kMaxGroup];
@@ -744,57 +781,86 @@ int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, hip
 int split_waves(int nb) { return nb <= 16 ? 1 : nb <= 32 ? 2 : nb <= 48 ? 3 : nb <= 64 ? 4 : 0; }
 
 template <int FMT, int MT, bool SILU>
-int launch_mt(const Group& g, uint8_t* Xq, const float* X, int nb, int M, hipStream_t st) {
-  if (nb == 1) return launch_cfg<FMT, MT, SILU, 1, 16, 1>(g, Xq, X, nb, M, st);
-  if (nb == 2) return launch_cfg<FMT, MT, SILU, 1, 8, 1>(g, Xq, X, nb, M, st);
-  if (nb == 4) return launch_cfg<FMT, MT, SILU, 1, 4, 1>(g, Xq, X, nb, M, st);
-  if (nb == 8) return launch_cfg<FMT, MT, SILU, 1, 2, 1>(g, Xq, X, nb, M, st);
-  if (nb <= 16) return launch_cfg<FMT, MT, SILU, 1, 1, 1, 2>(g, Xq, X, nb, M, st);
-  if (nb <= 32) return launch_cfg<FMT, MT, SILU, 1, 1, 2, 2>(g, Xq, X, nb, M, st);
-  if (nb <= 48) return launch_cfg<FMT, MT, SILU, 1, 1, 3, 2>(g, Xq, X, nb, M, st);
-  if (nb <= 64) return launch_cfg<FMT, MT, SILU, 1, 1, 4, 2>(g, Xq, X, nb, M, st);
-  return launch_cfg<FMT, MT, SILU, 2, 1, 4, 2>(g, Xq, X, nb, M, st);
+int launch_mt(const Group& g, uint8_t* Xq, const float* X, int nb, int M, bool stage,
+              hipStream_t st) {
+  if (nb == 1) return launch_cfg<FMT, MT, SILU, 1, 16, 1>(g, Xq, X, nb, M, stage, st);
+  if (nb == 2) return launch_cfg<FMT, MT, SILU, 1, 8, 1>(g, Xq, X, nb, M, stage, st);
+  if (nb == 4) return launch_cfg<FMT, MT, SILU, 1, 4, 1>(g, Xq, X, nb, M, stage, st);
+  if (nb == 8) return launch_cfg<FMT, MT, SILU, 1, 2, 1>(g, Xq, X, nb, M, stage, st);
+  if (nb <= 16) return launch_cfg<FMT, MT, SILU, 1, 1, 1, 2>(g, Xq, X, nb, M, stage, st);
+  if (nb <= 32) return launch_cfg<FMT, MT, SILU, 1, 1, 2, 2>(g, Xq, X, nb, M, stage, st);
+  if (nb <= 48) return launch_cfg<FMT, MT, SILU, 1, 1, 3, 2>(g, Xq, X, nb, M, stage, st);
+  if (nb <= 64) return launch_cfg<FMT, MT, SILU, 1, 1, 4, 2>(g, Xq, X, nb, M, stage, st);
+  return launch_cfg<FMT, MT, SILU, 2, 1, 4, 2>(g, Xq, X, nb, M, stage, st);
 }
 
 template <int FMT, bool SILU>
-int launch_fmt(const Group& g, uint8_t* Xq, const float* X, int M, int nb, hipStream_t st) {
+int launch_fmt(const Group& g, uint8_t* Xq, const float* X, int M, int nb, bool stage,
+               hipStream_t st) {
   switch (M) {
-    case 1: return launch_mt<FMT, 1, SILU>(g, Xq, X, nb, M, st);
-    case 2: return launch_mt<FMT, 2, SILU>(g, Xq, X, nb, M, st);
+    case 1: return launch_mt<FMT, 1, SILU>(g, Xq, X, nb, M, stage, st);
+    case 2: return launch_mt<FMT, 2, SILU>(g, Xq, X, nb, M, stage, st);
     case 3:
-    case 4: return launch_mt<FMT, 4, SILU>(g, Xq, X, nb, M, st);
+    case 4: return launch_mt<FMT, 4, SILU>(g, Xq, X, nb, M, stage, st);
     case 5:
     case 6:
     case 7:
     case 8:
       if (X) return -1;
-      return launch_mt<FMT, 8, SILU>(g, Xq, X, nb, M, st);
+      return launch_mt<FMT, 8, SILU>(g, Xq, X, nb, M, stage, st);
     default: return -1;
   }
 }
 
 template <bool SILU>
 int launch_any(int fmt, const Group& g, uint8_t* Xq, const float* X, int M, int64_t K,
-               hipStream_t st) {
+               bool stage, hipStream_t st) {
   const int64_t nb = K / kQK;
   if (nb > 0x7fffffffLL) return -1;
   switch (fmt) {
-    case 10: return launch_fmt<10, SILU>(g, Xq, X, M, (int)nb, st);
-    case 11: return launch_fmt<11, SILU>(g, Xq, X, M, (int)nb, st);
-    case 12: return launch_fmt<12, SILU>(g, Xq, X, M, (int)nb, st);
-    case 13: return launch_fmt<13, SILU>(g, Xq, X, M, (int)nb, st);
-    case 14: return launch_fmt<14, SILU>(g, Xq, X, M, (int)nb, st);
-    case 256 + 11: return launch_fmt<256 + 11, SILU>(g, Xq, X, M, (int)nb, st);
-    case 256 + 14: return launch_fmt<256 + 14, SILU>(g, Xq, X, M, (int)nb, st);
+    case 10: return launch_fmt<10, SILU>(g, Xq, X, M, (int)nb, stage, st);
+    case 11: return launch_fmt<11, SILU>(g, Xq, X, M, (int)nb, stage, st);
+    case 12: return launch_fmt<12, SILU>(g, Xq, X, M, (int)nb, stage, st);
+    case 13: return launch_fmt<13, SILU>(g, Xq, X, M, (int)nb, stage, st);
+    case 14: return launch_fmt<14, SILU>(g, Xq, X, M, (int)nb, stage, st);
+    case 256 + 11: return launch_fmt<256 + 11, SILU>(g, Xq, X, M, (int)nb, stage, st);
+    case 256 + 14: return launch_fmt<256 + 14, SILU>(g, Xq, X, M, (int)nb, stage, st);
     default: return -1;
   }
 }
 
 }  // namespace
 
+namespace {
+
+// The staged form pays where the launch is large: its workgroups copy the q8_K
+// blocks (a few loads) instead of reading activation fragments from L2 per
+// lane (the plain form) or quantizing them again (the fused form).  Measured
+// with rows x M x blocks-per-row as the size (one process, cold weights): with
+// the q8_K blocks given, the staged form from 2^18 (Qwen3-8B gate/up at M = 1,
+// 393216: 12.48 -> 11.49 us; the q6_K LM head 151936 x 2048 at M = 1 61.8 ->
+// 43.7 us; q/k/v at M = 1, 98304, 5.11 against 5.37 us stays plain); from f32
+// activations, a quantizer launch of its own and the staged form from 2^19
+// (the head at M = 1 48.7 -> 46.6 us, at M = 2 68.4 -> 51.2 us, 8B gate/up at
+// M = 2 19.8 -> 15.1 us; 8B gate/up at M = 1 stays fused, 12.5 against 13.2).
+constexpr int64_t kStageWork = int64_t(1) << 18;
+constexpr int64_t kSplitQuantizerWork = int64_t(1) << 19;
+
+int64_t group_rows(const Group& g) {
+  int64_t r = 0;
+  for (int i = 0; i < g.count; ++i) r += g.N[i];
+  return r;
+}
+
+bool stage_pays(int64_t rows, int64_t M, int64_t K) {
+  return rows * M * (K / kQK) >= kStageWork;
+}
+
+}  // namespace
+
 int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st) {
-  uint8_t* xq = const_cast<uint8_t*>(Xq);  // read only in the plain form
-  return launch_any<false>(fmt, g, xq, nullptr, M, K, st);
+  uint8_t* xq = const_cast<uint8_t*>(Xq);  // read only in the plain and staged forms
+  return launch_any<false>(fmt, g, xq, nullptr, M, K, stage_pays(group_rows(g), M, K), st);
 }
 
 bool gemv_fusable(int64_t M, int64_t K) {
@@ -803,10 +869,14 @@ bool gemv_fusable(int64_t M, int64_t K) {
   return split_waves((int)nb) == 1 && M * nb <= (int64_t)kQB * kRG;
 }
 
+bool gemv_fuse_quantizer(int64_t M, int64_t K, int64_t rows) {
+  return gemv_fusable(M, K) && rows * M * (K / kQK) < kSplitQuantizerWork;
+}
+
 int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,
                       hipStream_t st) {
   if (!gemv_fusable(M, K)) return -1;
-  return launch_any<false>(fmt, g, Xq, X, M, K, st);
+  return launch_any<false>(fmt, g, Xq, X, M, K, false, st);
 }
 
 int launch_gemv_silu(int fmt, const Group& g, const uint8_t* Xq, const float* X, uint8_t* Xq_out,
@@ -814,9 +884,10 @@ int launch_gemv_silu(int fmt, const Group& g, const uint8_t* Xq, const float* X,
   if (g.count != 2 || g.N[0] != g.N[1]) return -1;
   if (X) {
     if (!gemv_fusable(M, K)) return -1;
-    return launch_any<true>(fmt, g, Xq_out, X, M, K, st);
+    return launch_any<true>(fmt, g, Xq_out, X, M, K, false, st);
   }
-  return launch_any<true>(fmt, g, const_cast<uint8_t*>(Xq), nullptr, M, K, st);
+  return launch_any<true>(fmt, g, const_cast<uint8_t*>(Xq), nullptr, M, K,
+                          stage_pays(group_rows(g), M, K), st);
 }
 
 }  // namespace gemmq

@@ -116,6 +116,9 @@ int launch_gemm_q6k(const GroupTiles& gt, int fmt, bool silu, const uint8_t* Xq,
 // each workgroup quantizing into its own LDS; Xq receives the q8_K blocks.
 // Taken when gemv_fusable(M, K): M <= 4 and M K / 256 small enough (see gemv.hip).
 bool gemv_fusable(int64_t M, int64_t K);
+// gemv_fusable and few enough rows (all matrices of the call) that quantizing in
+// every workgroup costs less than a quantizer launch of its own.
+bool gemv_fuse_quantizer(int64_t M, int64_t K, int64_t rows);
 int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,
                       hipStream_t st);
 // SiLU-gated product of a gate and an up matrix (g.W[0], g.W[1], equal N, output
