@@ -41,7 +41,8 @@ constexpr int64_t kSkinnyColTiles = 20480;
 // 9 <= M <= 16, and at 3 <= M <= 8 from this many output columns (below them
 // its 32-column workgroups are too few to fill the chip and the GEMV is faster:
 // measured on the Qwen3-1.7B shapes, v 1024 and down 2048 columns against the
-// 151936-column head)
+// 151936-column head) -- except at M <= 4 where the GEMV holds the activation in
+// LDS (M K/256 <= 32; the head at M = 3 / 4: 58.3 / 59.2 us against 85.9 / 86.0)
 constexpr int64_t kSkinnyQ6Cols = 16384;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
@@ -215,15 +216,16 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
 // with cols * t, while the GEMM at these M runs one 64-row tile per column tile
 // and costs about the same at any cols below a chip's worth of workgroups); the
 // GEMM beyond.  q6_K (either layout) takes its small-M kernel at 9 <= M <= 16,
-// and at 3 <= M <= 8 once the launch has kSkinnyQ6Cols columns.
-int pick_path(int fmt, int path, int64_t M, int64_t cols) {
+// and at 3 <= M <= 8 once the launch has kSkinnyQ6Cols columns, unless the GEMV
+// can hold the activation in LDS (gemv_fusable).
+int pick_path(int fmt, int path, int64_t M, int64_t K, int64_t cols) {
   if (path != GEMMQ_PATH_AUTO) return path;
   if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) {
     const int64_t t = (M + 15) / 16;
     if (t == 1 || cols * t <= kSkinnyColTiles) return GEMMQ_PATH_SKINNY;
   }
   if ((fmt == GEMMQ_Q6_K || fmt == GEMMQ_Q6_K_R) && M >= kSkinnyMinM && M <= kSkinnyQ6MaxM &&
-      (M > 8 || cols >= kSkinnyQ6Cols))
+      (M > 8 || (cols >= kSkinnyQ6Cols && !gemmq::gemv_fusable(M, K))))
     return GEMMQ_PATH_SKINNY;
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }
@@ -261,7 +263,7 @@ int gemmq_gemm_group(int fmt, int count, const void* const* W, float* const* Y,
   if (rc != GEMMQ_OK || M == 0 || rows == 0) return rc;
   if (!Xq) return GEMMQ_E_INVALID_ARG;
   if (!aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
-  const int p = pick_path(fmt, path, M, rows);
+  const int p = pick_path(fmt, path, M, K, rows);
   rc = shape_matmul(fmt, p, M, K);
   if (rc != GEMMQ_OK) return rc;
   const int dv = check_device();
@@ -283,7 +285,7 @@ int gemmq_linear_group(int fmt, int count, const void* const* W, float* const* Y
   if (rc != GEMMQ_OK || M == 0) return rc;
   if (!X || !Xq) return GEMMQ_E_INVALID_ARG;
   if (!aligned(X, 16) || !aligned(Xq, 4)) return GEMMQ_E_ALIGNMENT;
-  const int p = pick_path(fmt, path, M, rows);
+  const int p = pick_path(fmt, path, M, K, rows);
   if (rows > 0 && (rc = shape_matmul(fmt, p, M, K)) != GEMMQ_OK) return rc;
   const int dv = check_device();
   if (dv != GEMMQ_OK) return dv;
@@ -314,7 +316,7 @@ int gemmq_linear_silu_mul(int fmt, const void* Wg, const void* Wu, const float* 
   if (M == 0) return GEMMQ_OK;
   if (!X || !Xq || (N > 0 && !Y)) return GEMMQ_E_INVALID_ARG;
   if (!aligned(X, 16) || !aligned(Xq, 4) || (N > 0 && !aligned(Y, 4))) return GEMMQ_E_ALIGNMENT;
-  const int p = pick_path(fmt, path, M, 2 * N);  // as gemmq_linear_group on {Wg, Wu}
+  const int p = pick_path(fmt, path, M, K, 2 * N);  // as gemmq_linear_group on {Wg, Wu}
   if (N > 0 && (rc = shape_matmul(fmt, p, M, K)) != GEMMQ_OK) return rc;
   const int dv = check_device();
   if (dv != GEMMQ_OK) return dv;

@@ -200,15 +200,17 @@ def test_adversarial_blocks(dev, gq, orc, fmt, path):
     assert_within(y, yo, S, "adversarial")
 
 
-def _expected_path(gq, fmt, M, cols):
+def _expected_path(gq, fmt, M, cols, K):
     # GEMV up to M = 8 (q4_K: up to 2); the small-M MFMA kernels for q4_K at
     # 3 <= M <= 64 with one 16-row tile, or with t tiles while cols * t <= 20480,
-    # and for q6_K at 9 <= M <= 16, or at 3 <= M <= 8 from 16384 columns; the
-    # GEMM otherwise
+    # and for q6_K at 9 <= M <= 16, or at 3 <= M <= 8 from 16384 columns unless
+    # the GEMV holds the activation in LDS (M <= 4, M K/256 <= 32); the GEMM
+    # otherwise
     t = (M + 15) // 16
     if fmt == Q4 and 3 <= M <= 64 and (t == 1 or cols * t <= 20480):
         return gq.PATH_SKINNY
-    if fmt == Q6 and 3 <= M <= 16 and (M > 8 or cols >= 16384):
+    staged = M <= 4 and M * (K // 256) <= 32
+    if fmt == Q6 and 3 <= M <= 16 and (M > 8 or (cols >= 16384 and not staged)):
         return gq.PATH_SKINNY
     return gq.PATH_GEMV if M <= 8 else gq.PATH_GEMM
 
@@ -218,13 +220,13 @@ def _expected_path(gq, fmt, M, cols):
 def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
     # the automatic path takes the expected kernel family (the same bits as that
     # path forced); N = 7000 crosses the q4_K column bound between t = 2 and
-    # t = 3, N = 16384 the q6_K one at M = 3..8
+    # t = 3, N = 16384 the q6_K one at M = 5..8 (M = 3, 4 stay on the GEMV)
     log("dispatch fmt=%d N=%d" % (fmt, N))
     K = 512 if N < 1000 else 256
     for M in (1, 2, 3, 4, 5, 6, 8, 9, 16, 17, 32, 33, 48, 49, 64, 65):
         W, x, xq = _case(orc, fmt, M, N, K, seed=M + fmt)
         auto = to_host(gq.gemm(fmt, to_dev(W), to_dev(xq), M, N, K))
-        path = _expected_path(gq, fmt, M, N)
+        path = _expected_path(gq, fmt, M, N, K)
         forced = _run(gq, fmt, W, xq, M, N, K, path)
         assert np.array_equal(auto.view(np.uint32), forced.view(np.uint32)), M
         lin = to_host(gq.linear(fmt, to_dev(W), to_dev(x), N))
@@ -234,7 +236,7 @@ def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
 @pytest.mark.parametrize("N", [16383, 16384])
 def test_auto_dispatch_q6K_repacked(dev, gq, orc, N):
     # the repacked q6_K layout follows the q6_K choice (the small-M kernel at
-    # M = 9..16 and at 3..8 from 16384 columns, the GEMV below, the GEMM beyond)
+    # M = 9..16 and at 5..8 from 16384 columns, the GEMV below, the GEMM beyond)
     # with the original layout's bits
     import torch
 
@@ -245,7 +247,7 @@ def test_auto_dispatch_q6K_repacked(dev, gq, orc, N):
         Wd, xqd = to_dev(W), to_dev(xq)
         Wr = gq.repack(Q6, Wd, N, K)
         auto = to_host(gq.gemm(gq.FMT_Q6K_R, Wr, xqd, M, N, K))
-        path = _expected_path(gq, Q6, M, N)
+        path = _expected_path(gq, Q6, M, N, K)
         forced = to_host(gq.gemm(gq.FMT_Q6K_R, Wr, xqd, M, N, K, path=path))
         plain = to_host(gq.gemm(Q6, Wd, xqd, M, N, K, path=path))
         assert np.array_equal(auto.view(np.uint32), forced.view(np.uint32)), M

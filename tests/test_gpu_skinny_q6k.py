@@ -109,7 +109,7 @@ def test_skinny_q6k_extreme_blocks(dev, gq, orc, fmt, M):
 def test_skinny_q6k_group_and_linear(dev, gq, orc, M):
     # a group launch equals single calls; gemmq_linear_group on this path
     # gives the same bits (and so does its automatic choice at M > 8, and at
-    # M <= 8 past 16384 columns -- checked in the dispatch tests)
+    # 5 <= M <= 8 past 16384 columns -- checked in the dispatch tests)
     log("skinny q6_K group M=%d" % M)
     K = 2048
     Ns = [300, 64, 65]
