@@ -147,9 +147,11 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
  * walks each weight row once per tile of activation rows, and the reordered f32
  * sums are held to a 1e-5 scaled relative bound)
  * (steps a2..a5: in-kernel unpack; the path chosen by GEMMQ_PATH_AUTO: the decode
- * GEMV for M <= 8 -- for q4_K M <= 2 --, the small-M MFMA kernel for q4_K at
- * 3 <= M <= 64 when M <= 16 or when the launch's output columns times ceil(M/16)
- * are at most 20480, and for q6_K and q6_K_R at 9 <= M <= 16 and at 3 <= M <= 8
+ * GEMV for M <= 8 -- for q4_K M <= 2, and M = 3, 4 on launches large enough
+ * that it stages the activation in LDS (rows of at most 16 blocks, M*K/256 <=
+ * 64, output columns x M x K/256 >= 2^18) --, the small-M MFMA kernel for q4_K
+ * at 3 <= M <= 64 when M <= 16 or when the launch's output columns times
+ * ceil(M/16) are at most 20480, and for q6_K and q6_K_R at 9 <= M <= 16 and at 3 <= M <= 8
  * when the launch has at least 16384 output columns (at M <= 4 only where
  * M*K/256 > 32: below that the GEMV holds the activation in LDS and is faster),
  * the MFMA GEMM otherwise; the choice is made once per launch, from M, K and

@@ -215,11 +215,16 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
 // 16-row tile and for t > 1 tiles while cols * t <= kSkinnyColTiles (its time grows
 // with cols * t, while the GEMM at these M runs one 64-row tile per column tile
 // and costs about the same at any cols below a chip's worth of workgroups); the
-// GEMM beyond.  q6_K (either layout) takes its small-M kernel at 9 <= M <= 16,
+// GEMM beyond -- except q4_K at M = 3, 4 on launches where the GEMV holds the
+// activation in LDS (Qwen3-8B q/k/v at M = 3 9.8 against 11.0 us, gate/up 18.8
+// against 21.8; down, 48 blocks a row, stays: 18.5 against 13.5).  q6_K (either
+// layout) takes its small-M kernel at 9 <= M <= 16,
 // and at 3 <= M <= 8 once the launch has kSkinnyQ6Cols columns, unless the GEMV
 // can hold the activation in LDS (gemv_fusable).
 int pick_path(int fmt, int path, int64_t M, int64_t K, int64_t cols) {
   if (path != GEMMQ_PATH_AUTO) return path;
+  if (fmt == GEMMQ_Q4_K && M <= 4 && gemmq::gemv_holds_activation(M, K, cols))
+    return GEMMQ_PATH_GEMV;
   if (fmt == GEMMQ_Q4_K && M >= kSkinnyMinM && M <= kSkinnyMaxM) {
     const int64_t t = (M + 15) / 16;
     if (t == 1 || cols * t <= kSkinnyColTiles) return GEMMQ_PATH_SKINNY;

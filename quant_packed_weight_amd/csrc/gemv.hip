@@ -256,6 +256,13 @@ constexpr int fused_qb(int MT, int P, int RG) {
   return n < 4 ? n : 4;
 }
 
+// Blocks each wave of the staged form copies: the same count, up to eight (a
+// copy is three loads, not a quantization), so that it also serves M = 5..8.
+constexpr int stage_qb(int MT, int P, int RG) {
+  const int n = (MT * (P > 1 ? 16 / P : 16) + RG - 1) / RG;
+  return n < 8 ? n : 8;
+}
+
 // FMT: the GGUF type id (10 q2_K .. 14 q6_K), plus 256 for the repacked q3_K /
 // q6_K layout (repack.hip).  MT activation rows computed (>= M).  IT rounds of 16
 // blocks loaded together.  P rows per round.  KS waves share one row (P = 1):
@@ -590,7 +597,7 @@ __global__ __launch_bounds__(64 * KS * RG) void gemv_kernel(const GroupTiles gt,
     // the former; every load is unconditional (clamped), so the wait counts
     // are exact
     // blocks quantized per wave, at most
-    constexpr int QB = fused_qb(MT, P, NW);
+    constexpr int QB = STAGE ? stage_qb(MT, P, NW) : fused_qb(MT, P, NW);
     const int nq = M * nb;
     const int s0 = 16 * w;
     if constexpr (!STAGE) {
@@ -745,22 +752,30 @@ int launch_cfg(const Group& grp, uint8_t* Xq, const float* X, int nb, int M, boo
   GroupTiles gt;
   // X: the fused form; stage (X null): the same workgroups staging the q8_K
   // blocks at Xq in LDS, where the shape allows it (else the plain form)
-  if constexpr (IT == 1 && KS == 1 && MT <= 4) {
+  if constexpr (IT == 1 && KS == 1 && MT <= 8) {
     constexpr int RG = kRG;
-    // the kernel quantizes or stages up to fused_qb(MT, P, RG) blocks per wave
-    constexpr int QB = fused_qb(MT, P, RG);
-    const bool fits = M * nb <= kQB * RG && M * nb <= QB * RG;
-    if (X && !fits) return -1;
-    if (X || (stage && fits)) {
+    if (X) {
+      if constexpr (MT <= 4) {
+        // the kernel quantizes up to fused_qb(MT, P, RG) blocks per wave
+        constexpr int QB = fused_qb(MT, P, RG);
+        if (M * nb > kQB * RG || M * nb > QB * RG) return -1;
+        if (!group_tiles<SILU>(grp, RG * P * R, gt)) return -1;
+        const uint32_t tiles = gt.start[kMaxGroup];
+        if (tiles == 0) return 0;
+        hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU>), dim3(tiles),
+                           dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
+        return 0;
+      } else {
+        return -1;
+      }
+    }
+    // the staged form copies up to stage_qb(MT, P, RG) blocks per wave
+    if (stage && M * nb <= stage_qb(MT, P, RG) * RG) {
       if (!group_tiles<SILU>(grp, RG * P * R, gt)) return -1;
       const uint32_t tiles = gt.start[kMaxGroup];
       if (tiles == 0) return 0;
-      if (X)
-        hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU>), dim3(tiles),
-                           dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
-      else
-        hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU, true>), dim3(tiles),
-                           dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
+      hipLaunchKernelGGL((gemv_kernel<FMT, MT, IT, P, KS, R, RG, true, SILU, true>), dim3(tiles),
+                         dim3(64 * KS * RG), (size_t)M * nb * kXL, st, gt, Xq, X, nb, M);
       return 0;
     }
   } else {
@@ -867,6 +882,12 @@ bool gemv_fusable(int64_t M, int64_t K) {
   const int64_t nb = K / kQK;
   if (M < 1 || M > 4 || nb < 1 || nb > 16) return false;
   return split_waves((int)nb) == 1 && M * nb <= (int64_t)kQB * kRG;
+}
+
+bool gemv_holds_activation(int64_t M, int64_t K, int64_t rows) {
+  const int64_t nb = K / kQK;
+  if (M < 1 || M > 4 || nb < 1 || nb > 16 || M * nb > stage_qb(4, 1, kRG) * kRG) return false;
+  return stage_pays(rows, M, K);
 }
 
 bool gemv_fuse_quantizer(int64_t M, int64_t K, int64_t rows) {

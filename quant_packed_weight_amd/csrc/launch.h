@@ -119,6 +119,9 @@ bool gemv_fusable(int64_t M, int64_t K);
 // gemv_fusable and few enough rows (all matrices of the call) that quantizing in
 // every workgroup costs less than a quantizer launch of its own.
 bool gemv_fuse_quantizer(int64_t M, int64_t K, int64_t rows);
+// M <= 4, rows of at most 16 blocks, and a launch large enough (rows: all
+// matrices of the call) that the GEMV stages the activation in LDS.
+bool gemv_holds_activation(int64_t M, int64_t K, int64_t rows);
 int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,
                       hipStream_t st);
 // SiLU-gated product of a gate and an up matrix (g.W[0], g.W[1], equal N, output

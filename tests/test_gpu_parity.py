@@ -204,9 +204,13 @@ def _expected_path(gq, fmt, M, cols, K):
     # GEMV up to M = 8 (q4_K: up to 2); the small-M MFMA kernels for q4_K at
     # 3 <= M <= 64 with one 16-row tile, or with t tiles while cols * t <= 20480,
     # and for q6_K at 9 <= M <= 16, or at 3 <= M <= 8 from 16384 columns unless
-    # the GEMV holds the activation in LDS (M <= 4, M K/256 <= 32); the GEMM
-    # otherwise
+    # the GEMV holds the activation in LDS (M <= 4, M K/256 <= 32); q4_K at
+    # M = 3, 4 also stays on the GEMV where it stages the activation (rows of
+    # <= 16 blocks, M K/256 <= 64, cols x M x K/256 >= 2^18); the GEMM otherwise
     t = (M + 15) // 16
+    nb = K // 256
+    if fmt == Q4 and M <= 4 and nb <= 16 and M * nb <= 64 and cols * M * nb >= 1 << 18:
+        return gq.PATH_GEMV  # the GEMV holds the activation in LDS
     if fmt == Q4 and 3 <= M <= 64 and (t == 1 or cols * t <= 20480):
         return gq.PATH_SKINNY
     staged = M <= 4 and M * (K // 256) <= 32
@@ -231,6 +235,29 @@ def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
         assert np.array_equal(auto.view(np.uint32), forced.view(np.uint32)), M
         lin = to_host(gq.linear(fmt, to_dev(W), to_dev(x), N))
         assert np.array_equal(lin.view(np.uint32), auto.view(np.uint32)), M
+
+
+@pytest.mark.parametrize("M,K,N", [(3, 4096, 30000), (4, 4096, 30000), (4, 2048, 8192),
+                                   (3, 4096, 300), (3, 12288, 30000), (8, 4096, 30000)])
+def test_auto_dispatch_q4K_large_launches(dev, gq, orc, M, K, N):
+    # q4_K at M = 3, 4 stays on the GEMV where it holds the activation in LDS
+    # (large launches of rows of <= 16 blocks); small launches, long rows and
+    # M > 4 keep the small-M kernel.  The automatic path, the one-call layer and
+    # that path forced give the same bits; sampled outputs match the oracle.
+    log("dispatch q4_K large M=%d K=%d N=%d" % (M, K, N))
+    W, x, xq = _case(orc, Q4, M, N, K, seed=M + K + N)
+    Wd, xqd = to_dev(W), to_dev(xq)
+    auto = to_host(gq.gemm(Q4, Wd, xqd, M, N, K))
+    path = _expected_path(gq, Q4, M, N, K)
+    forced = _run(gq, Q4, W, xq, M, N, K, path)
+    assert np.array_equal(auto.view(np.uint32), forced.view(np.uint32))
+    lin = to_host(gq.linear(Q4, Wd, to_dev(x), N))
+    assert np.array_equal(lin.view(np.uint32), auto.view(np.uint32))
+    cols = np.array([0, 1, N // 3, N // 2, N - 2, N - 1])
+    Ws = np.ascontiguousarray(W[cols])
+    yo = orc.gemm_int(Q4, Ws, xq, M, len(cols), K)
+    _, S = orc.gemm_dequant(Q4, Ws, xq, M, len(cols), K)
+    assert_within(auto[:, cols], yo, S, "q4_K large dispatch")
 
 
 @pytest.mark.parametrize("N", [16383, 16384])
