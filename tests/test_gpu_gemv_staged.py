@@ -61,9 +61,12 @@ def _check_oracle(orc, fmt, W, xq, M, N, K, got, where):
 
 
 # (M, K, N): rows x M x K/256 = 320000 (staged when the q8_K blocks are given,
-# fused from f32 activations)
+# fused from f32 activations), and the staged form where the fused one does not
+# reach: 64 blocks at M = 4, the 8-row form at M = 6 and 8 (the layer call then
+# quantizes in a launch of its own)
 @pytest.mark.parametrize("fmt", [Q4, Q6, Q2, Q3, Q5, R + Q6])
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 20000), (2, 2048, 20000), (4, 1024, 20000)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 20000), (2, 2048, 20000), (4, 1024, 20000),
+                                   (4, 4096, 5000), (6, 2048, 20000), (8, 1024, 20000)])
 def test_staged_equals_plain_and_fused(dev, gq, orc, fmt, M, K, N):
     log("gemv staged fmt=%d M=%d K=%d N=%d" % (fmt, M, K, N))
     rng = np.random.default_rng(fmt + 7 * M + K)
@@ -100,11 +103,12 @@ def test_layer_split_quantizer(dev, gq, orc, fmt, M, K, N):
 
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 10000), (2, 4096, 10000)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 10000), (2, 4096, 10000), (6, 2048, 10000)])
 def test_silu_staged(dev, gq, fmt, M, K, N):
     # gate/up pairs: 2N x M x K/256 = 320000 (M = 1: fused from f32, staged from
-    # q8_K) and 640000 (M = 2: quantizer launch + staged); the first SUB / 2
-    # outputs equal a small call's (fused) bit for bit
+    # q8_K), 640000 (M = 2: quantizer launch + staged) and 960000 (M = 6: the
+    # 8-row staged form); the first SUB / 2 outputs equal a small call's (fused
+    # or plain) bit for bit
     log("gemv silu staged fmt=%d M=%d" % (fmt, M))
     rng = np.random.default_rng(200 + fmt + M)
     wg = synth.make_weights(rng, fmt, N, K)
