@@ -239,12 +239,13 @@ def time_graphs(graphs, steps, warmup):
     return (time.perf_counter() - t0) / steps
 
 
-def fused_launch(M, K):
+def fused_launch(M, K, rows):
     """Whether gemmq_linear_group runs this shape as one fused quantize + GEMV
     launch: the library's rule (gemv.hip: rows of at most 16 blocks, M <= 4,
-    M K/256 <= 32), restated here only to label the timings."""
+    M K/256 <= 32, and rows x M x K/256 below 2^19 -- larger calls quantize in a
+    launch of their own), restated here only to label the timings."""
     nb = K // 256
-    return 1 <= M <= 4 and 1 <= nb <= 16 and M * nb <= 32
+    return 1 <= M <= 4 and 1 <= nb <= 16 and M * nb <= 32 and rows * M * nb < (1 << 19)
 
 
 def launch_weights(layer, ms, copies):
@@ -282,7 +283,7 @@ def kernel_rates(layer, M, steps, copies, stream):
         if key not in layer.rot:
             layer.rot[key] = launch_weights(layer, ms, copies)
         ws = layer.rot[key]
-        fused = layer.fuse and fused_launch(M, ms[0].K)
+        fused = layer.fuse and fused_launch(M, ms[0].K, sum(m.N for m in ms))
         n = len(ms)
         m0 = ms[0]
         ya = (P * n)(*[layer.y[(M, m.name)].data_ptr() for m in ms])

@@ -39,10 +39,16 @@
 //    (the same q8k_block routine as the quantizer kernel) into LDS while the
 //    weights are in flight, and computes from LDS after one barrier.  That
 //    saves the quantizer launch; every workgroup repeats the quantization, so
-//    it is only used for rows of at most 16 blocks and M <= 4.
+//    it is only used for rows of at most 16 blocks and M <= 4, on launches
+//    small enough that a quantizer launch of its own would cost more.
+//  * The staged form (FUSED and STAGE) runs the same workgroups on q8_K blocks
+//    already in memory, each wave copying its share into LDS (three loads a
+//    block) instead of quantizing it: taken by large launches (rows x M x
+//    K/256 from 2^18), where the plain form's per-lane activation reads from L2
+//    and the fused form's repeated quantizing cost more, up to M = 8.
 //
 // Every output's arithmetic (per-lane block order, the xor tree and the wave
-// order) depends only on K, never on M or N, and is the same in both forms, so
+// order) depends only on K, never on M or N, and is the same in all forms, so
 // row m of an M-row call equals a one-row call on that row bit for bit.
 #include "device.h"
 #include "launch.h"

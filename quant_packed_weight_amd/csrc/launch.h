@@ -93,6 +93,8 @@ int launch_skinny_q6k(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t
 int launch_skinny_q6k_silu(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K,
                            hipStream_t st);
 
+// The GEMV on q8_K blocks at Xq: the plain form, or the staged one on large
+// launches (see gemv.hip).
 int launch_gemv(int fmt, const Group& g, const uint8_t* Xq, int M, int64_t K, hipStream_t st);
 
 int launch_gemm(int fmt, const Group& g, const uint8_t* Xq, int64_t M, int64_t K, hipStream_t st);
