@@ -103,12 +103,13 @@ def test_layer_split_quantizer(dev, gq, orc, fmt, M, K, N):
 
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
-@pytest.mark.parametrize("M,K,N", [(1, 4096, 10000), (2, 4096, 10000), (6, 2048, 10000)])
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 10000), (2, 4096, 10000), (2, 4096, 9999),
+                                   (6, 2048, 10000)])
 def test_silu_staged(dev, gq, fmt, M, K, N):
     # gate/up pairs: 2N x M x K/256 = 320000 (M = 1: fused from f32, staged from
     # q8_K), 640000 (M = 2: quantizer launch + staged) and 960000 (M = 6: the
-    # 8-row staged form); the first SUB / 2 outputs equal a small call's (fused
-    # or plain) bit for bit
+    # 8-row staged form; 9999 pairs leave a ragged last tile); the first SUB / 2
+    # outputs equal a small call's (fused or plain) bit for bit
     log("gemv silu staged fmt=%d M=%d" % (fmt, M))
     rng = np.random.default_rng(200 + fmt + M)
     wg = synth.make_weights(rng, fmt, N, K)
