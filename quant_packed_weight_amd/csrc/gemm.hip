@@ -558,9 +558,9 @@ __global__ __launch_bounds__(256, 2) void gemm_plane_kernel(const GroupTiles gt,
   }
   const int64_t NB = (SILU ? N >> 1 : N) * nb;
   // D register sets of loads in flight: super-block b + D is loaded while b is
-  // computed.  The 64-row form (small grids, one workgroup per CU or less)
-  // waits on memory latency at depth 1, and has the registers for a second
-  // set.
+  // computed.  The 64-row form (small grids: at most two workgroups per CU,
+  // often one) waits on memory latency at depth 1, and has the registers for a
+  // second set.
   constexpr int D = MT == 1 ? 2 : 1;
   XRegs<MIN> xr[D];
   WRegs<FMT> wr[D];
