@@ -242,10 +242,17 @@ def time_graphs(graphs, steps, warmup):
 def fused_launch(M, K, rows):
     """Whether gemmq_linear_group runs this shape as one fused quantize + GEMV
     launch: the library's rule (gemv.hip: rows of at most 16 blocks, M <= 4,
-    M K/256 <= 32, and rows x M x K/256 below 2^19 -- larger calls quantize in a
-    launch of their own), restated here only to label the timings."""
+    M K/256 <= 32, and rows x M x K/256 below 2^19, or below 2^18 where each
+    wave would quantize four blocks -- larger calls quantize in a launch of their
+    own), restated here only to label the timings."""
     nb = K // 256
-    return 1 <= M <= 4 and 1 <= nb <= 16 and M * nb <= 32 and rows * M * nb < (1 << 19)
+    if not (1 <= M <= 4 and 1 <= nb <= 16 and M * nb <= 32):
+        return False
+    work = rows * M * nb
+    mt = 1 if M <= 1 else 2 if M <= 2 else 4
+    p = {1: 16, 2: 8, 4: 4, 8: 2}.get(nb, 1)
+    qb = min(4, -(-mt * (16 // p if p > 1 else 16) // 8))
+    return work < (1 << 19) and not (qb >= 4 and work >= (1 << 18))
 
 
 def launch_weights(layer, ms, copies):

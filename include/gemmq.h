@@ -211,8 +211,9 @@ int gemmq_gemm_group(int fmt, int count, const void *const *W, float *const *Y, 
  * for every Y[g].  At decode shapes (GEMV path, M <= 4 and M*K/256 small) it is
  * one launch: every workgroup quantizes X into its own LDS while its weight
  * loads are in flight, and workgroup 0 also writes Xq -- unless the call is
- * large (rows x M x K/256 from 2^19), where quantizing once in a launch of its
- * own costs less.  Otherwise it enqueues the two launches.  Quantizing in the consuming launch is how the CPU
+ * large (rows x M x K/256 from 2^19, or from 2^18 where each wave would
+ * quantize four blocks, e.g. M = 3, 4 at K = 2048), where quantizing once in a
+ * launch of its own costs less.  Otherwise it enqueues the two launches.  Quantizing in the consuming launch is how the CPU
  * gemm_quant on the pages treats the int8 activation step, as part of the
  * matmul (molayo article, status row "src/").
  *   X      device, f32 [M, K], 16-byte aligned (as gemmq_quantize_q8K).

@@ -863,7 +863,10 @@ namespace {
 // 43.7 us; q/k/v at M = 1, 98304, 5.11 against 5.37 us stays plain); from f32
 // activations, a quantizer launch of its own and the staged form from 2^19
 // (the head at M = 1 48.7 -> 46.6 us, at M = 2 68.4 -> 51.2 us, 8B gate/up at
-// M = 2 19.8 -> 15.1 us; 8B gate/up at M = 1 stays fused, 12.5 against 13.2).
+// M = 2 19.8 -> 15.1 us; 8B gate/up at M = 1 stays fused, 12.5 against 13.2),
+// and from 2^18 where each fused wave would quantize four blocks (Qwen3-1.7B
+// gate/up at M = 3 / 4, 294912 / 393216: 9.2 / 9.9 -> 7.5 / 8.0 us; launches
+// below 2^18 stay fused, e.g. its q+k at M = 4 5.1 against 6.8 us).
 constexpr int64_t kStageWork = int64_t(1) << 18;
 constexpr int64_t kSplitQuantizerWork = int64_t(1) << 19;
 
@@ -897,7 +900,14 @@ bool gemv_holds_activation(int64_t M, int64_t K, int64_t rows) {
 }
 
 bool gemv_fuse_quantizer(int64_t M, int64_t K, int64_t rows) {
-  return gemv_fusable(M, K) && rows * M * (K / kQK) < kSplitQuantizerWork;
+  if (!gemv_fusable(M, K)) return false;
+  // blocks each wave of the fused launch would quantize (the kernel the
+  // launchers pick: MT rows computed, P rows side by side)
+  const int64_t nb = K / kQK, work = rows * M * nb;
+  const int MT = M <= 1 ? 1 : M <= 2 ? 2 : 4;
+  const int P = nb == 1 ? 16 : nb == 2 ? 8 : nb == 4 ? 4 : nb == 8 ? 2 : 1;
+  const int qb = fused_qb(MT, P, kRG);
+  return work < kSplitQuantizerWork && !(qb >= 4 && work >= kStageWork);
 }
 
 int launch_gemv_fused(int fmt, const Group& g, const float* X, uint8_t* Xq, int M, int64_t K,

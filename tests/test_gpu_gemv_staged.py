@@ -2,9 +2,9 @@
 
 Large decode launches (rows x M x blocks per row from 2^18) stage the q8_K
 blocks in each workgroup's LDS instead of reading activation fragments from L2
-per lane (the plain form); from f32 activations, launches from 2^19 run the
-quantizer on its own and then the staged form instead of quantizing in every
-workgroup (the fused form).  All three forms give every output the same integer
+per lane (the plain form); from f32 activations, launches from 2^19 (from 2^18
+where each wave would quantize four blocks) run the quantizer on its own and
+then the staged form instead of quantizing in every workgroup (the fused form).  All three forms give every output the same integer
 sums and f32 steps in the same order, so they must agree bit for bit: a large
 call's first rows against a call on those rows alone (small: plain or fused),
 the one-call layer against quantize + gemm (the GEMV path forced: from M = 3 the
@@ -83,10 +83,13 @@ def test_staged_equals_plain_and_fused(dev, gq, orc, fmt, M, K, N):
     _check_oracle(orc, fmt, W, xq, M, N, K, staged, "staged")
 
 
-# rows x M x K/256 = 640000: the one-call layer quantizes in a launch of its own
-# and runs the staged form; equal to the fused form on a few of its rows
+# rows x M x K/256 = 640000, and at M = 3, 4 with rows of 8 blocks (four blocks a
+# wave to quantize) 294912 and 262400: the one-call layer quantizes in a launch
+# of its own and runs the staged form; 262080 (M = 4) stays fused.  Equal to the
+# fused form on a few of its rows either way
 @pytest.mark.parametrize("fmt", [Q4, Q6, R + Q6])
-@pytest.mark.parametrize("M,K,N", [(2, 4096, 20000), (1, 2048, 80000)])
+@pytest.mark.parametrize("M,K,N", [(2, 4096, 20000), (1, 2048, 80000), (3, 2048, 12288),
+                                   (4, 2048, 8200), (4, 2048, 8190)])
 def test_layer_split_quantizer(dev, gq, orc, fmt, M, K, N):
     log("gemv layer split fmt=%d M=%d K=%d N=%d" % (fmt, M, K, N))
     rng = np.random.default_rng(100 + fmt + M + K)
@@ -104,12 +107,13 @@ def test_layer_split_quantizer(dev, gq, orc, fmt, M, K, N):
 
 @pytest.mark.parametrize("fmt", [Q4, Q6])
 @pytest.mark.parametrize("M,K,N", [(1, 4096, 10000), (2, 4096, 10000), (2, 4096, 9999),
-                                   (6, 2048, 10000)])
+                                   (6, 2048, 10000), (3, 2048, 6144)])
 def test_silu_staged(dev, gq, fmt, M, K, N):
     # gate/up pairs: 2N x M x K/256 = 320000 (M = 1: fused from f32, staged from
-    # q8_K), 640000 (M = 2: quantizer launch + staged) and 960000 (M = 6: the
-    # 8-row staged form; 9999 pairs leave a ragged last tile); the first SUB / 2
-    # outputs equal a small call's (fused or plain) bit for bit
+    # q8_K), 640000 (M = 2: quantizer launch + staged), 960000 (M = 6: the
+    # 8-row staged form; 9999 pairs leave a ragged last tile) and 294912 (M = 3,
+    # rows of 8 blocks: quantizer launch + staged); the first SUB / 2 outputs
+    # equal a small call's (fused or plain) bit for bit
     log("gemv silu staged fmt=%d M=%d" % (fmt, M))
     rng = np.random.default_rng(200 + fmt + M)
     wg = synth.make_weights(rng, fmt, N, K)
