@@ -21,7 +21,10 @@
 //    quarter q takes the low (q < 2) or high nibbles of ql bytes
 //    64 hh + 32 (q & 1) + 16 jb + 8 h .. +7 and bits 2q, 2q+1 of qh bytes
 //    32 hh + 16 jb + 8 h .. +7 -- each lane reads its own 96 of the block's
-//    192 quant bytes, no byte twice in the wave;
+//    192 quant bytes, no byte twice in the wave -- straight from memory, or
+//    (plain layout, rows of more than 8 super-blocks) from a copy of the
+//    wave's 32 blocks in LDS made with 16-byte loads, which costs the L1 a
+//    fraction of the tag lookups;
 //  * per sub-block one MFMA gives I_j = sum q x over its 16 weights for 32
 //    rows x 32 columns; the lane's output registers sit in its own column, so
 //    the scale is a per-lane integer: acc += sc_j * I_j (24-bit multiply-add,
@@ -136,6 +139,82 @@ __device__ __forceinline__ void sk6_load_w(Sk6W& r, const uint8_t* mat, int64_t 
   }
 }
 
+// Weight staging (plain layout).  A lane of the MFMA layout wants 8-byte runs
+// of its own column, so loading them straight from memory makes every 16-lane
+// group of every load touch 16 rows' cache lines, one L1 tag lookup each:
+// about 1300 lookups per wave and super-block, and at one lookup per clock that
+// bounds the launch.  Instead each wave first copies its 32 columns' blocks
+// into LDS -- each 16-lane group one column's 208 leading bytes with 16-byte
+// loads, a few lines per group -- and then reads the runs from there.  Column
+// c's slot starts at dword kSlot * c (an odd stride, so the lanes' dword reads
+// fall in different banks); block byte i sits at slot byte s + i, s the
+// block's start mod 4 (0 or 2); dword 52 holds the bytes that carry d.
+constexpr int kSlot = 57;               // dwords per column slot
+constexpr int kWaveStage = 32 * kSlot;  // dwords per wave
+
+// A tile column's row: its matrix and its first block's index.
+struct Sk6Src {
+  const uint8_t* mat;
+  int64_t blk;
+};
+
+// `blk(c)`: the first byte of tile column c's current block.
+template <typename Blk>
+__device__ __forceinline__ void sk6_stage(uint32_t* sw, const Blk& blk, int lane) {
+  const int k = lane & 15;  // 16-byte piece k of the slot (k < 13)
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+    const int c = 4 * r + (lane >> 4);
+    if (k < 13) {
+      // from the block's start rounded down to a dword: 208 bytes, all inside
+      // this block or the one before it (s = 2 only past a matrix's first block)
+      const uint8_t* wb = blk(c);
+      const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(wb) & 3u);
+      const u32x4 v = ld16(wb - sh + 16 * k);
+      uint32_t* d = sw + kSlot * c + 4 * k;
+      d[0] = v.x;
+      d[1] = v.y;
+      d[2] = v.z;
+      d[3] = v.w;
+    }
+  }
+}
+
+// The bytes that hold d of the block at wb, into column c's slot: s = 2, the
+// dword ending at block byte 209; s = 0, bytes 208 and 209 alone (the dword
+// from 208 would pass the block's end).
+__device__ __forceinline__ void sk6_stage_d(uint32_t* sw, const uint8_t* wb, int c) {
+  const uint32_t sh = (uint32_t)(reinterpret_cast<uintptr_t>(wb) & 3u);
+  sw[kSlot * c + 52] = sh ? ld4(wb - sh + 208) : (uint32_t)ld2(wb + 208);
+}
+
+// The lane's runs from its column's slot sl (block start shift s, 0 or 2): the
+// same values sk6_load_w reads from memory.
+__device__ __forceinline__ void sk6_read_w(Sk6W& r, const uint32_t* sl, uint32_t s, int h) {
+  auto run = [&](int o) -> uint2 {  // block bytes o .. o + 7, o a multiple of 8
+    const uint32_t* p = sl + (o >> 2);
+    const uint32_t r0 = p[0], r1 = p[1], r2 = p[2];
+    return make_uint2(__builtin_amdgcn_alignbyte(r1, r0, s), __builtin_amdgcn_alignbyte(r2, r1, s));
+  };
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int q1 = 0; q1 < 2; ++q1)
+#pragma unroll
+      for (int jb = 0; jb < 2; ++jb) r.ql[hh][q1][jb] = run(64 * hh + 32 * q1 + 16 * jb + 8 * h);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) r.qh[hh][jb] = run(128 + 32 * hh + 16 * jb + 8 * h);
+  // scales: block bytes 192..207; d: 208, 209
+  uint32_t w[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) w[i] = sl[48 + i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r.sc[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], s);
+  r.d = s ? w[4] >> 16 : w[4] & 0xffffu;
+}
+
 __device__ __forceinline__ void sk6_load_x(Sk6X& r, const uint8_t* xb, bool ok, int h) {
   if (ok) {
 #pragma unroll
@@ -229,52 +308,81 @@ __device__ __forceinline__ float silu_mul_f32(float g, float u) {
 // gate/up pair as one virtual matrix of 2N rows (row 2p gate row p of gt.W[0],
 // row 2p+1 up row p of gt.W[1]); lanes n and n ^ 1 hold one output column's
 // gate and up.
-template <int FMT, bool SILU, int RL>
-__global__ __launch_bounds__(64 * kMaxKS) void skinny_q6k_kernel(const GroupTiles gt,
-                                                                  const uint8_t* __restrict__ Xq,
-                                                                  int M, int nb, int bpw) {
+// STG: the staged weight loads (plain layout), the M <= 8 form held to four
+// waves per SIMD (two workgroups per CU) as the direct form has.
+template <int FMT, bool SILU, int RL, bool STG>
+__global__ __launch_bounds__(64 * kMaxKS, STG ? (RL == 4 ? 4 : 2) : 1) void skinny_q6k_kernel(
+    const GroupTiles gt, const uint8_t* __restrict__ Xq, int M, int nb, int bpw) {
   constexpr bool RP = FMT > 255;
-  __shared__ float red[kMaxKS][RL][64];
+  // per wave: (STG) its staged blocks, and after its last super-block its
+  // partial sums for the reduction
+  constexpr int kStride = STG ? kWaveStage : RL * 64;
+  __shared__ uint32_t stage[kMaxKS * kStride];
+  static_assert(RL * 64 <= kStride, "partial sums fit a wave's area");
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int ks = (int)(blockDim.x >> 6);
   const int lane = lane_id(), n = lane & 31, h = lane >> 5;
   const TileMatrix tm = tile_matrix(gt, blockIdx.x);
   const int64_t N = tm.N;  // SILU: 2 x the output columns
   const int64_t col = (int64_t)tm.local * 32 + n;
-  const int64_t colc = col < N ? col : N - 1;
-  const uint8_t* mat;
-  int64_t blk0;
-  if constexpr (SILU) {
-    mat = (colc & 1) ? gt.W[1] : tm.W;
-    blk0 = (colc >> 1) * nb;
-  } else {
-    mat = tm.W;
-    blk0 = colc * nb;
-  }
   const int64_t NB = (SILU ? N >> 1 : N) * nb;  // repacked: blocks in the matrix
+  // the matrix and first block of tile column c (past N: the last column)
+  auto column = [&](int c) -> Sk6Src {
+    const int64_t cl = (int64_t)tm.local * 32 + c;
+    const int64_t cc = cl < N ? cl : N - 1;
+    if constexpr (SILU) return Sk6Src{(cc & 1) ? gt.W[1] : tm.W, (cc >> 1) * nb};
+    else return Sk6Src{tm.W, cc * nb};
+  };
+  const Sk6Src own = column(n);
   const bool xok = n < M;
   const uint8_t* xrow = Xq + (int64_t)(xok ? n : M - 1) * nb * kQ8KBytes;
   const int b0 = wave * bpw, b1 = b0 + bpw < nb ? b0 + bpw : nb;
+  uint32_t* sw = stage + wave * kStride;
 
   float y[RL];
 #pragma unroll
   for (int i = 0; i < RL; ++i) y[i] = 0.f;
   for (int b = b0; b < b1; ++b) {
-    Sk6W w;
-    Sk6X x;
-    sk6_load_w<RP>(w, mat, blk0 + b, NB, h);
-    sk6_load_x(x, xrow + (int64_t)b * kQ8KBytes, xok, h);
-    sk6_compute<RL>(w, x, h, y);
+    if constexpr (STG) {
+      static_assert(!RP, "the staged loads read the plain block layout");
+      // the first byte of tile column c's block b
+      auto blk = [&](int c) -> const uint8_t* {
+        const Sk6Src t = column(c);
+        return t.mat + (t.blk + b) * kQ6KBytes;
+      };
+      sk6_stage(sw, blk, lane);
+      const uint8_t* mine = own.mat + (own.blk + b) * kQ6KBytes;
+      if (h == 0) sk6_stage_d(sw, mine, n);
+      Sk6X x;
+      sk6_load_x(x, xrow + (int64_t)b * kQ8KBytes, xok, h);
+      // the copies are read by other lanes of this wave only
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      Sk6W w;
+      const uint32_t s = (uint32_t)(reinterpret_cast<uintptr_t>(mine) & 3u);
+      sk6_read_w(w, sw + kSlot * n, s, h);
+      sk6_compute<RL>(w, x, h, y);
+      // every lane's reads of this block precede the next block's copies
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      Sk6W w;
+      Sk6X x;
+      sk6_load_w<RP>(w, own.mat, own.blk + b, NB, h);
+      sk6_load_x(x, xrow + (int64_t)b * kQ8KBytes, xok, h);
+      sk6_compute<RL>(w, x, h, y);
+    }
   }
   if (ks > 1) {
+    float* red = reinterpret_cast<float*>(sw);
 #pragma unroll
-    for (int i = 0; i < RL; ++i) red[wave][i][lane] = y[i];
+    for (int i = 0; i < RL; ++i) red[64 * i + lane] = y[i];
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int i = 0; i < RL; ++i) {
-      float v = red[0][i][lane];
-      for (int k = 1; k < ks; ++k) v += red[k][i][lane];
+      float v = red[64 * i + lane];
+      for (int k = 1; k < ks; ++k) v += reinterpret_cast<const float*>(stage + k * kStride)[64 * i + lane];
       y[i] = v;
     }
   }
@@ -295,10 +403,22 @@ template <int FMT, bool SILU>
 void launch_rl(const GroupTiles& gt, const uint8_t* Xq, int M, int nb, int ks, int bpw,
                hipStream_t st) {
   const dim3 grid(gt.start[kMaxGroup]), block(64 * ks);
+  // staged weight loads for the plain layout on rows of more than 8
+  // super-blocks (several per wave); elsewhere the direct loads measured faster
+  // (the same bits either way)
+  if constexpr (FMT == 14) {
+    if (nb > 8) {
+      if (M <= 8)
+        hipLaunchKernelGGL((skinny_q6k_kernel<FMT, SILU, 4, true>), grid, block, 0, st, gt, Xq, M, nb, bpw);
+      else
+        hipLaunchKernelGGL((skinny_q6k_kernel<FMT, SILU, 8, true>), grid, block, 0, st, gt, Xq, M, nb, bpw);
+      return;
+    }
+  }
   if (M <= 8)
-    hipLaunchKernelGGL((skinny_q6k_kernel<FMT, SILU, 4>), grid, block, 0, st, gt, Xq, M, nb, bpw);
+    hipLaunchKernelGGL((skinny_q6k_kernel<FMT, SILU, 4, false>), grid, block, 0, st, gt, Xq, M, nb, bpw);
   else
-    hipLaunchKernelGGL((skinny_q6k_kernel<FMT, SILU, 8>), grid, block, 0, st, gt, Xq, M, nb, bpw);
+    hipLaunchKernelGGL((skinny_q6k_kernel<FMT, SILU, 8, false>), grid, block, 0, st, gt, Xq, M, nb, bpw);
 }
 
 }  // namespace

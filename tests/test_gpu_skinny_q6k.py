@@ -82,12 +82,14 @@ def test_skinny_q6k_rows_independent_of_call(dev, gq, orc, K):
 
 @pytest.mark.parametrize("fmt", [Q6, Q6R])
 @pytest.mark.parametrize("M", [8, 16])
-def test_skinny_q6k_extreme_blocks(dev, gq, orc, fmt, M):
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_skinny_q6k_extreme_blocks(dev, gq, orc, fmt, M, K):
     # scales at -128 and 127, quants at 0 and 63, f16 d at large, tiny,
-    # subnormal and negative values, activations at +-amax
-    log("skinny q6_K extreme blocks fmt=%d M=%d" % (fmt, M))
+    # subnormal and negative values, activations at +-amax; K = 4096 takes the
+    # plain layout's staged loads (blocks at both 4-byte phases)
+    log("skinny q6_K extreme blocks fmt=%d M=%d K=%d" % (fmt, M, K))
     rng = np.random.default_rng(77)
-    N, K = 48, 2048
+    N = 48
     nb = K // 256
     W = synth.make_weights(rng, Q6, N, K).reshape(N * nb, 210).copy()
     d = np.array([65504.0, 6.0e-8, -3.5, 1.0, 2.0 ** -20], dtype=np.float16)
