@@ -374,15 +374,15 @@ __global__ __launch_bounds__(64 * kMaxKS, STG ? (RL == 4 ? 4 : 2) : 1) void skin
     }
   }
   if (ks > 1) {
-    float* red = reinterpret_cast<float*>(sw);
+    // the partial sums' bits in the wave's own area, added in wave order
 #pragma unroll
-    for (int i = 0; i < RL; ++i) red[64 * i + lane] = y[i];
+    for (int i = 0; i < RL; ++i) sw[64 * i + lane] = __builtin_bit_cast(uint32_t, y[i]);
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int i = 0; i < RL; ++i) {
-      float v = red[64 * i + lane];
-      for (int k = 1; k < ks; ++k) v += reinterpret_cast<const float*>(stage + k * kStride)[64 * i + lane];
+      float v = __builtin_bit_cast(float, stage[64 * i + lane]);
+      for (int k = 1; k < ks; ++k) v += __builtin_bit_cast(float, stage[k * kStride + 64 * i + lane]);
       y[i] = v;
     }
   }
