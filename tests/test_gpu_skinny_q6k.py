@@ -108,12 +108,13 @@ def test_skinny_q6k_extreme_blocks(dev, gq, orc, fmt, M, K):
 
 
 @pytest.mark.parametrize("M", [3, 8, 11, 16])
-def test_skinny_q6k_group_and_linear(dev, gq, orc, M):
+@pytest.mark.parametrize("K", [2048, 4096])
+def test_skinny_q6k_group_and_linear(dev, gq, orc, M, K):
     # a group launch equals single calls; gemmq_linear_group on this path
     # gives the same bits (and so does its automatic choice at M > 8, and at
     # 5 <= M <= 8 past 16384 columns -- checked in the dispatch tests)
-    log("skinny q6_K group M=%d" % M)
-    K = 2048
+    # (K = 4096: the plain layout's staged loads)
+    log("skinny q6_K group M=%d K=%d" % (M, K))
     Ns = [300, 64, 65]
     rng = np.random.default_rng(80 + M)
     Ws = [synth.make_weights(rng, Q6, N, K) for N in Ns]
