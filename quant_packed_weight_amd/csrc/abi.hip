@@ -42,8 +42,15 @@ constexpr int64_t kSkinnyColTiles = 20480;
 // its 32-column workgroups are too few to fill the chip and the GEMV is faster:
 // measured on the Qwen3-1.7B shapes, v 1024 and down 2048 columns against the
 // 151936-column head) -- except at M <= 4 where the GEMV holds the activation in
-// LDS (M K/256 <= 32; the head at M = 3 / 4: 58.3 / 59.2 us against 85.9 / 86.0)
+// LDS (M K/256 <= 32; the head at M = 3 / 4: 58.3 / 59.2 us against 85.9 / 86.0).
+// Plain q6_K on rows of more than 8 super-blocks, where the kernel stages its
+// weight blocks in LDS, also from columns x super-blocks = kSkinnyQ6Work at
+// M = 5..8 (where the GEMV runs its 8-row form): at M = 8 4096 x 4096 12.4
+// against 14.8 us, Qwen3-8B down 4096 x 12288 27.7 against 34.3, 8192 x 4096
+// 14.7 against 27.2; below it the GEMV stays ahead (1024 x 4096 10.4 against
+// 10.8, 2048 x 6144 13.7 against 15.7).
 constexpr int64_t kSkinnyQ6Cols = 16384;
+constexpr int64_t kSkinnyQ6Work = int64_t(1) << 16;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 // the largest M the small-M kernel takes in this format (0: not available)
@@ -220,7 +227,8 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
 // against 21.8; down, 48 blocks a row, stays: 18.5 against 13.5).  q6_K (either
 // layout) takes its small-M kernel at 9 <= M <= 16,
 // and at 3 <= M <= 8 once the launch has kSkinnyQ6Cols columns, unless the GEMV
-// can hold the activation in LDS (gemv_fusable).
+// can hold the activation in LDS (gemv_fusable); plain q6_K at 5 <= M <= 8 on
+// rows of more than 8 super-blocks also from kSkinnyQ6Work columns x blocks.
 int pick_path(int fmt, int path, int64_t M, int64_t K, int64_t cols) {
   if (path != GEMMQ_PATH_AUTO) return path;
   if (fmt == GEMMQ_Q4_K && M <= 4 && gemmq::gemv_holds_activation(M, K, cols))
@@ -231,6 +239,9 @@ int pick_path(int fmt, int path, int64_t M, int64_t K, int64_t cols) {
   }
   if ((fmt == GEMMQ_Q6_K || fmt == GEMMQ_Q6_K_R) && M >= kSkinnyMinM && M <= kSkinnyQ6MaxM &&
       (M > 8 || (cols >= kSkinnyQ6Cols && !gemmq::gemv_fusable(M, K))))
+    return GEMMQ_PATH_SKINNY;
+  const int64_t nb = K / 256;
+  if (fmt == GEMMQ_Q6_K && M >= 5 && M <= 8 && nb > 8 && cols * nb >= kSkinnyQ6Work)
     return GEMMQ_PATH_SKINNY;
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }
