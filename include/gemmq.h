@@ -155,7 +155,8 @@ int gemmq_quantize_q8K(const float *X, void *Xq, int64_t M, int64_t K, void *str
  * when the launch has at least 16384 output columns (at M <= 4 only where
  * M*K/256 > 32: below that the GEMV holds the activation in LDS and is faster),
  * and for plain q6_K at 5 <= M <= 8 on rows of more than 8 super-blocks also
- * when output columns x K/256 >= 2^16, the MFMA GEMM otherwise; the choice is made once per launch, from M, K and
+ * when output columns x K/256 >= 2^16, at M = 3, 4 on rows of more than 64
+ * when it is >= 2^18, the MFMA GEMM otherwise; the choice is made once per launch, from M, K and
  * the sum of the N of the matrices it serves).
  *   fmt  GEMMQ_Q2_K, GEMMQ_Q3_K, GEMMQ_Q4_K, GEMMQ_Q5_K, GEMMQ_Q6_K, or a
  *        repacked GEMMQ_Q3_K_R / GEMMQ_Q6_K_R (weights from gemmq_repack).

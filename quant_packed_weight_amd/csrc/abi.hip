@@ -48,9 +48,13 @@ constexpr int64_t kSkinnyColTiles = 20480;
 // M = 5..8 (where the GEMV runs its 8-row form): at M = 8 4096 x 4096 12.4
 // against 14.8 us, Qwen3-8B down 4096 x 12288 27.7 against 34.3, 8192 x 4096
 // 14.7 against 27.2; below it the GEMV stays ahead (1024 x 4096 10.4 against
-// 10.8, 2048 x 6144 13.7 against 15.7).
+// 10.8, 2048 x 6144 13.7 against 15.7).  At M = 3, 4 the same holds only on rows
+// of more than 64 super-blocks (the GEMV's two-round form) from kSkinnyQ6LongWork:
+// 5120 x 17408 37.4 against 60.7 us, 4096 x 20480 40.7 against 49.5, while
+// 2048 x 17408 (139264) stays on the GEMV, 25.7 against 34.8.
 constexpr int64_t kSkinnyQ6Cols = 16384;
 constexpr int64_t kSkinnyQ6Work = int64_t(1) << 16;
+constexpr int64_t kSkinnyQ6LongWork = int64_t(1) << 18;
 std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 
 // the largest M the small-M kernel takes in this format (0: not available)
@@ -228,7 +232,8 @@ int check_group(int fmt, int count, const void* const* W, float* const* Y, const
 // layout) takes its small-M kernel at 9 <= M <= 16,
 // and at 3 <= M <= 8 once the launch has kSkinnyQ6Cols columns, unless the GEMV
 // can hold the activation in LDS (gemv_fusable); plain q6_K at 5 <= M <= 8 on
-// rows of more than 8 super-blocks also from kSkinnyQ6Work columns x blocks.
+// rows of more than 8 super-blocks also from kSkinnyQ6Work columns x blocks, and
+// at M = 3, 4 on rows of more than 64 from kSkinnyQ6LongWork.
 int pick_path(int fmt, int path, int64_t M, int64_t K, int64_t cols) {
   if (path != GEMMQ_PATH_AUTO) return path;
   if (fmt == GEMMQ_Q4_K && M <= 4 && gemmq::gemv_holds_activation(M, K, cols))
@@ -242,6 +247,8 @@ int pick_path(int fmt, int path, int64_t M, int64_t K, int64_t cols) {
     return GEMMQ_PATH_SKINNY;
   const int64_t nb = K / 256;
   if (fmt == GEMMQ_Q6_K && M >= 5 && M <= 8 && nb > 8 && cols * nb >= kSkinnyQ6Work)
+    return GEMMQ_PATH_SKINNY;
+  if (fmt == GEMMQ_Q6_K && M >= 3 && M <= 4 && nb > 64 && cols * nb >= kSkinnyQ6LongWork)
     return GEMMQ_PATH_SKINNY;
   return M <= 8 ? GEMMQ_PATH_GEMV : GEMMQ_PATH_GEMM;
 }

@@ -207,8 +207,8 @@ def _expected_path(gq, fmt, M, cols, K):
     # the GEMV holds the activation in LDS (M <= 4, M K/256 <= 32); q4_K at
     # M = 3, 4 also stays on the GEMV where it stages the activation (rows of
     # <= 16 blocks, M K/256 <= 64, cols x M x K/256 >= 2^18); plain q6_K at
-    # 5 <= M <= 8 on rows of more than 8 blocks also from cols x K/256 = 2^16;
-    # the GEMM otherwise
+    # 5 <= M <= 8 on rows of more than 8 blocks also from cols x K/256 = 2^16,
+    # and at M = 3, 4 on rows of more than 64 blocks from 2^18; the GEMM otherwise
     t = (M + 15) // 16
     nb = K // 256
     if fmt == Q4 and M <= 4 and nb <= 16 and M * nb <= 64 and cols * M * nb >= 1 << 18:
@@ -219,6 +219,8 @@ def _expected_path(gq, fmt, M, cols, K):
     if fmt == Q6 and 3 <= M <= 16 and (M > 8 or (cols >= 16384 and not staged)):
         return gq.PATH_SKINNY
     if fmt == Q6 and 5 <= M <= 8 and nb > 8 and cols * nb >= 1 << 16:
+        return gq.PATH_SKINNY
+    if fmt == Q6 and 3 <= M <= 4 and nb > 64 and cols * nb >= 1 << 18:
         return gq.PATH_SKINNY
     return gq.PATH_GEMV if M <= 8 else gq.PATH_GEMM
 
@@ -243,18 +245,22 @@ def test_auto_dispatch_and_linear(dev, gq, orc, fmt, N):
 
 @pytest.mark.parametrize("M,K,N", [(5, 4096, 4096), (8, 4096, 4095), (6, 2304, 7282),
                                    (8, 2304, 7281), (8, 2048, 8192), (3, 4096, 8192),
-                                   (8, 12288, 1366)])
+                                   (8, 12288, 1366), (3, 16640, 4034), (4, 16640, 4032),
+                                   (4, 16384, 8192)])
 def test_auto_dispatch_q6K_long_rows(dev, gq, orc, M, K, N):
     # plain q6_K at M = 5..8 on rows of more than 8 blocks takes the small-M
-    # kernel from output columns x K/256 = 2^16 (each pair of cases straddles
-    # it); rows of 8 blocks and M = 3, 4 keep the GEMV.  The automatic path
+    # kernel from output columns x K/256 = 2^16, at M = 3, 4 on rows of more
+    # than 64 blocks from 2^18 (each pair of cases straddles a bound); rows of
+    # 8 blocks, and of 64 at M = 3, 4, keep the GEMV.  The automatic path
     # equals the expected path forced, and sampled outputs the oracle.
     log("dispatch q6_K long rows M=%d K=%d N=%d" % (M, K, N))
     W, x, xq = _case(orc, Q6, M, N, K, seed=M + K + N)
     auto = to_host(gq.gemm(Q6, to_dev(W), to_dev(xq), M, N, K))
     path = _expected_path(gq, Q6, M, N, K)
     nb = K // 256
-    assert (path == gq.PATH_SKINNY) == (5 <= M <= 8 and nb > 8 and N * nb >= 1 << 16)
+    want = (5 <= M <= 8 and nb > 8 and N * nb >= 1 << 16) or (
+        3 <= M <= 4 and nb > 64 and N * nb >= 1 << 18)
+    assert (path == gq.PATH_SKINNY) == want
     forced = _run(gq, Q6, W, xq, M, N, K, path)
     assert np.array_equal(auto.view(np.uint32), forced.view(np.uint32))
     cols = np.array([0, N // 3, N // 2, N - 1])
